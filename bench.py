@@ -1,0 +1,176 @@
+"""Throughput of one draft-tree step (build + tree attention + verify + compact) on one GPU.
+
+Default workload: the TALON tree on the Llama-3-8B attention-layer shape (1 sequence,
+32 query / 8 KV heads, head dim 128, bf16, KV prefix 2048, budget B = 60, root Top-K 10,
+gate alpha 0.1, vocab 128256, greedy verification). Inputs are seeded synthetic arrays
+resident in HBM before timing starts. Prints one JSON line.
+
+The ``cpu_baseline`` leg times the float64 CPU oracle on the same workload (a bounded
+number of steps) and is the only part of this file that touches the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
+METRIC = "draft-tree verify steps/sec + tree tokens/sec, % roofline, Llama-3-8B shape"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2_talon_llama3_8b")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps for cpu_baseline (0: skip)")
+    return ap.parse_args()
+
+
+def algorithmic_work(step, wl):
+    """Bytes (and flops) each stage must move/compute for this step, from the built tree."""
+    import numpy as np
+    cfg = wl.cfg
+    esz = 2 if cfg.dtype == "bf16" else 4
+    n_nodes = step.tree.n_nodes.cpu().numpy()
+    depth = step.tree.depth.cpu().numpy()
+    layers = step.tree.layers.cpu().numpy()
+    anc = step.tree.anc.cpu().numpy().view(np.uint64)
+    plen = step.verify_out[1].cpu().numpy()
+    out = {"build": {"bytes": 0.0}, "attention": {"bytes": 0.0, "flops": 0.0},
+           "verify": {"bytes": 0.0}, "compact": {"bytes": 0.0}}
+    for s in range(cfg.S):
+        N = int(n_nodes[s])
+        P = int(wl.P[s])
+        if cfg.build == "talon":
+            rows = int(np.sum(depth[s, :N] < int(layers[s])))  # nodes whose rows were expanded
+            out["build"]["bytes"] += rows * cfg.V * esz
+        vis = sum(bin(int(w)).count("1") for w in anc[s, :N].ravel())
+        out["attention"]["bytes"] += (2 * P * cfg.Hkv * cfg.D + 2 * N * cfg.Hkv * cfg.D
+                                      + 2 * N * cfg.Hq * cfg.D) * esz
+        out["attention"]["flops"] += 4.0 * cfg.Hq * cfg.D * (N * P + vis)
+        out["verify"]["bytes"] += N * cfg.V * esz
+        out["compact"]["bytes"] += 4 * int(plen[s]) * cfg.Hkv * cfg.D * esz
+    return out
+
+
+def cpu_baseline(wl, steps: int):
+    from threadpoolctl import threadpool_limits
+    from oracle import step as ostep
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ostep.run_step(wl)
+        dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole oracle steps (build, attention, verify, compact) of the same "
+                      f"workload, float64 numpy, one thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path in this build)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    from draft_tree_verification_build_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from draft_tree_verification_build_amd import build_lib
+        build_lib.build()
+    from draft_tree_verification_build_amd.step import DraftTreeStep
+    from workloads import make_workload
+    from workloads.configs import CONFIG_ORDER
+
+    seed = args.seed if args.seed is not None else CONFIG_ORDER.index(args.config) + 1
+    wl = make_workload(args.config, seed)
+    cfg = wl.cfg
+    step = DraftTreeStep(wl, "cuda")
+    stream = torch.cuda.current_stream()
+    stages = ["build", "attention", "verify", "compact"]
+    fns = [step.build, step.attention, step.verify, step.compact]
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    st = step.ws_status()
+    if any(v != 0 for v in st.values()):
+        print(f"device status after warmup: {st}", file=sys.stderr)
+        return 1
+
+    # whole-step timing
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-stage timing with events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for j, fn in enumerate(fns):
+            fn()
+            ev[k][j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(args.steps)]))
+                for j, name in enumerate(stages)}
+
+    work = algorithmic_work(step, wl)
+    ms = wall * 1e3 / args.steps
+    steps_s = args.steps / wall
+    tree_tokens = float(step.tree.n_nodes.sum().item() - cfg.S)  # draft nodes, root excluded
+    stage_report = {}
+    for name in stages:
+        t = stage_ms[name] * 1e-3
+        w = work[name]
+        gbs = w["bytes"] / t / 1e9 if t > 0 else 0.0
+        rep = {"ms": stage_ms[name], "bytes": w["bytes"], "GB/s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        if "flops" in w:
+            tf = w["flops"] / t / 1e12 if t > 0 else 0.0
+            peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+            rep.update({"flops": w["flops"], "TFLOP/s": tf, "mfma_frac": tf / peak})
+        stage_report[name] = rep
+    dom = max(stages, key=lambda n: stage_ms[n])
+    d = stage_report[dom]
+    if dom == "attention" and d["flops"] / max(d["bytes"], 1) > (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": d["TFLOP/s"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": d["mfma_frac"], "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["hbm_frac"], "traffic": None}
+    roof["kernel"] = dom
+
+    out = {
+        "metric": METRIC, "value": steps_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "seed": seed, "S": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "D": cfg.D, "P": cfg.P, "V": cfg.V, "N": cfg.N, "build": cfg.build,
+                   "verify": cfg.verify},
+        "tree_tokens_per_s": tree_tokens * steps_s,
+        "roofline": roof,
+        "stages": stage_report,
+    }
+    if args.cpu_steps > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

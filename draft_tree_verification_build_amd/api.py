@@ -1,0 +1,199 @@
+"""Python binding of libdtv: argument marshalling only.
+
+Every function takes device tensors (torch is used for device memory and streams) and
+forwards raw pointers and sizes to the C entry point of the same name; all computation
+happens in the HIP kernels. Errors raise DtvError with the library's message. There is
+no CPU fallback: without libdtv.so the first call raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import DtvTree
+
+F32, BF16 = 0, 1
+
+
+class DtvError(RuntimeError):
+    def __init__(self, name: str, code: int):
+        lib = _lib.load()
+        msg = lib.dtv_last_error().decode() or lib.dtv_status_str(code).decode()
+        super().__init__(f"{name} failed ({code}: {lib.dtv_status_str(code).decode()}): {msg}")
+        self.code = code
+
+
+def _call(name: str, *args) -> None:
+    lib = _lib.load()
+    rc = getattr(lib, name)(*args)
+    if rc != 0:
+        raise DtvError(name, rc)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdtv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Workspace:
+    """Zero-filled device scratch buffers, one per (purpose, size), kept for reuse."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self._bufs: dict = {}
+
+    def get(self, key, nbytes: int) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self._bufs[key] = buf
+        return buf
+
+    def status(self, key, stream=None) -> int:
+        """Synchronise and return (and clear) the device status of one workspace."""
+        buf = self._bufs[key]
+        return _lib.load().dtv_ws_status(buf.data_ptr(), _stream(stream))
+
+
+class Tree:
+    """Device arrays of S draft trees with n_cap slots each (slot 0 = root)."""
+
+    def __init__(self, S: int, n_cap: int, device, parent: torch.Tensor | None = None,
+                 token: torch.Tensor | None = None):
+        """``parent``/``token`` ([S][n_cap] int32, device) may be given for trees drafted elsewhere."""
+        self.S, self.n_cap = int(S), int(n_cap)
+        self.words = (self.n_cap + 63) // 64
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.n_nodes = torch.zeros(S, **i32)
+        self.parent = parent if parent is not None else torch.full((S, n_cap), -1, **i32)
+        self.token = token if token is not None else torch.full((S, n_cap), -1, **i32)
+        for t in (self.parent, self.token):
+            if t.shape != (S, n_cap) or t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("parent/token must be contiguous int32 [S][n_cap]")
+        self.depth = torch.zeros((S, n_cap), **i32)
+        self.row = torch.zeros((S, n_cap), **i32)
+        self.score = torch.zeros((S, n_cap), dtype=torch.float64, device=dev)
+        self.anc = torch.zeros((S, n_cap, self.words), dtype=torch.int64, device=dev)
+        self.layers = torch.zeros(S, **i32)
+        self._c = DtvTree(self.n_cap, self.words, self.n_nodes.data_ptr(), self.parent.data_ptr(),
+                          self.token.data_ptr(), self.depth.data_ptr(), self.row.data_ptr(),
+                          self.score.data_ptr(), self.anc.data_ptr(), self.layers.data_ptr())
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+# ----------------------------------------------------------------------------- calls
+
+def row_stats(table: torch.Tensor, K: int, ws: Workspace, row_idx: torch.Tensor | None = None,
+              stream=None):
+    """Per row of a [R][V] table: (max, argmax, lse, topk[R][K])."""
+    V = table.shape[-1]
+    R = table.numel() // V if row_idx is None else row_idx.numel()
+    dt = _dtype_code(table)
+    dev = table.device
+    maxv = torch.empty(R, dtype=torch.float32, device=dev)
+    amax = torch.empty(R, dtype=torch.int32, device=dev)
+    lse = torch.empty(R, dtype=torch.float64, device=dev)
+    topk = torch.empty((R, max(K, 1)), dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    nb = lib.dtv_row_stats_ws_bytes(R, V, K, dt)
+    buf = ws.get("row_stats", nb)
+    _call("dtv_row_stats", _ptr(table), dt, R, V, _ptr(row_idx), K, _ptr(maxv), _ptr(amax), _ptr(lse),
+          _ptr(topk) if K > 0 else None, buf.data_ptr(), buf.numel(), _stream(stream))
+    return maxv, amax, lse, topk[:, :K]
+
+
+def tree_build_given(tree: Tree, ws: Workspace, stream=None) -> None:
+    lib = _lib.load()
+    buf = ws.get("given", lib.dtv_tree_build_given_ws_bytes(tree.S))
+    _call("dtv_tree_build_given", tree.c, tree.S, buf.data_ptr(), buf.numel(), _stream(stream))
+
+
+def tree_build_talon(tree: Tree, draft: torch.Tensor, B: int, K: int, alpha: float, ws: Workspace,
+                     stream=None) -> None:
+    """draft: [S][R][V] rows keyed by slot."""
+    S, R, V = draft.shape
+    dt = _dtype_code(draft)
+    lib = _lib.load()
+    buf = ws.get("talon", lib.dtv_tree_build_talon_ws_bytes(S, B, K, V, dt))
+    _call("dtv_tree_build_talon", tree.c, S, _ptr(draft), dt, R, V, B, K, float(alpha),
+          buf.data_ptr(), buf.numel(), _stream(stream))
+
+
+def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, P_max: int,
+              tree: Tree, ws: Workspace, scale: float | None = None, o: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """q [S][n_cap][Hq][D]; k, v [S][Hkv][P_cap][D]; P [S] int32 (device)."""
+    S, n_cap, Hq, D = q.shape
+    Hkv, P_cap = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.zeros_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    buf = ws.get("attn", lib.dtv_tree_attn_ws_bytes(S, n_cap, Hq, Hkv, D, P_max, dt))
+    _call("dtv_tree_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(P), P_cap, int(P_max), tree.c, S, Hq, Hkv,
+          D, dt, float(scale), _ptr(o), buf.data_ptr(), buf.numel(), _stream(stream))
+    return o
+
+
+def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None, stream=None):
+    """target [S][R][V]. Returns (path [S][n_cap], path_len [S], bonus [S], argmax [S][n_cap])."""
+    S, R, V = target.shape
+    dt = _dtype_code(target)
+    dev = target.device
+    if out is None:
+        out = (torch.full((S, tree.n_cap), -1, dtype=torch.int32, device=dev),
+               torch.zeros(S, dtype=torch.int32, device=dev),
+               torch.zeros(S, dtype=torch.int32, device=dev),
+               torch.zeros((S, tree.n_cap), dtype=torch.int32, device=dev))
+    path, plen, bonus, amax = out
+    lib = _lib.load()
+    buf = ws.get("verify_greedy", lib.dtv_tree_verify_greedy_ws_bytes(S, tree.n_cap, V, dt))
+    _call("dtv_tree_verify_greedy", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
+          _ptr(bonus), _ptr(amax), buf.data_ptr(), buf.numel(), _stream(stream))
+    return out
+
+
+def kv_compact(k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, path: torch.Tensor,
+               path_len: torch.Tensor, P_new: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    S, Hkv, P_cap, D = k.shape
+    dt = _dtype_code(k)
+    if P_new is None:
+        P_new = torch.empty_like(P)
+    _call("dtv_kv_compact", _ptr(k), _ptr(v), _ptr(P), _ptr(P_new), P_cap, _ptr(path), _ptr(path_len),
+          path.shape[1], S, Hkv, D, dt, _stream(stream))
+    return P_new
+
+
+def bookkeeping(accepted, draft_steps: int, gamma: float) -> dict:
+    """Host-side E[A], eta and Speedup from logged counts."""
+    import numpy as np
+    acc = np.ascontiguousarray(np.asarray(accepted, dtype=np.int32))
+    out = np.zeros(4, dtype=np.float64)
+    _call("dtv_bookkeeping", acc.ctypes.data, int(acc.size), int(draft_steps), float(gamma), out.ctypes.data)
+    return {"E_A": out[0], "eta": out[1], "speedup": out[2], "L": out[3]}

@@ -1,0 +1,483 @@
+// C entry points of libdtv: argument checks on the host, workspace carving, launches.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dtv.h"
+#include "dtv_internal.h"
+#include "rowstats.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive 256-byte aligned regions out of a workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += up(count * sizeof(T));
+    return p;
+  }
+};
+
+int esize_of(int dtype) { return dtype == DTV_BF16 ? 2 : 4; }
+bool dtype_ok(int dtype) { return dtype == DTV_F32 || dtype == DTV_BF16; }
+int nch_of(int V, int dtype) { return dtype == DTV_BF16 ? dtv::chunks_of<1>(V) : dtv::chunks_of<0>(V); }
+
+int check_tree(const dtv_tree* t) {
+  REQUIRE(t != nullptr, DTV_EINVAL, "tree is NULL");
+  REQUIRE(t->n_cap >= 1 && t->n_cap <= 1024, DTV_EUNSUPPORTED, "n_cap %d outside 1..1024", t->n_cap);
+  REQUIRE(t->words >= (t->n_cap + 63) / 64 && t->words <= 16, DTV_ECAPACITY,
+          "words %d cannot hold %d slots", t->words, t->n_cap);
+  REQUIRE(t->n_nodes && t->parent && t->token && t->depth && t->row && t->score && t->anc && t->layers,
+          DTV_EINVAL, "a tree array is NULL");
+  return DTV_OK;
+}
+
+dtv::TreeArgs tree_args(const dtv_tree* t) {
+  dtv::TreeArgs a;
+  a.n_cap = t->n_cap;
+  a.words = t->words;
+  a.n_nodes = t->n_nodes;
+  a.parent = t->parent;
+  a.token = t->token;
+  a.depth = t->depth;
+  a.row = t->row;
+  a.score = t->score;
+  a.anc = reinterpret_cast<uint64_t*>(t->anc);
+  a.layers = t->layers;
+  return a;
+}
+
+int launched(int rc) {
+  if (rc != 0) return fail(DTV_EHIP, "kernel launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return DTV_OK;
+}
+
+// ------------------------------------------------------------------ layouts
+
+struct RowStatsLayout {
+  dtv::WsHeader* hdr;
+  dtv::ChunkStat* st;
+  float* cval;
+  int* cidx;
+  unsigned* tickets;
+  float* mval;
+  size_t bytes;
+};
+RowStatsLayout row_stats_layout(void* ws, int R, int V, int K, int dtype) {
+  const int nch = nch_of(V, dtype);
+  const size_t KK = K > 0 ? K : 1;
+  Carver c(ws);
+  RowStatsLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.st = c.take<dtv::ChunkStat>(static_cast<size_t>(R) * nch);
+  L.cval = c.take<float>(static_cast<size_t>(R) * nch * KK);
+  L.cidx = c.take<int>(static_cast<size_t>(R) * nch * KK);
+  L.tickets = c.take<unsigned>(R);
+  L.mval = c.take<float>(static_cast<size_t>(R) * KK);
+  L.bytes = c.off;
+  return L;
+}
+
+struct TalonLayout {
+  dtv::WsHeader* hdr;
+  dtv::ChunkStat* st;
+  float* cval;
+  int* cidx;
+  unsigned* tickets;
+  double* rlse;
+  float* rv;
+  int* ri;
+  int* rcnt;
+  size_t bytes;
+};
+TalonLayout talon_layout(void* ws, int S, int B, int K, int V, int dtype) {
+  const int nch = nch_of(V, dtype);
+  const size_t rows = static_cast<size_t>(S) * B;
+  Carver c(ws);
+  TalonLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.st = c.take<dtv::ChunkStat>(rows * nch);
+  L.cval = c.take<float>(rows * nch * K);
+  L.cidx = c.take<int>(rows * nch * K);
+  L.tickets = c.take<unsigned>(rows);
+  L.rlse = c.take<double>(rows);
+  L.rv = c.take<float>(rows * K);
+  L.ri = c.take<int>(rows * K);
+  L.rcnt = c.take<int>(rows);
+  L.bytes = c.off;
+  return L;
+}
+
+struct AttnPlan {
+  int n_mtiles, n_split, kps;
+};
+// Splits each (sequence, KV head, 128-row tile) over enough key ranges to give the
+// 256 compute units about two workgroups each; ranges are multiples of 64 keys.
+AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max) {
+  AttnPlan p;
+  const int g = Hq / Hkv;
+  p.n_mtiles = (g * n_cap + 127) / 128;
+  const int tiles = S * Hkv * p.n_mtiles;
+  const int T = P_max + n_cap;
+  int want = (512 + tiles - 1) / tiles;
+  const int max_split = (T + 255) / 256;
+  if (want > max_split) want = max_split;
+  if (want > 32) want = 32;
+  if (want < 1) want = 1;
+  int kps = (T + want - 1) / want;
+  kps = (kps + 63) / 64 * 64;
+  p.kps = kps;
+  p.n_split = (T + kps - 1) / kps;
+  return p;
+}
+
+struct AttnLayout {
+  dtv::WsHeader* hdr;
+  float* part_o;
+  float* part_ml;
+  unsigned* tickets;
+  size_t bytes;
+};
+AttnLayout attn_layout(void* ws, int S, int Hkv, int D, const AttnPlan& p) {
+  const size_t tiles = static_cast<size_t>(S) * Hkv * p.n_mtiles;
+  const size_t np = p.n_split > 1 ? tiles * p.n_split * 128 : 0;
+  Carver c(ws);
+  AttnLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.part_o = c.take<float>(np * D);
+  L.part_ml = c.take<float>(np * 2);
+  L.tickets = c.take<unsigned>(tiles);
+  L.bytes = c.off;
+  return L;
+}
+
+struct VerifyLayout {
+  dtv::WsHeader* hdr;
+  unsigned long long* best;
+  unsigned* tickets;
+  size_t bytes;
+};
+VerifyLayout verify_layout(void* ws, int S, int n_cap) {
+  Carver c(ws);
+  VerifyLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.best = c.take<unsigned long long>(static_cast<size_t>(S) * n_cap);
+  L.tickets = c.take<unsigned>(S);
+  L.bytes = c.off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dtv_status_str(int status) {
+  switch (status) {
+    case DTV_OK: return "ok";
+    case DTV_EINVAL: return "invalid argument";
+    case DTV_EUNSUPPORTED: return "unsupported";
+    case DTV_ECAPACITY: return "capacity exceeded";
+    case DTV_EWORKSPACE: return "workspace too small";
+    case DTV_EHIP: return "HIP error";
+    case DTV_EDEVICE: return "device-side error";
+    default: return "unknown status";
+  }
+}
+
+const char* dtv_last_error(void) { return g_msg; }
+
+int dtv_ws_status(const void* ws, void* stream) {
+  REQUIRE(ws != nullptr, DTV_EINVAL, "workspace is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess)
+    return fail(DTV_EHIP, "stream synchronize failed: %s", hipGetErrorString(hipGetLastError()));
+  int err = 0;
+  if (hipMemcpy(&err, ws, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(DTV_EHIP, "reading the workspace status failed");
+  if (err != 0) {
+    int zero = 0;
+    if (hipMemcpy(const_cast<void*>(ws), &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess)
+      return fail(DTV_EHIP, "clearing the workspace status failed");
+  }
+  switch (err) {
+    case dtv::kErrNone: return DTV_OK;
+    case dtv::kErrCapacity: return fail(DTV_ECAPACITY, "a kernel ran out of capacity");
+    case dtv::kErrTimeout: return fail(DTV_EDEVICE, "a bounded grid-wide wait timed out");
+    case dtv::kErrBadTree: return fail(DTV_EDEVICE, "a parent is not an earlier slot");
+    default: return fail(DTV_EDEVICE, "device error %d", err);
+  }
+}
+
+// ---------------------------------------------------------------- row statistics
+
+size_t dtv_row_stats_ws_bytes(int32_t R, int32_t V, int32_t K, int dtype) {
+  if (R < 1 || V < 1 || K < 0 || !dtype_ok(dtype)) return 0;
+  return row_stats_layout(nullptr, R, V, K, dtype).bytes;
+}
+
+int dtv_row_stats(const void* table, int dtype, int32_t R, int32_t V, const int32_t* row_idx,
+                  int32_t K, float* maxv, int32_t* argmax, double* lse, int32_t* topk,
+                  void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(table != nullptr, DTV_EINVAL, "table is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(R >= 1 && V >= 1, DTV_EINVAL, "R=%d V=%d", R, V);
+  REQUIRE(K >= 0 && K <= 1024 && K <= V, DTV_EUNSUPPORTED, "K=%d must be in 0..min(V,1024)", K);
+  REQUIRE(K == 0 || topk != nullptr, DTV_EINVAL, "topk is NULL while K > 0");
+  REQUIRE(nch_of(V, dtype) <= 64 && static_cast<long>(nch_of(V, dtype)) * K <= 8192, DTV_EUNSUPPORTED,
+          "V=%d with K=%d exceeds the merge capacity (chunks * K <= 8192, chunks <= 64)", V, K);
+  const RowStatsLayout L = row_stats_layout(ws, R, V, K, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  dtv::RowStatsArgs a;
+  a.table = table;
+  a.R = R;
+  a.V = V;
+  a.K = K;
+  a.nch = nch_of(V, dtype);
+  a.row_idx = row_idx;
+  a.maxv = maxv;
+  a.argmax = argmax;
+  a.lse = lse;
+  a.topk = topk;
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.cval = L.cval;
+  a.cidx = L.cidx;
+  a.tickets = L.tickets;
+  a.mval = L.mval;
+  return launched(dtv::launch_row_stats(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- given trees
+
+size_t dtv_tree_build_given_ws_bytes(int32_t S) { return S >= 1 ? up(sizeof(dtv::WsHeader)) : 0; }
+
+int dtv_tree_build_given(const dtv_tree* tree, int32_t S, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(S >= 1, DTV_EINVAL, "S=%d", S);
+  REQUIRE(ws != nullptr && ws_bytes >= dtv_tree_build_given_ws_bytes(S), DTV_EWORKSPACE, "workspace too small");
+  return launched(dtv::launch_given(tree_args(tree), S, static_cast<dtv::WsHeader*>(ws),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- TALON
+
+size_t dtv_tree_build_talon_ws_bytes(int32_t S, int32_t B, int32_t K, int32_t V, int dtype) {
+  if (S < 1 || B < 1 || K < 1 || V < 1 || !dtype_ok(dtype)) return 0;
+  return talon_layout(nullptr, S, B, K, V, dtype).bytes;
+}
+
+int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int dtype, int32_t R,
+                         int32_t V, int32_t B, int32_t K, double alpha, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(draft != nullptr, DTV_EINVAL, "draft is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && S <= 64, DTV_EUNSUPPORTED, "S=%d outside 1..64", S);
+  REQUIRE(static_cast<long>(S) * tree->n_cap <= 2048, DTV_EUNSUPPORTED, "S*n_cap=%ld exceeds 2048",
+          static_cast<long>(S) * tree->n_cap);
+  REQUIRE(V >= 1, DTV_EINVAL, "V=%d", V);
+  REQUIRE(B >= 1, DTV_EINVAL, "B=%d", B);
+  REQUIRE(B + 1 <= tree->n_cap, DTV_ECAPACITY, "B+1=%d exceeds n_cap=%d", B + 1, tree->n_cap);
+  REQUIRE(R >= B + 1, DTV_EINVAL, "R=%d rows cannot key %d slots", R, B + 1);
+  REQUIRE(K >= 1 && K <= 64, DTV_EUNSUPPORTED, "K=%d outside 1..64", K);
+  REQUIRE(static_cast<long>(B) * K <= 4096, DTV_EUNSUPPORTED, "B*K=%ld exceeds 4096", static_cast<long>(B) * K);
+  REQUIRE(nch_of(V, dtype) <= 32 && nch_of(V, dtype) * K <= 2048, DTV_EUNSUPPORTED,
+          "V=%d with K=%d exceeds the merge capacity (chunks * K <= 2048, chunks <= 32)", V, K);
+  REQUIRE(alpha >= 0.0 && alpha <= 1.0, DTV_EINVAL, "alpha=%g outside [0,1]", alpha);
+  const TalonLayout L = talon_layout(ws, S, B, K, V, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  const int grid = dtv::talon_max_grid(dtype == DTV_BF16 ? 1 : 0);
+  REQUIRE(grid >= 1, DTV_EHIP, "cannot size the cooperative grid");
+  dtv::TalonArgs a;
+  a.tree = tree_args(tree);
+  a.draft = draft;
+  a.R = R;
+  a.V = V;
+  a.S = S;
+  a.B = B;
+  a.K = K;
+  a.nch = nch_of(V, dtype);
+  a.log_alpha = alpha > 0.0 ? log(alpha) : -INFINITY;
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.cval = L.cval;
+  a.cidx = L.cidx;
+  a.tickets = L.tickets;
+  a.rlse = L.rlse;
+  a.rv = L.rv;
+  a.ri = L.ri;
+  a.rcnt = L.rcnt;
+  return launched(dtv::launch_talon(a, dtype == DTV_BF16 ? 1 : 0, grid, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- attention
+
+size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t P_max, int dtype) {
+  if (S < 1 || n_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P_max < 0 || !dtype_ok(dtype)) return 0;
+  if (dtype != DTV_BF16) return up(sizeof(dtv::WsHeader));
+  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max)).bytes;
+}
+
+int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                  int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                  int dtype, float scale, void* o, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(q && k && v && P && o, DTV_EINVAL, "q, k, v, P or o is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && Hq >= 1 && Hkv >= 1, DTV_EINVAL, "S=%d Hq=%d Hkv=%d", S, Hq, Hkv);
+  REQUIRE(Hq % Hkv == 0, DTV_EINVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(P_max >= 0 && P_cap >= P_max + tree->n_cap, DTV_ECAPACITY,
+          "P_cap=%d cannot hold P_max=%d plus %d tree slots", P_cap, P_max, tree->n_cap);
+  REQUIRE(scale > 0.f && isfinite(scale), DTV_EINVAL, "scale=%g", scale);
+  if (dtype == DTV_BF16) {
+    REQUIRE(D == 64 || D == 128, DTV_EUNSUPPORTED, "bf16 attention supports D=64 or 128, got %d", D);
+  } else {
+    REQUIRE(D >= 4 && D <= 128 && D % 4 == 0, DTV_EUNSUPPORTED, "fp32 attention needs D%%4==0, D<=128, got %d", D);
+    REQUIRE(P_max + tree->n_cap <= 16384, DTV_EUNSUPPORTED, "fp32 attention supports at most 16384 keys");
+  }
+  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max);
+  size_t need = dtv_tree_attn_ws_bytes(S, tree->n_cap, Hq, Hkv, D, P_max, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  dtv::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.P = P;
+  a.P_cap = P_cap;
+  a.n_nodes = tree->n_nodes;
+  a.anc = reinterpret_cast<const uint64_t*>(tree->anc);
+  a.n_cap = tree->n_cap;
+  a.words = tree->words;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.g = Hq / Hkv;
+  a.scale = scale;
+  a.n_mtiles = plan.n_mtiles;
+  a.n_split = plan.n_split;
+  a.kps = plan.kps;
+  if (dtype == DTV_BF16) {
+    const AttnLayout L = attn_layout(ws, S, Hkv, D, plan);
+    a.part_o = L.part_o;
+    a.part_ml = L.part_ml;
+    a.tickets = L.tickets;
+    a.hdr = L.hdr;
+  } else {
+    a.hdr = static_cast<dtv::WsHeader*>(ws);
+  }
+  return launched(dtv::launch_attn(a, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- greedy verification
+
+size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype) {
+  if (S < 1 || n_cap < 1 || V < 1 || !dtype_ok(dtype)) return 0;
+  return verify_layout(nullptr, S, n_cap).bytes;
+}
+
+int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype, int32_t R,
+                           int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                           int32_t* argmax_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(target && path && path_len && bonus, DTV_EINVAL, "target, path, path_len or bonus is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && R >= 1 && V >= 1, DTV_EINVAL, "S=%d R=%d V=%d", S, R, V);
+  const VerifyLayout L = verify_layout(ws, S, tree->n_cap);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  dtv::VerifyArgs a;
+  a.tree = tree_args(tree);
+  a.target = target;
+  a.R = R;
+  a.V = V;
+  a.nch = nch_of(V, dtype);
+  a.path = path;
+  a.path_len = path_len;
+  a.bonus = bonus;
+  a.argmax_out = argmax_out;
+  a.best = L.best;
+  a.tickets = L.tickets;
+  a.hdr = L.hdr;
+  return launched(dtv::launch_verify_greedy(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- compaction
+
+int dtv_kv_compact(void* k, void* v, const int32_t* P, int32_t* P_new, int32_t P_cap, const int32_t* path,
+                   const int32_t* path_len, int32_t n_cap, int32_t S, int32_t Hkv, int32_t D, int dtype,
+                   void* stream) {
+  REQUIRE(k && v && P && P_new && path && path_len, DTV_EINVAL, "a pointer is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && Hkv >= 1 && n_cap >= 1 && P_cap >= n_cap, DTV_EINVAL, "S=%d Hkv=%d n_cap=%d P_cap=%d",
+          S, Hkv, n_cap, P_cap);
+  const int es = esize_of(dtype);
+  REQUIRE(D >= 1 && (D * es) % 16 == 0 && D * es <= 512, DTV_EUNSUPPORTED,
+          "row of D=%d elements must be a multiple of 16 bytes and at most 512", D);
+  dtv::CompactArgs a;
+  a.k = k;
+  a.v = v;
+  a.P = P;
+  a.P_new = P_new;
+  a.P_cap = P_cap;
+  a.path = path;
+  a.path_len = path_len;
+  a.n_cap = n_cap;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.esize = es;
+  return launched(dtv::launch_compact(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- bookkeeping
+
+int dtv_bookkeeping(const int32_t* accepted_h, int32_t n_passes, int64_t draft_steps, double gamma,
+                    double* out_h) {
+  REQUIRE(accepted_h && out_h, DTV_EINVAL, "accepted_h or out_h is NULL");
+  REQUIRE(n_passes >= 1, DTV_EINVAL, "need at least one verification pass");
+  REQUIRE(draft_steps >= 0 && gamma >= 0.0, DTV_EINVAL, "draft_steps and gamma must be >= 0");
+  double L = 0.0;
+  for (int32_t t = 0; t < n_passes; ++t) {
+    REQUIRE(accepted_h[t] >= 0, DTV_EINVAL, "A_%d = %d < 0", t, accepted_h[t]);
+    L += static_cast<double>(accepted_h[t]) + 1.0;
+  }
+  const double EA = L / n_passes;
+  const double eta = static_cast<double>(draft_steps) / n_passes;
+  out_h[0] = EA;
+  out_h[1] = eta;
+  out_h[2] = EA / (1.0 + gamma * eta);
+  out_h[3] = L;
+  return DTV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// Device helpers shared by the gfx950 kernels of the draft-tree step.
+//
+// Every kernel here runs with 256-thread workgroups (4 wave64s). Logit rows are read as
+// 16-byte vectors (8 bf16 or 4 fp32 values); element e of load i of thread t in a chunk
+// sits at index  chunk_base + i * 256 * VEC + t * VEC + e, so a (load, thread, element)
+// triple orders like the vocabulary index, which tie-breaking relies on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dtv {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+constexpr int kLoads = 4;                 // 16-byte loads per thread per chunk
+
+// ---------------------------------------------------------------- values and keys
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Order-preserving unsigned key of a finite float: larger value <=> larger key, -0 == +0.
+// Key 0 is never produced by a finite value and marks an empty element.
+__device__ __forceinline__ uint32_t f32_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0) u = 0;                       // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_f32(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o, 64);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Block-wide reductions; `red` is a __shared__ scratch of at least kWaves entries of T.
+// Every thread returns the result. Contains two __syncthreads().
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  T r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_min(T v, T* red) {
+  v = wave_min(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  T r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = red[i] < r ? red[i] : r;
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  T r = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r += red[i];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix sum over the block in thread order; `scan` holds kBlock ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scan, int* total) {
+  const int t = threadIdx.x;
+  scan[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kBlock; o <<= 1) {
+    int a = (t >= o) ? scan[t - o] : 0;
+    __syncthreads();
+    scan[t] += a;
+    __syncthreads();
+  }
+  int incl = scan[t];
+  *total = scan[kBlock - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// ---------------------------------------------------------------- cross-workgroup signalling
+//
+// The eight XCDs of an MI355X each have their own L2, so data one workgroup hands to
+// another must not sit dirty in one XCD's L2. An agent-scope fence makes ordinary stores
+// visible by writing back the whole L2, which costs microseconds per call; instead, every
+// value that crosses workgroups here is written with st_cc (a relaxed agent-scope atomic
+// store: a store the hardware keeps coherent across XCDs) and read with ld_cc (its load
+// counterpart). Before a workgroup signals (ticket or barrier), every wave waits for its
+// outstanding memory operations to complete (drain), so the data is in place before the
+// signalling atomic is performed.
+
+template <typename T>
+__device__ __forceinline__ void st_cc(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_cc(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's memory operations have completed (no compiler reordering across).
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ unsigned atomic_add_cc(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in every thread of the workgroup that arrives last (count reaches n).
+// The counter is reset to 0 by that workgroup so the next launch can reuse it. Data the
+// arriving workgroups produced must have been written with st_cc and is read with ld_cc.
+__device__ __forceinline__ bool last_arrival(unsigned* counter, unsigned n, int* flag_lds) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomic_add_cc(counter, 1u);
+    const int last = (prev == n - 1) ? 1 : 0;
+    if (last) st_cc(counter, 0u);
+    *flag_lds = last;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
+// Barrier over a co-resident grid (launched cooperatively). `bar[0]` counts arrivals,
+// `bar[1]` is the generation. The wait is bounded: after `limit` polls it gives up,
+// writes `timeout_code` into `*err` and returns false (callers then stop their loops).
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned nblocks, int* err,
+                                             int timeout_code, int* flag_lds) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const unsigned gen = ld_cc(&bar[1]);
+    drain();  // the generation is read before this workgroup arrives
+    const unsigned prev = atomic_add_cc(&bar[0], 1u);
+    if (prev == nblocks - 1) {
+      st_cc(&bar[0], 0u);
+      drain();
+      atomic_add_cc(&bar[1], 1u);
+    } else {
+      long polls = 0;
+      const long limit = 40000000;
+      while (ld_cc(&bar[1]) == gen) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > limit) {
+          atomicExch(err, timeout_code);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    *flag_lds = ok;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
+// ---------------------------------------------------------------- error codes in workspaces
+// The first 256 bytes of every workspace hold: int err; unsigned bar[2]; unsigned exit_count.
+struct WsHeader {
+  int err;
+  unsigned bar[2];
+  unsigned exit_count;
+  unsigned pad[60];
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+
+enum : int { kErrNone = 0, kErrCapacity = 1, kErrTimeout = 2, kErrBadTree = 3 };
+
+}  // namespace dtv

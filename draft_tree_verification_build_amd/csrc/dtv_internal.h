@@ -1,0 +1,109 @@
+// Host/device argument blocks and launch wrappers shared between the kernel sources and
+// the C entry points (api.cpp). Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dtv {
+
+struct ChunkStat;
+
+struct TreeArgs {
+  int n_cap, words;
+  int* n_nodes;
+  int* parent;
+  int* token;
+  int* depth;
+  int* row;
+  double* score;
+  uint64_t* anc;
+  int* layers;
+};
+
+struct TalonArgs {
+  TreeArgs tree;
+  const void* draft;
+  int R, V, S, B, K, nch;
+  double log_alpha;
+  WsHeader* hdr;
+  ChunkStat* st;       // [S][B][nch]
+  float* cval;         // [S][B][nch][K]
+  int* cidx;           // [S][B][nch][K]
+  unsigned* tickets;   // [S][B]
+  double* rlse;        // [S][B]
+  float* rv;           // [S][B][K]
+  int* ri;             // [S][B][K]
+  int* rcnt;           // [S][B]
+};
+
+struct RowStatsArgs {
+  const void* table;
+  int R, V, K, nch;
+  const int* row_idx;
+  float* maxv;
+  int* argmax;
+  double* lse;
+  int* topk;
+  WsHeader* hdr;
+  ChunkStat* st;       // [R][nch]
+  float* cval;         // [R][nch][K]
+  int* cidx;
+  unsigned* tickets;   // [R]
+  float* mval;         // [R][K] merged values (scratch)
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int* P;
+  int P_cap;
+  const int* n_nodes;
+  const uint64_t* anc;
+  int n_cap, words;
+  int S, Hq, Hkv, D, g;
+  float scale;          // softmax scale (1/sqrt(D) by default)
+  int n_mtiles, n_split, kps;  // 128-row query tiles, key splits, keys per split
+  float* part_o;        // [S*Hkv*n_mtiles][n_split][128][D]
+  float* part_ml;       // [S*Hkv*n_mtiles][n_split][128][2]
+  unsigned* tickets;    // [S*Hkv*n_mtiles]
+  WsHeader* hdr;
+};
+
+struct VerifyArgs {
+  TreeArgs tree;
+  const void* target;
+  int R, V, nch;
+  int* path;
+  int* path_len;
+  int* bonus;
+  int* argmax_out;
+  unsigned long long* best;  // [S][n_cap]
+  unsigned* tickets;         // [S]
+  WsHeader* hdr;
+};
+
+struct CompactArgs {
+  void* k;
+  void* v;
+  const int* P;
+  int* P_new;
+  int P_cap;
+  const int* path;
+  const int* path_len;
+  int n_cap, S, Hkv, D, esize;
+};
+
+int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st);
+int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st);
+int talon_max_grid(int dtype);
+int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
+int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
+int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
+int launch_compact(const CompactArgs& a, hipStream_t st);
+
+}  // namespace dtv

@@ -1,0 +1,451 @@
+// Vocab-wide row statistics on gfx950: max, argmax, log-sum-exp and top-K of logit rows.
+//
+// A row of V logits is cut into chunks of kBlock * kLoads * VEC elements (8192 bf16 or
+// 4096 fp32); one 256-thread workgroup reads a chunk with coalesced 16-byte loads, keeps
+// it in registers, and reduces it to a ChunkStat plus its sorted top-K list. The chunks of
+// a row are then merged (by whichever workgroup finishes the row last). Everything that
+// orders values uses exact order-preserving integer keys of the stored values, so argmax
+// and top-K are exact; log-sum-exp accumulates exp(x - max) in float64.
+#pragma once
+
+#include "common.h"
+#include "fexp.h"
+
+namespace dtv {
+
+struct ChunkStat {
+  float maxv;      // largest value of the chunk
+  int argmax;      // lowest index holding it
+  double sumexp;   // sum over the chunk of exp(x - maxv), float64
+  int cnt;         // entries in the chunk's top-K list
+  int pad;
+};
+
+template <int DT>  // 0: fp32 rows, 1: bf16 rows
+struct RowT {
+  static constexpr int VEC = DT ? 8 : 4;           // values per 16-byte load
+  static constexpr int E = kLoads * VEC;            // values per thread per chunk
+  static constexpr int CHUNK = kBlock * E;          // values per chunk
+  static constexpr int KEYBITS = DT ? 16 : 32;      // bits of the exact ordering key
+  static constexpr int ESIZE = DT ? 2 : 4;
+};
+
+template <int DT>
+__host__ __device__ constexpr int chunks_of(int V) {
+  return (V + RowT<DT>::CHUNK - 1) / RowT<DT>::CHUNK;
+}
+
+// Shared-memory scratch used by the chunk routines.
+struct RowSmem {
+  double redd[kWaves];
+  float redf[kWaves];
+  unsigned redu[kWaves];
+  int redi[kWaves];
+  // per-wave partial results of chunk_reduce
+  double wse[kWaves];
+  float wmax[kWaves];
+  uint32_t wkey[kWaves];
+  int warg[kWaves];
+  int wnv[kWaves];
+  int wcnt[kWaves];
+  uint32_t wtau[kWaves];
+  int ncand;
+  int flag;
+  double exptab[64];  // table of exp_nonpos; filled by row_smem_init
+};
+
+// Must run in every thread at kernel start, followed by __syncthreads().
+__device__ __forceinline__ void row_smem_init(RowSmem& sm) { exp_table_load(sm.exptab); }
+
+constexpr int kCandCap = 512;   // candidate slots of the small-K selection (sortbuf entries)
+
+// Loads chunk `c` of `row` into registers. Out-of-range elements get key 0 and -inf.
+// Full, aligned chunks issue their four 16-byte loads back to back before using any.
+template <int DT>
+__device__ __forceinline__ void load_chunk(const void* row, int V, int c, float (&x)[RowT<DT>::E],
+                                           uint32_t (&key)[RowT<DT>::E]) {
+  using R = RowT<DT>;
+  const int t = threadIdx.x;
+  const int base = c * R::CHUNK;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
+  if (aligned && base + R::CHUNK <= V) {
+    uint4 raw[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int i0 = base + i * kBlock * R::VEC + t * R::VEC;
+      raw[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
+                                               static_cast<size_t>(i0) * R::ESIZE);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      if (DT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[i * 8 + e] = bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[i * 4 + e] = __uint_as_float(w[e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R::E; ++j) key[j] = f32_key(x[j]) >> (32 - R::KEYBITS);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int i0 = base + i * kBlock * R::VEC + t * R::VEC;
+#pragma unroll
+    for (int e = 0; e < R::VEC; ++e) {
+      const int ix = i0 + e;
+      if (ix < V) {
+        const float f = DT ? bf16_to_f32(static_cast<const uint16_t*>(row)[ix])
+                           : static_cast<const float*>(row)[ix];
+        x[i * R::VEC + e] = f;
+        key[i * R::VEC + e] = f32_key(f) >> (32 - R::KEYBITS);
+      } else {
+        x[i * R::VEC + e] = -INFINITY;
+        key[i * R::VEC + e] = 0u;
+      }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ int elem_index(int c, int i, int e) {
+  using R = RowT<DT>;
+  return c * R::CHUNK + (i * kBlock + static_cast<int>(threadIdx.x)) * R::VEC + e;
+}
+
+// Sort `n` (a power of two) 64-bit keys in shared memory, descending.
+__device__ __forceinline__ void bitonic_sort_desc(unsigned long long* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kBlock) {
+        const int p = i ^ j;
+        if (p > i) {
+          const unsigned long long x = a[i], y = a[p];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned long long sort_key(float v, int idx) {
+  return (static_cast<unsigned long long>(f32_key(v)) << 32) |
+         static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int sort_key_index(unsigned long long k) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k & 0xFFFFFFFFull));
+}
+__device__ __forceinline__ float sort_key_value(unsigned long long k) {
+  return key_to_f32(static_cast<uint32_t>(k >> 32));
+}
+
+__host__ __device__ constexpr int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Number of chunk elements (of this wave) whose key is >= thr; wave-uniform, scalar.
+template <int DT>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[RowT<DT>::E], uint32_t thr) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < RowT<DT>::E; ++j) n += __popcll(__ballot(key[j] >= thr));
+  return n;
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__device__ __forceinline__ float bf16key_to_f32(uint32_t k16) {
+  return bf16_to_f32(static_cast<uint16_t>((k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu)));
+}
+
+// Reduces the chunk in registers. Writes *st (thread 0) and, when K > 0, the chunk's top-K
+// (value, index) sorted by (value desc, index asc) into out_val/out_idx (global, st_cc).
+//
+// Per wave, without block barriers: maximum and its lowest index, float64 sum of
+// exp(x - wave max), valid count. Top-K, for K <= 32: every wave takes the K-th largest of
+// its 64 lane maxima (bisection with one ballot per step); the largest of those, tau, is a
+// lower bound of the chunk's K-th largest value (that wave alone has K values >= tau), so
+// the chunk's top-K are among the values >= tau, usually barely more than K of them. They
+// are gathered in shared memory and ranked exactly by (value desc, index asc). If ties make
+// the candidates overflow, or K > 32, each wave instead bisects the key space for its own
+// K-th largest value (ballot counts over all its elements), resolves ties at the threshold
+// in index order with lane-prefix counts, and the <= 4K wave candidates are ranked (K <= 32)
+// or sorted. `sortbuf` holds at least max(kCandCap, pow2_at_least(4 * K)) entries.
+template <int DT>
+__device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key)[RowT<DT>::E], int c,
+                             int V, int K, ChunkStat* st, float* out_val, int* out_idx,
+                             unsigned long long* sortbuf, RowSmem& sm) {
+  using R = RowT<DT>;
+  const int w = threadIdx.x >> 6;
+  // ---- wave max, lowest index of the max, sum of exp, valid count
+  uint32_t lmk = 0;
+#pragma unroll
+  for (int j = 0; j < R::E; ++j) lmk = key[j] > lmk ? key[j] : lmk;
+  const uint32_t km = wave_max(lmk);
+  int am = 0x7FFFFFFF;
+#pragma unroll
+  for (int i = kLoads - 1; i >= 0; --i)
+#pragma unroll
+    for (int e = R::VEC - 1; e >= 0; --e)
+      if (key[i * R::VEC + e] == km) am = elem_index<DT>(c, i, e);
+  am = wave_min(am);
+  int nv = 0;
+#pragma unroll
+  for (int j = 0; j < R::E; ++j) nv += __popcll(__ballot(key[j] != 0u));
+  const float mw = (km == 0u) ? -INFINITY : (DT ? bf16key_to_f32(km) : key_to_f32(km));
+  double se = 0.0;
+  if (km != 0u) {
+    const double md = static_cast<double>(mw);
+#pragma unroll
+    for (int j = 0; j < R::E; ++j)
+      if (key[j] != 0u) se += exp_nonpos(static_cast<double>(x[j]) - md, sm.exptab);
+  }
+  se = wave_sum(se);
+  const bool small = K <= 32;
+  if (small && K > 0) {  // K-th largest lane maximum of this wave
+    uint32_t lo = 1u;
+    if (__popcll(__ballot(lmk != 0u)) >= K) {
+      uint32_t hi = km + 1u;
+      while (hi - lo > 1u) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (__popcll(__ballot(lmk >= mid)) >= K) lo = mid; else hi = mid;
+      }
+    }
+    if ((threadIdx.x & 63) == 0) sm.wtau[w] = lo;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sm.wkey[w] = km;
+    sm.warg[w] = am;
+    sm.wse[w] = se;
+    sm.wmax[w] = mw;
+    sm.wnv[w] = nv;
+    sm.wcnt[w] = 0;
+  }
+  if (threadIdx.x == 0) sm.ncand = 0;
+  __syncthreads();
+
+  // ---- chunk results
+  int nvalid = 0;
+  for (int q = 0; q < kWaves; ++q) nvalid += sm.wnv[q];
+  const int kk = K < nvalid ? K : nvalid;
+  if (threadIdx.x == 0) {  // read by the workgroup that merges the row
+    uint32_t KM = 0;
+    int AM = 0x7FFFFFFF;
+    float M = -INFINITY;
+    for (int q = 0; q < kWaves; ++q)
+      if (sm.wkey[q] > KM) {
+        KM = sm.wkey[q];
+        M = sm.wmax[q];
+      }
+    double S = 0.0;
+    for (int q = 0; q < kWaves; ++q) {
+      if (sm.wkey[q] == KM && sm.warg[q] < AM) AM = sm.warg[q];
+      if (sm.wkey[q] != 0u) S += sm.wse[q] * exp(static_cast<double>(sm.wmax[q]) - static_cast<double>(M));
+    }
+    st_cc(&st->maxv, M);
+    st_cc(&st->argmax, AM);
+    st_cc(&st->sumexp, S);
+    st_cc(&st->cnt, kk);
+  }
+  if (kk <= 0) {
+    __syncthreads();
+    return;
+  }
+
+  if (small) {
+    uint32_t tau = 1u;
+    for (int q = 0; q < kWaves; ++q) tau = sm.wtau[q] > tau ? sm.wtau[q] : tau;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+      for (int e = 0; e < R::VEC; ++e)
+        if (key[i * R::VEC + e] >= tau) {
+          const int pos = atomicAdd(&sm.ncand, 1);
+          if (pos < kCandCap) sortbuf[pos] = sort_key(x[i * R::VEC + e], elem_index<DT>(c, i, e));
+        }
+    __syncthreads();
+    const int n = sm.ncand;
+    if (n <= kCandCap) {
+      for (int e = threadIdx.x; e < n; e += kBlock) {
+        const unsigned long long me = sortbuf[e];
+        int rank = 0;
+        for (int e2 = 0; e2 < n; ++e2) rank += sortbuf[e2] > me ? 1 : 0;
+        if (rank < kk) {
+          st_cc(&out_val[rank], sort_key_value(me));
+          st_cc(&out_idx[rank], sort_key_index(me));
+        }
+      }
+      __syncthreads();
+      return;
+    }
+    __syncthreads();  // too many ties at tau: exact per-wave selection below
+  }
+
+  const int P2 = pow2_at_least(kWaves * K);
+  const bool big = kWaves * K > 128;
+  if (big) {
+    for (int i = threadIdx.x; i < P2; i += kBlock) sortbuf[i] = 0ull;
+    __syncthreads();
+  }
+  // ---- the wave's own top-K by bisection of the key space
+  const int kw = K < nv ? K : nv;
+  if (kw > 0) {
+    uint32_t lo = 1u, hi = km + 1u;  // count(>= lo) >= kw > count(>= hi)
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      if (wave_count_ge<DT>(key, mid) >= kw) lo = mid; else hi = mid;
+    }
+    const uint32_t tau = lo;
+    const int cnt_gt = wave_count_ge<DT>(key, tau + 1u);
+    const int cnt_eq = wave_count_ge<DT>(key, tau) - cnt_gt;
+    const int need = kw - cnt_gt;   // ties at tau to take, lowest index first
+    int base = 0;                   // ties of this wave in earlier loads
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      int below = 0, tot = 0;
+      if (cnt_eq > need) {
+#pragma unroll
+        for (int e = 0; e < R::VEC; ++e) {
+          const unsigned long long m = __ballot(key[i * R::VEC + e] == tau);
+          below += lanes_below(m);
+          tot += __popcll(m);
+        }
+      }
+      int own = 0;
+#pragma unroll
+      for (int e = 0; e < R::VEC; ++e) {
+        const uint32_t k = key[i * R::VEC + e];
+        bool take = k > tau;
+        if (k == tau) {
+          take = (cnt_eq > need) ? (base + below + own < need) : true;
+          ++own;
+        }
+        if (take) {
+          const int pos = atomicAdd(&sm.wcnt[w], 1);
+          sortbuf[w * K + pos] = sort_key(x[i * R::VEC + e], elem_index<DT>(c, i, e));
+        }
+      }
+      base += tot;
+    }
+  }
+  __syncthreads();
+  if (!big) {
+    // rank of each wave candidate among all of them (keys are unique)
+    for (int e = threadIdx.x; e < kWaves * K; e += kBlock) {
+      const int q = e / K, j = e % K;
+      if (j >= sm.wcnt[q]) continue;
+      const unsigned long long me = sortbuf[e];
+      int rank = 0;
+      for (int q2 = 0; q2 < kWaves; ++q2)
+        for (int j2 = 0; j2 < sm.wcnt[q2]; ++j2) rank += sortbuf[q2 * K + j2] > me ? 1 : 0;
+      if (rank < kk) {
+        st_cc(&out_val[rank], sort_key_value(me));
+        st_cc(&out_idx[rank], sort_key_index(me));
+      }
+    }
+  } else {
+    bitonic_sort_desc(sortbuf, P2);
+    for (int i = threadIdx.x; i < kk; i += kBlock) {
+      st_cc(&out_val[i], sort_key_value(sortbuf[i]));
+      st_cc(&out_idx[i], sort_key_index(sortbuf[i]));
+    }
+  }
+  __syncthreads();
+}
+
+// Shared staging area of row_merge: CAP entries of all chunk lists together.
+constexpr int kMergeMaxChunks = 64;
+
+template <int CAP>
+struct MergeSmem {
+  unsigned long long key[CAP];  // sort keys of every chunk's list, list c at c*K
+  int cnt[kMergeMaxChunks];
+  float maxv[kMergeMaxChunks];
+  int argmax[kMergeMaxChunks];
+  double sumexp[kMergeMaxChunks];
+};
+
+// Merges the ChunkStats and sorted top-K lists of the `nch` chunks of one row (written by
+// other workgroups with st_cc). The lists are first copied into shared memory (one
+// parallel pass of coherent loads); each entry's rank in the merged order is then the
+// count of entries of all lists that precede it (binary search in the sorted lists).
+// Outputs (thread 0): maxv, argmax, lse; all threads: topK (value, index) into rv/ri, all
+// written with st_cc. Requires nch <= 64 and nch * K <= CAP. Returns min(K, entries).
+template <int CAP>
+__device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx, int nch, int K,
+                         float* maxv, int* argmax, double* lse, float* rv, int* ri, RowSmem& sm,
+                         MergeSmem<CAP>& ms) {
+  for (int c = threadIdx.x; c < nch; c += kBlock) {  // one parallel round of loads
+    ms.cnt[c] = ld_cc(&st[c].cnt);
+    ms.maxv[c] = ld_cc(&st[c].maxv);
+    ms.argmax[c] = ld_cc(&st[c].argmax);
+    ms.sumexp[c] = ld_cc(&st[c].sumexp);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    int am = 0;
+    for (int c = 0; c < nch; ++c) {
+      if (ms.maxv[c] > M) {  // chunks are in index order: the first maximum has the lowest index
+        M = ms.maxv[c];
+        am = ms.argmax[c];
+      }
+    }
+    double s = 0.0;
+    for (int c = 0; c < nch; ++c)
+      s += ms.sumexp[c] * exp(static_cast<double>(ms.maxv[c]) - static_cast<double>(M));
+    if (maxv) st_cc(maxv, M);
+    if (argmax) st_cc(argmax, am);
+    if (lse) st_cc(lse, static_cast<double>(M) + log(s));
+  }
+  int total = 0;
+  for (int c = 0; c < nch; ++c) total += ms.cnt[c];
+  const int kk = K < total ? K : total;
+  if (kk <= 0) {
+    __syncthreads();
+    return 0;
+  }
+  for (int e = threadIdx.x; e < nch * K; e += kBlock) {
+    const int c = e / K, j = e % K;
+    if (j < ms.cnt[c]) ms.key[e] = sort_key(ld_cc(&cval[e]), ld_cc(&cidx[e]));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nch * K; e += kBlock) {
+    const int c = e / K, j = e % K;
+    if (j >= ms.cnt[c]) continue;
+    const unsigned long long me = ms.key[e];
+    int rank = j;
+    for (int c2 = 0; c2 < nch; ++c2) {
+      if (c2 == c) continue;
+      int a = 0, b = ms.cnt[c2];  // entries of list c2 greater than me
+      const unsigned long long* l2 = ms.key + c2 * K;
+      while (a < b) {
+        const int m = (a + b) >> 1;
+        if (l2[m] > me) a = m + 1; else b = m;
+      }
+      rank += a;
+    }
+    if (rank < kk) {
+      st_cc(&rv[rank], sort_key_value(me));
+      st_cc(&ri[rank], sort_key_index(me));
+    }
+  }
+  __syncthreads();
+  return kk;
+}
+
+}  // namespace dtv

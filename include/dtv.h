@@ -1,0 +1,185 @@
+/*
+ * dtv.h - C ABI of one speculative-decoding draft-tree step on an MI355X (gfx950).
+ *
+ * The step has four parts: build a draft tree under a node budget, run tree-masked
+ * attention over the KV prefix and each node's ancestors, verify the nodes against the
+ * target, and move the accepted path's keys and values behind the prefix.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless the argument name ends in `_h` (host).
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL = the default stream)
+ *   and returns; nothing is synchronised.
+ * - The caller owns every buffer. The library allocates nothing; calls that need scratch
+ *   take a caller-provided workspace `ws` of `ws_bytes` bytes, sized by the matching
+ *   `*_ws_bytes` query and zero-filled by the caller once after allocation (the
+ *   library keeps it consistent afterwards). One workspace must not be used by two
+ *   calls that may run at the same time.
+ * - Argument errors are detected on the host before any launch and returned as a
+ *   negative dtv_status; a launch failure returns DTV_EHIP. Errors found by a kernel
+ *   (capacity exceeded on the device, a bounded wait that ran out) are recorded in the
+ *   workspace and read with dtv_ws_status(), which synchronises the stream.
+ *   dtv_last_error() returns a message for the last failing call of the thread.
+ * - Logit tables are `[S][R][V]`, row-major, of the given dtype; a node's rows are
+ *   addressed through the tree's `row` array. Stored values are compared exactly;
+ *   ties go to the lowest index.
+ * - No C++ exception crosses this interface.
+ *
+ * Tree layout (slot numbering)
+ * ----------------------------
+ * Slot 0 of every sequence is the root (the last committed token, whose key/value is not
+ * cached yet); draft nodes follow in topological order (parent[i] < i). Every per-node
+ * array is `[S][n_cap]`; `anc` is `[S][n_cap][words]` with bit (j % 64) of word (j / 64)
+ * set when slot j is an ancestor-or-self of the node.
+ */
+#ifndef DTV_H
+#define DTV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DTV_OK = 0,
+  DTV_EINVAL = -1,        /* bad argument (null pointer, negative size, inconsistent shape) */
+  DTV_EUNSUPPORTED = -2,  /* valid but not implemented (dtype, head dim, K or budget too large) */
+  DTV_ECAPACITY = -3,     /* a tree would not fit its n_cap slots or words */
+  DTV_EWORKSPACE = -4,    /* workspace missing or smaller than the *_ws_bytes query */
+  DTV_EHIP = -5,          /* a HIP call or kernel launch failed */
+  DTV_EDEVICE = -6        /* a kernel reported an error in the workspace (dtv_ws_status) */
+} dtv_status;
+
+typedef enum { DTV_F32 = 0, DTV_BF16 = 1 } dtv_dtype;
+
+/* Device arrays of a batch of S trees (see "Tree layout" above). */
+typedef struct dtv_tree {
+  int32_t n_cap;      /* slots per sequence, root included */
+  int32_t words;      /* 64-bit mask words per node, >= ceil(n_cap / 64) */
+  int32_t* n_nodes;   /* [S] nodes in each tree, root included */
+  int32_t* parent;    /* [S][n_cap] parent slot, -1 at the root */
+  int32_t* token;     /* [S][n_cap] token id, -1 at the root */
+  int32_t* depth;     /* [S][n_cap] root = 0 */
+  int32_t* row;       /* [S][n_cap] row of the node in the draft and target tables */
+  double* score;      /* [S][n_cap] log path score (sum of draft log-probabilities) */
+  uint64_t* anc;      /* [S][n_cap][words] ancestor-or-self bitmask */
+  int32_t* layers;    /* [S] draft passes (layers of draft rows) the build consumed */
+} dtv_tree;
+
+const char* dtv_status_str(int status);
+const char* dtv_last_error(void);
+
+/* Synchronise `stream` and return the device-side status recorded in a workspace
+ * (DTV_OK, DTV_ECAPACITY, DTV_EDEVICE), clearing it. */
+int dtv_ws_status(const void* ws, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Row statistics (vocab-wide softmax normaliser, argmax and top-K).
+ *
+ * The TALON page (sections 5.2.1-5.2.2) scores candidates with products of draft
+ * probabilities and initialises the root layer with TopK of the draft distribution;
+ * the OPT-Tree summary (section 2) accepts the target's highest-probability token;
+ * the concept page ("The protocol") compares p(x) with q(x). All need, per row:
+ * maximum, index of the maximum, log-sum-exp and the K largest entries.
+ *
+ * For each of R rows `rows[r]` of a `[R][V]` table (or row `row_idx[r]` when row_idx is
+ * not NULL): maxv[r] (float), argmax[r] (lowest index of the maximum), lse[r] (double,
+ * log sum_j exp(x_j)), and, when K > 0, topk[r][0..K) = indices of the K largest values,
+ * largest first, ties by lowest index. Any output pointer may be NULL. Requires
+ * 1 <= K <= min(V, 1024) or K = 0.
+ */
+size_t dtv_row_stats_ws_bytes(int32_t R, int32_t V, int32_t K, int dtype);
+int dtv_row_stats(const void* table, int dtype, int32_t R, int32_t V, const int32_t* row_idx,
+                  int32_t K, float* maxv, int32_t* argmax, double* lse, int32_t* topk,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Tree build: given shape (random trees drafted elsewhere).
+ *
+ * The caller fills n_nodes, parent and token; the call writes depth, row (= slot),
+ * score (= 0), layers (= 0) and the ancestor-or-self mask that tree attention needs
+ * (OPT-Tree summary, section 2: all tree tokens verified in one pass with a tree mask).
+ * A parent that is not an earlier slot is reported as DTV_EDEVICE by dtv_ws_status.
+ */
+size_t dtv_tree_build_given_ws_bytes(int32_t S);
+int dtv_tree_build_given(const dtv_tree* tree, int32_t S, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Tree build: TALON budget-driven hybrid expansion (TALON page, sections 5.1-5.2).
+ *
+ * Layer 1 is the K most probable root children (no gate; at most B). Every later layer
+ * pools the K most probable children of each node of the previous layer, scores them
+ * with the log path score s(c) = s(parent) + log p_d(token | parent), keeps those with
+ * s(c) >= log(alpha) + max s (the anchor), and, when more pass than budget remains,
+ * the best by score (ties: lower parent slot, then lower rank). New nodes take slots in
+ * (parent slot, rank) order. The build stops when B draft nodes exist (N = B + 1).
+ * Draft rows are keyed by slot: node i expands with table row i, so `draft` holds
+ * R >= B + 1 rows per sequence. The whole layer loop runs in one launch.
+ * Limits: 1 <= B < n_cap <= 1024, 1 <= K <= 64, B * K <= 4096, 0 <= alpha <= 1.
+ */
+size_t dtv_tree_build_talon_ws_bytes(int32_t S, int32_t B, int32_t K, int32_t V, int dtype);
+int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int dtype,
+                         int32_t R, int32_t V, int32_t B, int32_t K, double alpha,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Tree attention (OPT-Tree summary, section 2; concept page, "Why it is a win").
+ *
+ * For node i of sequence s and query head h (KV head kv = h / (Hq / Hkv)):
+ *   o[s][i][h] = sum_j softmax_j(scale * q[s][i][h] . k[s][kv][j]) v[s][kv][j]
+ * over the prefix j < P[s] and the tree keys j = P[s] + a for every ancestor-or-self a
+ * of i (the tree's keys and values sit at cache positions P[s] + slot).
+ * Layouts: q, o `[S][n_cap][Hq][D]`; k, v `[S][Hkv][P_cap][D]`; P `[S]` (device) with
+ * P[s] + n_nodes[s] <= P_cap, and P_max >= every P[s] (host bound, sizes the grid).
+ * Rows of o for slots >= n_nodes[s] are not written. bf16 runs on MFMA with fp32
+ * accumulation; f32 runs in fp32. D must be 64 or 128; Hq % Hkv == 0.
+ */
+size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t P_max, int dtype);
+int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                  int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv,
+                  int32_t D, int dtype, float scale, void* o, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Greedy verification (OPT-Tree summary, section 2; GOOSE page, section 2C).
+ *
+ * a[v] = argmax of target row row[v]; node c matches when token[c] == a[parent[c]];
+ * the accepted node v* is the deepest node whose whole root path matches (lowest slot
+ * among equals). Outputs per sequence: path[s][0..A] = slots root .. v* (by depth),
+ * path_len[s] = A + 1, bonus[s] = a[v*]; optional argmax_out[s][n_cap] = a.
+ * `target` is `[S][R][V]`.
+ */
+size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype);
+int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype,
+                           int32_t R, int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                           int32_t* argmax_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * KV compaction (concept page, "The protocol", step 4: append the accepted tokens).
+ *
+ * For every sequence and KV head: cache[P + k] <- cache[P + path[k]] for k < path_len,
+ * for both k and v (in place, all reads before any write), and P_new[s] = P[s] +
+ * path_len[s]. P_new may alias P. Layout as in dtv_tree_attn; path `[S][n_cap]`.
+ */
+int dtv_kv_compact(void* k, void* v, const int32_t* P, int32_t* P_new, int32_t P_cap,
+                   const int32_t* path, const int32_t* path_len, int32_t n_cap, int32_t S,
+                   int32_t Hkv, int32_t D, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Draft-efficiency bookkeeping (TALON page, section 5.3). Host only.
+ *
+ * accepted_h[t] = A_t accepted draft tokens of verification pass t (t < n_passes),
+ * draft_steps = N_d, gamma = draft-to-target cost ratio. Writes out_h[0..4] =
+ * { E[A] = L / N_v with L = sum (A_t + 1), eta = N_d / N_v, Speedup = E[A] / (1 + gamma*eta),
+ *   L }.
+ */
+int dtv_bookkeeping(const int32_t* accepted_h, int32_t n_passes, int64_t draft_steps,
+                    double gamma, double* out_h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DTV_H */

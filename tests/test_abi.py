@@ -1,0 +1,116 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares,
+sizes workspaces, and rejects bad arguments before any launch (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import bookkeeping as obook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dtv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from draft_tree_verification_build_amd import _lib, build_lib
+    if not os.path.exists(_lib.LIB_PATH):
+        build_lib.build()
+    return _lib.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dtv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_signatures_cover_header(lib):
+    from draft_tree_verification_build_amd._lib import SIGNATURES
+    assert set(declared_symbols()) == set(SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.dtv_status_str(0) == b"ok"
+    assert lib.dtv_status_str(-4) == b"workspace too small"
+
+
+def test_workspace_queries(lib):
+    assert lib.dtv_row_stats_ws_bytes(10, 32000, 512, 1) > 0
+    assert lib.dtv_row_stats_ws_bytes(0, 32000, 512, 1) == 0
+    assert lib.dtv_tree_build_talon_ws_bytes(1, 60, 10, 128256, 1) > 0
+    assert lib.dtv_tree_attn_ws_bytes(1, 61, 32, 8, 128, 2048, 1) > 0
+    assert lib.dtv_tree_attn_ws_bytes(1, 61, 32, 7, 128, 2048, 1) == 0   # Hq % Hkv != 0
+    assert lib.dtv_tree_verify_greedy_ws_bytes(1, 61, 128256, 1) > 0
+
+
+def _fake_tree(n_cap=61, words=1):
+    from draft_tree_verification_build_amd._lib import DtvTree
+    p = 0x1000  # never dereferenced: every call below fails its host-side checks first
+    return DtvTree(n_cap, words, p, p, p, p, p, p, p, p)
+
+
+def test_talon_argument_checks(lib):
+    t = _fake_tree()
+    ws = ctypes.c_void_p(0x2000)
+    call = lambda **kw: lib.dtv_tree_build_talon(
+        ctypes.byref(kw.get("tree", t)), kw.get("S", 1), ctypes.c_void_p(0x3000), kw.get("dtype", 1),
+        kw.get("R", 61), kw.get("V", 1000), kw.get("B", 60), kw.get("K", 10), kw.get("alpha", 0.1),
+        ws, kw.get("ws_bytes", 1 << 30), None)
+    assert call(K=65) == -2
+    assert call(B=61) == -3                 # B + 1 > n_cap
+    assert call(alpha=1.5) == -1
+    assert call(R=10) == -1
+    assert call(dtype=7) == -2
+    assert call(ws_bytes=16) == -4
+    assert call(tree=_fake_tree(words=0)) == -3
+    assert lib.dtv_tree_build_talon(None, 1, None, 1, 61, 1000, 60, 10, 0.1, None, 0, None) == -1
+    assert b"n_cap" in lib.dtv_last_error() or len(lib.dtv_last_error()) > 0
+
+
+def test_attention_argument_checks(lib):
+    t = _fake_tree()
+    p = ctypes.c_void_p(0x4000)
+    call = lambda **kw: lib.dtv_tree_attn(p, p, p, p, kw.get("P_cap", 2200), kw.get("P_max", 2048),
+                                          ctypes.byref(t), 1, kw.get("Hq", 32), kw.get("Hkv", 8),
+                                          kw.get("D", 128), kw.get("dtype", 1), kw.get("scale", 0.088),
+                                          p, p, kw.get("ws_bytes", 1 << 30), None)
+    assert call(Hkv=7) == -1
+    assert call(D=96) == -2
+    assert call(P_cap=2048) == -3
+    assert call(scale=0.0) == -1
+    assert call(ws_bytes=64) == -4
+    assert call(dtype=0, P_max=20000, P_cap=30000) == -2   # fp32 path limited to 16384 keys
+
+
+def test_compaction_argument_checks(lib):
+    p = ctypes.c_void_p(0x4000)
+    assert lib.dtv_kv_compact(p, p, p, p, 100, p, p, 61, 1, 8, 100, 1, None) == -2   # 200-byte rows
+    assert lib.dtv_kv_compact(None, p, p, p, 100, p, p, 61, 1, 8, 128, 1, None) == -1
+
+
+@pytest.mark.parametrize("acc,nd,gamma", [([3, 0, 5], 6, 0.0), ([2, 4], 8, 0.1), ([0] * 5, 0, 0.3),
+                                          ([7, 1, 2, 9, 0, 3], 17, 0.02)])
+def test_bookkeeping_matches_oracle(lib, acc, nd, gamma):
+    from draft_tree_verification_build_amd.api import bookkeeping
+    got = bookkeeping(acc, nd, gamma)
+    ref = obook.bookkeeping(acc, nd, gamma)
+    assert got["E_A"] == ref["E_A"] and got["eta"] == ref["eta"] and got["L"] == ref["L"]
+    assert got["speedup"] == pytest.approx(ref["speedup"], rel=1e-15)
+
+
+def test_bookkeeping_rejects_bad_counts(lib):
+    a = np.array([1, -1], dtype=np.int32)
+    out = np.zeros(4)
+    assert lib.dtv_bookkeeping(a.ctypes.data, 2, 3, 0.1, out.ctypes.data) == -1
+    assert lib.dtv_bookkeeping(a.ctypes.data, 0, 3, 0.1, out.ctypes.data) == -1
