@@ -143,6 +143,20 @@ def tree_build_talon(tree: Tree, draft: torch.Tensor, B: int, K: int, alpha: flo
           buf.data_ptr(), buf.numel(), _stream(stream))
 
 
+def tree_build_spine(tree: Tree, spine: torch.Tensor, widths, draft: torch.Tensor, ws: Workspace,
+                     stream=None) -> None:
+    """spine [S][n_spine] int32 (device); widths: host ints per fork; draft [S][R][V] keyed by slot."""
+    import numpy as np
+    S, R, V = draft.shape
+    n_spine = spine.shape[1]
+    w = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    dt = _dtype_code(draft)
+    lib = _lib.load()
+    buf = ws.get("spine", lib.dtv_tree_build_spine_ws_bytes(S, int(w.size), int(w.max(initial=0)), V, dt))
+    _call("dtv_tree_build_spine", tree.c, S, _ptr(spine), n_spine, w.ctypes.data, int(w.size), _ptr(draft), dt,
+          R, V, buf.data_ptr(), buf.numel(), _stream(stream))
+
+
 def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, P_max: int,
               tree: Tree, ws: Workspace, scale: float | None = None, o: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
@@ -176,6 +190,27 @@ def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None
     buf = ws.get("verify_greedy", lib.dtv_tree_verify_greedy_ws_bytes(S, tree.n_cap, V, dt))
     _call("dtv_tree_verify_greedy", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
           _ptr(bonus), _ptr(amax), buf.data_ptr(), buf.numel(), _stream(stream))
+    return out
+
+
+def tree_verify_sample(tree: Tree, target: torch.Tensor, draft: torch.Tensor, u_acc: torch.Tensor,
+                       u_res: torch.Tensor, ws: Workspace, out=None, stream=None):
+    """target, draft [S][R][V]; u_acc, u_res [S][n_cap] (uint32 bits in an int32 tensor).
+    Returns (path [S][n_cap], path_len [S], bonus [S])."""
+    S, R, V = target.shape
+    dt = _dtype_code(target)
+    if _dtype_code(draft) != dt:
+        raise TypeError("target and draft must share a dtype")
+    dev = target.device
+    if out is None:
+        out = (torch.full((S, tree.n_cap), -1, dtype=torch.int32, device=dev),
+               torch.zeros(S, dtype=torch.int32, device=dev),
+               torch.zeros(S, dtype=torch.int32, device=dev))
+    path, plen, bonus = out[:3]
+    lib = _lib.load()
+    buf = ws.get("verify_sample", lib.dtv_tree_verify_sample_ws_bytes(S, tree.n_cap, V, dt))
+    _call("dtv_tree_verify_sample", tree.c, S, _ptr(target), _ptr(draft), dt, R, V, _ptr(u_acc), _ptr(u_res),
+          _ptr(path), _ptr(plen), _ptr(bonus), buf.data_ptr(), buf.numel(), _stream(stream))
     return out
 
 

@@ -131,6 +131,34 @@ TalonLayout talon_layout(void* ws, int S, int B, int K, int V, int dtype) {
   return L;
 }
 
+struct SpineLayout {
+  dtv::WsHeader* hdr;
+  dtv::ChunkStat* st;
+  float* cval;
+  int* cidx;
+  unsigned* tickets;
+  double* rlse;
+  float* rv;
+  int* ri;
+  size_t bytes;
+};
+SpineLayout spine_layout(void* ws, int S, int F, int K, int V, int dtype) {
+  const int nch = nch_of(V, dtype);
+  const size_t rows = static_cast<size_t>(S) * F;
+  Carver c(ws);
+  SpineLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.st = c.take<dtv::ChunkStat>(rows * nch);
+  L.cval = c.take<float>(rows * nch * K);
+  L.cidx = c.take<int>(rows * nch * K);
+  L.tickets = c.take<unsigned>(rows);
+  L.rlse = c.take<double>(rows);
+  L.rv = c.take<float>(rows * K);
+  L.ri = c.take<int>(rows * K);
+  L.bytes = c.off;
+  return L;
+}
+
 struct AttnPlan {
   int n_mtiles, n_split, kps;
 };
@@ -186,6 +214,30 @@ VerifyLayout verify_layout(void* ws, int S, int n_cap) {
   L.hdr = c.take<dtv::WsHeader>(1);
   L.best = c.take<unsigned long long>(static_cast<size_t>(S) * n_cap);
   L.tickets = c.take<unsigned>(S);
+  L.bytes = c.off;
+  return L;
+}
+
+struct SampleLayout {
+  dtv::WsHeader* hdr;
+  dtv::ChunkStat* st;
+  unsigned* rtick;
+  double* lse;
+  unsigned* stick;
+  double* pbuf;
+  size_t bytes;
+};
+SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
+  const int nch = nch_of(V, dtype);
+  const size_t rows = static_cast<size_t>(S) * n_cap * 2;
+  Carver c(ws);
+  SampleLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.st = c.take<dtv::ChunkStat>(rows * nch);
+  L.rtick = c.take<unsigned>(rows);
+  L.lse = c.take<double>(rows);
+  L.stick = c.take<unsigned>(S);
+  L.pbuf = c.take<double>(static_cast<size_t>(S) * 2 * V);
   L.bytes = c.off;
   return L;
 }
@@ -335,6 +387,70 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
   return launched(dtv::launch_talon(a, dtype == DTV_BF16 ? 1 : 0, grid, static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- GOOSE spine
+
+size_t dtv_tree_build_spine_ws_bytes(int32_t S, int32_t F, int32_t max_width, int32_t V, int dtype) {
+  if (S < 1 || F < 1 || max_width < 0 || V < 1 || !dtype_ok(dtype)) return 0;
+  return spine_layout(nullptr, S, F, max_width + 1, V, dtype).bytes;
+}
+
+int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, int32_t n_spine,
+                         const int32_t* widths_h, int32_t F, const void* draft, int dtype, int32_t R,
+                         int32_t V, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(draft != nullptr && widths_h != nullptr, DTV_EINVAL, "draft or widths_h is NULL");
+  REQUIRE(n_spine == 0 || spine != nullptr, DTV_EINVAL, "spine is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && n_spine >= 0 && V >= 1, DTV_EINVAL, "S=%d n_spine=%d V=%d", S, n_spine, V);
+  REQUIRE(F >= 1 && F <= dtv::kSpineMaxForks, DTV_EUNSUPPORTED, "F=%d outside 1..%d", F, dtv::kSpineMaxForks);
+  REQUIRE(F <= n_spine + 1, DTV_EINVAL, "forks must be the root or spine nodes (F=%d, n_spine=%d)", F, n_spine);
+  int total = 0, wmax = 0;
+  for (int f = 0; f < F; ++f) {
+    REQUIRE(widths_h[f] >= 0 && widths_h[f] <= 64, DTV_EUNSUPPORTED, "width[%d]=%d outside 0..64", f, widths_h[f]);
+    REQUIRE(widths_h[f] + (f < n_spine ? 1 : 0) <= V, DTV_EINVAL, "width[%d]=%d needs a larger vocabulary", f,
+            widths_h[f]);
+    total += widths_h[f];
+    wmax = widths_h[f] > wmax ? widths_h[f] : wmax;
+  }
+  const int N = 1 + n_spine + total;
+  REQUIRE(N <= tree->n_cap, DTV_ECAPACITY, "tree of %d nodes exceeds n_cap=%d", N, tree->n_cap);
+  REQUIRE(R >= F, DTV_EINVAL, "R=%d rows cannot key %d forks", R, F);
+  const int K = wmax + 1;
+  REQUIRE(nch_of(V, dtype) <= 32 && nch_of(V, dtype) * K <= 2048, DTV_EUNSUPPORTED,
+          "V=%d with width %d exceeds the merge capacity", V, wmax);
+  const SpineLayout L = spine_layout(ws, S, F, K, V, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  dtv::SpineArgs a;
+  memset(&a, 0, sizeof(a));
+  a.tree = tree_args(tree);
+  a.spine = spine;
+  a.draft = draft;
+  a.R = R;
+  a.V = V;
+  a.S = S;
+  a.n_spine = n_spine;
+  a.F = F;
+  a.K = K;
+  a.nch = nch_of(V, dtype);
+  a.n_nodes = N;
+  int off = 0;
+  for (int f = 0; f < F; ++f) {
+    a.width[f] = widths_h[f];
+    a.offset[f] = off;
+    off += widths_h[f];
+  }
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.cval = L.cval;
+  a.cidx = L.cidx;
+  a.tickets = L.tickets;
+  a.rlse = L.rlse;
+  a.rv = L.rv;
+  a.ri = L.ri;
+  return launched(dtv::launch_spine(a, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- attention
 
 size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv, int32_t D,
@@ -429,6 +545,44 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
   a.tickets = L.tickets;
   a.hdr = L.hdr;
   return launched(dtv::launch_verify_greedy(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- rejection sampling
+
+size_t dtv_tree_verify_sample_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype) {
+  if (S < 1 || n_cap < 1 || V < 1 || !dtype_ok(dtype)) return 0;
+  return sample_layout(nullptr, S, n_cap, V, dtype).bytes;
+}
+
+int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, const void* draft, int dtype,
+                           int32_t R, int32_t V, const uint32_t* u_acc, const uint32_t* u_res, int32_t* path,
+                           int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(target && draft && u_acc && u_res && path && path_len && bonus, DTV_EINVAL, "a pointer is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && R >= 1 && V >= 1, DTV_EINVAL, "S=%d R=%d V=%d", S, R, V);
+  const SampleLayout L = sample_layout(ws, S, tree->n_cap, V, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  dtv::SampleArgs a;
+  a.tree = tree_args(tree);
+  a.target = target;
+  a.draft = draft;
+  a.R = R;
+  a.V = V;
+  a.nch = nch_of(V, dtype);
+  a.u_acc = u_acc;
+  a.u_res = u_res;
+  a.path = path;
+  a.path_len = path_len;
+  a.bonus = bonus;
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.rtick = L.rtick;
+  a.lse = L.lse;
+  a.stick = L.stick;
+  a.pbuf = L.pbuf;
+  return launched(dtv::launch_verify_sample(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- compaction

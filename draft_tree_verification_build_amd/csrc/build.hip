@@ -291,6 +291,112 @@ __global__ __launch_bounds__(kBlock) void talon_kernel(TalonArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ GOOSE spine trees
+//
+// GOOSE page, section 2A: a deep chain of context-match tokens (the spine) with wide,
+// shallow branches forking at spine nodes. Slots 1..n_spine hold the spine (slot k has
+// parent k-1); fork f (slot f, the root or a spine node) then gets width[f] depth-1
+// branches, the most probable tokens of its draft row that are not its spine child's token,
+// in slots 1 + n_spine + offset[f] + j. The spine holds the lowest slots, which is what
+// lets a greedy walk that prefers low slots follow the spine first (section 2C).
+//
+// One workgroup per (sequence, fork, chunk of the fork's draft row); the workgroup that
+// completes a fork row merges its chunks and writes that fork's branch nodes. Branch
+// scores are log p_d(token | fork) (spine nodes carry no draft score).
+
+constexpr int kSpineMaxK = 65;
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void spine_kernel(SpineArgs a) {
+  __shared__ RowSmem rs;
+  __shared__ MergeSmem<kTalonMergeCap> ms;
+  __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * 128) > kCandCap ? pow2_at_least(kWaves * 128)
+                                                                              : kCandCap];
+  using Rw = RowT<DT>;
+  row_smem_init(rs);
+  __syncthreads();
+  const int nch = a.nch;
+  const int K = a.K;
+  const int cap = a.tree.n_cap;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int f = bid % a.F;
+  const int s = bid / a.F;
+  const size_t tb = static_cast<size_t>(s) * cap;
+  const int words = a.tree.words;
+
+  if (f == 0 && c == 0) {  // root and spine chain of sequence s
+    for (int k = threadIdx.x; k <= a.n_spine; k += kBlock) {
+      const size_t o = tb + k;
+      a.tree.parent[o] = k - 1;
+      a.tree.token[o] = (k == 0) ? -1 : a.spine[static_cast<size_t>(s) * a.n_spine + k - 1];
+      a.tree.depth[o] = k;
+      a.tree.row[o] = k;
+      a.tree.score[o] = 0.0;
+      uint64_t* an = a.tree.anc + o * words;
+      for (int w = 0; w < words; ++w) {  // bits 0..k
+        const int lo = w * 64;
+        const int nb = k + 1 - lo;
+        an[w] = nb <= 0 ? 0ull : (nb >= 64 ? ~0ull : ((1ull << nb) - 1ull));
+      }
+    }
+    if (threadIdx.x == 0) {
+      a.tree.n_nodes[s] = a.n_nodes;
+      a.tree.layers[s] = 1;
+    }
+  }
+  const int wf = a.width[f];
+  if (wf <= 0) return;
+  const int kf = wf + 1 < a.V ? wf + 1 : a.V;   // one spare for the skipped spine token
+  const char* row = static_cast<const char*>(a.draft) +
+                    (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
+  float x[Rw::E];
+  uint32_t key[Rw::E];
+  load_chunk<DT>(row, a.V, c, x, key);
+  const size_t rf = static_cast<size_t>(s) * a.F + f;
+  const size_t ci = rf * nch + c;
+  chunk_reduce<DT>(x, key, c, a.V, kf, &a.st[ci], a.cval + ci * K, a.cidx + ci * K, sortbuf, rs);
+  if (!last_arrival(&a.tickets[rf], nch, &rs.flag)) return;
+  // the chunk lists were written with stride K; merge with that stride, keep kf entries
+  const int n = row_merge(a.st + rf * nch, a.cval + rf * nch * K, a.cidx + rf * nch * K, nch, K,
+                          nullptr, nullptr, &a.rlse[rf], a.rv + rf * K, a.ri + rf * K, rs, ms);
+  if (threadIdx.x == 0) {
+    const double lse = ld_cc(&a.rlse[rf]);
+    const int skip = (f < a.n_spine) ? a.spine[static_cast<size_t>(s) * a.n_spine + f] : -1;
+    int j = 0;
+    for (int r = 0; r < n && r < kf && j < wf; ++r) {
+      const int tok = ld_cc(&a.ri[rf * K + r]);
+      if (tok == skip) continue;
+      const int slot = 1 + a.n_spine + a.offset[f] + j;
+      const size_t o = tb + slot;
+      a.tree.parent[o] = f;
+      a.tree.token[o] = tok;
+      a.tree.depth[o] = f + 1;
+      a.tree.row[o] = slot;
+      a.tree.score[o] = static_cast<double>(ld_cc(&a.rv[rf * K + r])) - lse;
+      uint64_t* an = a.tree.anc + o * words;
+      for (int w = 0; w < words; ++w) {  // bits 0..f plus the node itself
+        const int lo = w * 64;
+        const int nb = f + 1 - lo;
+        uint64_t bits = nb <= 0 ? 0ull : (nb >= 64 ? ~0ull : ((1ull << nb) - 1ull));
+        if ((slot >> 6) == w) bits |= 1ull << (slot & 63);
+        an[w] = bits;
+      }
+      ++j;
+    }
+  }
+}
+
+int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
+  const dim3 grid(a.S * a.F * a.nch);
+  if (dtype == 1)
+    hipLaunchKernelGGL(spine_kernel<1>, grid, dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(spine_kernel<0>, grid, dim3(kBlock), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st) {
   void* args[] = {const_cast<TalonArgs*>(&a)};
   hipError_t e;

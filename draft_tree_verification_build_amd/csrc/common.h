@@ -111,21 +111,30 @@ __device__ __forceinline__ T block_sum(T v, T* red) {
   return r;
 }
 
-// Exclusive prefix sum over the block in thread order; `scan` holds kBlock ints.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* scan, int* total) {
-  const int t = threadIdx.x;
-  scan[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kBlock; o <<= 1) {
-    int a = (t >= o) ? scan[t - o] : 0;
-    __syncthreads();
-    scan[t] += a;
-    __syncthreads();
+// Exclusive prefix sum over the block in thread order (wave scans, then wave offsets).
+// `wsum` is shared scratch of at least kWaves entries; *total receives the block sum.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  T inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
   }
-  int incl = scan[t];
-  *total = scan[kBlock - 1];
+  T exc = __shfl_up(inc, 1, 64);
+  if (lane == 0) exc = T(0);
+  if (lane == 63) wsum[w] = inc;
   __syncthreads();
-  return incl - v;
+  T before = T(0), tot = T(0);
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    if (q < w) before += wsum[q];
+    tot += wsum[q];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + exc;
 }
 
 // ---------------------------------------------------------------- cross-workgroup signalling

@@ -39,6 +39,25 @@ struct TalonArgs {
   int* rcnt;           // [S][B]
 };
 
+constexpr int kSpineMaxForks = 128;
+
+struct SpineArgs {
+  TreeArgs tree;
+  const int* spine;    // [S][n_spine]
+  const void* draft;
+  int R, V, S, n_spine, F, K, nch, n_nodes;
+  int width[kSpineMaxForks];
+  int offset[kSpineMaxForks];   // exclusive prefix of width
+  WsHeader* hdr;
+  ChunkStat* st;       // [S][F][nch]
+  float* cval;         // [S][F][nch][K]
+  int* cidx;
+  unsigned* tickets;   // [S][F]
+  double* rlse;        // [S][F]
+  float* rv;           // [S][F][K]
+  int* ri;
+};
+
 struct RowStatsArgs {
   const void* table;
   int R, V, K, nch;
@@ -87,6 +106,24 @@ struct VerifyArgs {
   WsHeader* hdr;
 };
 
+struct SampleArgs {
+  TreeArgs tree;
+  const void* target;
+  const void* draft;
+  int R, V, nch;
+  const uint32_t* u_acc;     // [S][n_cap]
+  const uint32_t* u_res;     // [S][n_cap]
+  int* path;
+  int* path_len;
+  int* bonus;
+  WsHeader* hdr;
+  ChunkStat* st;             // [S][n_cap][2][nch]
+  unsigned* rtick;           // [S][n_cap][2]
+  double* lse;               // [S][n_cap][2]  (0: target, 1: draft)
+  unsigned* stick;           // [S]
+  double* pbuf;              // [S][2][V] residual distributions
+};
+
 struct CompactArgs {
   void* k;
   void* v;
@@ -101,9 +138,11 @@ struct CompactArgs {
 int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st);
 int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st);
 int talon_max_grid(int dtype);
+int launch_spine(const SpineArgs& a, int dtype, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
+int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st);
 int launch_compact(const CompactArgs& a, hipStream_t st);
 
 }  // namespace dtv

@@ -49,12 +49,18 @@ class DraftTreeStep:
             self.tree.n_nodes.fill_(self.N)
         else:
             self.tree = api.Tree(self.S, self.N, dev)
+        if cfg.build == "spine":
+            self.spine = torch.from_numpy(np.asarray(wl.spine, dtype=np.int32)).to(dev)
+            self.widths = np.asarray(wl.widths, dtype=np.int32)
         self.o = torch.zeros_like(self.q)
         self.verify_out = (torch.full((self.S, self.N), -1, dtype=torch.int32, device=dev),
                            torch.zeros(self.S, dtype=torch.int32, device=dev),
                            torch.zeros(self.S, dtype=torch.int32, device=dev),
                            torch.zeros((self.S, self.N), dtype=torch.int32, device=dev))
         self.P_new = torch.zeros_like(self.P)
+        if cfg.verify == "sample":
+            self.u_acc = torch.from_numpy(np.asarray(wl.u_acc, dtype=np.uint32).view(np.int32)).to(dev)
+            self.u_res = torch.from_numpy(np.asarray(wl.u_res, dtype=np.uint32).view(np.int32)).to(dev)
 
     # -- stages ---------------------------------------------------------------------
     def build(self, stream=None):
@@ -63,6 +69,8 @@ class DraftTreeStep:
             api.tree_build_given(self.tree, self.ws, stream=stream)
         elif cfg.build == "talon":
             api.tree_build_talon(self.tree, self.draft, cfg.B, cfg.K, cfg.alpha, self.ws, stream=stream)
+        elif cfg.build == "spine":
+            api.tree_build_spine(self.tree, self.spine, self.widths, self.draft, self.ws, stream=stream)
         else:
             raise NotImplementedError(f"build mode {cfg.build!r} is not built yet")
 
@@ -71,9 +79,11 @@ class DraftTreeStep:
                       stream=stream)
 
     def verify(self, stream=None):
-        if self.cfg.verify != "greedy":
-            raise NotImplementedError(f"verification mode {self.cfg.verify!r} is not built yet")
-        api.tree_verify_greedy(self.tree, self.target, self.ws, out=self.verify_out, stream=stream)
+        if self.cfg.verify == "greedy":
+            api.tree_verify_greedy(self.tree, self.target, self.ws, out=self.verify_out, stream=stream)
+        else:
+            api.tree_verify_sample(self.tree, self.target, self.draft, self.u_acc, self.u_res, self.ws,
+                                   out=self.verify_out, stream=stream)
 
     def compact(self, stream=None):
         path, plen = self.verify_out[0], self.verify_out[1]

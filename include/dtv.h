@@ -125,6 +125,24 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
                          void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Tree build: GOOSE anisotropic spine tree (GOOSE page, sections 2A and 2C).
+ *
+ * A deep chain of context-match tokens with shallow, wide branches at its nodes:
+ * slots 1..n_spine hold spine[s][0..n_spine) as a chain (slot k has parent k-1); forks
+ * are slots 0..F-1 (the root and the first spine nodes, F <= n_spine + 1), and fork f gets
+ * widths_h[f] depth-1 branch nodes whose tokens are the most probable tokens of draft row
+ * f that differ from the token of f's spine child (slot f+1), in slots
+ * 1 + n_spine + sum(widths_h[0..f)) + j, j in rank order. The spine holds the lowest
+ * slots, so a greedy walk that prefers low slots follows the spine first. Branch scores
+ * are log p_d(token | fork); spine nodes score 0. spine is `[S][n_spine]` (device);
+ * widths_h is a host array of F entries in 0..64; draft is `[S][R][V]` keyed by slot.
+ */
+size_t dtv_tree_build_spine_ws_bytes(int32_t S, int32_t F, int32_t max_width, int32_t V, int dtype);
+int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, int32_t n_spine,
+                         const int32_t* widths_h, int32_t F, const void* draft, int dtype, int32_t R,
+                         int32_t V, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Tree attention (OPT-Tree summary, section 2; concept page, "Why it is a win").
  *
  * For node i of sequence s and query head h (KV head kv = h / (Hq / Hkv)):
@@ -156,6 +174,25 @@ size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int 
 int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype,
                            int32_t R, int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
                            int32_t* argmax_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Rejection-sampling verification (concept page, "The protocol", steps 3-4).
+ *
+ * The chain rule of the page, applied to a tree: starting at the root, with
+ * p = softmax(target row of v) and q = softmax(draft row of v) (rows row[v] of the
+ * `[S][R][V]` tables; temperature 1), the children c of v are tried in slot order with
+ * u = (u_acc[s][c] + 1/2) 2^-32: c is accepted when q(x_c) > 0 and u < p(x_c)/q(x_c), or
+ * when q(x_c) = 0 < p(x_c); after each rejection p <- (p - q)+ / sum (p - q)+ (kept if the
+ * sum is 0). The walk moves to the accepted child; when no child is accepted, or v is a
+ * leaf, the bonus token is the smallest k with sum_{j<=k} p_j > u * sum p (ascending
+ * float64 prefix sums, u from u_res[s][v]). Outputs as dtv_tree_verify_greedy. Decisions
+ * are taken in float64; the result depends only on the inputs and the uniforms.
+ */
+size_t dtv_tree_verify_sample_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype);
+int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, const void* draft,
+                           int dtype, int32_t R, int32_t V, const uint32_t* u_acc, const uint32_t* u_res,
+                           int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* ---------------------------------------------------------------------------------
  * KV compaction (concept page, "The protocol", step 4: append the accepted tokens).

@@ -283,3 +283,130 @@ def test_step_end_to_end(name, seed, ov, planted):
     assert int(step.P_new[0]) == res["P_new"]
     kk = step.k.view(torch.int16).cpu().numpy().view(np.uint16) if cfg.dtype == "bf16" else step.k.cpu().numpy()
     np.testing.assert_array_equal(kk[0], res["k"])
+
+
+SPINE_CASES = [
+    ("c3_goose_spine", 3, {"P": 16}),
+    ("c3_goose_spine", 34, {"P": 16, "V": 700, "spine_p": 0.9}),
+    ("c3_goose_spine", 35, {"P": 16, "V": 5000, "n_spine": 10, "n_forks": 11, "fork_width": 9, "S": 2}),
+    ("c3_goose_spine", 36, {"P": 16, "V": 900, "dtype": "f32", "n_spine": 5, "n_forks": 3, "fork_width": 2}),
+    ("c3_goose_spine", 37, {"P": 16, "V": 64, "n_spine": 70, "n_forks": 71, "fork_width": 1}),
+]
+
+
+@pytest.mark.parametrize("name,seed,ov", SPINE_CASES)
+def test_spine_build(name, seed, ov):
+    need_gpu()
+    wl = make_workload(name, seed, **ov)
+    cfg = wl.cfg
+    tree = dtv.Tree(cfg.S, cfg.N, DEV)
+    ws = dtv.Workspace(DEV)
+    dtv.tree_build_spine(tree, torch.from_numpy(wl.spine.astype(np.int32)).to(DEV), wl.widths,
+                         to_device(wl.draft, cfg.dtype, DEV), ws)
+    assert ws.status("spine") == 0
+    g = tree_to_numpy(tree)
+    for s in range(cfg.S):
+        assert_tree_equal(g, s, ostep.build_tree(wl, s), tree.words)
+
+
+def _upload_tree_with_rows(otrees, n_cap):
+    S = len(otrees)
+    par = np.full((S, n_cap), -1, dtype=np.int32)
+    tok = np.full((S, n_cap), -1, dtype=np.int32)
+    rows = np.zeros((S, n_cap), dtype=np.int32)
+    for s, t in enumerate(otrees):
+        par[s, :t.N] = t.parent
+        tok[s, :t.N] = t.token
+        rows[s, :t.N] = t.row
+    tree = dtv.Tree(S, n_cap, DEV, parent=torch.from_numpy(par).to(DEV), token=torch.from_numpy(tok).to(DEV))
+    tree.n_nodes.copy_(torch.tensor([t.N for t in otrees], dtype=torch.int32))
+    ws = dtv.Workspace(DEV)
+    dtv.tree_build_given(tree, ws)
+    tree.row.copy_(torch.from_numpy(rows))
+    torch.cuda.synchronize()
+    return tree
+
+
+SAMPLE_CASES = [
+    ("c5_batched_llama2_70b", 5, {"P": 16}),
+    ("c5_batched_llama2_70b", 51, {"P": 16, "V": 300, "S": 3}),
+    ("c5_batched_llama2_70b", 52, {"P": 16, "V": 64, "S": 4, "B": 40, "max_depth": 1}),   # stars: many rejections
+    ("c5_batched_llama2_70b", 53, {"P": 16, "V": 5000, "S": 2, "B": 200, "max_depth": 60}),
+    ("c5_batched_llama2_70b", 54, {"P": 16, "V": 1000, "S": 2, "dtype": "f32", "noise_sigma": 0.0}),  # p = q
+    ("c1_tiny", 55, {"verify": "sample", "B": 30}),
+]
+
+
+@pytest.mark.parametrize("name,seed,ov", SAMPLE_CASES)
+def test_verify_sample(name, seed, ov):
+    need_gpu()
+    wl = make_workload(name, seed, **ov)
+    cfg = wl.cfg
+    otrees = [ostep.build_tree(wl, s) for s in range(cfg.S)]
+    tree = _upload_tree_with_rows(otrees, cfg.N)
+    ws = dtv.Workspace(DEV)
+    ua = torch.from_numpy(wl.u_acc.view(np.int32)).to(DEV)
+    ur = torch.from_numpy(wl.u_res.view(np.int32)).to(DEV)
+    tgt = to_device(wl.target, cfg.dtype, DEV)
+    drf = to_device(wl.draft, cfg.dtype, DEV)
+    for rep in range(2):   # the workspace is reused by the second call
+        path, plen, bonus = dtv.tree_verify_sample(tree, tgt, drf, ua, ur, ws)
+        assert ws.status("verify_sample") == 0
+        for s in range(cfg.S):
+            t = otrees[s]
+            ref = overify.sample(t.parent, t.token, t.row, lambda r: orows.decode(wl.target[s, r], cfg.dtype),
+                                 lambda r: orows.decode(wl.draft[s, r], cfg.dtype), wl.u_acc[s], wl.u_res[s])
+            A = int(plen[s]) - 1
+            assert A == ref["A"], (s, A, ref["A"])
+            assert list(path[s, :A + 1].cpu().numpy()) == ref["path"]
+            assert int(bonus[s]) == ref["bonus"], (s, int(bonus[s]), ref["bonus"])
+
+
+def test_verify_sample_opt_tree():
+    """Rejection sampling on an OPT-Tree-shaped tree (rows keyed by build identity)."""
+    need_gpu()
+    wl = make_workload("c4_opt_llama2_7b", 4, P=16, V=2000, n=64, max_layers=4)
+    cfg = wl.cfg
+    ot = ostep.build_tree(wl, 0)
+    tree = _upload_tree_with_rows([ot], cfg.N)
+    ws = dtv.Workspace(DEV)
+    path, plen, bonus = dtv.tree_verify_sample(
+        tree, to_device(wl.target, cfg.dtype, DEV), to_device(wl.draft, cfg.dtype, DEV),
+        torch.from_numpy(wl.u_acc.view(np.int32)).to(DEV), torch.from_numpy(wl.u_res.view(np.int32)).to(DEV), ws)
+    ref = overify.sample(ot.parent, ot.token, ot.row, lambda r: orows.decode(wl.target[0, r], cfg.dtype),
+                         lambda r: orows.decode(wl.draft[0, r], cfg.dtype), wl.u_acc[0], wl.u_res[0])
+    A = int(plen[0]) - 1
+    assert A == ref["A"] and list(path[0, :A + 1].cpu().numpy()) == ref["path"] and int(bonus[0]) == ref["bonus"]
+
+
+@pytest.mark.parametrize("name,seed,ov", [
+    ("c3_goose_spine", 3, {}),
+    ("c5_batched_llama2_70b", 5, {}),
+])
+def test_step_end_to_end_all_sequences(name, seed, ov):
+    need_gpu()
+    wl = make_workload(name, seed, **ov)
+    cfg = wl.cfg
+    step = DraftTreeStep(wl, DEV)
+    step.run()
+    st = step.ws_status()
+    assert all(v == 0 for v in st.values()), st
+    res = ostep.run_step(wl, with_attention=False)
+    g = tree_to_numpy(step.tree)
+    path, plen, bonus, _ = [t.cpu() for t in step.verify_out]
+    kk = step.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vv = step.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for s in range(cfg.S):
+        r = res[s]
+        assert_tree_equal(g, s, r["tree"], step.tree.words, check_scores=(cfg.build != "given"))
+        A = int(plen[s]) - 1
+        assert A == r["verify"]["A"] and list(path[s, :A + 1].numpy()) == r["verify"]["path"]
+        assert int(bonus[s]) == r["verify"]["bonus"]
+        assert int(step.P_new[s]) == r["P_new"]
+        np.testing.assert_array_equal(kk[s], r["k"])
+        np.testing.assert_array_equal(vv[s], r["v"])
+
+
+def test_attention_c3_sampled():
+    need_gpu()
+    _attn_check(make_workload("c3_goose_spine", 3), pairs_per_seq=40)
