@@ -157,6 +157,17 @@ def tree_build_spine(tree: Tree, spine: torch.Tensor, widths, draft: torch.Tenso
           R, V, buf.data_ptr(), buf.numel(), _stream(stream))
 
 
+def tree_build_opt(tree: Tree, draft: torch.Tensor, n: int, delta: float, max_layers: int, ws: Workspace,
+                   stream=None) -> None:
+    """draft [S][R][V]: row 0 is the root's, row 1+(l-1)*n+p the one of layer l's node p."""
+    S, R, V = draft.shape
+    dt = _dtype_code(draft)
+    lib = _lib.load()
+    buf = ws.get("opt", lib.dtv_tree_build_opt_ws_bytes(S, n, V, max_layers, dt))
+    _call("dtv_tree_build_opt", tree.c, S, _ptr(draft), dt, R, V, int(n), float(delta), int(max_layers),
+          buf.data_ptr(), buf.numel(), _stream(stream))
+
+
 def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, P_max: int,
               tree: Tree, ws: Workspace, scale: float | None = None, o: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:

@@ -159,6 +159,64 @@ SpineLayout spine_layout(void* ws, int S, int F, int K, int V, int dtype) {
   return L;
 }
 
+struct OptLayout {
+  dtv::WsHeader* hdr;
+  dtv::ChunkStat* st;
+  float* cval;
+  int* cidx;
+  unsigned* tickets;
+  double* rlse;
+  float* rv;
+  int* ri;
+  int* rcnt;
+  double* lo;
+  unsigned* ccount;
+  void* cand;
+  double* lscore;
+  int* lparent;
+  int* ltoken;
+  double* bscore;
+  int* blayer;
+  int* bpos;
+  int* bcount;
+  double* Eprev;
+  int* done;
+  int* nlayers;
+  size_t bytes;
+};
+constexpr int kOptCandCap = 4096;
+OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
+  const int nch = nch_of(V, dtype);
+  const size_t Kmax = static_cast<size_t>(n < V ? n : V);
+  const size_t rows = static_cast<size_t>(S) * n;
+  Carver c(ws);
+  OptLayout L;
+  L.hdr = c.take<dtv::WsHeader>(1);
+  L.st = c.take<dtv::ChunkStat>(rows * nch);
+  L.cval = c.take<float>(rows * nch * Kmax);
+  L.cidx = c.take<int>(rows * nch * Kmax);
+  L.tickets = c.take<unsigned>(rows);
+  L.rlse = c.take<double>(rows);
+  L.rv = c.take<float>(rows * Kmax);
+  L.ri = c.take<int>(rows * Kmax);
+  L.rcnt = c.take<int>(rows);
+  L.lo = c.take<double>(S);
+  L.ccount = c.take<unsigned>(S);
+  L.cand = c.take<char>(static_cast<size_t>(S) * kOptCandCap * 16);
+  L.lscore = c.take<double>(rows * max_layers);
+  L.lparent = c.take<int>(rows * max_layers);
+  L.ltoken = c.take<int>(rows * max_layers);
+  L.bscore = c.take<double>(rows);
+  L.blayer = c.take<int>(rows);
+  L.bpos = c.take<int>(rows);
+  L.bcount = c.take<int>(S);
+  L.Eprev = c.take<double>(S);
+  L.done = c.take<int>(S);
+  L.nlayers = c.take<int>(S);
+  L.bytes = c.off;
+  return L;
+}
+
 struct AttnPlan {
   int n_mtiles, n_split, kps;
 };
@@ -449,6 +507,88 @@ int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, 
   a.rv = L.rv;
   a.ri = L.ri;
   return launched(dtv::launch_spine(a, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- OPT-Tree
+
+size_t dtv_tree_build_opt_ws_bytes(int32_t S, int32_t n, int32_t V, int32_t max_layers, int dtype) {
+  if (S < 1 || n < 1 || V < 1 || max_layers < 1 || !dtype_ok(dtype)) return 0;
+  return opt_layout(nullptr, S, n, V, max_layers, dtype).bytes;
+}
+
+int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int dtype, int32_t R, int32_t V,
+                       int32_t n, double delta, int32_t max_layers, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(draft != nullptr, DTV_EINVAL, "draft is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && V >= 1, DTV_EINVAL, "S=%d V=%d", S, V);
+  REQUIRE(n >= 1 && n + 1 <= tree->n_cap, DTV_ECAPACITY, "n+1=%d exceeds n_cap=%d", n + 1, tree->n_cap);
+  REQUIRE(n <= 1023, DTV_EUNSUPPORTED, "n=%d exceeds 1023", n);
+  REQUIRE(max_layers >= 1 && max_layers <= 64, DTV_EUNSUPPORTED, "max_layers=%d outside 1..64", max_layers);
+  REQUIRE(delta >= 0.0 && isfinite(delta), DTV_EINVAL, "delta=%g", delta);
+  REQUIRE(static_cast<long>(R) >= 1 + static_cast<long>(max_layers - 1) * n, DTV_EINVAL,
+          "R=%d rows cannot key %d layers of %d nodes", R, max_layers, n);
+  const int nch = nch_of(V, dtype);
+  const int Kmax = n < V ? n : V;
+  REQUIRE(nch <= 64 && static_cast<long>(nch) * Kmax <= 8192, DTV_EUNSUPPORTED,
+          "V=%d with n=%d exceeds the merge capacity", V, n);
+  const OptLayout L = opt_layout(ws, S, n, V, max_layers, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dtv::OptArgs a;
+  memset(&a, 0, sizeof(a));
+  a.tree = tree_args(tree);
+  a.draft = draft;
+  a.R = R;
+  a.V = V;
+  a.S = S;
+  a.n = n;
+  a.nch = nch;
+  a.max_layers = max_layers;
+  a.delta = delta;
+  a.Wcap = n;
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.cval = L.cval;
+  a.cidx = L.cidx;
+  a.tickets = L.tickets;
+  a.rlse = L.rlse;
+  a.rv = L.rv;
+  a.ri = L.ri;
+  a.rcnt = L.rcnt;
+  a.lo = L.lo;
+  a.ccount = L.ccount;
+  a.ccap = kOptCandCap;
+  a.cand = static_cast<dtv::OptCand*>(L.cand);
+  a.lscore = L.lscore;
+  a.lparent = L.lparent;
+  a.ltoken = L.ltoken;
+  a.bscore = L.bscore;
+  a.blayer = L.blayer;
+  a.bpos = L.bpos;
+  a.bcount = L.bcount;
+  a.Eprev = L.Eprev;
+  a.done = L.done;
+  a.nlayers = L.nlayers;
+  if (dtv::launch_opt_init(a, st)) return launched(-1);
+  // the frontier width of every layer follows from n and V alone: layer 1 expands the
+  // root; layer l keeps min(n, W_l * min(n, V)) nodes, which are layer l+1's frontier
+  long W = 1;
+  const long per_row = n < V ? n : V;
+  for (int layer = 1; layer <= max_layers; ++layer) {
+    a.layer = layer;
+    a.W = static_cast<int>(W);
+    const long need = (n + W - 1) / W;                 // reported per row so that W*m >= n
+    long K = need > 8 ? need : 8;
+    if (K > per_row) K = per_row;
+    a.K = static_cast<int>(K);
+    if (dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st)) return launched(-1);
+    long kept = W * per_row;
+    if (kept > n) kept = n;
+    W = kept;
+  }
+  return launched(dtv::launch_opt_finalize(a, st));
 }
 
 // ---------------------------------------------------------------- attention

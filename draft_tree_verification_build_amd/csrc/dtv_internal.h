@@ -58,6 +58,40 @@ struct SpineArgs {
   int* ri;
 };
 
+struct OptCand;
+
+struct OptArgs {
+  TreeArgs tree;
+  const void* draft;
+  int R, V, S, n, nch, max_layers;
+  double delta;
+  // per layer (set by the host before each layer's launches)
+  int layer, W, Wcap, K;
+  WsHeader* hdr;
+  ChunkStat* st;          // [S][Wcap][nch]
+  float* cval;            // [S][Wcap][nch][Kmax]
+  int* cidx;
+  unsigned* tickets;      // [S][Wcap]
+  double* rlse;           // [S][Wcap]
+  float* rv;              // [S][Wcap][Kmax]
+  int* ri;
+  int* rcnt;              // [S][Wcap]
+  double* lo;             // [S]
+  unsigned* ccount;       // [S]
+  int ccap;
+  OptCand* cand;          // [S][ccap]
+  double* lscore;         // [S][max_layers][n] per layer, frontier order
+  int* lparent;           // parent's frontier position in the previous layer
+  int* ltoken;
+  double* bscore;         // [S][n] best n so far: score desc, layer asc, position asc
+  int* blayer;
+  int* bpos;
+  int* bcount;            // [S]
+  double* Eprev;          // [S]
+  int* done;              // [S]
+  int* nlayers;           // [S]
+};
+
 struct RowStatsArgs {
   const void* table;
   int R, V, K, nch;
@@ -139,6 +173,9 @@ int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st);
 int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st);
 int talon_max_grid(int dtype);
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st);
+int launch_opt_init(const OptArgs& a, hipStream_t st);
+int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
+int launch_opt_finalize(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);

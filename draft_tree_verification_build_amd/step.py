@@ -69,6 +69,8 @@ class DraftTreeStep:
             api.tree_build_given(self.tree, self.ws, stream=stream)
         elif cfg.build == "talon":
             api.tree_build_talon(self.tree, self.draft, cfg.B, cfg.K, cfg.alpha, self.ws, stream=stream)
+        elif cfg.build == "opt":
+            api.tree_build_opt(self.tree, self.draft, cfg.n, cfg.delta, cfg.max_layers, self.ws, stream=stream)
         elif cfg.build == "spine":
             api.tree_build_spine(self.tree, self.spine, self.widths, self.draft, self.ws, stream=stream)
         else:

@@ -143,6 +143,27 @@ int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, 
                          int32_t V, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Tree build: OPT-Tree greedy expected-acceptance maximisation (OPT-Tree summary, sec. 3).
+ *
+ * Layer by layer, every frontier node proposes its children with score = its score +
+ * log p_d(token | node) (a float64 sum of logs); the layer keeps the n best candidates
+ * (ties: lower frontier position, then lower rank in the row), which become the next
+ * frontier, ordered by (parent position, rank). After layer l, E_l = sum of exp(score)
+ * over the best n nodes of all layers so far (ties: earlier layer, then position); the
+ * drafting stops when E_l - E_{l-1} < delta (E_0 = 0) or after max_layers layers. The
+ * tree is the best n nodes (root-closed, since a child never scores above its parent),
+ * numbered by (layer, position). Row identity: the node at position p of layer l uses
+ * row 1 + (l-1)*n + p of `draft` (`[S][R][V]`, R >= 1 + (max_layers-1)*n + ...); the root
+ * uses row 0. tree.row receives these identities (the target rows of verification).
+ * Limits: n <= 1023, n < n_cap, max_layers <= 64; more than 4096 candidates within the
+ * selection bound of one layer (extreme ties) is reported as DTV_ECAPACITY.
+ */
+size_t dtv_tree_build_opt_ws_bytes(int32_t S, int32_t n, int32_t V, int32_t max_layers, int dtype);
+int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int dtype, int32_t R,
+                       int32_t V, int32_t n, double delta, int32_t max_layers, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Tree attention (OPT-Tree summary, section 2; concept page, "Why it is a win").
  *
  * For node i of sequence s and query head h (KV head kv = h / (Hq / Hkv)):

@@ -410,3 +410,55 @@ def test_step_end_to_end_all_sequences(name, seed, ov):
 def test_attention_c3_sampled():
     need_gpu()
     _attn_check(make_workload("c3_goose_spine", 3), pairs_per_seq=40)
+
+
+OPT_CASES = [
+    ("c4_opt_llama2_7b", 4, {"P": 16}),
+    ("c4_opt_llama2_7b", 41, {"P": 16, "V": 2000, "n": 64, "max_layers": 5}),
+    ("c4_opt_llama2_7b", 42, {"P": 16, "V": 50, "n": 100, "max_layers": 4, "delta": 0.0}),
+    ("c4_opt_llama2_7b", 43, {"P": 16, "V": 3, "n": 20, "max_layers": 4, "delta": 0.0}),
+    ("c4_opt_llama2_7b", 44, {"P": 16, "V": 3000, "n": 40, "max_layers": 3, "dtype": "f32", "S": 2}),
+    ("c4_opt_llama2_7b", 45, {"P": 16, "V": 9000, "n": 200, "max_layers": 6, "delta": 0.05, "draft_sigma": 2.0}),
+]
+
+
+@pytest.mark.parametrize("name,seed,ov", OPT_CASES)
+def test_opt_build(name, seed, ov):
+    need_gpu()
+    wl = make_workload(name, seed, **ov)
+    cfg = wl.cfg
+    tree = dtv.Tree(cfg.S, cfg.N, DEV)
+    ws = dtv.Workspace(DEV)
+    d = to_device(wl.draft, cfg.dtype, DEV)
+    for rep in range(2):   # the workspace is reused by the second call
+        dtv.tree_build_opt(tree, d, cfg.n, cfg.delta, cfg.max_layers, ws)
+        assert ws.status("opt") == 0
+        g = tree_to_numpy(tree)
+        for s in range(cfg.S):
+            ot = ostep.build_tree(wl, s)
+            assert_tree_equal(g, s, ot, tree.words)
+            assert int(g["layers"][s]) == ot.layers
+
+
+def test_attention_c4_sampled():
+    need_gpu()
+    _attn_check(make_workload("c4_opt_llama2_7b", 4), pairs_per_seq=40)
+
+
+def test_step_end_to_end_c4():
+    need_gpu()
+    wl = make_workload("c4_opt_llama2_7b", 4)
+    step = DraftTreeStep(wl, DEV)
+    step.run()
+    st = step.ws_status()
+    assert all(v == 0 for v in st.values()), st
+    r = ostep.run_step(wl, with_attention=False)[0]
+    g = tree_to_numpy(step.tree)
+    assert_tree_equal(g, 0, r["tree"], step.tree.words)
+    path, plen, bonus, _ = [t.cpu() for t in step.verify_out]
+    A = int(plen[0]) - 1
+    assert A == r["verify"]["A"] and list(path[0, :A + 1].numpy()) == r["verify"]["path"]
+    assert int(bonus[0]) == r["verify"]["bonus"]
+    assert int(step.P_new[0]) == r["P_new"]
+    kk = step.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(kk[0], r["k"])
