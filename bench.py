@@ -42,7 +42,14 @@ def parse():
 
 
 def algorithmic_work(step, wl):
-    """Bytes (and flops) each stage must move/compute for this step, from the built tree."""
+    """Bytes (and flops) each stage must move/compute for this step, from the built tree.
+
+    Build: every draft row the builder expands, read once. Attention: prefix K/V once per
+    KV head, tree K/V, Q in and O out; flops 4*Hq*D per visible (query, key) pair. Verify:
+    greedy reads each node's target row once; sampling reads each node's target and draft
+    rows once (residual passes come on top). Compaction: K and V rows of the path, read and
+    written once.
+    """
     import numpy as np
     cfg = wl.cfg
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -53,17 +60,27 @@ def algorithmic_work(step, wl):
     plen = step.verify_out[1].cpu().numpy()
     out = {"build": {"bytes": 0.0}, "attention": {"bytes": 0.0, "flops": 0.0},
            "verify": {"bytes": 0.0}, "compact": {"bytes": 0.0}}
+    row = cfg.V * esz
     for s in range(cfg.S):
         N = int(n_nodes[s])
         P = int(wl.P[s])
         if cfg.build == "talon":
-            rows = int(np.sum(depth[s, :N] < int(layers[s])))  # nodes whose rows were expanded
-            out["build"]["bytes"] += rows * cfg.V * esz
+            out["build"]["bytes"] += int(np.sum(depth[s, :N] < int(layers[s]))) * row
+        elif cfg.build == "spine":
+            out["build"]["bytes"] += int(np.sum(np.asarray(wl.widths) > 0)) * row
+        elif cfg.build == "opt":
+            W, rows = 1, 0
+            for _ in range(int(layers[s])):
+                rows += W
+                W = min(cfg.n, W * min(cfg.n, cfg.V))
+            out["build"]["bytes"] += rows * row
+        else:  # given shape: parents and masks only
+            out["build"]["bytes"] += N * (3 * 4 + 8 + 8 * step.tree.words)
         vis = sum(bin(int(w)).count("1") for w in anc[s, :N].ravel())
         out["attention"]["bytes"] += (2 * P * cfg.Hkv * cfg.D + 2 * N * cfg.Hkv * cfg.D
                                       + 2 * N * cfg.Hq * cfg.D) * esz
         out["attention"]["flops"] += 4.0 * cfg.Hq * cfg.D * (N * P + vis)
-        out["verify"]["bytes"] += N * cfg.V * esz
+        out["verify"]["bytes"] += N * row * (1 if cfg.verify == "greedy" else 2)
         out["compact"]["bytes"] += 4 * int(plen[s]) * cfg.Hkv * cfg.D * esz
     return out
 

@@ -218,18 +218,32 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
 }
 
 struct AttnPlan {
-  int n_mtiles, n_split, kps;
+  int wide, n_mtiles, n_split, kps, mcap;
 };
-// Splits each (sequence, KV head, 128-row tile) over enough key ranges to give the
-// 256 compute units about two workgroups each; ranges are multiples of 64 keys.
-AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max) {
+// Query rows of a KV head (GQA heads packed, M = g * n_cap). Small row counts use
+// 128-row tiles (one 32-row group per wave); from 256 rows on, attn_wide_kernel gives
+// each wave two groups and spreads the ceil(M/32) groups evenly over ceil(groups/8)
+// tiles. Key ranges are split so the 256 compute units see about two workgroups each;
+// ranges are multiples of 64 keys and no shorter than `min_keys`.
+AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int dtype) {
   AttnPlan p;
   const int g = Hq / Hkv;
-  p.n_mtiles = (g * n_cap + 127) / 128;
-  const int tiles = S * Hkv * p.n_mtiles;
+  const int M = g * n_cap;
   const int T = P_max + n_cap;
+  p.wide = (dtype == DTV_BF16 && M >= 256) ? 1 : 0;
+  int min_keys = 256;
+  if (p.wide) {
+    const int G = (M + 31) / 32;
+    p.n_mtiles = (G + 7) / 8;
+    p.mcap = G * 32;
+    min_keys = 512;
+  } else {
+    p.n_mtiles = (M + 127) / 128;
+    p.mcap = p.n_mtiles * 128;
+  }
+  const int tiles = S * Hkv * p.n_mtiles;
   int want = (512 + tiles - 1) / tiles;
-  const int max_split = (T + 255) / 256;
+  const int max_split = (T + min_keys - 1) / min_keys;
   if (want > max_split) want = max_split;
   if (want > 32) want = 32;
   if (want < 1) want = 1;
@@ -249,7 +263,7 @@ struct AttnLayout {
 };
 AttnLayout attn_layout(void* ws, int S, int Hkv, int D, const AttnPlan& p) {
   const size_t tiles = static_cast<size_t>(S) * Hkv * p.n_mtiles;
-  const size_t np = p.n_split > 1 ? tiles * p.n_split * 128 : 0;
+  const size_t np = p.n_split > 1 ? static_cast<size_t>(S) * Hkv * p.n_split * p.mcap : 0;
   Carver c(ws);
   AttnLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
@@ -597,7 +611,7 @@ size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv,
                               int32_t P_max, int dtype) {
   if (S < 1 || n_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P_max < 0 || !dtype_ok(dtype)) return 0;
   if (dtype != DTV_BF16) return up(sizeof(dtv::WsHeader));
-  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max)).bytes;
+  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max, dtype)).bytes;
 }
 
 int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
@@ -618,7 +632,7 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
     REQUIRE(D >= 4 && D <= 128 && D % 4 == 0, DTV_EUNSUPPORTED, "fp32 attention needs D%%4==0, D<=128, got %d", D);
     REQUIRE(P_max + tree->n_cap <= 16384, DTV_EUNSUPPORTED, "fp32 attention supports at most 16384 keys");
   }
-  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max);
+  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max, dtype);
   size_t need = dtv_tree_attn_ws_bytes(S, tree->n_cap, Hq, Hkv, D, P_max, dtype);
   REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   dtv::AttnArgs a;
@@ -639,9 +653,11 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
   a.D = D;
   a.g = Hq / Hkv;
   a.scale = scale;
+  a.wide = plan.wide;
   a.n_mtiles = plan.n_mtiles;
   a.n_split = plan.n_split;
   a.kps = plan.kps;
+  a.mcap = plan.mcap;
   if (dtype == DTV_BF16) {
     const AttnLayout L = attn_layout(ws, S, Hkv, D, plan);
     a.part_o = L.part_o;

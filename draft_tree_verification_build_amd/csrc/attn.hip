@@ -117,32 +117,41 @@ __global__ __launch_bounds__(kBlock) void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   for (int kb = k_lo; kb < k_hi; kb += kKeyBlock) {
-    // ---- stage K (row-major) and V (transposed) of keys kb .. kb+63
-    constexpr int KV_VECS = kKeyBlock * D / 8;       // 16-byte vectors per tile
-#pragma unroll
-    for (int i = 0; i < KV_VECS / kBlock; ++i) {
-      const int vi = t + kBlock * i;
-      const int key = vi / (D / 8), dc = vi % (D / 8);
-      const int kk = kb + key;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (kk < k_hi) val = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(kk) * D + dc * 8);
-      *reinterpret_cast<uint4*>(&sm.ks[key * KS + dc * 8]) = val;
-    }
+    // ---- stage K (row-major) and V (transposed) of keys kb .. kb+63. All eight 16-byte
+    //      loads are issued before any LDS store so their latencies overlap; each loads a
+    //      clamped (valid) key unconditionally and is zeroed by a select past the range
+    //      end, since a load under a branch gets a wait of its own.
     {
-      constexpr int KPT = kKeyBlock * D / 8 / kBlock;  // keys per thread (4 for D=128)
-      const int dc = t % (D / 8), kg = t / (D / 8);
-      Frag8 vv[KPT];
+      constexpr int NV = kKeyBlock * D / 8 / kBlock;   // 16-byte vectors per thread (4 for D=128)
+      uint4 kr[NV];
+      Frag8 vv[NV];
+      const int dcv = t % (D / 8), kg = t / (D / 8);
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int kk = kb + kg * KPT + u;
-        vv[u].u = make_uint4(0u, 0u, 0u, 0u);
-        if (kk < k_hi) vv[u].u = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(kk) * D + dc * 8);
+      for (int i = 0; i < NV; ++i) {
+        const int vi = t + kBlock * i;
+        const int kk = kb + vi / (D / 8);
+        kr[i] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(min(kk, k_hi - 1)) * D + (vi % (D / 8)) * 8);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t* dst = &sm.vt[(dc * 8 + e) * VS + kg * KPT];
+      for (int u = 0; u < NV; ++u) {
+        const int kk = kb + kg * NV + u;
+        vv[u].u = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(min(kk, k_hi - 1)) * D + dcv * 8);
+      }
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) dst[u] = vv[u].s[e];
+      for (int i = 0; i < NV; ++i) {
+        const int vi = t + kBlock * i;
+        const int key = vi / (D / 8);
+        if (kb + key >= k_hi) kr[i] = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sm.ks[key * KS + (vi % (D / 8)) * 8]) = kr[i];
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (kb + kg * NV + u >= k_hi) vv[u].u = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t* dst = &sm.vt[(dcv * 8 + e) * VS + kg * NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) dst[u] = vv[u].s[e];
       }
     }
     __syncthreads();
@@ -402,6 +411,7 @@ __global__ __launch_bounds__(kBlock) void attn_f32_kernel(AttnArgs a) {
 }
 
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st) {
+  if (dtype == 1 && a.wide) return launch_attn_wide(a, st);
   if (dtype == 1) {
     const dim3 grid(a.S * a.Hkv * a.n_split * a.n_mtiles);
     if (a.D == 128)

@@ -1,0 +1,472 @@
+// Tree attention for large query sets (bf16, MFMA), gfx950.
+//
+// Same computation as attn_bf16_kernel (attn.hip): each node attends to the prefix and to
+// its ancestors; GQA rows (node, head of the KV group) are packed so a K/V tile serves all
+// of them. This variant is organised for MFMA throughput when a KV head has hundreds of
+// query rows:
+//
+// * Every wave owns two 32-row groups (64 query rows), so each K and V fragment it reads
+//   from LDS feeds two v_mfma_f32_32x32x16_bf16 instead of one, halving LDS traffic per
+//   flop; a workgroup (4 waves) covers up to 8 row groups.
+// * The G = ceil(M/32) row groups of a KV head are spread evenly over ceil(G/8) tiles, so
+//   ragged row counts (M = 8*65 or 513) do not leave a tile with one row.
+// * K/V are double-buffered in LDS: the global loads of block b+1 are issued before block
+//   b is computed and land in the other buffer afterwards, one barrier per 64-key block.
+// * The tree mask and the key-range tail are applied only in blocks that need them; the
+//   softmax scale is folded into one fma per score (exp2 domain), P is converted with the
+//   native packed bf16 conversion.
+// * Workgroup numbering is XCD-aware: all tiles of one (sequence, KV head, key split)
+//   share an XCD, hence its L2, since they stream the same keys and values.
+//
+// Key splits write (m, l, unnormalised O) partials per query row; attn_combine_rows merges
+// them.
+#include "dtv_internal.h"
+
+namespace dtv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 wbf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float wf32x16;
+
+constexpr int kWBlock = 64;   // keys per LDS block
+constexpr int kNumXcd = 8;    // XCDs of an MI355X; consecutive workgroups go to consecutive XCDs
+
+union WFrag8 {
+  wbf16x8 v;
+  uint4 u;
+  uint2 h[2];
+  uint16_t s[8];
+};
+
+template <int D>
+struct WideSmem {
+  static constexpr int KS = D + 8;          // K row stride (elements)
+  static constexpr int VS = kWBlock + 4;    // V^T row stride (elements)
+  alignas(16) uint16_t ks[2][kWBlock * KS];
+  alignas(16) uint16_t vt[2][D * VS];
+  alignas(16) float alpha[kWaves][2][32];
+  alignas(16) float ml[kWaves][2][32][2];
+};
+
+// One thread's share of a 64-key K/V block, held in registers between the global loads
+// and the LDS stores: K vectors i (key (t + 256 i) / (D/8), dims 8 * ((t + 256 i) % (D/8)));
+// V keys kg*NV + u of dims 8*dc .. 8*dc+7 (dc = t % (D/8), kg = t / (D/8)).
+template <int D>
+struct WidePrefetch {
+  static constexpr int NV = kWBlock * D / 8 / kBlock;   // 16-byte vectors per thread (4 or 2)
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;                  // named members keep them in registers
+  __device__ __forceinline__ uint4& k(int i) { return i == 0 ? k0 : i == 1 ? k1 : i == 2 ? k2 : k3; }
+  __device__ __forceinline__ uint4& v(int i) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
+  __device__ __forceinline__ const uint4& k(int i) const { return i == 0 ? k0 : i == 1 ? k1 : i == 2 ? k2 : k3; }
+  __device__ __forceinline__ const uint4& v(int i) const { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
+};
+
+__device__ __forceinline__ uint32_t half_of(const uint4& x, int e) {
+  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Loads keys kb .. kb+63 (clamped to the last valid key k_hi-1; the extra copies are
+// masked out of the softmax, so they need no zeroing). Every load is unconditional so
+// that all of them are in flight together.
+template <int D>
+__device__ __forceinline__ WidePrefetch<D> wide_fetch(const uint16_t* kbase, const uint16_t* vbase, int kb, int k_hi) {
+  constexpr int NV = WidePrefetch<D>::NV;
+  WidePrefetch<D> r;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = t + kBlock * i;
+    const int key = vi / (D / 8), dc = vi % (D / 8);
+    r.k(i) = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(min(kb + key, k_hi - 1)) * D + dc * 8);
+  }
+  const int dc = t % (D / 8), kg = t / (D / 8);
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    r.v(u) = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(min(kb + kg * NV + u, k_hi - 1)) * D + dc * 8);
+  return r;
+}
+
+// Stores a prefetched block into LDS buffer `buf`: K row-major, V transposed (V^T[d][key]).
+template <int D>
+__device__ __forceinline__ void wide_stage(WideSmem<D>& sm, int buf, const WidePrefetch<D>& r) {
+  constexpr int KS = WideSmem<D>::KS;
+  constexpr int VS = WideSmem<D>::VS;
+  constexpr int NV = WidePrefetch<D>::NV;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int vi = t + kBlock * i;
+    const int key = vi / (D / 8), dc = vi % (D / 8);
+    *reinterpret_cast<uint4*>(&sm.ks[buf][key * KS + dc * 8]) = r.k(i);
+  }
+  const int dc = t % (D / 8), kg = t / (D / 8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint16_t* dst = &sm.vt[buf][(dc * 8 + e) * VS + kg * NV];
+    if constexpr (NV == 4) {
+      uint2 w;
+      w.x = half_of(r.v(0), e) | (half_of(r.v(1), e) << 16);
+      w.y = half_of(r.v(2), e) | (half_of(r.v(3), e) << 16);
+      *reinterpret_cast<uint2*>(dst) = w;
+    } else {
+      static_assert(NV == 2, "D is 64 or 128");
+      *reinterpret_cast<uint32_t*>(dst) = half_of(r.v(0), e) | (half_of(r.v(1), e) << 16);
+    }
+  }
+}
+
+// Visibility of keys kb .. kb+63 to one query row as a 64-bit mask (bit o: key kb + o).
+// Cache positions below P are the prefix, visible to every node; position P + j is tree
+// node j, visible when bit j of the row's ancestor mask is set; keys at or past k_hi
+// belong to another split or do not exist. Requires kb < k_hi <= P + n_nodes, so every
+// ancestor word read is inside the row's mask. Padding rows (ok false) see the prefix only.
+__device__ __forceinline__ uint64_t block_visibility(int kb, int P, int k_hi, const uint64_t* anc, bool ok) {
+  const int nr = k_hi - kb;
+  const uint64_t in_range = nr >= 64 ? ~0ull : ((1ull << nr) - 1ull);
+  const int np = P - kb;
+  const uint64_t prefix = np >= 64 ? ~0ull : (np <= 0 ? 0ull : ((1ull << np) - 1ull));
+  uint64_t tree = 0ull;
+  if (np < 64 && ok) {
+    if (np > 0) {
+      tree = anc[0] << np;
+    } else {
+      const int j0 = -np, wi = j0 >> 6, sh = j0 & 63;
+      const uint64_t lo = anc[wi];
+      tree = lo >> sh;
+      if (sh != 0 && kb + (64 - sh) < k_hi) tree |= anc[wi + 1] << (64 - sh);
+    }
+  }
+  return (prefix | tree) & in_range;
+}
+
+// Writes one 32-row group of O: normalised bf16 rows when the keys are not split, else
+// the unnormalised fp32 rows and their (m, l) as partials. A lane holds O rows
+// (i/4)*8 + 4h + i%4 of the group, column nt*32 + lr of tile nt.
+template <int D>
+__device__ __forceinline__ void wide_store(const AttnArgs& a, const wf32x16 (&oo)[D / 32], const float (*ml)[2],
+                                           int s, int kv, int sp, int grp, int M, int h, int lr) {
+  constexpr int NT = D / 32;
+  const int g = a.g;
+  const size_t prow0 = ((static_cast<size_t>(s) * a.Hkv + kv) * a.n_split + sp) * static_cast<size_t>(a.mcap);
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rl = q4 * 8 + 4 * h + b;
+      const int rr = grp * 32 + rl;
+      if (rr >= M) continue;
+      if (a.n_split == 1) {
+        const float l = ml[rl][1];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        __bf16* orow = static_cast<__bf16*>(a.o) +
+                       ((static_cast<size_t>(s) * a.n_cap + rr / g) * a.Hq + kv * g + rr % g) * D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) orow[nt * 32 + lr] = static_cast<__bf16>(oo[nt][q4 * 4 + b] * inv);
+      } else {
+        float* prow = a.part_o + (prow0 + rr) * D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) prow[nt * 32 + lr] = oo[nt][q4 * 4 + b];
+      }
+    }
+  if (a.n_split > 1 && h == 0) {
+    const int rr = grp * 32 + lr;
+    if (rr < M) {
+      a.part_ml[(prow0 + rr) * 2 + 0] = ml[lr][0];
+      a.part_ml[(prow0 + rr) * 2 + 1] = ml[lr][1];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
+  __shared__ WideSmem<D> sm;
+  constexpr int KS = WideSmem<D>::KS;
+  constexpr int VS = WideSmem<D>::VS;
+  constexpr int NKS = D / 16;
+  constexpr int NT = D / 32;
+
+  // ---- XCD-aware decode: the tiles of unit u = (s, kv, split) share XCD u % 8
+  const int bid = blockIdx.x;
+  const int xcd = bid % kNumXcd;
+  const int local = bid / kNumXcd;
+  const int tm = local % a.n_mtiles;
+  const int u = (local / a.n_mtiles) * kNumXcd + xcd;
+  if (u >= a.S * a.Hkv * a.n_split) return;
+  const int sp = u % a.n_split;
+  const int kv = (u / a.n_split) % a.Hkv;
+  const int s = u / (a.n_split * a.Hkv);
+
+  const int N = a.n_nodes[s];
+  const int g = a.g;
+  const int M = g * N;
+  const int P = a.P[s];
+  if (N > a.n_cap || P < 0 || P + N > a.P_cap) {
+    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    return;
+  }
+  const int G = (M + 31) / 32;
+  const int gl = tm * G / a.n_mtiles, gh = (tm + 1) * G / a.n_mtiles;
+  if (gl >= gh) return;
+  const int T = P + N;
+  const int k_lo = sp * a.kps;
+  const int k_hi = min(k_lo + a.kps, T);
+
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform
+  const int lane = t & 63;
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+  const int gA = gl + 2 * w, gB = gl + 2 * w + 1;
+  const bool actA = gA < gh, actB = gB < gh;
+  const int rA = gA * 32 + lr, rB = gB * 32 + lr;
+  const bool okA = actA && rA < M, okB = actB && rB < M;
+  const int nodeA = okA ? rA / g : 0, nodeB = okB ? rB / g : 0;
+
+  const size_t kvoff = (static_cast<size_t>(s) * a.Hkv + kv) * a.P_cap * static_cast<size_t>(D);
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + kvoff;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + kvoff;
+  const uint64_t* ancA = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeA) * a.words;
+  const uint64_t* ancB = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeB) * a.words;
+
+  WFrag8 qA[NKS], qB[NKS];
+  {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const uint16_t* qa = q + ((static_cast<size_t>(s) * a.n_cap + nodeA) * a.Hq + kv * g + (okA ? rA % g : 0)) * D;
+    const uint16_t* qb = q + ((static_cast<size_t>(s) * a.n_cap + nodeB) * a.Hq + kv * g + (okB ? rB % g : 0)) * D;
+    // Unconditional loads: a padding row (past M) reads row 0's query, which is valid
+    // memory; its scores stay finite and its output is never stored.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qA[ks].u = *reinterpret_cast<const uint4*>(qa + ks * 16 + 8 * h);
+      qB[ks].u = *reinterpret_cast<const uint4*>(qb + ks * 16 + 8 * h);
+    }
+  }
+
+  wf32x16 oA[NT], oB[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      oA[nt][i] = 0.f;
+      oB[nt][i] = 0.f;
+    }
+  float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kWBlock - 1) / kWBlock : 0;
+  WidePrefetch<D> pf;
+  if (nblk > 0) {
+    pf = wide_fetch<D>(kbase, vbase, k_lo, k_hi);
+    wide_stage<D>(sm, 0, pf);
+  }
+  // Nothing may be outstanding at the loop head: otherwise the wait inserted for the
+  // query registers inside the loop also waits for the block prefetch.
+  drain();
+  __syncthreads();
+
+  for (int b = 0; b < nblk; ++b) {
+    const int kb = k_lo + b * kWBlock;
+    const int cur = b & 1;
+    const bool more = b + 1 < nblk;
+    // Visibility of this block's keys (tree keys or the range tail only); the ancestor
+    // words are read before the prefetch is issued so that waiting for them does not
+    // wait for the prefetch.
+    const bool need_mask = (kb + kWBlock > P) || (kb + kWBlock > k_hi);
+    uint64_t visA = ~0ull, visB = ~0ull;
+    if (need_mask) {
+      visA = block_visibility(kb, P, k_hi, ancA, okA) >> (4 * h);
+      visB = block_visibility(kb, P, k_hi, ancB, okB) >> (4 * h);
+    }
+    if (more) pf = wide_fetch<D>(kbase, vbase, kb + kWBlock, k_hi);
+
+    if (actA) {
+      // ---- S^T = K Q^T for both row groups; each K fragment feeds two MFMAs
+      wf32x16 sA[2], sB[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sA[kt][i] = 0.f;
+          sB[kt][i] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          WFrag8 kf;
+          kf.u = *reinterpret_cast<const uint4*>(&sm.ks[cur][(kt * 32 + lr) * KS + ks * 16 + 8 * h]);
+          sA[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qA[ks].v, sA[kt], 0, 0, 0);
+          sB[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qB[ks].v, sB[kt], 0, 0, 0);
+        }
+      }
+      // ---- masks (tree block, range tail) only where a block needs them
+      auto softmax = [&](wf32x16 (&sc)[2], uint64_t vis, float& m_run, float& l_run) -> float {
+        if (need_mask) {
+          // element (kt, i) of a lane is key kb + kt*32 + (i/4)*8 + 4h + i%4
+          const uint32_t v_lo = static_cast<uint32_t>(vis), v_hi = static_cast<uint32_t>(vis >> 32);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t bits = kt == 0 ? v_lo : v_hi;
+              if (!((bits >> ((i >> 2) * 8 + (i & 3))) & 1u)) sc[kt][i] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+        // Lazy rescaling: the reference max m_run only moves when the block's max exceeds
+        // it by more than 8 (log2 units), so p <= 2^8 and the O rescale is rare. The final
+        // division by l makes the result independent of the reference chosen.
+        float alpha = 1.f;
+        if (mx > m_run + 8.f) {
+          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+          l_run *= alpha;
+          m_run = mx;
+        }
+        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, -mref));
+            sc[kt][i] = p;
+            sum += p;
+          }
+        l_run += sum;
+        return alpha;
+      };
+      const float alA = softmax(sA, visA, mA, lA);
+      const float alB = softmax(sB, visB, mB, lB);
+      // ---- rescale O; a lane holds O rows (i/4)*8 + 4h + i%4. Applied unconditionally
+      //      (alpha is mostly 1): a branch around it makes the compiler keep two copies
+      //      of the accumulators and spill.
+      {
+        if (h == 0) {
+          sm.alpha[w][0][lr] = alA;
+          sm.alpha[w][1][lr] = alB;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 fa = *reinterpret_cast<const float4*>(&sm.alpha[w][0][q4 * 8 + 4 * h]);
+          const float4 fb = *reinterpret_cast<const float4*>(&sm.alpha[w][1][q4 * 8 + 4 * h]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            oA[nt][q4 * 4 + 0] *= fa.x;
+            oA[nt][q4 * 4 + 1] *= fa.y;
+            oA[nt][q4 * 4 + 2] *= fa.z;
+            oA[nt][q4 * 4 + 3] *= fa.w;
+            oB[nt][q4 * 4 + 0] *= fb.x;
+            oB[nt][q4 * 4 + 1] *= fb.y;
+            oB[nt][q4 * 4 + 2] *= fb.z;
+            oB[nt][q4 * 4 + 3] *= fb.w;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      // ---- O += P V; each V fragment feeds two MFMAs
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        WFrag8 pa, pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pa.v[j] = static_cast<__bf16>(sA[k2 >> 1][8 * (k2 & 1) + j]);
+          pb.v[j] = static_cast<__bf16>(sB[k2 >> 1][8 * (k2 & 1) + j]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          WFrag8 vf;
+          const uint16_t* vrow = &sm.vt[cur][(nt * 32 + lr) * VS + 16 * k2 + 4 * h];
+          vf.h[0] = *reinterpret_cast<const uint2*>(vrow);
+          vf.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
+          oA[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa.v, vf.v, oA[nt], 0, 0, 0);
+          oB[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb.v, vf.v, oB[nt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) wide_stage<D>(sm, cur ^ 1, pf);
+    __syncthreads();
+  }
+
+  // ---- row statistics in the O layout
+  const float ltA = lA + __shfl_xor(lA, 32, 64);
+  const float ltB = lB + __shfl_xor(lB, 32, 64);
+  if (h == 0) {
+    sm.ml[w][0][lr][0] = mA;
+    sm.ml[w][0][lr][1] = ltA;
+    sm.ml[w][1][lr][0] = mB;
+    sm.ml[w][1][lr][1] = ltB;
+  }
+  __syncthreads();
+  if (actA) wide_store<D>(a, oA, sm.ml[w][0], s, kv, sp, gA, M, h, lr);
+  if (actB) wide_store<D>(a, oB, sm.ml[w][1], s, kv, sp, gB, M, h, lr);
+}
+
+// Merges the key splits of every query row of the wide kernel (partials indexed by row).
+template <int D>
+__global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = kBlock / TPR;
+  const int rows_per_head = a.mcap;
+  const int blocks_per_head = (rows_per_head + RPB - 1) / RPB;
+  const int head = blockIdx.x / blocks_per_head;   // (s, kv)
+  const int rr = (blockIdx.x % blocks_per_head) * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  const int kv = head % a.Hkv;
+  const int s = head / a.Hkv;
+  const int N = a.n_nodes[s];
+  if (N > a.n_cap || rr >= a.g * N) return;
+  float mx = -INFINITY;
+  for (int q = 0; q < a.n_split; ++q) {
+    const size_t pr = (static_cast<size_t>(head) * a.n_split + q) * rows_per_head + rr;
+    const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[pr * 2]);
+    if (ml.y > 0.f) mx = fmaxf(mx, ml.x);
+  }
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = 0; q < a.n_split; ++q) {
+    const size_t pr = (static_cast<size_t>(head) * a.n_split + q) * rows_per_head + rr;
+    const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[pr * 2]);
+    if (ml.y > 0.f) {
+      const float sc = __builtin_amdgcn_exp2f(ml.x - mx);
+      L += ml.y * sc;
+      const float4 o = *reinterpret_cast<const float4*>(&a.part_o[pr * D + c4 * 4]);
+      acc.x += o.x * sc;
+      acc.y += o.y * sc;
+      acc.z += o.z * sc;
+      acc.w += o.w * sc;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __bf16* orow = static_cast<__bf16*>(a.o) +
+                 ((static_cast<size_t>(s) * a.n_cap + rr / a.g) * a.Hq + kv * a.g + rr % a.g) * D + c4 * 4;
+  orow[0] = static_cast<__bf16>(acc.x * inv);
+  orow[1] = static_cast<__bf16>(acc.y * inv);
+  orow[2] = static_cast<__bf16>(acc.z * inv);
+  orow[3] = static_cast<__bf16>(acc.w * inv);
+}
+
+int launch_attn_wide(const AttnArgs& a, hipStream_t st) {
+  const int units = a.S * a.Hkv * a.n_split;
+  const int grid = ((units + kNumXcd - 1) / kNumXcd) * kNumXcd * a.n_mtiles;
+  if (a.D == 128)
+    hipLaunchKernelGGL(attn_wide_kernel<128>, dim3(grid), dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_wide_kernel<64>, dim3(grid), dim3(kBlock), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (a.n_split > 1) {
+    const int rpb = kBlock / (a.D / 4);
+    const int blocks = a.S * a.Hkv * ((a.mcap + rpb - 1) / rpb);
+    if (a.D == 128)
+      hipLaunchKernelGGL(attn_combine_rows_kernel<128>, dim3(blocks), dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_combine_rows_kernel<64>, dim3(blocks), dim3(kBlock), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
+}
+
+}  // namespace dtv

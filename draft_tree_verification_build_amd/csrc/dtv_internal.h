@@ -120,9 +120,11 @@ struct AttnArgs {
   int n_cap, words;
   int S, Hq, Hkv, D, g;
   float scale;          // softmax scale (1/sqrt(D) by default)
-  int n_mtiles, n_split, kps;  // 128-row query tiles, key splits, keys per split
-  float* part_o;        // [S*Hkv*n_mtiles][n_split][128][D]
-  float* part_ml;       // [S*Hkv*n_mtiles][n_split][128][2]
+  int wide;             // 1: attn_wide_kernel (two 32-row groups per wave), 0: attn_bf16_kernel
+  int n_mtiles, n_split, kps;  // query tiles per KV head, key splits, keys per split
+  int mcap;             // partial rows per (sequence, KV head, split)
+  float* part_o;        // [S*Hkv][n_split][mcap][D] (wide) or [S*Hkv*n_mtiles][n_split][128][D]
+  float* part_ml;       // same rows, (m, l) pairs
   unsigned* tickets;    // [S*Hkv*n_mtiles]
   WsHeader* hdr;
 };
@@ -178,6 +180,7 @@ int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
 int launch_opt_finalize(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
+int launch_attn_wide(const AttnArgs& a, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st);
 int launch_compact(const CompactArgs& a, hipStream_t st);

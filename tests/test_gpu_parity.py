@@ -191,6 +191,10 @@ def test_attention_edges(P, B):
 @pytest.mark.parametrize("name,ov,pairs", [
     ("c5_batched_llama2_70b", {"V": 64}, 24),
     ("c5_batched_llama2_70b", {"V": 64, "Hq": 8, "Hkv": 8, "D": 64}, 40),
+    # 512 packed rows per KV head at head_dim 64 (two-group-per-wave kernel, D=64)
+    ("c5_batched_llama2_70b", {"V": 64, "S": 2, "Hq": 32, "Hkv": 4, "D": 64, "B": 63}, 40),
+    # 328 rows = 11 row groups over two tiles (5 + 6): a wave with a single group
+    ("c5_batched_llama2_70b", {"V": 64, "S": 3, "P": 1000, "B": 40}, 40),
 ])
 def test_attention_large_sampled(name, ov, pairs):
     need_gpu()
