@@ -421,9 +421,7 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
   if (rc) return rc;
   REQUIRE(draft != nullptr, DTV_EINVAL, "draft is NULL");
   REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
-  REQUIRE(S >= 1 && S <= 64, DTV_EUNSUPPORTED, "S=%d outside 1..64", S);
-  REQUIRE(static_cast<long>(S) * tree->n_cap <= 2048, DTV_EUNSUPPORTED, "S*n_cap=%ld exceeds 2048",
-          static_cast<long>(S) * tree->n_cap);
+  REQUIRE(S >= 1, DTV_EINVAL, "S=%d", S);
   REQUIRE(V >= 1, DTV_EINVAL, "V=%d", V);
   REQUIRE(B >= 1, DTV_EINVAL, "B=%d", B);
   REQUIRE(B + 1 <= tree->n_cap, DTV_ECAPACITY, "B+1=%d exceeds n_cap=%d", B + 1, tree->n_cap);
@@ -435,8 +433,6 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
   REQUIRE(alpha >= 0.0 && alpha <= 1.0, DTV_EINVAL, "alpha=%g outside [0,1]", alpha);
   const TalonLayout L = talon_layout(ws, S, B, K, V, dtype);
   REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
-  const int grid = dtv::talon_max_grid(dtype == DTV_BF16 ? 1 : 0);
-  REQUIRE(grid >= 1, DTV_EHIP, "cannot size the cooperative grid");
   dtv::TalonArgs a;
   a.tree = tree_args(tree);
   a.draft = draft;
@@ -456,7 +452,7 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
   a.rv = L.rv;
   a.ri = L.ri;
   a.rcnt = L.rcnt;
-  return launched(dtv::launch_talon(a, dtype == DTV_BF16 ? 1 : 0, grid, static_cast<hipStream_t>(stream)));
+  return launched(dtv::launch_talon(a, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- GOOSE spine

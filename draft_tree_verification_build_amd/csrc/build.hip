@@ -5,10 +5,11 @@
 // of each node of the previous layer, scores them with the product of draft
 // probabilities along the path (kept as a sum of logs), keeps those within a factor
 // alpha of the best (the anchor) and, if more pass than budget remains, the best by
-// score. The whole layer loop is one cooperative launch: every workgroup reduces chunks
-// of the frontier's draft rows (phase A), a grid barrier publishes the row results, and
-// every workgroup then runs the same deterministic selection (phase B) so that all of
-// them know the next frontier without a second barrier; workgroup 0 writes the nodes.
+// score. Rows are keyed by slot, and only slots 0..B-1 can ever be expanded (the node in
+// slot B completes the budget), so the vocab-wide part does not depend on the tree: one
+// data-parallel launch reduces draft rows 0..B-1 of every sequence (Top-K and log-sum-exp
+// per row, one workgroup per row chunk), and a second launch runs the whole layer loop
+// of one sequence inside one workgroup on those small per-row lists.
 #include "dtv_internal.h"
 #include "rowstats.h"
 
@@ -69,222 +70,268 @@ int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st) {
 
 constexpr int kTalonMaxK = 64;
 constexpr int kTalonMaxPool = 4096;
-constexpr int kTalonMaxS = 64;
 constexpr int kTalonMergeCap = 2048;  // chunks_of(V) * K must not exceed this
-constexpr int kTalonTreeCap = 2048;   // S * n_cap must not exceed this
 
-struct TalonSmem {
-  RowSmem rs;
-  MergeSmem<kTalonMergeCap> ms;
-  unsigned long long sortbuf[pow2_at_least(kWaves * kTalonMaxK) > kCandCap ? pow2_at_least(kWaves * kTalonMaxK)
-                                                                           : kCandCap];
-  double pool[kTalonMaxPool];     // scores of the candidate pool of one sequence
-  int ptok[kTalonMaxPool];        // tokens of the candidate pool
-  double tscore[kTalonTreeCap];   // every node's log path score, all sequences
-  short tpar[kTalonTreeCap];      // every node's parent slot, all sequences
-  int gated[1024];                // per frontier row: entries passing the gate
-  int kept[1024];                 // per frontier row: entries kept
-  int scan[kBlock];
-  int cnt[kTalonMaxS], start[kTalonMaxS], width[kTalonMaxS], done[kTalonMaxS], nlayers[kTalonMaxS];
-  int flag;
-};
-
+// Phase 1: one workgroup per (sequence, row f < B, chunk). The workgroup that completes a
+// row merges its chunks into the row's Top-K (value, token), count and log-sum-exp.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void talon_kernel(TalonArgs a) {
-  __shared__ TalonSmem sm;
+__global__ __launch_bounds__(kBlock) void talon_rows_kernel(TalonArgs a) {
+  __shared__ RowSmem rs;
+  __shared__ MergeSmem<kTalonMergeCap> ms;
+  __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * kTalonMaxK) > kCandCap
+                                            ? pow2_at_least(kWaves * kTalonMaxK) : kCandCap];
   using Rw = RowT<DT>;
+  row_smem_init(rs);
+  __syncthreads();
   const int nch = a.nch;
   const int K = a.K;
-  const int B = a.B;
-  const int cap = a.tree.n_cap;
-  const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
-
-  row_smem_init(sm.rs);
-  for (int s = threadIdx.x; s < a.S; s += kBlock) {
-    sm.cnt[s] = 0;
-    sm.start[s] = 0;
-    sm.width[s] = 1;
-    sm.done[s] = 0;
-    sm.nlayers[s] = 0;
-    sm.tscore[s * cap] = 0.0;
-    sm.tpar[s * cap] = -1;
-  }
-  __syncthreads();
-
+  const int c = blockIdx.x % nch;
+  const int rf = blockIdx.x / nch;       // s * B + f
+  const int s = rf / a.B, f = rf % a.B;  // row f of sequence s is draft row f (rows keyed by slot)
+  const char* row = static_cast<const char*>(a.draft) +
+                    (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
   float x[Rw::E];
   uint32_t key[Rw::E];
-  int layer = 0;
-  bool ok = true;
-  for (;;) {
-    ++layer;
-    // ---------------- phase A: reduce the frontier rows chunk by chunk
-    int total = 0;
-    for (int s = 0; s < a.S; ++s) total += sm.done[s] ? 0 : sm.width[s] * nch;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-      int rest = item, s = 0;
-      for (; s < a.S; ++s) {
-        const int n = sm.done[s] ? 0 : sm.width[s] * nch;
-        if (rest < n) break;
-        rest -= n;
-      }
-      const int f = rest / nch, c = rest % nch;
-      const int slot = sm.start[s] + f;              // rows are keyed by slot
-      const char* row = static_cast<const char*>(a.draft) +
-                        (static_cast<size_t>(s) * a.R + slot) * row_bytes;
-      load_chunk<DT>(row, a.V, c, x, key);
-      const size_t rf = static_cast<size_t>(s) * B + f;
-      const size_t ci = rf * nch + c;
-      chunk_reduce<DT>(x, key, c, a.V, K, &a.st[ci], a.cval + ci * K, a.cidx + ci * K, sm.sortbuf, sm.rs);
-      if (last_arrival(&a.tickets[rf], nch, &sm.flag)) {
-        const int n = row_merge(a.st + rf * nch, a.cval + rf * nch * K, a.cidx + rf * nch * K, nch, K,
-                                nullptr, nullptr, &a.rlse[rf], a.rv + rf * K, a.ri + rf * K, sm.rs, sm.ms);
-        if (threadIdx.x == 0) st_cc(&a.rcnt[rf], n);
-      }
+  load_chunk<DT>(row, a.V, c, x, key);
+  const size_t ci = static_cast<size_t>(rf) * nch + c;
+  chunk_reduce<DT>(x, key, c, a.V, K, &a.st[ci], a.cval + ci * K, a.cidx + ci * K, sortbuf, rs);
+  if (last_arrival(&a.tickets[rf], nch, &rs.flag)) {
+    const size_t rb = static_cast<size_t>(rf) * nch;
+    const int n = row_merge(a.st + rb, a.cval + rb * K, a.cidx + rb * K, nch, K, nullptr, nullptr,
+                            &a.rlse[rf], a.rv + static_cast<size_t>(rf) * K, a.ri + static_cast<size_t>(rf) * K,
+                            rs, ms);
+    if (threadIdx.x == 0) a.rcnt[rf] = n;
+  }
+}
+
+struct TalonSelSmem {
+  double redd[kWaves];
+  int redi[kWaves];
+  unsigned long long redu[kWaves];
+  double lp[kTalonMaxPool];     // log p_d of every row's list entries, row f at f*K
+  int tok[kTalonMaxPool];       // their tokens
+  double csc[kTalonMaxPool];    // scores of the current layer's candidates, e = f*K + j
+  unsigned long long ckey[kTalonMaxPool];   // their order keys while selecting (0: not gated)
+  int rcnt[1024];               // list length of every row
+  double tscore[1024];          // log path score of every slot
+  short tpar[1024];             // parent of every slot
+  int gated[1024];              // per frontier row: candidates passing the gate
+  int kept[1024];               // per frontier row: candidates kept
+  int rowbase[1024];            // per frontier row: first new slot - (cnt + 1)
+  int scan[kBlock];
+  int hist[kBlock];             // radix-selection histogram (256 digits)
+  int sel_digit, sel_rem;
+  int cnt, start, width, layers, carry;
+};
+
+// Keeps the `room` best candidates (ckey[e] != 0) by (key desc, e asc) and counts them per
+// frontier row into kept[]: radix selection of the room-th largest key T (8 bits a pass,
+// starting at the first byte where the candidate keys differ), then every key above T and,
+// of the keys equal to T, those with the lowest e. Requires more than `room` candidates.
+__device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int room) {
+  unsigned long long kmax = 0ull, kmin = ~0ull;
+  for (int e = threadIdx.x; e < n; e += kBlock) {
+    const unsigned long long k = sm.ckey[e];
+    if (k != 0ull) {
+      kmax = k > kmax ? k : kmax;
+      kmin = k < kmin ? k : kmin;
     }
-    if (!grid_barrier(a.hdr->bar, gridDim.x, &a.hdr->err, kErrTimeout, &sm.flag)) {
-      ok = false;
+  }
+  kmax = block_max(kmax, sm.redu);
+  kmin = block_min(kmin, sm.redu);
+  const unsigned long long diff = kmax ^ kmin;
+  int top = 0;   // highest byte where keys differ
+  for (int b = 7; b >= 0; --b)
+    if ((diff >> (8 * b)) & 0xFFull) {
+      top = b;
       break;
     }
-
-    // ---------------- phase B: the same selection in every workgroup
-    int all_done = 1;
-    for (int s = 0; s < a.S; ++s) {
-      if (sm.done[s]) continue;
-      const int W = sm.width[s];
-      const int cnt = sm.cnt[s];
-      const int room = B - cnt;
-      const size_t rf0 = static_cast<size_t>(s) * B;
-      const size_t tb = static_cast<size_t>(s) * cap;
-      // pool scores: s(c) = s(parent) + log p_d(token | parent)
-      for (int e = threadIdx.x; e < W * K; e += kBlock) {
-        const int f = e / K, j = e % K;
-        double v = -INFINITY;
-        int tok = -1;
-        if (j < ld_cc(&a.rcnt[rf0 + f])) {
-          v = sm.tscore[tb + sm.start[s] + f] +
-              (static_cast<double>(ld_cc(&a.rv[(rf0 + f) * K + j])) - ld_cc(&a.rlse[rf0 + f]));
-          tok = ld_cc(&a.ri[(rf0 + f) * K + j]);
-        }
-        sm.pool[e] = v;
-        sm.ptok[e] = tok;
+  unsigned long long mask = top == 7 ? 0ull : (~0ull << (8 * (top + 1)));
+  unsigned long long prefix = kmax & mask;
+  int rem = room;
+  for (int shift = 8 * top; shift >= 0; shift -= 8) {
+    sm.hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kBlock) {
+      const unsigned long long k = sm.ckey[e];
+      if (k != 0ull && (k & mask) == prefix) atomicAdd(&sm.hist[(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l owns digits 255-4l .. 252-4l; find the digit whose cumulative count from
+      // the top first reaches rem
+      const int l = threadIdx.x;
+      const int c0 = sm.hist[255 - 4 * l], c1 = sm.hist[254 - 4 * l];
+      const int c2 = sm.hist[253 - 4 * l], c3 = sm.hist[252 - 4 * l];
+      const int mine = c0 + c1 + c2 + c3;
+      int inc = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (l >= o) inc += y;
       }
-      __syncthreads();
-      if (layer == 1) {
-        // robust initialisation: the root's Top-K, at most the budget, no gate
-        if (threadIdx.x == 0) {
-          const int n = ld_cc(&a.rcnt[rf0]);
-          sm.kept[0] = n < room ? n : room;
+      const int above = inc - mine;
+      if (above < rem && rem <= inc) {
+        int acc = above, d = 255 - 4 * l;
+        const int cs[4] = {c0, c1, c2, c3};
+        for (int q = 0; q < 4; ++q) {
+          if (acc + cs[q] >= rem) {
+            d = 255 - 4 * l - q;
+            break;
+          }
+          acc += cs[q];
         }
+        sm.sel_digit = d;
+        sm.sel_rem = rem - acc;
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<unsigned long long>(sm.sel_digit) << shift;
+    mask |= 0xFFull << shift;
+    rem = sm.sel_rem;
+    __syncthreads();
+  }
+  const unsigned long long T = prefix;   // rem = how many keys equal to T are kept
+  for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = 0;
+  __syncthreads();
+  int carry_eq = 0;
+  for (int e0 = 0; e0 < n; e0 += kBlock) {
+    const int e = e0 + threadIdx.x;
+    const unsigned long long k = e < n ? sm.ckey[e] : 0ull;
+    const int eq = (k != 0ull && k == T) ? 1 : 0;
+    int tot = 0;
+    const int before = carry_eq + block_exclusive_scan(eq, sm.scan, &tot);
+    if (k != 0ull && (k > T || (eq && before < rem))) atomicAdd(&sm.kept[e / K], 1);
+    carry_eq += tot;
+  }
+  __syncthreads();
+}
+
+// Phase 2: the layer loop of sequence blockIdx.x in one workgroup. The row lists of phase 1
+// (visible after the kernel boundary) are copied into shared memory in one parallel pass,
+// and every step of a layer is a parallel pass over the layer's candidates e = f*K + j
+// (frontier row f, rank j), so no thread walks a dependent chain of shared-memory reads.
+__global__ __launch_bounds__(kBlock) void talon_select_kernel(TalonArgs a) {
+  __shared__ TalonSelSmem sm;
+  const int s = blockIdx.x;
+  const int K = a.K;
+  const int B = a.B;
+  const size_t rf0 = static_cast<size_t>(s) * B;
+  const size_t tb = static_cast<size_t>(s) * a.tree.n_cap;
+  for (int f = threadIdx.x; f < B; f += kBlock) sm.rcnt[f] = a.rcnt[rf0 + f];
+  for (int e = threadIdx.x; e < B * K; e += kBlock) {
+    const int f = e / K;
+    sm.lp[e] = static_cast<double>(a.rv[rf0 * K + e]) - a.rlse[rf0 + f];
+    sm.tok[e] = a.ri[rf0 * K + e];
+  }
+  if (threadIdx.x == 0) {
+    sm.cnt = 0;
+    sm.start = 0;
+    sm.width = 1;
+    sm.layers = 0;
+    sm.tscore[0] = 0.0;
+    sm.tpar[0] = -1;
+  }
+  __syncthreads();
+  for (int layer = 1;; ++layer) {
+    const int W = sm.width, cnt = sm.cnt, start = sm.start;
+    const int room = B - cnt;
+    const int n = W * K;
+    // candidate scores s(c) = s(parent) + log p_d(token | parent); frontier row f is slot start + f
+    for (int e = threadIdx.x; e < n; e += kBlock) {
+      const int f = e / K, j = e % K, r = start + f;
+      sm.csc[e] = j < sm.rcnt[r] ? sm.tscore[r] + sm.lp[r * K + j] : -INFINITY;
+    }
+    __syncthreads();
+    if (layer == 1) {
+      // robust initialisation: the root's Top-K, at most the budget, no gate
+      if (threadIdx.x == 0) sm.kept[0] = sm.rcnt[0] < room ? sm.rcnt[0] : room;
+      __syncthreads();
+    } else {
+      double mx = -INFINITY;
+      for (int f = threadIdx.x; f < W; f += kBlock) mx = fmax(mx, sm.csc[f * K]);
+      const double anchor = block_max(mx, sm.redd);
+      const double thr = a.log_alpha + anchor;
+      // row lists are sorted, so the gated entries of a row are a prefix of it
+      int tg = 0;
+      for (int f = threadIdx.x; f < W; f += kBlock) {
+        int g = 0;
+        for (int j = 0; j < K; ++j) g += sm.csc[f * K + j] >= thr ? 1 : 0;
+        sm.gated[f] = g;
+        tg += g;
+      }
+      tg = block_sum(tg, sm.redi);
+      if (tg <= room) {
+        for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = sm.gated[f];
         __syncthreads();
       } else {
-        double mx = -INFINITY;
-        for (int f = threadIdx.x; f < W; f += kBlock) mx = fmax(mx, sm.pool[f * K]);
-        const double anchor = block_max(mx, sm.rs.redd);
-        const double thr = a.log_alpha + anchor;
-        int tg = 0;
-        for (int f = threadIdx.x; f < W; f += kBlock) {
-          int g = 0;
-          while (g < K && sm.pool[f * K + g] >= thr) ++g;
-          sm.gated[f] = g;
-          tg += g;
-        }
-        tg = block_sum(tg, sm.rs.redi);
-        if (tg <= room) {
-          for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = sm.gated[f];
-          __syncthreads();
-        } else {
-          // budget respect: keep the `room` best gated candidates, ordered by
-          // (score desc, parent slot asc, rank asc); kept entries of a row are a prefix
-          for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = 0;
-          __syncthreads();
-          for (int e = threadIdx.x; e < W * K; e += kBlock) {
-            const int f = e / K, j = e % K;
-            if (j >= sm.gated[f]) continue;
-            const double v = sm.pool[e];
-            int rank = j;
-            for (int f2 = 0; f2 < W && rank < room; ++f2) {
-              if (f2 == f) continue;
-              const int g2 = sm.gated[f2];
-              int c2 = 0;
-              if (f2 < f) {
-                while (c2 < g2 && sm.pool[f2 * K + c2] >= v) ++c2;
-              } else {
-                while (c2 < g2 && sm.pool[f2 * K + c2] > v) ++c2;
-              }
-              rank += c2;
-            }
-            if (rank < room) atomicAdd(&sm.kept[f], 1);
-          }
-          __syncthreads();
-        }
+        // budget respect: the `room` best gated candidates by (score desc, parent slot
+        // asc, rank asc) = (key desc, e asc)
+        for (int e = threadIdx.x; e < n; e += kBlock)
+          sm.ckey[e] = (e % K) < sm.gated[e / K] ? dkey(sm.csc[e]) : 0ull;
+        __syncthreads();
+        talon_budget_select(sm, n, K, W, room);
       }
-      // new slots in (parent slot, rank) order; every workgroup records parents and
-      // scores in shared memory, workgroup 0 also writes the node arrays
-      int carry = 0;
-      for (int f0 = 0; f0 < W; f0 += kBlock) {
-        const int f = f0 + threadIdx.x;
-        const int mine = (f < W) ? sm.kept[f] : 0;
-        int tot = 0;
-        const int ex = block_exclusive_scan(mine, sm.scan, &tot);
-        if (f < W) {
-          const int parent = sm.start[s] + f;
-          for (int j = 0; j < mine; ++j) {
-            const int slot = cnt + 1 + carry + ex + j;
-            const double sc = sm.pool[f * K + j];
-            sm.tscore[tb + slot] = sc;
-            sm.tpar[tb + slot] = static_cast<short>(parent);
-            if (blockIdx.x == 0) {
-              const size_t o = tb + slot;
-              a.tree.parent[o] = parent;
-              a.tree.token[o] = sm.ptok[f * K + j];
-              a.tree.depth[o] = layer;
-              a.tree.row[o] = slot;
-              a.tree.score[o] = sc;
-            }
-          }
-        }
-        carry += tot;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        sm.start[s] = cnt + 1;
-        sm.width[s] = carry;
-        sm.cnt[s] = cnt + carry;
-        sm.nlayers[s] = layer;
-        if (sm.cnt[s] >= B || carry == 0) sm.done[s] = 1;
-        if (carry == 0) atomicExch(&a.hdr->err, kErrCapacity);
-      }
-      __syncthreads();
-      if (!sm.done[s]) all_done = 0;
     }
-    if (all_done) break;
+    // new slots in (parent slot, rank) order: row f's kept entries follow those of rows < f
+    int carry = 0;
+    for (int f0 = 0; f0 < W; f0 += kBlock) {
+      const int f = f0 + threadIdx.x;
+      int tot = 0;
+      const int ex = block_exclusive_scan(f < W ? sm.kept[f] : 0, sm.scan, &tot);
+      if (f < W) sm.rowbase[f] = carry + ex;
+      carry += tot;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kBlock) {
+      const int f = e / K, j = e % K;
+      if (j >= sm.kept[f]) continue;
+      const int parent = start + f;
+      const int slot = cnt + 1 + sm.rowbase[f] + j;
+      const double sc = sm.csc[e];
+      sm.tscore[slot] = sc;
+      sm.tpar[slot] = static_cast<short>(parent);
+      const size_t o = tb + slot;
+      a.tree.parent[o] = parent;
+      a.tree.token[o] = sm.tok[parent * K + j];
+      a.tree.depth[o] = layer;
+      a.tree.row[o] = slot;
+      a.tree.score[o] = sc;
+    }
+    if (threadIdx.x == 0) {
+      sm.start = cnt + 1;
+      sm.width = carry;
+      sm.cnt = cnt + carry;
+      sm.layers = layer;
+      sm.carry = carry;
+      if (carry == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    }
+    __syncthreads();
+    if (sm.cnt >= B || sm.carry == 0) break;
   }
 
-  // ---------------- outputs of workgroup 0: root, counts and ancestor masks
-  if (blockIdx.x != 0 || !ok) return;
-  for (int s = threadIdx.x; s < a.S; s += kBlock) {
-    const size_t b = static_cast<size_t>(s) * cap;
-    a.tree.parent[b] = -1;
-    a.tree.token[b] = -1;
-    a.tree.depth[b] = 0;
-    a.tree.row[b] = 0;
-    a.tree.score[b] = 0.0;
-    a.tree.n_nodes[s] = sm.cnt[s] + 1;
-    a.tree.layers[s] = sm.nlayers[s];
+  // root, counts and ancestor-or-self masks
+  const int nn = sm.cnt + 1;
+  if (threadIdx.x == 0) {
+    a.tree.parent[tb] = -1;
+    a.tree.token[tb] = -1;
+    a.tree.depth[tb] = 0;
+    a.tree.row[tb] = 0;
+    a.tree.score[tb] = 0.0;
+    a.tree.n_nodes[s] = nn;
+    a.tree.layers[s] = sm.layers;
   }
   const int words = a.tree.words;
-  for (int e = threadIdx.x; e < a.S * cap; e += kBlock) {
-    const int s = e / cap, i = e % cap;
-    if (i > sm.cnt[s]) continue;
+  for (int i = threadIdx.x; i < nn; i += kBlock) {
     uint64_t acc[kMaxWords];
 #pragma unroll
     for (int w = 0; w < kMaxWords; ++w) acc[w] = 0;
-    for (int j = i; j >= 0; j = (j > 0) ? sm.tpar[s * cap + j] : -1) {
+    for (int j = i; j >= 0; j = (j > 0) ? sm.tpar[j] : -1) {
 #pragma unroll
       for (int u = 0; u < kMaxWords; ++u)
         if (u == (j >> 6)) acc[u] |= 1ull << (j & 63);
     }
-    uint64_t* an = a.tree.anc + static_cast<size_t>(e) * words;
+    uint64_t* an = a.tree.anc + (tb + i) * words;
 #pragma unroll
     for (int w = 0; w < kMaxWords; ++w)
       if (w < words) an[w] = acc[w];
@@ -397,33 +444,15 @@ int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st) {
-  void* args[] = {const_cast<TalonArgs*>(&a)};
-  hipError_t e;
+int launch_talon(const TalonArgs& a, int dtype, hipStream_t st) {
+  const dim3 grid(a.S * a.B * a.nch);
   if (dtype == 1)
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&talon_kernel<1>), dim3(grid),
-                                   dim3(kBlock), args, 0, st);
+    hipLaunchKernelGGL(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&talon_kernel<0>), dim3(grid),
-                                   dim3(kBlock), args, 0, st);
-  return e == hipSuccess ? 0 : -1;
-}
-
-int talon_max_grid(int dtype) {
-  // one workgroup per compute unit; queried once per device and dtype
-  static int cached[64][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  int& c = cached[dev][dtype ? 1 : 0];
-  if (c > 0) return c;
-  int ncu = 0, per = 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  hipError_t e = (dtype == 1)
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(&talon_kernel<1>), kBlock, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(&talon_kernel<0>), kBlock, 0);
-  if (e != hipSuccess || per < 1) return -1;
-  c = ncu;
-  return c;
+    hipLaunchKernelGGL(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  hipLaunchKernelGGL(talon_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace dtv

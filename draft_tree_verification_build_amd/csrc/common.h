@@ -70,6 +70,13 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Order-preserving 64-bit key of a double: larger value, larger key; -0 and +0 share one.
+__device__ __forceinline__ unsigned long long dkey(double d) {
+  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(d));
+  if ((u << 1) == 0) u = 0;
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
 // Block-wide reductions; `red` is a __shared__ scratch of at least kWaves entries of T.
 // Every thread returns the result. Contains two __syncthreads().
 template <typename T>

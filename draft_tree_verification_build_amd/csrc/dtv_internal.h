@@ -172,8 +172,7 @@ struct CompactArgs {
 };
 
 int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st);
-int launch_talon(const TalonArgs& a, int dtype, int grid, hipStream_t st);
-int talon_max_grid(int dtype);
+int launch_talon(const TalonArgs& a, int dtype, hipStream_t st);
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st);
 int launch_opt_init(const OptArgs& a, hipStream_t st);
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);

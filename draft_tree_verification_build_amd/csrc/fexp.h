@@ -37,21 +37,63 @@ __device__ __forceinline__ void exp_table_load(double* t) {
   for (int j = threadIdx.x; j < 64; j += blockDim.x) t[j] = kExp2_64[j];
 }
 
-// exp(d) for d <= 0 (d = -inf gives 0). `t` is the shared-memory copy of kExp2_64.
+// exp(d) for d <= 0 (d = -inf or NaN gives 0). `t` is the shared-memory copy of kExp2_64.
+// Branch-free, so that a caller's unrolled loop keeps all its table reads in flight.
 __device__ __forceinline__ double exp_nonpos(double d, const double* t) {
-  if (d < -745.0) return 0.0;
+  const bool under = !(d >= -745.0);
+  const double dc = under ? -745.0 : d;
   const double kInv = 0x1.71547652b82fep+6;   // 64 / ln2
   const double kL1 = 0x1.62e42fefa0000p-7;    // ln2/64, leading 36 bits
   const double kL2 = 0x1.cf79abc9e3b3ap-46;   // ln2/64 - kL1
-  const double k = rint(d * kInv);
+  const double k = rint(dc * kInv);
   const int n = static_cast<int>(k);
-  const double r = fma(-k, kL2, fma(-k, kL1, d));
+  const double r = fma(-k, kL2, fma(-k, kL1, dc));
   double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
   p = fma(r, p, 1.0 / 6.0);
   p = fma(r, p, 0.5);
   p = fma(r, p, 1.0);
   p = fma(r, p, 1.0);
-  return ldexp(t[n & 63] * p, n >> 6);
+  const double e = ldexp(t[n & 63] * p, n >> 6);
+  return under ? 0.0 : e;
+}
+
+// sum_j exp(x[j] - m) for x[j] <= m (entries of -inf contribute 0), each term as in
+// exp_nonpos. Groups of G terms are written in three passes (reductions, table reads,
+// scaling) so that the group's table reads are in flight together; G bounds the extra
+// registers.
+template <int N, int G = 8>
+__device__ __forceinline__ double exp_nonpos_sum(const float (&x)[N], double m, const double* t) {
+  static_assert(N % G == 0, "N must be a multiple of G");
+  const double kInv = 0x1.71547652b82fep+6;
+  const double kL1 = 0x1.62e42fefa0000p-7;
+  const double kL2 = 0x1.cf79abc9e3b3ap-46;
+  double s = 0.0;
+#pragma unroll
+  for (int g0 = 0; g0 < N; g0 += G) {
+    double p[G];
+    int n[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const double d = static_cast<double>(x[g0 + j]) - m;
+      const bool under = !(d >= -745.0);
+      const double dc = under ? -745.0 : d;
+      const double k = rint(dc * kInv);
+      n[j] = static_cast<int>(k);
+      const double r = fma(-k, kL2, fma(-k, kL1, dc));
+      double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+      q = fma(r, q, 1.0 / 6.0);
+      q = fma(r, q, 0.5);
+      q = fma(r, q, 1.0);
+      q = fma(r, q, 1.0);
+      p[j] = under ? 0.0 : q;
+    }
+    double tv[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) tv[j] = t[n[j] & 63];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s += ldexp(tv[j] * p[j], n[j] >> 6);
+  }
+  return s;
 }
 
 }  // namespace dtv

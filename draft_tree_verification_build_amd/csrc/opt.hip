@@ -40,12 +40,6 @@ __device__ __forceinline__ bool cand_before(const OptCand& a, const OptCand& b) 
   return a.j < b.j;
 }
 
-// Order-preserving 64-bit key of a double (larger value, larger key).
-__device__ __forceinline__ unsigned long long dkey(double d) {
-  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(d));
-  if ((u << 1) == 0) u = 0;  // -0 == +0
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
 
 // In-place bitonic sort of n (power of two) elements of shared memory by `before`.
 template <typename T, typename Cmp>

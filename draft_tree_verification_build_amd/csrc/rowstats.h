@@ -46,7 +46,6 @@ struct RowSmem {
   float wmax[kWaves];
   uint32_t wkey[kWaves];
   int warg[kWaves];
-  int wnv[kWaves];
   int wcnt[kWaves];
   uint32_t wtau[kWaves];
   int ncand;
@@ -60,36 +59,55 @@ __device__ __forceinline__ void row_smem_init(RowSmem& sm) { exp_table_load(sm.e
 constexpr int kCandCap = 512;   // candidate slots of the small-K selection (sortbuf entries)
 
 // Loads chunk `c` of `row` into registers. Out-of-range elements get key 0 and -inf.
-// Full, aligned chunks issue their four 16-byte loads back to back before using any.
+// For a 16-byte aligned row every thread issues its four 16-byte loads back to back
+// before using any: a vector past the row end is loaded from the row's last full vector
+// (valid memory) and masked, and only the one vector that straddles the row end (V not a
+// multiple of VEC) re-reads its valid elements one by one. Unaligned rows take scalar
+// loads throughout.
 template <int DT>
 __device__ __forceinline__ void load_chunk(const void* row, int V, int c, float (&x)[RowT<DT>::E],
                                            uint32_t (&key)[RowT<DT>::E]) {
   using R = RowT<DT>;
   const int t = threadIdx.x;
   const int base = c * R::CHUNK;
+  const int vfull = V / R::VEC;   // full 16-byte vectors in the row
   const bool aligned = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0);
-  if (aligned && base + R::CHUNK <= V) {
+  if (aligned && vfull > 0) {
     uint4 raw[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int i0 = base + i * kBlock * R::VEC + t * R::VEC;
-      raw[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
-                                               static_cast<size_t>(i0) * R::ESIZE);
+      const int vi = (base + i * kBlock * R::VEC) / R::VEC + t;
+      const int vc = vi < vfull ? vi : vfull - 1;
+      raw[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(row) + static_cast<size_t>(vc) * 16);
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+      const int vi = (base + i * kBlock * R::VEC) / R::VEC + t;
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-      if (DT) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x[i * 8 + e] = bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
-      } else {
+      for (int e = 0; e < R::VEC; ++e) {
+        float f;
+        if (DT)
+          f = bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu));
+        else
+          f = __uint_as_float(w[e]);
+        const bool ok = vi < vfull;
+        x[i * R::VEC + e] = ok ? f : -INFINITY;
+        key[i * R::VEC + e] = ok ? (f32_key(f) >> (32 - R::KEYBITS)) : 0u;
+      }
+      if (vi == vfull && vfull * R::VEC < V) {   // the straddling vector
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[i * 4 + e] = __uint_as_float(w[e]);
+        for (int e = 0; e < R::VEC; ++e) {
+          const int ix = vi * R::VEC + e;
+          if (ix < V) {
+            const float f = DT ? bf16_to_f32(static_cast<const uint16_t*>(row)[ix])
+                               : static_cast<const float*>(row)[ix];
+            x[i * R::VEC + e] = f;
+            key[i * R::VEC + e] = f32_key(f) >> (32 - R::KEYBITS);
+          }
+        }
       }
     }
-#pragma unroll
-    for (int j = 0; j < R::E; ++j) key[j] = f32_key(x[j]) >> (32 - R::KEYBITS);
     return;
   }
 #pragma unroll
@@ -203,16 +221,12 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     for (int e = R::VEC - 1; e >= 0; --e)
       if (key[i * R::VEC + e] == km) am = elem_index<DT>(c, i, e);
   am = wave_min(am);
-  int nv = 0;
-#pragma unroll
-  for (int j = 0; j < R::E; ++j) nv += __popcll(__ballot(key[j] != 0u));
+  // in-range elements of the chunk (padding has key 0; a stored -inf does not)
+  const int nvalid = min(max(V - c * R::CHUNK, 0), R::CHUNK);
   const float mw = (km == 0u) ? -INFINITY : (DT ? bf16key_to_f32(km) : key_to_f32(km));
   double se = 0.0;
-  if (km != 0u) {
-    const double md = static_cast<double>(mw);
-#pragma unroll
-    for (int j = 0; j < R::E; ++j)
-      if (key[j] != 0u) se += exp_nonpos(static_cast<double>(x[j]) - md, sm.exptab);
+  if (km != 0u) {  // wave-uniform; padding elements hold -inf and contribute exp(-inf) = 0
+    se = exp_nonpos_sum<R::E>(x, static_cast<double>(mw), sm.exptab);
   }
   se = wave_sum(se);
   const bool small = K <= 32;
@@ -232,15 +246,12 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     sm.warg[w] = am;
     sm.wse[w] = se;
     sm.wmax[w] = mw;
-    sm.wnv[w] = nv;
     sm.wcnt[w] = 0;
   }
   if (threadIdx.x == 0) sm.ncand = 0;
   __syncthreads();
 
   // ---- chunk results
-  int nvalid = 0;
-  for (int q = 0; q < kWaves; ++q) nvalid += sm.wnv[q];
   const int kk = K < nvalid ? K : nvalid;
   if (threadIdx.x == 0) {  // read by the workgroup that merges the row
     uint32_t KM = 0;
@@ -254,7 +265,7 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     double S = 0.0;
     for (int q = 0; q < kWaves; ++q) {
       if (sm.wkey[q] == KM && sm.warg[q] < AM) AM = sm.warg[q];
-      if (sm.wkey[q] != 0u) S += sm.wse[q] * exp(static_cast<double>(sm.wmax[q]) - static_cast<double>(M));
+      if (sm.wkey[q] != 0u) S += sm.wse[q] * exp_nonpos(static_cast<double>(sm.wmax[q]) - static_cast<double>(M), sm.exptab);
     }
     st_cc(&st->maxv, M);
     st_cc(&st->argmax, AM);
@@ -302,6 +313,9 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     __syncthreads();
   }
   // ---- the wave's own top-K by bisection of the key space
+  int nv = 0;   // in-range elements of this wave
+#pragma unroll
+  for (int j = 0; j < R::E; ++j) nv += __popcll(__ballot(key[j] != 0u));
   const int kw = K < nv ? K : nv;
   if (kw > 0) {
     uint32_t lo = 1u, hi = km + 1u;  // count(>= lo) >= kw > count(>= hi)
@@ -396,21 +410,21 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     ms.sumexp[c] = ld_cc(&st[c].sumexp);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    int am = 0;
-    for (int c = 0; c < nch; ++c) {
-      if (ms.maxv[c] > M) {  // chunks are in index order: the first maximum has the lowest index
-        M = ms.maxv[c];
-        am = ms.argmax[c];
-      }
+  if (threadIdx.x < 64) {  // wave 0: lane c holds chunk c (nch <= 64)
+    const int c = threadIdx.x;
+    const float mc = c < nch ? ms.maxv[c] : -INFINITY;
+    const float M = wave_max(mc);
+    // chunks are in index order: the first chunk reaching the maximum has the lowest index
+    const int first = wave_min(c < nch && mc == M ? c : 0x7FFFFFFF);
+    double term = 0.0;
+    if (c < nch && mc != -INFINITY)
+      term = ms.sumexp[c] * exp_nonpos(static_cast<double>(mc) - static_cast<double>(M), sm.exptab);
+    const double s = wave_sum(term);
+    if (c == 0) {
+      if (maxv) st_cc(maxv, M);
+      if (argmax) st_cc(argmax, ms.argmax[first < nch ? first : 0]);
+      if (lse) st_cc(lse, static_cast<double>(M) + log(s));
     }
-    double s = 0.0;
-    for (int c = 0; c < nch; ++c)
-      s += ms.sumexp[c] * exp(static_cast<double>(ms.maxv[c]) - static_cast<double>(M));
-    if (maxv) st_cc(maxv, M);
-    if (argmax) st_cc(argmax, am);
-    if (lse) st_cc(lse, static_cast<double>(M) + log(s));
   }
   int total = 0;
   for (int c = 0; c < nch; ++c) total += ms.cnt[c];
@@ -424,20 +438,32 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     if (j < ms.cnt[c]) ms.key[e] = sort_key(ld_cc(&cval[e]), ld_cc(&cidx[e]));
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < nch * K; e += kBlock) {
+  const int n = nch * K;
+  if (n <= 1024) {  // absent entries count as key 0, below every real key
+    for (int e = threadIdx.x; e < n; e += kBlock)
+      if ((e % K) >= ms.cnt[e / K]) ms.key[e] = 0ull;
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < n; e += kBlock) {
     const int c = e / K, j = e % K;
     if (j >= ms.cnt[c]) continue;
     const unsigned long long me = ms.key[e];
-    int rank = j;
-    for (int c2 = 0; c2 < nch; ++c2) {
-      if (c2 == c) continue;
-      int a = 0, b = ms.cnt[c2];  // entries of list c2 greater than me
-      const unsigned long long* l2 = ms.key + c2 * K;
-      while (a < b) {
-        const int m = (a + b) >> 1;
-        if (l2[m] > me) a = m + 1; else b = m;
+    int rank = 0;
+    if (n <= 1024) {
+      // count the larger keys of all lists (keys are unique); independent broadcast reads
+      for (int e2 = 0; e2 < n; ++e2) rank += ms.key[e2] > me ? 1 : 0;
+    } else {
+      rank = j;
+      for (int c2 = 0; c2 < nch; ++c2) {
+        if (c2 == c) continue;
+        int a = 0, b = ms.cnt[c2];  // entries of list c2 greater than me (binary search)
+        const unsigned long long* l2 = ms.key + c2 * K;
+        while (a < b) {
+          const int m = (a + b) >> 1;
+          if (l2[m] > me) a = m + 1; else b = m;
+        }
+        rank += a;
       }
-      rank += a;
     }
     if (rank < kk) {
       st_cc(&rv[rank], sort_key_value(me));

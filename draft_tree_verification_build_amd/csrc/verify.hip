@@ -4,9 +4,9 @@
 // largest value and its lowest index and folds it into the node's 64-bit best key with
 // one atomic max ((value key << 32) | ~index, so larger value wins, then lower index).
 // The workgroup that completes a sequence last walks its tree: node c matches when its
-// token equals the argmax at its parent; a node is accepted when no node on its root path
-// fails (one AND of its ancestor mask with the failure mask); the deepest accepted node,
-// lowest slot first, ends the path.
+// token equals the argmax at its parent; a node is accepted when every node on its root
+// path matches (checked by following parent links in shared memory); the deepest accepted
+// node, lowest slot first, ends the path.
 #include "dtv_internal.h"
 #include "rowstats.h"
 
@@ -16,9 +16,11 @@ constexpr int kVerifyMaxNodes = 1024;
 constexpr int kVerifyMaxWords = 16;
 
 struct VerifySmem {
-  RowSmem rs;
-  int a[kVerifyMaxNodes];
-  unsigned long long fail[kVerifyMaxWords];
+  int a[kVerifyMaxNodes];       // target argmax at every node
+  short par[kVerifyMaxNodes];   // parent slot
+  short dep[kVerifyMaxNodes];   // depth
+  int tok[kVerifyMaxNodes];     // drafted token
+  unsigned char bad[kVerifyMaxNodes];   // 1: token differs from the argmax at the parent
   unsigned long long redu[kWaves];
   int flag;
 };
@@ -59,29 +61,37 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   if (threadIdx.x == 0) atomicMax(&a.best[tb + i], best);
   if (!last_arrival(&a.tickets[s], static_cast<unsigned>(N * nch), &sm.flag)) return;
 
-  // ---- the walk, by the last workgroup of sequence s
-  const int words = a.tree.words;
+  // ---- the walk, by the last workgroup of sequence s. Everything it needs is loaded in
+  //      one parallel pass; acceptance then follows parent links in shared memory.
   for (int v = threadIdx.x; v < N; v += kBlock) {
     const unsigned long long b = __hip_atomic_load(&a.best[tb + v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.a[v] = sort_key_index(b);
-    a.best[tb + v] = 0ull;  // ready for the next call
-    if (a.argmax_out) a.argmax_out[tb + v] = sm.a[v];
-  }
-  for (int w = threadIdx.x; w < kVerifyMaxWords; w += kBlock) sm.fail[w] = 0ull;
-  __syncthreads();
-  for (int v = 1 + threadIdx.x; v < N; v += kBlock) {
     const int p = a.tree.parent[tb + v];
-    if (a.tree.token[tb + v] != sm.a[p]) atomicOr(&sm.fail[v >> 6], 1ull << (v & 63));
+    const int tok = a.tree.token[tb + v];
+    const int d = a.tree.depth[tb + v];
+    a.best[tb + v] = 0ull;  // ready for the next call
+    const int am = sort_key_index(b);
+    sm.a[v] = am;
+    sm.tok[v] = tok;
+    sm.par[v] = static_cast<short>(v == 0 ? -1 : p);
+    sm.dep[v] = static_cast<short>(d);
+    if (a.argmax_out) a.argmax_out[tb + v] = am;
   }
   __syncthreads();
-  // deepest accepted node, lowest slot among equals: maximise (depth << 20) | (2^20 - 1 - slot)
+  // a node is bad when its token is not the target argmax at its parent (or its parent
+  // link is not an earlier slot, which also bounds every walk below)
+  for (int v = threadIdx.x; v < N; v += kBlock) {
+    const int p = sm.par[v];
+    sm.bad[v] = (v > 0 && (p < 0 || p >= v || sm.tok[v] != sm.a[p])) ? 1 : 0;
+  }
+  __syncthreads();
+  // deepest accepted node, lowest slot among equals: maximise (depth << 20) | (2^20 - 1 - slot);
+  // node v is accepted when no node on its root path is bad (slots grow away from the root)
   unsigned long long pick = 0;
   for (int v = threadIdx.x; v < N; v += kBlock) {
-    const uint64_t* an = a.tree.anc + (tb + v) * words;
     bool ok = true;
-    for (int w = 0; w < words; ++w) ok = ok && ((an[w] & sm.fail[w]) == 0ull);
+    for (int u = v; u > 0 && ok; u = sm.par[u]) ok = !sm.bad[u];
     if (ok) {
-      const unsigned long long key2 = (static_cast<unsigned long long>(a.tree.depth[tb + v]) << 20) |
+      const unsigned long long key2 = (static_cast<unsigned long long>(sm.dep[v]) << 20) |
                                       static_cast<unsigned long long>(0xFFFFF - v);
       pick = key2 > pick ? key2 : pick;
     }
@@ -89,10 +99,8 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   pick = block_max(pick, sm.redu);
   const int vstar = 0xFFFFF - static_cast<int>(pick & 0xFFFFFull);
   const int A = static_cast<int>(pick >> 20);
-  const uint64_t* an = a.tree.anc + (tb + vstar) * words;
-  for (int u = threadIdx.x; u < N; u += kBlock)
-    if ((an[u >> 6] >> (u & 63)) & 1ull) a.path[tb + a.tree.depth[tb + u]] = u;
   if (threadIdx.x == 0) {
+    for (int u = vstar; u >= 0; u = sm.par[u]) a.path[tb + sm.dep[u]] = u;
     a.path_len[s] = A + 1;
     a.bonus[s] = sm.a[vstar];
   }

@@ -116,8 +116,11 @@ int dtv_tree_build_given(const dtv_tree* tree, int32_t S, void* ws, size_t ws_by
  * the best by score (ties: lower parent slot, then lower rank). New nodes take slots in
  * (parent slot, rank) order. The build stops when B draft nodes exist (N = B + 1).
  * Draft rows are keyed by slot: node i expands with table row i, so `draft` holds
- * R >= B + 1 rows per sequence. The whole layer loop runs in one launch.
- * Limits: 1 <= B < n_cap <= 1024, 1 <= K <= 64, B * K <= 4096, 0 <= alpha <= 1.
+ * R >= B + 1 rows per sequence. Only slots 0..B-1 can be expanded, so the call reduces
+ * rows 0..B-1 of every sequence in one data-parallel launch (Top-K and log-sum-exp per
+ * row) and runs each sequence's layer loop in a second launch, one workgroup per sequence.
+ * Limits: 1 <= B < n_cap <= 1024, 1 <= K <= 64, B * K <= 4096, 0 <= alpha <= 1,
+ * chunks * K <= 2048 (chunks = ceil(V / 8192) for bf16, ceil(V / 4096) for fp32).
  */
 size_t dtv_tree_build_talon_ws_bytes(int32_t S, int32_t B, int32_t K, int32_t V, int dtype);
 int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int dtype,
