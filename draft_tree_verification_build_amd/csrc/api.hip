@@ -218,34 +218,27 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
 }
 
 struct AttnPlan {
-  int wide, n_mtiles, n_split, kps, mcap;
+  int gpw, n_mtiles, n_split, kps, mcap;
 };
-// Query rows of a KV head (GQA heads packed, M = g * n_cap). Small row counts use
-// 128-row tiles (one 32-row group per wave); from 256 rows on, attn_wide_kernel gives
-// each wave two groups and spreads the ceil(M/32) groups evenly over ceil(groups/8)
-// tiles. Key ranges are split so the 256 compute units see about two workgroups each;
-// ranges are multiples of 64 keys and no shorter than `min_keys`.
+// Query rows of a KV head: M = g * n_cap (GQA heads packed), in ceil(M/32) groups of 32.
+// A bf16 tile is 4 waves of `gpw` groups: two groups per wave from 256 rows on, else one.
+// Key ranges are split so the 256 compute units see about two workgroups each; ranges are
+// multiples of 64 keys and no shorter than `min_keys` (each split costs a partial O row).
 AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int dtype) {
   AttnPlan p;
   const int g = Hq / Hkv;
   const int M = g * n_cap;
   const int T = P_max + n_cap;
-  p.wide = (dtype == DTV_BF16 && M >= 256) ? 1 : 0;
-  int min_keys = 256;
-  if (p.wide) {
-    const int G = (M + 31) / 32;
-    p.n_mtiles = (G + 7) / 8;
-    p.mcap = G * 32;
-    min_keys = 512;
-  } else {
-    p.n_mtiles = (M + 127) / 128;
-    p.mcap = p.n_mtiles * 128;
-  }
+  const int G = (M + 31) / 32;
+  p.gpw = (dtype == DTV_BF16 && M >= 256) ? 2 : 1;
+  p.n_mtiles = (G + 4 * p.gpw - 1) / (4 * p.gpw);
+  p.mcap = G * 32;
+  const int min_keys = p.gpw == 2 ? 512 : 256;
   const int tiles = S * Hkv * p.n_mtiles;
   int want = (512 + tiles - 1) / tiles;
   const int max_split = (T + min_keys - 1) / min_keys;
   if (want > max_split) want = max_split;
-  if (want > 32) want = 32;
+  if (want > dtv::kAttnMaxSplit) want = dtv::kAttnMaxSplit;
   if (want < 1) want = 1;
   int kps = (T + want - 1) / want;
   kps = (kps + 63) / 64 * 64;
@@ -258,18 +251,15 @@ struct AttnLayout {
   dtv::WsHeader* hdr;
   float* part_o;
   float* part_ml;
-  unsigned* tickets;
   size_t bytes;
 };
 AttnLayout attn_layout(void* ws, int S, int Hkv, int D, const AttnPlan& p) {
-  const size_t tiles = static_cast<size_t>(S) * Hkv * p.n_mtiles;
   const size_t np = p.n_split > 1 ? static_cast<size_t>(S) * Hkv * p.n_split * p.mcap : 0;
   Carver c(ws);
   AttnLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
   L.part_o = c.take<float>(np * D);
   L.part_ml = c.take<float>(np * 2);
-  L.tickets = c.take<unsigned>(tiles);
   L.bytes = c.off;
   return L;
 }
@@ -649,7 +639,7 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
   a.D = D;
   a.g = Hq / Hkv;
   a.scale = scale;
-  a.wide = plan.wide;
+  a.gpw = plan.gpw;
   a.n_mtiles = plan.n_mtiles;
   a.n_split = plan.n_split;
   a.kps = plan.kps;
@@ -658,7 +648,6 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
     const AttnLayout L = attn_layout(ws, S, Hkv, D, plan);
     a.part_o = L.part_o;
     a.part_ml = L.part_ml;
-    a.tickets = L.tickets;
     a.hdr = L.hdr;
   } else {
     a.hdr = static_cast<dtv::WsHeader*>(ws);

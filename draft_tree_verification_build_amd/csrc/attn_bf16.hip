@@ -1,47 +1,51 @@
-// Tree attention for large query sets (bf16, MFMA), gfx950.
+// Tree-masked attention, bf16 on MFMA (gfx950).
 //
-// Same computation as attn_bf16_kernel (attn.hip): each node attends to the prefix and to
-// its ancestors; GQA rows (node, head of the KV group) are packed so a K/V tile serves all
-// of them. This variant is organised for MFMA throughput when a KV head has hundreds of
-// query rows:
+// Each node attends to the prefix and to its ancestors (position P + j is visible to node
+// i when bit j of i's ancestor mask is set). Grouped-query heads are packed: for KV head kv
+// the g = Hq / Hkv query heads of every node form M = g * n_nodes rows (row r = node r / g,
+// head kv * g + r % g), so a K/V tile is read once for all of them.
 //
-// * Every wave owns two 32-row groups (64 query rows), so each K and V fragment it reads
-//   from LDS feeds two v_mfma_f32_32x32x16_bf16 instead of one, halving LDS traffic per
-//   flop; a workgroup (4 waves) covers up to 8 row groups.
-// * The G = ceil(M/32) row groups of a KV head are spread evenly over ceil(G/8) tiles, so
-//   ragged row counts (M = 8*65 or 513) do not leave a tile with one row.
-// * K/V are double-buffered in LDS: the global loads of block b+1 are issued before block
-//   b is computed and land in the other buffer afterwards, one barrier per 64-key block.
-// * The tree mask and the key-range tail are applied only in blocks that need them; the
-//   softmax scale is folded into one fma per score (exp2 domain), P is converted with the
-//   native packed bf16 conversion.
+// * S^T = K Q^T and O += P V with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Computing
+//   S^T rather than S leaves every lane holding 16 keys of one query row, exactly the
+//   operand layout the P V product needs, so P never leaves registers.
+// * A workgroup has 4 waves; each wave owns GPW 32-row groups (GPW = 2 for large query
+//   sets: every K and V fragment read from LDS then feeds two MFMAs, halving LDS traffic
+//   per flop). The ceil(M/32) row groups of a KV head are spread evenly over the tiles, so
+//   ragged row counts do not leave a tile nearly empty.
+// * K/V are double-buffered in LDS (K row-major, V transposed): the global loads of block
+//   b+1 are issued before block b is computed and land in the other buffer afterwards, one
+//   barrier per 64-key block. Every load is unconditional (clamped to a valid key) so all
+//   of them are in flight together.
+// * The tree mask and the key-range tail are applied only in blocks that need them, from
+//   one 64-bit visibility word per row and block. The softmax runs in the exp2 domain with
+//   the scale folded into one fma per score and a lazily moved reference maximum.
 // * Workgroup numbering is XCD-aware: all tiles of one (sequence, KV head, key split)
 //   share an XCD, hence its L2, since they stream the same keys and values.
 //
 // Key splits write (m, l, unnormalised O) partials per query row; attn_combine_rows merges
-// them.
+// them (a kernel boundary makes the partials of all XCDs visible).
 #include "dtv_internal.h"
 
 namespace dtv {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 wbf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float wf32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int kWBlock = 64;   // keys per LDS block
+constexpr int kKeyBlock = 64;   // keys per LDS block
 constexpr int kNumXcd = 8;    // XCDs of an MI355X; consecutive workgroups go to consecutive XCDs
 
-union WFrag8 {
-  wbf16x8 v;
+union Frag8 {
+  bf16x8 v;
   uint4 u;
   uint2 h[2];
   uint16_t s[8];
 };
 
 template <int D>
-struct WideSmem {
+struct AttnSmem {
   static constexpr int KS = D + 8;          // K row stride (elements)
-  static constexpr int VS = kWBlock + 4;    // V^T row stride (elements)
-  alignas(16) uint16_t ks[2][kWBlock * KS];
+  static constexpr int VS = kKeyBlock + 4;    // V^T row stride (elements)
+  alignas(16) uint16_t ks[2][kKeyBlock * KS];
   alignas(16) uint16_t vt[2][D * VS];
   alignas(16) float alpha[kWaves][2][32];
   alignas(16) float ml[kWaves][2][32][2];
@@ -51,8 +55,8 @@ struct WideSmem {
 // and the LDS stores: K vectors i (key (t + 256 i) / (D/8), dims 8 * ((t + 256 i) % (D/8)));
 // V keys kg*NV + u of dims 8*dc .. 8*dc+7 (dc = t % (D/8), kg = t / (D/8)).
 template <int D>
-struct WidePrefetch {
-  static constexpr int NV = kWBlock * D / 8 / kBlock;   // 16-byte vectors per thread (4 or 2)
+struct KvPrefetch {
+  static constexpr int NV = kKeyBlock * D / 8 / kBlock;   // 16-byte vectors per thread (4 or 2)
   uint4 k0, k1, k2, k3, v0, v1, v2, v3;                  // named members keep them in registers
   __device__ __forceinline__ uint4& k(int i) { return i == 0 ? k0 : i == 1 ? k1 : i == 2 ? k2 : k3; }
   __device__ __forceinline__ uint4& v(int i) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
@@ -69,9 +73,9 @@ __device__ __forceinline__ uint32_t half_of(const uint4& x, int e) {
 // masked out of the softmax, so they need no zeroing). Every load is unconditional so
 // that all of them are in flight together.
 template <int D>
-__device__ __forceinline__ WidePrefetch<D> wide_fetch(const uint16_t* kbase, const uint16_t* vbase, int kb, int k_hi) {
-  constexpr int NV = WidePrefetch<D>::NV;
-  WidePrefetch<D> r;
+__device__ __forceinline__ KvPrefetch<D> kv_fetch(const uint16_t* kbase, const uint16_t* vbase, int kb, int k_hi) {
+  constexpr int NV = KvPrefetch<D>::NV;
+  KvPrefetch<D> r;
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -88,10 +92,10 @@ __device__ __forceinline__ WidePrefetch<D> wide_fetch(const uint16_t* kbase, con
 
 // Stores a prefetched block into LDS buffer `buf`: K row-major, V transposed (V^T[d][key]).
 template <int D>
-__device__ __forceinline__ void wide_stage(WideSmem<D>& sm, int buf, const WidePrefetch<D>& r) {
-  constexpr int KS = WideSmem<D>::KS;
-  constexpr int VS = WideSmem<D>::VS;
-  constexpr int NV = WidePrefetch<D>::NV;
+__device__ __forceinline__ void kv_stage(AttnSmem<D>& sm, int buf, const KvPrefetch<D>& r) {
+  constexpr int KS = AttnSmem<D>::KS;
+  constexpr int VS = AttnSmem<D>::VS;
+  constexpr int NV = KvPrefetch<D>::NV;
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -143,7 +147,7 @@ __device__ __forceinline__ uint64_t block_visibility(int kb, int P, int k_hi, co
 // the unnormalised fp32 rows and their (m, l) as partials. A lane holds O rows
 // (i/4)*8 + 4h + i%4 of the group, column nt*32 + lr of tile nt.
 template <int D>
-__device__ __forceinline__ void wide_store(const AttnArgs& a, const wf32x16 (&oo)[D / 32], const float (*ml)[2],
+__device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D / 32], const float (*ml)[2],
                                            int s, int kv, int sp, int grp, int M, int h, int lr) {
   constexpr int NT = D / 32;
   const int g = a.g;
@@ -177,11 +181,12 @@ __device__ __forceinline__ void wide_store(const AttnArgs& a, const wf32x16 (&oo
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
-  __shared__ WideSmem<D> sm;
-  constexpr int KS = WideSmem<D>::KS;
-  constexpr int VS = WideSmem<D>::VS;
+template <int D, int GPW>
+__global__ __launch_bounds__(kBlock, 3 - GPW) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(GPW == 1 || GPW == 2, "one or two 32-row groups per wave");
+  __shared__ AttnSmem<D> sm;
+  constexpr int KS = AttnSmem<D>::KS;
+  constexpr int VS = AttnSmem<D>::VS;
   constexpr int NKS = D / 16;
   constexpr int NT = D / 32;
 
@@ -216,8 +221,8 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
   const int lane = t & 63;
   const int h = lane >> 5;
   const int lr = lane & 31;
-  const int gA = gl + 2 * w, gB = gl + 2 * w + 1;
-  const bool actA = gA < gh, actB = gB < gh;
+  const int gA = gl + GPW * w, gB = gA + 1;
+  const bool actA = gA < gh, actB = GPW == 2 && gB < gh;
   const int rA = gA * 32 + lr, rB = gB * 32 + lr;
   const bool okA = actA && rA < M, okB = actB && rB < M;
   const int nodeA = okA ? rA / g : 0, nodeB = okB ? rB / g : 0;
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
   const uint64_t* ancA = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeA) * a.words;
   const uint64_t* ancB = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeB) * a.words;
 
-  WFrag8 qA[NKS], qB[NKS];
+  Frag8 qA[NKS], qB[NKS];
   {
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     const uint16_t* qa = q + ((static_cast<size_t>(s) * a.n_cap + nodeA) * a.Hq + kv * g + (okA ? rA % g : 0)) * D;
@@ -238,11 +243,11 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       qA[ks].u = *reinterpret_cast<const uint4*>(qa + ks * 16 + 8 * h);
-      qB[ks].u = *reinterpret_cast<const uint4*>(qb + ks * 16 + 8 * h);
+      if constexpr (GPW == 2) qB[ks].u = *reinterpret_cast<const uint4*>(qb + ks * 16 + 8 * h);
     }
   }
 
-  wf32x16 oA[NT], oB[NT];
+  f32x16 oA[NT], oB[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -253,11 +258,11 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
   float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kWBlock - 1) / kWBlock : 0;
-  WidePrefetch<D> pf;
+  const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kKeyBlock - 1) / kKeyBlock : 0;
+  KvPrefetch<D> pf;
   if (nblk > 0) {
-    pf = wide_fetch<D>(kbase, vbase, k_lo, k_hi);
-    wide_stage<D>(sm, 0, pf);
+    pf = kv_fetch<D>(kbase, vbase, k_lo, k_hi);
+    kv_stage<D>(sm, 0, pf);
   }
   // Nothing may be outstanding at the loop head: otherwise the wait inserted for the
   // query registers inside the loop also waits for the block prefetch.
@@ -265,23 +270,23 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
   __syncthreads();
 
   for (int b = 0; b < nblk; ++b) {
-    const int kb = k_lo + b * kWBlock;
+    const int kb = k_lo + b * kKeyBlock;
     const int cur = b & 1;
     const bool more = b + 1 < nblk;
     // Visibility of this block's keys (tree keys or the range tail only); the ancestor
     // words are read before the prefetch is issued so that waiting for them does not
     // wait for the prefetch.
-    const bool need_mask = (kb + kWBlock > P) || (kb + kWBlock > k_hi);
+    const bool need_mask = (kb + kKeyBlock > P) || (kb + kKeyBlock > k_hi);
     uint64_t visA = ~0ull, visB = ~0ull;
     if (need_mask) {
       visA = block_visibility(kb, P, k_hi, ancA, okA) >> (4 * h);
-      visB = block_visibility(kb, P, k_hi, ancB, okB) >> (4 * h);
+      if constexpr (GPW == 2) visB = block_visibility(kb, P, k_hi, ancB, okB) >> (4 * h);
     }
-    if (more) pf = wide_fetch<D>(kbase, vbase, kb + kWBlock, k_hi);
+    if (more) pf = kv_fetch<D>(kbase, vbase, kb + kKeyBlock, k_hi);
 
     if (actA) {
       // ---- S^T = K Q^T for both row groups; each K fragment feeds two MFMAs
-      wf32x16 sA[2], sB[2];
+      f32x16 sA[2], sB[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -291,14 +296,14 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          WFrag8 kf;
+          Frag8 kf;
           kf.u = *reinterpret_cast<const uint4*>(&sm.ks[cur][(kt * 32 + lr) * KS + ks * 16 + 8 * h]);
           sA[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qA[ks].v, sA[kt], 0, 0, 0);
-          sB[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qB[ks].v, sB[kt], 0, 0, 0);
+          if constexpr (GPW == 2) sB[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qB[ks].v, sB[kt], 0, 0, 0);
         }
       }
       // ---- masks (tree block, range tail) only where a block needs them
-      auto softmax = [&](wf32x16 (&sc)[2], uint64_t vis, float& m_run, float& l_run) -> float {
+      auto softmax = [&](f32x16 (&sc)[2], uint64_t vis, float& m_run, float& l_run) -> float {
         if (need_mask) {
           // element (kt, i) of a lane is key kb + kt*32 + (i/4)*8 + 4h + i%4
           const uint32_t v_lo = static_cast<uint32_t>(vis), v_hi = static_cast<uint32_t>(vis >> 32);
@@ -339,7 +344,8 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
         return alpha;
       };
       const float alA = softmax(sA, visA, mA, lA);
-      const float alB = softmax(sB, visB, mB, lB);
+      float alB = 1.f;
+      if constexpr (GPW == 2) alB = softmax(sB, visB, mB, lB);
       // ---- rescale O; a lane holds O rows (i/4)*8 + 4h + i%4. Applied unconditionally
       //      (alpha is mostly 1): a branch around it makes the compiler keep two copies
       //      of the accumulators and spill.
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
       // ---- O += P V; each V fragment feeds two MFMAs
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
-        WFrag8 pa, pb;
+        Frag8 pa, pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           pa.v[j] = static_cast<__bf16>(sA[k2 >> 1][8 * (k2 & 1) + j]);
@@ -378,16 +384,16 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          WFrag8 vf;
+          Frag8 vf;
           const uint16_t* vrow = &sm.vt[cur][(nt * 32 + lr) * VS + 16 * k2 + 4 * h];
           vf.h[0] = *reinterpret_cast<const uint2*>(vrow);
           vf.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
           oA[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa.v, vf.v, oA[nt], 0, 0, 0);
-          oB[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb.v, vf.v, oB[nt], 0, 0, 0);
+          if constexpr (GPW == 2) oB[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb.v, vf.v, oB[nt], 0, 0, 0);
         }
       }
     }
-    if (more) wide_stage<D>(sm, cur ^ 1, pf);
+    if (more) kv_stage<D>(sm, cur ^ 1, pf);
     __syncthreads();
   }
 
@@ -401,12 +407,14 @@ __global__ __launch_bounds__(kBlock, 1) void attn_wide_kernel(AttnArgs a) {
     sm.ml[w][1][lr][1] = ltB;
   }
   __syncthreads();
-  if (actA) wide_store<D>(a, oA, sm.ml[w][0], s, kv, sp, gA, M, h, lr);
-  if (actB) wide_store<D>(a, oB, sm.ml[w][1], s, kv, sp, gB, M, h, lr);
+  if (actA) o_store<D>(a, oA, sm.ml[w][0], s, kv, sp, gA, M, h, lr);
+  if constexpr (GPW == 2)
+    if (actB) o_store<D>(a, oB, sm.ml[w][1], s, kv, sp, gB, M, h, lr);
 }
 
-// Merges the key splits of every query row of the wide kernel (partials indexed by row).
-template <int D>
+// Merges the key splits of every query row (partials indexed by row): O = sum_q O_q w_q / sum_q l_q w_q
+// with w_q = 2^(m_q - max m). One thread per 4 output values, D/4 threads per row.
+template <int D, int NS>
 __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   constexpr int TPR = D / 4;
   constexpr int RPB = kBlock / TPR;
@@ -419,25 +427,26 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   const int s = head / a.Hkv;
   const int N = a.n_nodes[s];
   if (N > a.n_cap || rr >= a.g * N) return;
-  float mx = -INFINITY;
-  for (int q = 0; q < a.n_split; ++q) {
-    const size_t pr = (static_cast<size_t>(head) * a.n_split + q) * rows_per_head + rr;
-    const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[pr * 2]);
-    if (ml.y > 0.f) mx = fmaxf(mx, ml.x);
-  }
-  float L = 0.f;
+  const size_t pr0 = static_cast<size_t>(head) * a.n_split * rows_per_head + rr;
+  float w[NS];
+  const float L = attn_split_weights<NS>(a.part_ml + pr0 * 2, static_cast<size_t>(rows_per_head) * 2, a.n_split, w);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q = 0; q < a.n_split; ++q) {
-    const size_t pr = (static_cast<size_t>(head) * a.n_split + q) * rows_per_head + rr;
-    const float2 ml = *reinterpret_cast<const float2*>(&a.part_ml[pr * 2]);
-    if (ml.y > 0.f) {
-      const float sc = __builtin_amdgcn_exp2f(ml.x - mx);
-      L += ml.y * sc;
-      const float4 o = *reinterpret_cast<const float4*>(&a.part_o[pr * D + c4 * 4]);
-      acc.x += o.x * sc;
-      acc.y += o.y * sc;
-      acc.z += o.z * sc;
-      acc.w += o.w * sc;
+#pragma unroll
+  for (int q0 = 0; q0 < NS; q0 += 8) {
+    if (q0 >= a.n_split) break;
+    float4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qq = min(q0 + u, a.n_split - 1);
+      o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float sc = w[q0 + u];   // 0 past n_split
+      acc.x += o[u].x * sc;
+      acc.y += o[u].y * sc;
+      acc.z += o[u].z * sc;
+      acc.w += o[u].w * sc;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -449,21 +458,36 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   orow[3] = static_cast<__bf16>(acc.w * inv);
 }
 
-int launch_attn_wide(const AttnArgs& a, hipStream_t st) {
+int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int units = a.S * a.Hkv * a.n_split;
   const int grid = ((units + kNumXcd - 1) / kNumXcd) * kNumXcd * a.n_mtiles;
-  if (a.D == 128)
-    hipLaunchKernelGGL(attn_wide_kernel<128>, dim3(grid), dim3(kBlock), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_wide_kernel<64>, dim3(grid), dim3(kBlock), 0, st, a);
+  if (a.D == 128) {
+    if (a.gpw == 2)
+      hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), dim3(grid), dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), dim3(grid), dim3(kBlock), 0, st, a);
+  } else {
+    if (a.gpw == 2)
+      hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), dim3(grid), dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), dim3(grid), dim3(kBlock), 0, st, a);
+  }
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.n_split > 1) {
     const int rpb = kBlock / (a.D / 4);
-    const int blocks = a.S * a.Hkv * ((a.mcap + rpb - 1) / rpb);
-    if (a.D == 128)
-      hipLaunchKernelGGL(attn_combine_rows_kernel<128>, dim3(blocks), dim3(kBlock), 0, st, a);
-    else
-      hipLaunchKernelGGL(attn_combine_rows_kernel<64>, dim3(blocks), dim3(kBlock), 0, st, a);
+    const dim3 blocks(a.S * a.Hkv * ((a.mcap + rpb - 1) / rpb));
+    const bool few = a.n_split <= 8;
+    if (a.D == 128) {
+      if (few)
+        hipLaunchKernelGGL((attn_combine_rows_kernel<128, 8>), blocks, dim3(kBlock), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_combine_rows_kernel<128, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
+    } else {
+      if (few)
+        hipLaunchKernelGGL((attn_combine_rows_kernel<64, 8>), blocks, dim3(kBlock), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_combine_rows_kernel<64, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
+    }
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

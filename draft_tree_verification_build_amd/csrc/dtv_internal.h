@@ -108,6 +108,33 @@ struct RowStatsArgs {
   float* mval;         // [R][K] merged values (scratch)
 };
 
+constexpr int kAttnMaxSplit = 32;   // key splits per (sequence, KV head, query tile)
+
+// Weights 2^(m_q - max) of the key splits of one query row, from its (m, l) partials at
+// ml[q * stride] (q < n <= NS). All loads are issued before any is used (a split index
+// past n re-reads split n-1 and gets weight 0). Returns the merged l.
+template <int NS>
+__device__ __forceinline__ float attn_split_weights(const float* ml, size_t stride, int n, float (&w)[NS]) {
+  float m[NS], l[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    const int qq = q < n ? q : n - 1;
+    const float2 v = *reinterpret_cast<const float2*>(ml + static_cast<size_t>(qq) * stride);
+    m[q] = v.x;
+    l[q] = (q < n) ? v.y : 0.f;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < NS; ++q) mx = l[q] > 0.f ? fmaxf(mx, m[q]) : mx;
+  float L = 0.f;
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    w[q] = l[q] > 0.f ? __builtin_amdgcn_exp2f(m[q] - mx) : 0.f;
+    L += l[q] * w[q];
+  }
+  return L;
+}
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -120,12 +147,11 @@ struct AttnArgs {
   int n_cap, words;
   int S, Hq, Hkv, D, g;
   float scale;          // softmax scale (1/sqrt(D) by default)
-  int wide;             // 1: attn_wide_kernel (two 32-row groups per wave), 0: attn_bf16_kernel
+  int gpw;              // bf16 kernel: 32-row query groups per wave (1 or 2)
   int n_mtiles, n_split, kps;  // query tiles per KV head, key splits, keys per split
   int mcap;             // partial rows per (sequence, KV head, split)
-  float* part_o;        // [S*Hkv][n_split][mcap][D] (wide) or [S*Hkv*n_mtiles][n_split][128][D]
+  float* part_o;        // [S*Hkv][n_split][mcap][D] unnormalised O of every key split
   float* part_ml;       // same rows, (m, l) pairs
-  unsigned* tickets;    // [S*Hkv*n_mtiles]
   WsHeader* hdr;
 };
 
@@ -179,7 +205,7 @@ int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
 int launch_opt_finalize(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
-int launch_attn_wide(const AttnArgs& a, hipStream_t st);
+int launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st);
 int launch_compact(const CompactArgs& a, hipStream_t st);
