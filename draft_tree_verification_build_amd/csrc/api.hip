@@ -218,22 +218,21 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
 }
 
 struct AttnPlan {
-  int gpw, n_mtiles, n_split, kps, mcap;
+  int n_mtiles, n_split, kps, mcap;
 };
-// Query rows of a KV head: M = g * n_cap (GQA heads packed), in ceil(M/32) groups of 32.
-// A bf16 tile is 4 waves of `gpw` groups: two groups per wave from 256 rows on, else one.
-// Key ranges are split so the 256 compute units see about two workgroups each; ranges are
-// multiples of 64 keys and no shorter than `min_keys` (each split costs a partial O row).
-AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int dtype) {
+// Query rows of a KV head: M = g * n_cap (GQA heads packed), in ceil(M/32) groups of 32;
+// a bf16 tile is 4 waves of one group each. Key ranges are split so the 256 compute units
+// see about two workgroups each; ranges are multiples of 64 keys and no shorter than 256
+// (each split costs a partial O row per query row).
+AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max) {
   AttnPlan p;
   const int g = Hq / Hkv;
   const int M = g * n_cap;
   const int T = P_max + n_cap;
   const int G = (M + 31) / 32;
-  p.gpw = (dtype == DTV_BF16 && M >= 256) ? 2 : 1;
-  p.n_mtiles = (G + 4 * p.gpw - 1) / (4 * p.gpw);
+  p.n_mtiles = (G + dtv::kWaves - 1) / dtv::kWaves;
   p.mcap = G * 32;
-  const int min_keys = p.gpw == 2 ? 512 : 256;
+  const int min_keys = 256;
   const int tiles = S * Hkv * p.n_mtiles;
   int want = (512 + tiles - 1) / tiles;
   const int max_split = (T + min_keys - 1) / min_keys;
@@ -597,7 +596,7 @@ size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv,
                               int32_t P_max, int dtype) {
   if (S < 1 || n_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P_max < 0 || !dtype_ok(dtype)) return 0;
   if (dtype != DTV_BF16) return up(sizeof(dtv::WsHeader));
-  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max, dtype)).bytes;
+  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max)).bytes;
 }
 
 int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
@@ -618,7 +617,7 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
     REQUIRE(D >= 4 && D <= 128 && D % 4 == 0, DTV_EUNSUPPORTED, "fp32 attention needs D%%4==0, D<=128, got %d", D);
     REQUIRE(P_max + tree->n_cap <= 16384, DTV_EUNSUPPORTED, "fp32 attention supports at most 16384 keys");
   }
-  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max, dtype);
+  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max);
   size_t need = dtv_tree_attn_ws_bytes(S, tree->n_cap, Hq, Hkv, D, P_max, dtype);
   REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   dtv::AttnArgs a;
@@ -639,7 +638,6 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
   a.D = D;
   a.g = Hq / Hkv;
   a.scale = scale;
-  a.gpw = plan.gpw;
   a.n_mtiles = plan.n_mtiles;
   a.n_split = plan.n_split;
   a.kps = plan.kps;

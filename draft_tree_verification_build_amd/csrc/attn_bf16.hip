@@ -8,10 +8,10 @@
 // * S^T = K Q^T and O += P V with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Computing
 //   S^T rather than S leaves every lane holding 16 keys of one query row, exactly the
 //   operand layout the P V product needs, so P never leaves registers.
-// * A workgroup has 4 waves; each wave owns GPW 32-row groups (GPW = 2 for large query
-//   sets: every K and V fragment read from LDS then feeds two MFMAs, halving LDS traffic
-//   per flop). The ceil(M/32) row groups of a KV head are spread evenly over the tiles, so
-//   ragged row counts do not leave a tile nearly empty.
+// * A workgroup has 4 waves, each owning one 32-row group; two workgroups share a compute
+//   unit so that one's softmax overlaps the other's MFMAs. The ceil(M/32) row groups of a
+//   KV head are spread evenly over the tiles, so ragged row counts do not leave a tile
+//   nearly empty.
 // * K/V are double-buffered in LDS (K row-major, V transposed): the global loads of block
 //   b+1 are issued before block b is computed and land in the other buffer afterwards, one
 //   barrier per 64-key block. Every load is unconditional (clamped to a valid key) so all
@@ -47,8 +47,8 @@ struct AttnSmem {
   static constexpr int VS = kKeyBlock + 4;    // V^T row stride (elements)
   alignas(16) uint16_t ks[2][kKeyBlock * KS];
   alignas(16) uint16_t vt[2][D * VS];
-  alignas(16) float alpha[kWaves][2][32];
-  alignas(16) float ml[kWaves][2][32][2];
+  alignas(16) float alpha[kWaves][32];
+  alignas(16) float ml[kWaves][32][2];
 };
 
 // One thread's share of a 64-key K/V block, held in registers between the global loads
@@ -181,9 +181,8 @@ __device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D 
   }
 }
 
-template <int D, int GPW>
-__global__ __launch_bounds__(kBlock, 3 - GPW) void attn_bf16_kernel(AttnArgs a) {
-  static_assert(GPW == 1 || GPW == 2, "one or two 32-row groups per wave");
+template <int D>
+__global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ AttnSmem<D> sm;
   constexpr int KS = AttnSmem<D>::KS;
   constexpr int VS = AttnSmem<D>::VS;
@@ -221,41 +220,33 @@ __global__ __launch_bounds__(kBlock, 3 - GPW) void attn_bf16_kernel(AttnArgs a) 
   const int lane = t & 63;
   const int h = lane >> 5;
   const int lr = lane & 31;
-  const int gA = gl + GPW * w, gB = gA + 1;
-  const bool actA = gA < gh, actB = GPW == 2 && gB < gh;
-  const int rA = gA * 32 + lr, rB = gB * 32 + lr;
-  const bool okA = actA && rA < M, okB = actB && rB < M;
-  const int nodeA = okA ? rA / g : 0, nodeB = okB ? rB / g : 0;
+  const int grp = gl + w;          // this wave's 32-row group
+  const bool act = grp < gh;
+  const int r = grp * 32 + lr;     // this lane's query row (lanes lr and lr + 32 share it)
+  const bool ok = act && r < M;
+  const int node = ok ? r / g : 0;
 
   const size_t kvoff = (static_cast<size_t>(s) * a.Hkv + kv) * a.P_cap * static_cast<size_t>(D);
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + kvoff;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + kvoff;
-  const uint64_t* ancA = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeA) * a.words;
-  const uint64_t* ancB = a.anc + (static_cast<size_t>(s) * a.n_cap + nodeB) * a.words;
+  const uint64_t* anc = a.anc + (static_cast<size_t>(s) * a.n_cap + node) * a.words;
 
-  Frag8 qA[NKS], qB[NKS];
+  Frag8 qf[NKS];
   {
-    const uint16_t* q = static_cast<const uint16_t*>(a.q);
-    const uint16_t* qa = q + ((static_cast<size_t>(s) * a.n_cap + nodeA) * a.Hq + kv * g + (okA ? rA % g : 0)) * D;
-    const uint16_t* qb = q + ((static_cast<size_t>(s) * a.n_cap + nodeB) * a.Hq + kv * g + (okB ? rB % g : 0)) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((static_cast<size_t>(s) * a.n_cap + node) * a.Hq + kv * g + (ok ? r % g : 0)) * D;
     // Unconditional loads: a padding row (past M) reads row 0's query, which is valid
     // memory; its scores stay finite and its output is never stored.
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qA[ks].u = *reinterpret_cast<const uint4*>(qa + ks * 16 + 8 * h);
-      if constexpr (GPW == 2) qB[ks].u = *reinterpret_cast<const uint4*>(qb + ks * 16 + 8 * h);
-    }
+    for (int ks = 0; ks < NKS; ++ks) qf[ks].u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * h);
   }
 
-  f32x16 oA[NT], oB[NT];
+  f32x16 oacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      oA[nt][i] = 0.f;
-      oB[nt][i] = 0.f;
-    }
-  float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
+    for (int i = 0; i < 16; ++i) oacc[nt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;   // reference max (log2 units) and row sum
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kKeyBlock - 1) / kKeyBlock : 0;
@@ -277,119 +268,93 @@ __global__ __launch_bounds__(kBlock, 3 - GPW) void attn_bf16_kernel(AttnArgs a) 
     // words are read before the prefetch is issued so that waiting for them does not
     // wait for the prefetch.
     const bool need_mask = (kb + kKeyBlock > P) || (kb + kKeyBlock > k_hi);
-    uint64_t visA = ~0ull, visB = ~0ull;
-    if (need_mask) {
-      visA = block_visibility(kb, P, k_hi, ancA, okA) >> (4 * h);
-      if constexpr (GPW == 2) visB = block_visibility(kb, P, k_hi, ancB, okB) >> (4 * h);
-    }
+    uint64_t vis = ~0ull;
+    if (need_mask) vis = block_visibility(kb, P, k_hi, anc, ok) >> (4 * h);
     if (more) pf = kv_fetch<D>(kbase, vbase, kb + kKeyBlock, k_hi);
 
-    if (actA) {
-      // ---- S^T = K Q^T for both row groups; each K fragment feeds two MFMAs
-      f32x16 sA[2], sB[2];
+    if (act) {
+      // ---- S^T = K Q^T for two 32-key tiles; lane holds keys kb + kt*32 + (i/4)*8 + 4h + i%4
+      f32x16 sc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sA[kt][i] = 0.f;
-          sB[kt][i] = 0.f;
-        }
+        for (int i = 0; i < 16; ++i) sc[kt][i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           Frag8 kf;
           kf.u = *reinterpret_cast<const uint4*>(&sm.ks[cur][(kt * 32 + lr) * KS + ks * 16 + 8 * h]);
-          sA[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qA[ks].v, sA[kt], 0, 0, 0);
-          if constexpr (GPW == 2) sB[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qB[ks].v, sB[kt], 0, 0, 0);
+          sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, sc[kt], 0, 0, 0);
         }
       }
       // ---- masks (tree block, range tail) only where a block needs them
-      auto softmax = [&](f32x16 (&sc)[2], uint64_t vis, float& m_run, float& l_run) -> float {
-        if (need_mask) {
-          // element (kt, i) of a lane is key kb + kt*32 + (i/4)*8 + 4h + i%4
-          const uint32_t v_lo = static_cast<uint32_t>(vis), v_hi = static_cast<uint32_t>(vis >> 32);
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const uint32_t bits = kt == 0 ? v_lo : v_hi;
-              if (!((bits >> ((i >> 2) * 8 + (i & 3))) & 1u)) sc[kt][i] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
+      if (need_mask) {
+        const uint32_t v_lo = static_cast<uint32_t>(vis), v_hi = static_cast<uint32_t>(vis >> 32);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-        // Lazy rescaling: the reference max m_run only moves when the block's max exceeds
-        // it by more than 8 (log2 units), so p <= 2^8 and the O rescale is rare. The final
-        // division by l makes the result independent of the reference chosen.
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t bits = kt == 0 ? v_lo : v_hi;
+            if (!((bits >> ((i >> 2) * 8 + (i & 3))) & 1u)) sc[kt][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      // ---- lazy rescaling: the reference max only moves when the block's max exceeds it
+      //      by more than 8 (log2 units), so p <= 2^8 and the O rescale is rare (the final
+      //      division by l makes the result independent of the reference). The branch is
+      //      wave-uniform.
+      if (__ballot(mx > m_run + 8.f) != 0ull) {
         float alpha = 1.f;
         if (mx > m_run + 8.f) {
           alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
           l_run *= alpha;
           m_run = mx;
         }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-        float sum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, -mref));
-            sc[kt][i] = p;
-            sum += p;
-          }
-        l_run += sum;
-        return alpha;
-      };
-      const float alA = softmax(sA, visA, mA, lA);
-      float alB = 1.f;
-      if constexpr (GPW == 2) alB = softmax(sB, visB, mB, lB);
-      // ---- rescale O; a lane holds O rows (i/4)*8 + 4h + i%4. Applied unconditionally
-      //      (alpha is mostly 1): a branch around it makes the compiler keep two copies
-      //      of the accumulators and spill.
-      {
-        if (h == 0) {
-          sm.alpha[w][0][lr] = alA;
-          sm.alpha[w][1][lr] = alB;
-        }
+        // a lane holds O rows (i/4)*8 + 4h + i%4 of the group
+        if (h == 0) sm.alpha[w][lr] = alpha;
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 fa = *reinterpret_cast<const float4*>(&sm.alpha[w][0][q4 * 8 + 4 * h]);
-          const float4 fb = *reinterpret_cast<const float4*>(&sm.alpha[w][1][q4 * 8 + 4 * h]);
+          const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[w][q4 * 8 + 4 * h]);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            oA[nt][q4 * 4 + 0] *= fa.x;
-            oA[nt][q4 * 4 + 1] *= fa.y;
-            oA[nt][q4 * 4 + 2] *= fa.z;
-            oA[nt][q4 * 4 + 3] *= fa.w;
-            oB[nt][q4 * 4 + 0] *= fb.x;
-            oB[nt][q4 * 4 + 1] *= fb.y;
-            oB[nt][q4 * 4 + 2] *= fb.z;
-            oB[nt][q4 * 4 + 3] *= fb.w;
+            oacc[nt][q4 * 4 + 0] *= al.x;
+            oacc[nt][q4 * 4 + 1] *= al.y;
+            oacc[nt][q4 * 4 + 2] *= al.z;
+            oacc[nt][q4 * 4 + 3] *= al.w;
           }
         }
         __builtin_amdgcn_wave_barrier();
       }
-      // ---- O += P V; each V fragment feeds two MFMAs
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, -mref));
+          sc[kt][i] = p;
+          sum += p;
+        }
+      l_run += sum;
+      // ---- O += P V over four 16-key steps; the A operand of step k2 is p values
+      //      8*(k2%2) .. +7 of key tile k2/2
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
-        Frag8 pa, pb;
+        Frag8 pf8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pa.v[j] = static_cast<__bf16>(sA[k2 >> 1][8 * (k2 & 1) + j]);
-          pb.v[j] = static_cast<__bf16>(sB[k2 >> 1][8 * (k2 & 1) + j]);
-        }
+        for (int j = 0; j < 8; ++j) pf8.v[j] = static_cast<__bf16>(sc[k2 >> 1][8 * (k2 & 1) + j]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           Frag8 vf;
           const uint16_t* vrow = &sm.vt[cur][(nt * 32 + lr) * VS + 16 * k2 + 4 * h];
           vf.h[0] = *reinterpret_cast<const uint2*>(vrow);
           vf.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
-          oA[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa.v, vf.v, oA[nt], 0, 0, 0);
-          if constexpr (GPW == 2) oB[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb.v, vf.v, oB[nt], 0, 0, 0);
+          oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf8.v, vf.v, oacc[nt], 0, 0, 0);
         }
       }
     }
@@ -398,18 +363,13 @@ __global__ __launch_bounds__(kBlock, 3 - GPW) void attn_bf16_kernel(AttnArgs a) 
   }
 
   // ---- row statistics in the O layout
-  const float ltA = lA + __shfl_xor(lA, 32, 64);
-  const float ltB = lB + __shfl_xor(lB, 32, 64);
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (h == 0) {
-    sm.ml[w][0][lr][0] = mA;
-    sm.ml[w][0][lr][1] = ltA;
-    sm.ml[w][1][lr][0] = mB;
-    sm.ml[w][1][lr][1] = ltB;
+    sm.ml[w][lr][0] = m_run;
+    sm.ml[w][lr][1] = l_tot;
   }
   __syncthreads();
-  if (actA) o_store<D>(a, oA, sm.ml[w][0], s, kv, sp, gA, M, h, lr);
-  if constexpr (GPW == 2)
-    if (actB) o_store<D>(a, oB, sm.ml[w][1], s, kv, sp, gB, M, h, lr);
+  if (act) o_store<D>(a, oacc, sm.ml[w], s, kv, sp, grp, M, h, lr);
 }
 
 // Merges the key splits of every query row (partials indexed by row): O = sum_q O_q w_q / sum_q l_q w_q
@@ -461,17 +421,10 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
 int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int units = a.S * a.Hkv * a.n_split;
   const int grid = ((units + kNumXcd - 1) / kNumXcd) * kNumXcd * a.n_mtiles;
-  if (a.D == 128) {
-    if (a.gpw == 2)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), dim3(grid), dim3(kBlock), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), dim3(grid), dim3(kBlock), 0, st, a);
-  } else {
-    if (a.gpw == 2)
-      hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), dim3(grid), dim3(kBlock), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), dim3(grid), dim3(kBlock), 0, st, a);
-  }
+  if (a.D == 128)
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.n_split > 1) {
     const int rpb = kBlock / (a.D / 4);

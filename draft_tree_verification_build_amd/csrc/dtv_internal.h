@@ -147,7 +147,6 @@ struct AttnArgs {
   int n_cap, words;
   int S, Hq, Hkv, D, g;
   float scale;          // softmax scale (1/sqrt(D) by default)
-  int gpw;              // bf16 kernel: 32-row query groups per wave (1 or 2)
   int n_mtiles, n_split, kps;  // query tiles per KV head, key splits, keys per split
   int mcap;             // partial rows per (sequence, KV head, split)
   float* part_o;        // [S*Hkv][n_split][mcap][D] unnormalised O of every key split
