@@ -284,10 +284,12 @@ struct SampleLayout {
   dtv::ChunkStat* st;
   unsigned* rtick;
   double* lse;
-  unsigned* stick;
+  unsigned long long* gbar;
+  double* xch;
   double* pbuf;
   size_t bytes;
 };
+constexpr int kSampleMaxGroup = 32;   // workgroups per sequence in the walk
 SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   const int nch = nch_of(V, dtype);
   const size_t rows = static_cast<size_t>(S) * n_cap * 2;
@@ -297,7 +299,9 @@ SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   L.st = c.take<dtv::ChunkStat>(rows * nch);
   L.rtick = c.take<unsigned>(rows);
   L.lse = c.take<double>(rows);
-  L.stick = c.take<unsigned>(S);
+  L.gbar = c.take<unsigned long long>(S);
+  // one exchange slot per rejection (at most n_cap - 1) and one for the bonus draw
+  L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * 64);
   L.pbuf = c.take<double>(static_cast<size_t>(S) * 2 * V);
   L.bytes = c.off;
   return L;
@@ -719,8 +723,18 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
   a.st = L.st;
   a.rtick = L.rtick;
   a.lse = L.lse;
-  a.stick = L.stick;
+  a.gbar = L.gbar;
+  a.xch = L.xch;
+  a.max_pass = tree->n_cap + 1;
   a.pbuf = L.pbuf;
+  // the walk's groups must all be resident at once: about one workgroup per compute unit
+  // in total (far below what the device holds), at most kSampleMaxGroup per sequence
+  const int max_blocks = dtv::sample_walk_max_blocks(dtype == DTV_BF16 ? 1 : 0);
+  REQUIRE(max_blocks >= S, DTV_EUNSUPPORTED, "S=%d sequences exceed the %d co-resident walk workgroups",
+          S, max_blocks);
+  int G = (max_blocks < 256 ? max_blocks : 256) / S;
+  if (G > kSampleMaxGroup) G = kSampleMaxGroup;
+  a.G = G < 1 ? 1 : G;
   return launched(dtv::launch_verify_sample(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 

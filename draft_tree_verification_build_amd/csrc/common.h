@@ -165,6 +165,10 @@ __device__ __forceinline__ T ld_cc(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Agent-scope acquire: after it, this workgroup's loads see everything made visible before
+// the observed signal (the L1/L2 copies this CU might still hold are invalidated).
+__device__ __forceinline__ void acquire_cc() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 // Wait until this wave's memory operations have completed (no compiler reordering across).
 __device__ __forceinline__ void drain() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -185,41 +189,41 @@ __device__ __forceinline__ bool last_arrival(unsigned* counter, unsigned n, int*
   if (threadIdx.x == 0) {
     const unsigned prev = atomic_add_cc(counter, 1u);
     const int last = (prev == n - 1) ? 1 : 0;
-    if (last) st_cc(counter, 0u);
+    if (last) {
+      st_cc(counter, 0u);
+      acquire_cc();
+    }
     *flag_lds = last;
   }
   __syncthreads();
   return *flag_lds != 0;
 }
 
-// Barrier over a co-resident grid (launched cooperatively). `bar[0]` counts arrivals,
-// `bar[1]` is the generation. The wait is bounded: after `limit` polls it gives up,
-// writes `timeout_code` into `*err` and returns false (callers then stop their loops).
-__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned nblocks, int* err,
-                                             int timeout_code, int* flag_lds) {
+// Barrier over a co-resident group of `n` workgroups on a 64-bit arrival counter that only
+// ever grows: arrival a belongs to barrier instance a / n, which is complete once the
+// counter reaches (a / n + 1) * n. The counter is only ever changed by atomic adds (no
+// reset store races with them); the caller zeroes it before the group's first barrier (in
+// an earlier launch). The wait is bounded: after `limit` polls it writes `timeout_code`
+// into `*err` and returns false (callers then stop their loops).
+__device__ __forceinline__ bool group_barrier(unsigned long long* counter, unsigned n, int* err,
+                                              int timeout_code, int* flag_lds) {
   drain();
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
-    const unsigned gen = ld_cc(&bar[1]);
-    drain();  // the generation is read before this workgroup arrives
-    const unsigned prev = atomic_add_cc(&bar[0], 1u);
-    if (prev == nblocks - 1) {
-      st_cc(&bar[0], 0u);
-      drain();
-      atomic_add_cc(&bar[1], 1u);
-    } else {
-      long polls = 0;
-      const long limit = 40000000;
-      while (ld_cc(&bar[1]) == gen) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++polls > limit) {
-          atomicExch(err, timeout_code);
-          ok = 0;
-          break;
-        }
+    const unsigned long long a = __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long target = (a / n + 1) * n;
+    long polls = 0;
+    const long limit = 40000000;
+    while (ld_cc(counter) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls > limit) {
+        atomicExch(err, timeout_code);
+        ok = 0;
+        break;
       }
     }
+    acquire_cc();
     *flag_lds = ok;
   }
   __syncthreads();

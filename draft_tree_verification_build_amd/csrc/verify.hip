@@ -135,7 +135,6 @@ struct SampleSmem {
   int flag;
   int first;
   int pick;
-  int nk;
   int accept;
 };
 
@@ -144,51 +143,203 @@ __device__ __forceinline__ float row_value(const void* row, int j) {
   return DT ? bf16_to_f32(static_cast<const uint16_t*>(row)[j]) : static_cast<const float*>(row)[j];
 }
 
-// Smallest k with sum_{j<=k} w_j > u * sum_j w_j (ascending float64 prefix sums), where
-// w_j = weight(j). Threads take contiguous index segments in order.
-template <typename W>
-__device__ int inverse_cdf(int V, double u, W weight, SampleSmem& sm) {
-  const int seg = (V + kBlock - 1) / kBlock;
-  const int j0 = threadIdx.x * seg;
-  const int j1 = min(V, j0 + seg);
+// The VEC logits of 16-byte vector vi of a row (VEC = 8 bf16 or 4 fp32).
+template <int DT>
+__device__ __forceinline__ void row_vec(const void* row, int vi, float (&x)[RowT<DT>::VEC]) {
+  const uint4 raw = reinterpret_cast<const uint4*>(row)[vi];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < RowT<DT>::VEC; ++e)
+    x[e] = DT ? bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) : __uint_as_float(w[e]);
+}
+
+// The walk's view of the current distribution p at node v: softmax of the target row
+// (pc null) or the normalised residual pc / zc; q is the softmax of the draft row. A
+// "unit" is a 16-byte vector of VEC consecutive logits when `vec` (rows 16-byte aligned,
+// V a multiple of VEC), else a single entry.
+template <int DT>
+struct WalkDist {
+  static constexpr int VEC = RowT<DT>::VEC;
+  const void* trow;
+  const void* drow;
+  double lt, ld;
+  const double* pc;
+  double zc;
+  const double* tab;
+  bool vec;
+
+  __device__ int width() const { return vec ? VEC : 1; }
+  __device__ double p(int j) const {
+    return pc ? ld_cc(pc + j) / zc : exp_nonpos(static_cast<double>(row_value<DT>(trow, j)) - lt, tab);
+  }
+  __device__ double q(int j) const {
+    return exp_nonpos(static_cast<double>(row_value<DT>(drow, j)) - ld, tab);
+  }
+  // p of the entries of unit a into out[0 .. width)
+  __device__ void p_unit(int a, double (&out)[VEC]) const {
+    if (!vec) {
+      out[0] = p(a);
+      return;
+    }
+    if (pc) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) out[e] = ld_cc(pc + static_cast<size_t>(a) * VEC + e) / zc;
+    } else {
+      float x[VEC];
+      row_vec<DT>(trow, a, x);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) out[e] = exp_nonpos(static_cast<double>(x[e]) - lt, tab);
+    }
+  }
+  __device__ void q_unit(int a, double (&out)[VEC]) const {
+    if (!vec) {
+      out[0] = q(a);
+      return;
+    }
+    float x[VEC];
+    row_vec<DT>(drow, a, x);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) out[e] = exp_nonpos(static_cast<double>(x[e]) - ld, tab);
+  }
+};
+
+// The G workgroups of a sequence share every V-wide pass: workgroup gi owns units
+// [u0, u1). Every exchange (one per pass) publishes into a slot of its own that no
+// workgroup has read before in this launch: per-workgroup slice sums plus two values the
+// owner of the next child's token adds (see the walk). Every workgroup then adds the
+// sums in workgroup order, so all of them see identical totals and take identical
+// decisions. A fresh slot per exchange matters on a multi-XCD GPU: re-reading one
+// location that another XCD rewrote can return this XCD's older cached copy.
+constexpr int kXchStride = 64;   // doubles per exchange slot (G <= 32 sums + 2 values)
+
+struct WalkGroup {
+  int gi, G;
+  int u0, u1;                 // this workgroup's units
+  unsigned long long* bar;    // the group's arrival counter
+  double* xch;                // [max_pass][kXchStride] exchange slots
+  int max_pass;
+  int* err;
+  int pass;                   // exchanges so far
+};
+
+// Publishes this workgroup's slice value (and, from the owner, extra values into slot
+// entries G and G+1), waits for the group and copies the slot into sm_vals[0 .. G+2).
+// Returns false on a barrier timeout or when the slots are exhausted.
+__device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0, double e1, double* sm_vals,
+                               int* flag) {
+  if (g.pass >= g.max_pass) {
+    if (threadIdx.x == 0) atomicExch(g.err, kErrCapacity);
+    return false;
+  }
+  double* slot = g.xch + static_cast<size_t>(g.pass) * kXchStride;
+  if (threadIdx.x == 0) {
+    st_cc(&slot[g.gi], mine);
+    if (owner) {
+      st_cc(&slot[g.G], e0);
+      st_cc(&slot[g.G + 1], e1);
+    }
+  }
+  ++g.pass;
+  if (!group_barrier(g.bar, static_cast<unsigned>(g.G), g.err, kErrTimeout, flag)) return false;
+  for (int q = threadIdx.x; q < g.G + 2; q += kBlock) sm_vals[q] = ld_cc(&slot[q]);
+  __syncthreads();
+  return true;
+}
+
+// One rejection: out = max(p - q, 0) over this workgroup's units (st_cc, so the owner's
+// entries are visible to the group after the exchange); returns the block-wide slice sum.
+template <int DT>
+__device__ double residual_slice(const WalkDist<DT>& d, double* out, const WalkGroup& g, SampleSmem& sm) {
+  constexpr int VEC = WalkDist<DT>::VEC;
+  const int w = d.width();
   double loc = 0.0;
-  for (int j = j0; j < j1; ++j) loc += weight(j);
+#pragma unroll 2
+  for (int a = g.u0 + static_cast<int>(threadIdx.x); a < g.u1; a += kBlock) {
+    double pv[VEC], qv[VEC];
+    d.p_unit(a, pv);
+    d.q_unit(a, qv);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (e < w) {
+        const double r = fmax(pv[e] - qv[e], 0.0);
+        st_cc(out + static_cast<size_t>(a) * w + e, r);
+        loc += r;
+      }
+    }
+  }
+  return block_sum(loc, sm.rs.redd);
+}
+
+// Inverse CDF inside this workgroup's units, continuing a running sum `base` (the mass of
+// all earlier units): the smallest entry k with base + sum_{j<=k} p(j) > target, or -1 if
+// the slice does not reach it. Threads take contiguous runs of units in order, so one
+// block scan of the per-thread sums orders them as the row.
+template <int DT>
+__device__ int slice_inverse_cdf(const WalkDist<DT>& d, const WalkGroup& g, double base, double target,
+                                 SampleSmem& sm) {
+  constexpr int VEC = WalkDist<DT>::VEC;
+  const int w = d.width();
+  const int n = g.u1 - g.u0;
+  const int per = (n + kBlock - 1) / kBlock;
+  const int a0 = g.u0 + static_cast<int>(threadIdx.x) * per, a1 = min(g.u1, a0 + per);
+  double loc = 0.0;
+#pragma unroll 2
+  for (int a = a0; a < a1; ++a) {
+    double pv[VEC];
+    d.p_unit(a, pv);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (e < w) loc += pv[e];
+  }
   double total = 0.0;
-  const double excl = block_exclusive_scan(loc, sm.wsum, &total);
-  const double target = u * total;
-  if (threadIdx.x == 0) sm.first = kBlock;
+  const double excl = base + block_exclusive_scan(loc, sm.wsum, &total);
+  if (threadIdx.x == 0) {
+    sm.first = kBlock;
+    sm.pick = -1;
+  }
   __syncthreads();
-  if (j1 > j0 && excl + loc > target) atomicMin(&sm.first, static_cast<int>(threadIdx.x));
-  __syncthreads();
-  if (threadIdx.x == 0) sm.pick = -1;
+  if (a1 > a0 && excl + loc > target) atomicMin(&sm.first, static_cast<int>(threadIdx.x));
   __syncthreads();
   if (static_cast<int>(threadIdx.x) == sm.first) {
     double run = excl;
-    int k = j1 - 1;
-    for (int j = j0; j < j1; ++j) {
-      run += weight(j);
-      if (run > target) {
-        k = j;
-        break;
+    int k = -1;
+    for (int a = a0; a < a1 && k < 0; ++a) {
+      double pv[VEC];
+      d.p_unit(a, pv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        if (e < w) {
+          run += pv[e];
+          if (k < 0 && run > target) k = a * w + e;
+        }
       }
     }
-    sm.pick = k;
-  }
-  __syncthreads();
-  if (sm.pick < 0 && threadIdx.x == 0) {  // rounding left the target at the very end
-    int k = V - 1;
-    while (k > 0 && !(weight(k) > 0.0)) --k;
-    sm.pick = k;
+    sm.pick = k < 0 ? a1 * w - 1 : k;   // rounding between the two sums: end of the run
   }
   __syncthreads();
   return sm.pick;
 }
 
+// log-sum-exp of a row from its chunk statistics (nch <= 64), by wave 0; the result is
+// valid in lane 0.
+__device__ __forceinline__ double chunk_lse(const ChunkStat* st, int nch, const double* tab) {
+  const int c = threadIdx.x;
+  const float mc = c < nch ? ld_cc(&st[c].maxv) : -INFINITY;
+  const double sc = c < nch ? ld_cc(&st[c].sumexp) : 0.0;
+  const float M = wave_max(mc);
+  const double term = (c < nch && mc != -INFINITY)
+                          ? sc * exp_nonpos(static_cast<double>(mc) - static_cast<double>(M), tab) : 0.0;
+  const double sum = wave_sum(term);
+  return static_cast<double>(M) + log(sum);
+}
+
+// Phase 1: log-sum-exp of every node's target and draft rows, one workgroup per
+// (sequence, node, row, chunk); the last chunk of a row merges.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void verify_sample_kernel(SampleArgs a) {
-  __shared__ SampleSmem sm;
+__global__ __launch_bounds__(kBlock) void sample_lse_kernel(SampleArgs a) {
+  __shared__ RowSmem rs;
   using Rw = RowT<DT>;
-  row_smem_init(sm.rs);
+  row_smem_init(rs);
   __syncthreads();
   const int nch = a.nch;
   const int cap = a.tree.n_cap;
@@ -199,6 +350,9 @@ __global__ __launch_bounds__(kBlock) void verify_sample_kernel(SampleArgs a) {
   bid /= 2;
   const int i = bid % cap;
   const int s = bid / cap;
+  // the walk's group barrier counters start every call at zero
+  if (c == 0 && which == 0 && i == 0 && threadIdx.x == 0)
+    __hip_atomic_exchange(&a.gbar[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int N = a.tree.n_nodes[s];
   if (i >= N) return;
   if (N > cap) {
@@ -206,44 +360,66 @@ __global__ __launch_bounds__(kBlock) void verify_sample_kernel(SampleArgs a) {
     return;
   }
   const size_t tb = static_cast<size_t>(s) * cap;
-  const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
-  {
-    const int r = a.tree.row[tb + i];
-    const char* row = static_cast<const char*>(which ? a.draft : a.target) +
-                      (static_cast<size_t>(s) * a.R + r) * row_bytes;
-    float x[Rw::E];
-    uint32_t key[Rw::E];
-    load_chunk<DT>(row, a.V, c, x, key);
-    const size_t rr = (tb + i) * 2 + which;
-    chunk_reduce<DT>(x, key, c, a.V, 0, &a.st[rr * nch + c], nullptr, nullptr, nullptr, sm.rs);
-    if (last_arrival(&a.rtick[rr], nch, &sm.flag)) {
-      // log-sum-exp of the row from its chunks
-      if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int q = 0; q < nch; ++q) M = fmaxf(M, ld_cc(&a.st[rr * nch + q].maxv));
-        double sum = 0.0;
-        for (int q = 0; q < nch; ++q)
-          sum += ld_cc(&a.st[rr * nch + q].sumexp) *
-                 exp(static_cast<double>(ld_cc(&a.st[rr * nch + q].maxv)) - static_cast<double>(M));
-        st_cc(&a.lse[rr], static_cast<double>(M) + log(sum));
-      }
+  const int r = a.tree.row[tb + i];
+  const char* row = static_cast<const char*>(which ? a.draft : a.target) +
+                    (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
+  float x[Rw::E];
+  uint32_t key[Rw::E];
+  load_chunk<DT>(row, a.V, c, x, key);
+  const size_t rr = (tb + i) * 2 + which;
+  chunk_reduce<DT>(x, key, c, a.V, 0, &a.st[rr * nch + c], nullptr, nullptr, nullptr, rs);
+  if (last_arrival(&a.rtick[rr], nch, &rs.flag)) {
+    if (threadIdx.x < 64) {
+      const double l = chunk_lse(a.st + rr * nch, nch, rs.exptab);
+      if (threadIdx.x == 0) a.lse[rr] = l;   // read after the kernel boundary
     }
   }
-  if (!last_arrival(&a.stick[s], static_cast<unsigned>(N * 2 * nch), &sm.flag)) return;
+}
 
-  // ---------------- the walk of sequence s
+// Phase 2: the walk of sequence blockIdx.x / G, shared by its G workgroups (the group
+// barrier needs them all resident: the launch keeps the grid within what the device holds).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
+  __shared__ SampleSmem sm;
+  __shared__ double gvals[kXchStride];
+  using Rw = RowT<DT>;
+  row_smem_init(sm.rs);
+  const int s = blockIdx.x / a.G;
+  const int cap = a.tree.n_cap;
+  const int N = a.tree.n_nodes[s];
+  if (N < 1 || N > cap) {   // every workgroup of the group leaves: no barrier is entered
+    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    return;
+  }
+  const size_t tb = static_cast<size_t>(s) * cap;
+  const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.par[v] = static_cast<short>(a.tree.parent[tb + v]);
     sm.tok[v] = a.tree.token[tb + v];
-    sm.lset[v] = ld_cc(&a.lse[(tb + v) * 2 + 0]);
-    sm.lsed[v] = ld_cc(&a.lse[(tb + v) * 2 + 1]);
+    sm.lset[v] = a.lse[(tb + v) * 2 + 0];
+    sm.lsed[v] = a.lse[(tb + v) * 2 + 1];
   }
   __syncthreads();
+  const bool vec = (a.V % Rw::VEC) == 0 && (row_bytes % 16) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.draft)) & 15u) == 0;
+  WalkGroup grp;
+  grp.gi = blockIdx.x % a.G;
+  grp.G = a.G;
+  {
+    const int units = vec ? a.V / Rw::VEC : a.V;
+    grp.u0 = static_cast<int>(static_cast<long>(units) * grp.gi / a.G);
+    grp.u1 = static_cast<int>(static_cast<long>(units) * (grp.gi + 1) / a.G);
+  }
+  grp.bar = a.gbar + s;
+  grp.max_pass = a.max_pass;
+  grp.xch = a.xch + static_cast<size_t>(s) * a.max_pass * kXchStride;
+  grp.err = &a.hdr->err;
+  grp.pass = 0;
   double* P[2] = {a.pbuf + static_cast<size_t>(s) * 2 * a.V, a.pbuf + (static_cast<size_t>(s) * 2 + 1) * a.V};
   const double inv32 = 1.0 / 4294967296.0;
+  const bool lead = grp.gi == 0;
   int v = 0, A = 0;
-  int bonus = 0;
-  if (threadIdx.x == 0) a.path[tb] = 0;
+  if (lead && threadIdx.x == 0) a.path[tb] = 0;
   for (;;) {
     // children of v in slot order
     const int seg = (N + kBlock - 1) / kBlock;
@@ -256,19 +432,24 @@ __global__ __launch_bounds__(kBlock) void verify_sample_kernel(SampleArgs a) {
       if (sm.par[k] == v) sm.kids[pos++] = k;
     __syncthreads();
     const int r = a.tree.row[tb + v];
-    const void* trow = static_cast<const char*>(a.target) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
-    const void* drow = static_cast<const char*>(a.draft) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
-    const double lt = sm.lset[v], ld = sm.lsed[v];
-    int cur = -1;        // -1: p is softmax(target); else P[cur] / zc
-    double zc = 1.0;
+    WalkDist<DT> d;
+    d.trow = static_cast<const char*>(a.target) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
+    d.drow = static_cast<const char*>(a.draft) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
+    d.lt = sm.lset[v];
+    d.ld = sm.lsed[v];
+    d.pc = nullptr;
+    d.zc = 1.0;
+    d.tab = sm.rs.exptab;
+    d.vec = vec;
+    int cur = -1;
     int accepted = -1;
+    double px_next = 0.0;   // p at the next child's token, as published by the last exchange
     for (int q = 0; q < nk; ++q) {
       const int ch = sm.kids[q];
       if (threadIdx.x == 0) {
         const int x = sm.tok[ch];
-        const double px = (cur < 0) ? exp_nonpos(static_cast<double>(row_value<DT>(trow, x)) - lt, sm.rs.exptab)
-                                    : P[cur][x] / zc;
-        const double qx = exp_nonpos(static_cast<double>(row_value<DT>(drow, x)) - ld, sm.rs.exptab);
+        const double px = (q == 0) ? d.p(x) : px_next;   // the first try reads the target row
+        const double qx = d.q(x);
         const double u = (static_cast<double>(a.u_acc[tb + ch]) + 0.5) * inv32;
         sm.accept = (qx > 0.0) ? (u < px / qx ? 1 : 0) : (px > 0.0 ? 1 : 0);
       }
@@ -278,55 +459,115 @@ __global__ __launch_bounds__(kBlock) void verify_sample_kernel(SampleArgs a) {
         __syncthreads();
         break;
       }
-      // rejection: residual (p - q)+ into the other buffer
+      // rejection: residual (p - q)+ into the other buffer; kept only if it sums to > 0.
+      // The owner of the next child's token publishes, for that token, the new residual
+      // and the current p (used if the residual sums to 0).
       const int nxt = (cur == 0) ? 1 : 0;
-      double loc = 0.0;
-      for (int j = threadIdx.x; j < a.V; j += kBlock) {
-        const double pj = (cur < 0) ? exp_nonpos(static_cast<double>(row_value<DT>(trow, j)) - lt, sm.rs.exptab)
-                                    : P[cur][j] / zc;
-        const double qj = exp_nonpos(static_cast<double>(row_value<DT>(drow, j)) - ld, sm.rs.exptab);
-        const double rj = fmax(pj - qj, 0.0);
-        P[nxt][j] = rj;
-        loc += rj;
+      const double part = residual_slice<DT>(d, P[nxt], grp, sm);
+      const int xn = (q + 1 < nk) ? sm.tok[sm.kids[q + 1]] : -1;
+      const int xu = vec ? xn / Rw::VEC : xn;
+      const bool owner = xn >= 0 && xu >= grp.u0 && xu < grp.u1;
+      double e0 = 0.0, e1 = 0.0;
+      if (owner && threadIdx.x == 0) {
+        e1 = d.p(xn);
+        e0 = fmax(e1 - d.q(xn), 0.0);   // the entry residual_slice stored for xn
       }
-      const double z = block_sum(loc, sm.rs.redd);
-      if (z > 0.0) {  // otherwise p is kept
+      if (!group_exchange(grp, part, owner, e0, e1, gvals, &sm.flag)) return;
+      double z = 0.0;
+      for (int k = 0; k < grp.G; ++k) z += gvals[k];
+      if (z > 0.0) {
         cur = nxt;
-        zc = z;
+        d.pc = P[cur];
+        d.zc = z;
+        px_next = gvals[grp.G] / z;
+      } else {
+        px_next = gvals[grp.G + 1];
       }
-      __syncthreads();
     }
     if (accepted >= 0) {
       v = accepted;
       ++A;
-      if (threadIdx.x == 0) a.path[tb + A] = v;
+      if (lead && threadIdx.x == 0) a.path[tb + A] = v;
       continue;
     }
+    // bonus: inverse CDF of the current p with u_res[v]; slice masses first
     const double u = (static_cast<double>(a.u_res[tb + v]) + 0.5) * inv32;
-    if (cur < 0) {
-      bonus = inverse_cdf(a.V, u, [&](int j) {
-        return exp_nonpos(static_cast<double>(row_value<DT>(trow, j)) - lt, sm.rs.exptab);
-      }, sm);
-    } else {
-      const double* pc = P[cur];
-      const double z = zc;
-      bonus = inverse_cdf(a.V, u, [&](int j) { return pc[j] / z; }, sm);
+    double mass = 0.0;
+    {
+      constexpr int VEC = Rw::VEC;
+      const int w = d.width();
+      double loc = 0.0;
+#pragma unroll 2
+      for (int a2 = grp.u0 + static_cast<int>(threadIdx.x); a2 < grp.u1; a2 += kBlock) {
+        double pv[VEC];
+        d.p_unit(a2, pv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (e < w) loc += pv[e];
+      }
+      mass = block_sum(loc, sm.rs.redd);
+    }
+    if (!group_exchange(grp, mass, false, 0.0, 0.0, gvals, &sm.flag)) return;
+    double total = 0.0;
+    for (int k = 0; k < grp.G; ++k) total += gvals[k];
+    const double target = u * total;
+    // the first workgroup whose slice takes the running sum past the target draws the
+    // token; if rounding leaves the target at the end, the last slice with mass does
+    double before = 0.0, mybase = 0.0;
+    int owner = -1, last_pos = 0;
+    for (int k = 0; k < grp.G; ++k) {
+      if (k == grp.gi) mybase = before;
+      if (owner < 0 && gvals[k] > 0.0 && before + gvals[k] > target) owner = k;
+      if (gvals[k] > 0.0) last_pos = k;
+      before += gvals[k];
+    }
+    if (owner < 0) owner = last_pos;
+    if (grp.gi == owner) {
+      int k = slice_inverse_cdf<DT>(d, grp, mybase, target, sm);
+      if (threadIdx.x == 0) {
+        const int hi = grp.u1 * d.width() - 1, lo = grp.u0 * d.width();
+        if (k < 0) k = hi;
+        while (k > lo && !(d.p(k) > 0.0)) --k;   // the drawn entry carries mass
+        a.bonus[s] = k;
+      }
     }
     break;
   }
-  if (threadIdx.x == 0) {
-    a.path_len[s] = A + 1;
-    a.bonus[s] = bonus;
-  }
+  if (lead && threadIdx.x == 0) a.path_len[s] = A + 1;
 }
 
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st) {
   const dim3 grid(S * a.tree.n_cap * 2 * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(verify_sample_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(sample_lse_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(verify_sample_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(sample_lse_kernel<0>, grid, dim3(kBlock), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  // An ordinary launch on the caller's stream: the grid (S * G) is at most the number of
+  // workgroups the device holds at once, so every group is resident together once the
+  // stream reaches this kernel. (A cooperative launch is avoided: measured on MI355X it
+  // let consecutive walks share the group barrier and time out now and then.)
+  if (dtype == 1)
+    hipLaunchKernelGGL(sample_walk_kernel<1>, dim3(S * a.G), dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(sample_walk_kernel<0>, dim3(S * a.G), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Workgroups of the walk kernel that can be resident at once (queried once per device).
+int sample_walk_max_blocks(int dtype) {
+  static int cached[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int& c = cached[dev][dtype ? 1 : 0];
+  if (c > 0) return c;
+  int ncu = 0, per = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const void* fn = dtype ? reinterpret_cast<const void*>(&sample_walk_kernel<1>)
+                         : reinterpret_cast<const void*>(&sample_walk_kernel<0>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kBlock, 0) != hipSuccess || per < 1) return -1;
+  c = ncu * per;
+  return c;
 }
 
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st) {
