@@ -528,6 +528,7 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
   REQUIRE(S >= 1 && V >= 1, DTV_EINVAL, "S=%d V=%d", S, V);
   REQUIRE(n >= 1 && n + 1 <= tree->n_cap, DTV_ECAPACITY, "n+1=%d exceeds n_cap=%d", n + 1, tree->n_cap);
   REQUIRE(n <= 1023, DTV_EUNSUPPORTED, "n=%d exceeds 1023", n);
+  REQUIRE(V <= (1 << 22), DTV_EUNSUPPORTED, "V=%d exceeds 4194304", V);
   REQUIRE(max_layers >= 1 && max_layers <= 64, DTV_EUNSUPPORTED, "max_layers=%d outside 1..64", max_layers);
   REQUIRE(delta >= 0.0 && isfinite(delta), DTV_EINVAL, "delta=%g", delta);
   REQUIRE(static_cast<long>(R) >= 1 + static_cast<long>(max_layers - 1) * n, DTV_EINVAL,
@@ -586,6 +587,10 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
     long K = need > 8 ? need : 8;
     if (K > per_row) K = per_row;
     a.K = static_cast<int>(K);
+    long Kc = (K + nch - 1) / nch;
+    if (Kc < 2) Kc = 2;
+    if (Kc > K) Kc = K;
+    a.Kc = static_cast<int>(Kc);
     if (dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st)) return launched(-1);
     long kept = W * per_row;
     if (kept > n) kept = n;

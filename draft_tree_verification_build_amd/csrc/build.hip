@@ -12,6 +12,7 @@
 // of one sequence inside one workgroup on those small per-row lists.
 #include "dtv_internal.h"
 #include "rowstats.h"
+#include "select.h"
 
 namespace dtv {
 
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void talon_rows_kernel(TalonArgs a) {
 struct TalonSelSmem {
   double redd[kWaves];
   int redi[kWaves];
-  unsigned long long redu[kWaves];
+  RadixSmem rs;
   double lp[kTalonMaxPool];     // log p_d of every row's list entries, row f at f*K
   int tok[kTalonMaxPool];       // their tokens
   double csc[kTalonMaxPool];    // scores of the current layer's candidates, e = f*K + j
@@ -119,79 +120,16 @@ struct TalonSelSmem {
   int kept[1024];               // per frontier row: candidates kept
   int rowbase[1024];            // per frontier row: first new slot - (cnt + 1)
   int scan[kBlock];
-  int hist[kBlock];             // radix-selection histogram (256 digits)
-  int sel_digit, sel_rem;
   int cnt, start, width, layers, carry;
 };
 
 // Keeps the `room` best candidates (ckey[e] != 0) by (key desc, e asc) and counts them per
-// frontier row into kept[]: radix selection of the room-th largest key T (8 bits a pass,
-// starting at the first byte where the candidate keys differ), then every key above T and,
-// of the keys equal to T, those with the lowest e. Requires more than `room` candidates.
+// frontier row into kept[]: the room-th largest key T by radix selection, then every key
+// above T and, of the keys equal to T, those with the lowest e. Requires more than `room`
+// candidates.
 __device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int room) {
-  unsigned long long kmax = 0ull, kmin = ~0ull;
-  for (int e = threadIdx.x; e < n; e += kBlock) {
-    const unsigned long long k = sm.ckey[e];
-    if (k != 0ull) {
-      kmax = k > kmax ? k : kmax;
-      kmin = k < kmin ? k : kmin;
-    }
-  }
-  kmax = block_max(kmax, sm.redu);
-  kmin = block_min(kmin, sm.redu);
-  const unsigned long long diff = kmax ^ kmin;
-  int top = 0;   // highest byte where keys differ
-  for (int b = 7; b >= 0; --b)
-    if ((diff >> (8 * b)) & 0xFFull) {
-      top = b;
-      break;
-    }
-  unsigned long long mask = top == 7 ? 0ull : (~0ull << (8 * (top + 1)));
-  unsigned long long prefix = kmax & mask;
-  int rem = room;
-  for (int shift = 8 * top; shift >= 0; shift -= 8) {
-    sm.hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kBlock) {
-      const unsigned long long k = sm.ckey[e];
-      if (k != 0ull && (k & mask) == prefix) atomicAdd(&sm.hist[(k >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l owns digits 255-4l .. 252-4l; find the digit whose cumulative count from
-      // the top first reaches rem
-      const int l = threadIdx.x;
-      const int c0 = sm.hist[255 - 4 * l], c1 = sm.hist[254 - 4 * l];
-      const int c2 = sm.hist[253 - 4 * l], c3 = sm.hist[252 - 4 * l];
-      const int mine = c0 + c1 + c2 + c3;
-      int inc = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o, 64);
-        if (l >= o) inc += y;
-      }
-      const int above = inc - mine;
-      if (above < rem && rem <= inc) {
-        int acc = above, d = 255 - 4 * l;
-        const int cs[4] = {c0, c1, c2, c3};
-        for (int q = 0; q < 4; ++q) {
-          if (acc + cs[q] >= rem) {
-            d = 255 - 4 * l - q;
-            break;
-          }
-          acc += cs[q];
-        }
-        sm.sel_digit = d;
-        sm.sel_rem = rem - acc;
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<unsigned long long>(sm.sel_digit) << shift;
-    mask |= 0xFFull << shift;
-    rem = sm.sel_rem;
-    __syncthreads();
-  }
-  const unsigned long long T = prefix;   // rem = how many keys equal to T are kept
+  int rem = 0;
+  const unsigned long long T = radix_kth_desc(sm.ckey, n, room, sm.rs, &rem);
   for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = 0;
   __syncthreads();
   int carry_eq = 0;

@@ -66,7 +66,7 @@ struct OptArgs {
   int R, V, S, n, nch, max_layers;
   double delta;
   // per layer (set by the host before each layer's launches)
-  int layer, W, Wcap, K;
+  int layer, W, Wcap, K, Kc;   // K: entries a row reports; Kc: per chunk (nch * Kc >= K)
   WsHeader* hdr;
   ChunkStat* st;          // [S][Wcap][nch]
   float* cval;            // [S][Wcap][nch][Kmax]

@@ -8,9 +8,10 @@
 // The final tree is those best n nodes.
 //
 // The exact top-n of W rows x n children per layer (262144 candidates at n = 512) is found
-// without sorting them: each row only reports its top-m (m = max(8, ceil(n / W))) and its
-// log-sum-exp; the n-th best score among those W*m reported candidates is a lower bound
-// `lo` of the layer's n-th best score (n reported candidates reach it). A second pass over
+// without sorting them: each row only reports m = max(8, ceil(n / W)) of its best entries
+// (the best of its chunks' top ceil(m / chunks) lists) and its log-sum-exp; the n-th best
+// score among those W*m reported candidates is a lower bound `lo` of the layer's n-th best
+// score (a subset of the candidates reaches it n times). A second pass over
 // the rows gathers every candidate whose score is >= lo (a few hundred at the shapes of the
 // pages), and one workgroup selects exactly among them in shared memory.
 //
@@ -20,6 +21,7 @@
 // drafting has stopped makes every later launch return at once.
 #include "dtv_internal.h"
 #include "rowstats.h"
+#include "select.h"
 
 namespace dtv {
 
@@ -27,19 +29,17 @@ constexpr int kOptMergeCap = 8192;  // chunks * K of one row merge
 constexpr int kOptLdsCand = 4096;   // candidates selected in shared memory
 
 struct OptCand {
-  double score;
-  int f;   // frontier position of the parent
-  int j;   // vocabulary index (the token)
+  double score;   // log path score
+  uint32_t fj;    // (frontier position of the parent << 22) | token
+  float x;        // the token's draft logit
 };
 
-// (score desc, parent position asc, token asc): ranks candidates of one layer. Within a
-// row, equal logits rank by token index, so this is also (score desc, parent, rank).
-__device__ __forceinline__ bool cand_before(const OptCand& a, const OptCand& b) {
-  if (a.score != b.score) return a.score > b.score;
-  if (a.f != b.f) return a.f < b.f;
-  return a.j < b.j;
+// Frontier-order key of a candidate: (parent position asc, logit desc, token asc), i.e. a
+// parent's children in their row's rank order. Also breaks ties between equal scores.
+__device__ __forceinline__ unsigned long long front_key(const OptCand& c) {
+  return (static_cast<unsigned long long>(c.fj >> 22) << 54) |
+         (static_cast<unsigned long long>(~f32_key(c.x)) << 22) | (c.fj & 0x3FFFFFu);
 }
-
 
 // In-place bitonic sort of n (power of two) elements of shared memory by `before`.
 template <typename T, typename Cmp>
@@ -72,11 +72,15 @@ __device__ __forceinline__ double parent_score(const OptArgs& a, int s, int f) {
 
 // ------------------------------------------------------------------ 1. frontier rows
 
-template <int DT>
+// BIG: lists of up to 1024 per chunk (the root layer, K up to n); otherwise K <= 32, which
+// needs far less shared memory and lets several workgroups share a compute unit.
+template <int DT, bool BIG>
 __global__ __launch_bounds__(kBlock) void opt_rows_kernel(OptArgs a) {
+  constexpr int kMergeCap = BIG ? kOptMergeCap : 2048;
+  constexpr int kSort = BIG ? 4 * 1024 : kCandCap;
   __shared__ RowSmem rs;
-  __shared__ MergeSmem<kOptMergeCap> ms;
-  __shared__ unsigned long long sortbuf[4 * 1024];
+  __shared__ MergeSmem<kMergeCap> ms;
+  __shared__ unsigned long long sortbuf[kSort];
   using Rw = RowT<DT>;
   int bid = blockIdx.x;
   const int c = bid % a.nch;
@@ -93,10 +97,12 @@ __global__ __launch_bounds__(kBlock) void opt_rows_kernel(OptArgs a) {
   load_chunk<DT>(row, a.V, c, x, key);
   const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
   const size_t ci = rf * a.nch + c;
-  chunk_reduce<DT>(x, key, c, a.V, a.K, &a.st[ci], a.cval + ci * a.K, a.cidx + ci * a.K, sortbuf, rs);
+  // each chunk reports its top Kc (nch * Kc >= K): the row's merged K are then the best of
+  // those, a subset of the row's candidates, which is all the lower bound needs
+  chunk_reduce<DT>(x, key, c, a.V, a.Kc, &a.st[ci], a.cval + ci * a.Kc, a.cidx + ci * a.Kc, sortbuf, rs);
   if (!last_arrival(&a.tickets[rf], a.nch, &rs.flag)) return;
-  const int n = row_merge(a.st + rf * a.nch, a.cval + rf * a.nch * a.K, a.cidx + rf * a.nch * a.K, a.nch, a.K,
-                          nullptr, nullptr, &a.rlse[rf], a.rv + rf * a.K, a.ri + rf * a.K, rs, ms);
+  const int n = row_merge(a.st + rf * a.nch, a.cval + rf * a.nch * a.Kc, a.cidx + rf * a.nch * a.Kc, a.nch, a.Kc,
+                          nullptr, nullptr, &a.rlse[rf], a.rv + rf * a.K, a.ri + rf * a.K, rs, ms, a.K);
   if (threadIdx.x == 0) st_cc(&a.rcnt[rf], n);
 }
 
@@ -105,7 +111,9 @@ __global__ __launch_bounds__(kBlock) void opt_rows_kernel(OptArgs a) {
 struct OptBoundSmem {
   unsigned long long key[8192];
   int off[1024];
+  int cnt[1024];
   int wsum[kWaves];
+  RadixSmem rs;
 };
 
 __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
@@ -119,31 +127,33 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
     const int cnt = (f < a.W) ? a.rcnt[static_cast<size_t>(s) * a.Wcap + f] : 0;
     int tot = 0;
     const int ex = block_exclusive_scan(cnt, sm.wsum, &tot);
-    if (f < a.W) sm.off[f] = carry + ex;
+    if (f < a.W) {
+      sm.off[f] = carry + ex;
+      sm.cnt[f] = cnt;
+    }
     carry += tot;
   }
   const int total = carry;
-  const int P2 = pow2_at_least(total > 0 ? total : 1);
-  for (int e = threadIdx.x; e < P2; e += kBlock) sm.key[e] = 0ull;
-  __syncthreads();
+  __syncthreads();   // offsets of every row before the keys are placed
+  // every load is unconditional (all addresses are in the workspace), so an unrolled
+  // thread keeps them all in flight
+#pragma unroll 8
   for (int e = threadIdx.x; e < a.W * a.K; e += kBlock) {
     const int f = e / a.K, j = e % a.K;
     const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
-    if (j < a.rcnt[rf]) {
-      const double sc = parent_score(a, s, f) + (static_cast<double>(a.rv[rf * a.K + j]) - a.rlse[rf]);
-      sm.key[sm.off[f] + j] = dkey(sc);
-    }
+    const double sc = parent_score(a, s, f) + (static_cast<double>(a.rv[rf * a.K + j]) - a.rlse[rf]);
+    if (j < sm.cnt[f]) sm.key[sm.off[f] + j] = dkey(sc);
   }
   __syncthreads();
-  // descending sort of the keys; the n-th largest bounds the layer's n-th best score
-  bitonic_sort(sm.key, P2, [](unsigned long long x, unsigned long long y) { return x > y; });
+  // the n-th largest reported score bounds the layer's n-th best score from below
+  double lo = -INFINITY;
+  if (total >= a.n) {
+    int rem = 0;
+    const unsigned long long k = radix_kth_desc(sm.key, total, a.n, sm.rs, &rem);
+    const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    lo = __longlong_as_double(static_cast<long long>(u));
+  }
   if (threadIdx.x == 0) {
-    double lo = -INFINITY;
-    if (total >= a.n) {
-      const unsigned long long k = sm.key[a.n - 1];
-      const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-      lo = __longlong_as_double(static_cast<long long>(u));
-    }
     a.lo[s] = lo;
     a.ccount[s] = 0u;
   }
@@ -183,34 +193,52 @@ __global__ __launch_bounds__(kBlock) void opt_collect_kernel(OptArgs a) {
         if (pos < static_cast<unsigned>(a.ccap)) {
           OptCand* out = a.cand + static_cast<size_t>(s) * a.ccap + pos;
           out->score = sc;
-          out->f = f;
-          out->j = elem_index<DT>(c, i, e);
+          out->fj = (static_cast<uint32_t>(f) << 22) | static_cast<uint32_t>(elem_index<DT>(c, i, e));
+          out->x = x[i * Rw::VEC + e];
         }
       }
     }
 }
 
 // ------------------------------------------------------------------ 4. exact selection
+//
+// One workgroup per sequence. The layer keeps its n best gathered candidates: radix
+// selection of the n-th best score key, and of the candidates tied with it the first in
+// frontier order. The kept candidates are sorted by frontier key (their positions in the
+// next frontier) and then by (score desc, position asc); the new best-n list merges that
+// with the old one by binary-search ranks.
 
-struct OptSelectSmem {
-  OptCand c[kOptLdsCand];
-  OptCand merged[1024];
-  int pos[1024];
-  double red[kWaves];
-  int ired[kWaves];
-  int flag;
+struct OptKept {
+  unsigned long long key;   // frontier key, then unused
+  double score;
+  int pos;                  // frontier position
+  int pad;
+};
+struct OptBest {
+  double score;
+  int layer, pos;
 };
 
-// Rank of candidate x in a list sorted by `before` (number of list entries before it).
-template <typename Cmp>
-__device__ __forceinline__ int rank_in(const OptCand* list, int n, const OptCand& x, Cmp before) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int m = (lo + hi) >> 1;
-    if (before(list[m], x)) lo = m + 1; else hi = m;
-  }
-  return lo;
-}
+struct OptSelectSmem {
+  union {
+    struct {
+      OptCand c[kOptLdsCand];                // gathered candidates
+      unsigned long long key[kOptLdsCand];   // their score keys
+    } in;
+    struct {
+      OptKept k[1024];      // kept candidates
+      OptBest old[1024];    // previous best list
+      OptBest merged[1024];
+    } out;
+  } u;
+  unsigned long long tkey[1024];   // candidates tied at the n-th best score: frontier keys
+  int tidx[1024];
+  int keep_idx[1024];              // indices of the kept candidates
+  int scan[kWaves];
+  double red[kWaves];
+  RadixSmem rs;
+  int ntie, nkept;
+};
 
 __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   __shared__ OptSelectSmem sm;
@@ -225,81 +253,141 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     }
     return;
   }
-  const int P2 = pow2_at_least(C > 0 ? C : 1);
-  for (int e = threadIdx.x; e < P2; e += kBlock) {
-    if (e < C) {
-      sm.c[e] = a.cand[static_cast<size_t>(s) * a.ccap + e];
-    } else {
-      sm.c[e].score = -INFINITY;
-      sm.c[e].f = 0x7FFFFFFF;
-      sm.c[e].j = 0x7FFFFFFF;
-    }
+  // (unrolled so that a thread's global loads are all in flight before its first store)
+#pragma unroll 8
+  for (int e = threadIdx.x; e < C; e += kBlock) {
+    const OptCand cd = a.cand[static_cast<size_t>(s) * a.ccap + e];
+    sm.u.in.c[e] = cd;
+    sm.u.in.key[e] = dkey(cd.score);
+  }
+  if (threadIdx.x == 0) {
+    sm.ntie = 0;
+    sm.nkept = 0;
   }
   __syncthreads();
-  bitonic_sort(sm.c, P2, cand_before);     // best first
-  const int kept = C < n ? C : n;          // the layer keeps its best n
-  // frontier order of the kept candidates: (parent position, rank) = (f, score desc, j)
-  // written to the layer record; scores to the best-so-far merge below
+  // ---- the layer's n best
+  const int kept = C < n ? C : n;
+  if (C > n) {
+    int rem = 0;
+    const unsigned long long T = radix_kth_desc(sm.u.in.key, C, n, sm.rs, &rem);
+    for (int e = threadIdx.x; e < C; e += kBlock) {
+      const unsigned long long k = sm.u.in.key[e];
+      if (k > T) {
+        sm.keep_idx[atomicAdd(&sm.nkept, 1)] = e;
+      } else if (k == T) {
+        const int t = atomicAdd(&sm.ntie, 1);
+        if (t < 1024) {
+          sm.tkey[t] = front_key(sm.u.in.c[e]);
+          sm.tidx[t] = e;
+        }
+      }
+    }
+    __syncthreads();
+    if (sm.ntie > 1024) {   // more than 1024 candidates share the n-th best score: refuse
+      if (threadIdx.x == 0) {
+        atomicExch(&a.hdr->err, kErrCapacity);
+        a.done[s] = 1;
+      }
+      return;
+    }
+    const int nt = sm.ntie;
+    const int above = sm.nkept;   // = n - rem
+    for (int t = threadIdx.x; t < nt; t += kBlock) {
+      const unsigned long long me = sm.tkey[t];
+      int before = 0;
+      for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      if (before < rem) sm.keep_idx[above + before] = sm.tidx[t];
+    }
+  } else {
+    for (int e = threadIdx.x; e < C; e += kBlock) sm.keep_idx[e] = e;
+  }
+  __syncthreads();
+  // ---- frontier order: sort the kept candidates by frontier key
+  OptKept mine[4];
+  const int P2 = pow2_at_least(kept > 0 ? kept : 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + q * kBlock;
+    if (i < P2) {
+      if (i < kept) {
+        const OptCand cd = sm.u.in.c[sm.keep_idx[i]];
+        mine[q].key = front_key(cd);
+        mine[q].score = cd.score;
+      } else {
+        mine[q].key = ~0ull;
+        mine[q].score = -INFINITY;
+      }
+    }
+  }
+  __syncthreads();   // the candidate area is reused from here on
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x + q * kBlock;
+    if (i < P2) sm.u.out.k[i] = mine[q];
+  }
+  __syncthreads();
+  bitonic_sort(sm.u.out.k, P2, [](const OptKept& x, const OptKept& y) { return x.key < y.key; });
   const int l0 = a.layer - 1;
   const size_t lb = (static_cast<size_t>(s) * a.max_layers + l0) * n;
-  // position of each kept candidate in frontier order = number of kept candidates before it
-  for (int e = threadIdx.x; e < kept; e += kBlock) {
-    const OptCand me = sm.c[e];
-    int pos = 0;
-    for (int e2 = 0; e2 < kept; ++e2) {
-      const OptCand o = sm.c[e2];
-      const bool before = (o.f < me.f) || (o.f == me.f && (o.score > me.score || (o.score == me.score && o.j < me.j)));
-      pos += before ? 1 : 0;
-    }
-    a.lscore[lb + pos] = me.score;
-    a.lparent[lb + pos] = me.f;
-    a.ltoken[lb + pos] = me.j;
-    sm.pos[e] = pos;
+  for (int i = threadIdx.x; i < kept; i += kBlock) {
+    const OptKept k = sm.u.out.k[i];
+    a.lscore[lb + i] = k.score;
+    a.lparent[lb + i] = static_cast<int>(k.key >> 54);
+    a.ltoken[lb + i] = static_cast<int>(k.key & 0x3FFFFFull);
+    sm.u.out.k[i].pos = i;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < kept; e += kBlock) sm.c[e].f = sm.pos[e];  // now: position in the layer
-  __syncthreads();
-  // best n of all layers so far: merge the previous best (sorted by score desc, layer asc,
-  // position asc) with this layer's kept nodes (sorted by score desc, position asc)
+  // ---- this layer's nodes by (score desc, position asc); the old best list from global
+  bitonic_sort(sm.u.out.k, P2, [](const OptKept& x, const OptKept& y) {
+    if (x.score != y.score) return x.score > y.score;
+    return x.pos < y.pos;
+  });
   const int nb = a.bcount[s];
   const size_t bb = static_cast<size_t>(s) * n;
+#pragma unroll 4
+  for (int e = threadIdx.x; e < nb; e += kBlock) {
+    OptBest o;
+    o.score = a.bscore[bb + e];
+    o.layer = a.blayer[bb + e];
+    o.pos = a.bpos[bb + e];
+    sm.u.out.old[e] = o;
+  }
+  __syncthreads();
+  // ---- merge: rank = old entries before + this layer's entries before (both sorted)
   for (int e = threadIdx.x; e < nb + kept; e += kBlock) {
-    OptCand me;
+    OptBest me;
     int r;
-    if (e < nb) {
-      me.score = a.bscore[bb + e];
-      me.j = a.blayer[bb + e];
-      me.f = a.bpos[bb + e];
-      // entries of this layer before me (previous layers win ties)
+    if (e < nb) {   // old entry: this layer's entries before it have a strictly higher score
+      me = sm.u.out.old[e];
       int lo = 0, hi = kept;
       while (lo < hi) {
-        const int m = (lo + hi) >> 1;
-        if (sm.c[m].score > me.score) lo = m + 1; else hi = m;
+        const int mid = (lo + hi) >> 1;
+        if (sm.u.out.k[mid].score > me.score) lo = mid + 1; else hi = mid;
       }
       r = e + lo;
-    } else {
-      const int q = e - nb;
-      me.score = sm.c[q].score;
-      me.j = a.layer;
-      me.f = sm.c[q].f;
-      int lo = 0, hi = nb;  // previous entries with score >= mine come first
+    } else {        // this layer's entry: old entries with a score >= mine come first
+      const int i = e - nb;
+      me.score = sm.u.out.k[i].score;
+      me.layer = a.layer;
+      me.pos = sm.u.out.k[i].pos;
+      int lo = 0, hi = nb;
       while (lo < hi) {
-        const int m = (lo + hi) >> 1;
-        if (a.bscore[bb + m] >= me.score) lo = m + 1; else hi = m;
+        const int mid = (lo + hi) >> 1;
+        if (sm.u.out.old[mid].score >= me.score) lo = mid + 1; else hi = mid;
       }
-      // this layer's entries before me: q (the kept list is sorted by score desc, position asc)
-      r = q + lo;
+      r = i + lo;
     }
-    if (r < n) sm.merged[r] = me;
+    if (r < n) sm.u.out.merged[r] = me;
   }
   __syncthreads();
   const int nnew = (nb + kept) < n ? (nb + kept) : n;
   double part = 0.0;
   for (int e = threadIdx.x; e < nnew; e += kBlock) {
-    a.bscore[bb + e] = sm.merged[e].score;
-    a.blayer[bb + e] = sm.merged[e].j;
-    a.bpos[bb + e] = sm.merged[e].f;
-    part += exp(sm.merged[e].score);
+    const OptBest m = sm.u.out.merged[e];
+    a.bscore[bb + e] = m.score;
+    a.blayer[bb + e] = m.layer;
+    a.bpos[bb + e] = m.pos;
+    part += exp(m.score);
   }
   const double E = block_sum(part, sm.red);
   if (threadIdx.x == 0) {
@@ -396,10 +484,18 @@ int launch_opt_init(const OptArgs& a, hipStream_t st) {
 
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st) {
   const dim3 rows(a.S * a.W * a.nch);
-  if (dtype == 1)
-    hipLaunchKernelGGL(opt_rows_kernel<1>, rows, dim3(kBlock), 0, st, a);
-  else
-    hipLaunchKernelGGL(opt_rows_kernel<0>, rows, dim3(kBlock), 0, st, a);
+  const bool big = a.Kc > 32;
+  if (dtype == 1) {
+    if (big)
+      hipLaunchKernelGGL((opt_rows_kernel<1, true>), rows, dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((opt_rows_kernel<1, false>), rows, dim3(kBlock), 0, st, a);
+  } else {
+    if (big)
+      hipLaunchKernelGGL((opt_rows_kernel<0, true>), rows, dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((opt_rows_kernel<0, false>), rows, dim3(kBlock), 0, st, a);
+  }
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL(opt_bound_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;

@@ -397,12 +397,13 @@ struct MergeSmem {
 // other workgroups with st_cc). The lists are first copied into shared memory (one
 // parallel pass of coherent loads); each entry's rank in the merged order is then the
 // count of entries of all lists that precede it (binary search in the sorted lists).
-// Outputs (thread 0): maxv, argmax, lse; all threads: topK (value, index) into rv/ri, all
-// written with st_cc. Requires nch <= 64 and nch * K <= CAP. Returns min(K, entries).
+// Outputs (wave 0): maxv, argmax, lse; all threads: the top kout (default K) entries
+// (value, index) into rv/ri, all written with st_cc. Requires nch <= 64 and nch * K <= CAP.
+// Returns min(kout, entries).
 template <int CAP>
 __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx, int nch, int K,
                          float* maxv, int* argmax, double* lse, float* rv, int* ri, RowSmem& sm,
-                         MergeSmem<CAP>& ms) {
+                         MergeSmem<CAP>& ms, int kout = -1) {
   for (int c = threadIdx.x; c < nch; c += kBlock) {  // one parallel round of loads
     ms.cnt[c] = ld_cc(&st[c].cnt);
     ms.maxv[c] = ld_cc(&st[c].maxv);
@@ -428,7 +429,8 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
   }
   int total = 0;
   for (int c = 0; c < nch; ++c) total += ms.cnt[c];
-  const int kk = K < total ? K : total;
+  const int want = kout < 0 ? K : kout;   // entries of the merged list (chunk lists hold K)
+  const int kk = want < total ? want : total;
   if (kk <= 0) {
     __syncthreads();
     return 0;

@@ -158,8 +158,9 @@ int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, 
  * numbered by (layer, position). Row identity: the node at position p of layer l uses
  * row 1 + (l-1)*n + p of `draft` (`[S][R][V]`, R >= 1 + (max_layers-1)*n + ...); the root
  * uses row 0. tree.row receives these identities (the target rows of verification).
- * Limits: n <= 1023, n < n_cap, max_layers <= 64; more than 4096 candidates within the
- * selection bound of one layer (extreme ties) is reported as DTV_ECAPACITY.
+ * Limits: n <= 1023, n < n_cap, max_layers <= 64, V <= 4194304; more than 4096 candidates
+ * within the selection bound of one layer, or more than 1024 tied at the layer's n-th best
+ * score (extreme ties), is reported as DTV_ECAPACITY.
  */
 size_t dtv_tree_build_opt_ws_bytes(int32_t S, int32_t n, int32_t V, int32_t max_layers, int dtype);
 int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int dtype, int32_t R,
