@@ -217,14 +217,29 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
   return L;
 }
 
+// Compute units of the current device (queried once per device; 256 on an MI355X).
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] > 0) return cached[dev];
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1) return 256;
+  cached[dev] = ncu;
+  return ncu;
+}
+
 struct AttnPlan {
   int n_mtiles, n_split, kps, mcap;
 };
 // Query rows of a KV head: M = g * n_cap (GQA heads packed), in ceil(M/32) groups of 32;
-// a bf16 tile is 4 waves of one group each. Key ranges are split so the 256 compute units
-// see about two workgroups each; ranges are multiples of 64 keys and no shorter than 256
-// (each split costs a partial O row per query row).
-AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max) {
+// a bf16 tile is 4 waves of one group each. The key range of every tile is split into
+// n_split ranges (multiples of 64 keys, at least 256) chosen by a time model: workgroups run
+// in rounds of the device's resident slots (two per compute unit), a round costs one
+// 64-key block per block of its ranges, and every split adds an fp32 partial (m, l, O) per
+// query row that is written and read back once; measured on MI355X, a 64-key block round
+// takes about as long as moving 11 MB of partials.
+AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int D) {
   AttnPlan p;
   const int g = Hq / Hkv;
   const int M = g * n_cap;
@@ -233,16 +248,27 @@ AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max) {
   p.n_mtiles = (G + dtv::kWaves - 1) / dtv::kWaves;
   p.mcap = G * 32;
   const int min_keys = 256;
-  const int tiles = S * Hkv * p.n_mtiles;
-  int want = (512 + tiles - 1) / tiles;
-  const int max_split = (T + min_keys - 1) / min_keys;
-  if (want > max_split) want = max_split;
-  if (want > dtv::kAttnMaxSplit) want = dtv::kAttnMaxSplit;
-  if (want < 1) want = 1;
-  int kps = (T + want - 1) / want;
-  kps = (kps + 63) / 64 * 64;
-  p.kps = kps;
-  p.n_split = (T + kps - 1) / kps;
+  const long tiles = static_cast<long>(S) * Hkv * p.n_mtiles;
+  const long slots = 2L * device_cus();
+  const double partial_bytes = 2.0 * S * Hkv * static_cast<double>(p.mcap) * (D + 2) * 4.0;   // per split
+  const double bytes_per_block = 11.0e6;
+  int max_split = (T + min_keys - 1) / min_keys;
+  if (max_split > dtv::kAttnMaxSplit) max_split = dtv::kAttnMaxSplit;
+  int best_kps = (T + 63) / 64 * 64;
+  double best_cost = 1e300;
+  for (int want = 1; want <= max_split; ++want) {
+    int kps = (T + want - 1) / want;
+    kps = (kps + 63) / 64 * 64;
+    const int ns = (T + kps - 1) / kps;
+    const long rounds = (tiles * ns + slots - 1) / slots;
+    const double cost = static_cast<double>(rounds) * (kps / 64) + (ns > 1 ? ns * partial_bytes / bytes_per_block : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best_kps = kps;
+    }
+  }
+  p.kps = best_kps;
+  p.n_split = (T + best_kps - 1) / best_kps;
   return p;
 }
 
@@ -266,6 +292,7 @@ AttnLayout attn_layout(void* ws, int S, int Hkv, int D, const AttnPlan& p) {
 struct VerifyLayout {
   dtv::WsHeader* hdr;
   unsigned long long* best;
+  unsigned* ntick;
   unsigned* tickets;
   size_t bytes;
 };
@@ -274,6 +301,7 @@ VerifyLayout verify_layout(void* ws, int S, int n_cap) {
   VerifyLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
   L.best = c.take<unsigned long long>(static_cast<size_t>(S) * n_cap);
+  L.ntick = c.take<unsigned>(static_cast<size_t>(S) * n_cap);
   L.tickets = c.take<unsigned>(S);
   L.bytes = c.off;
   return L;
@@ -605,7 +633,7 @@ size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv,
                               int32_t P_max, int dtype) {
   if (S < 1 || n_cap < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || P_max < 0 || !dtype_ok(dtype)) return 0;
   if (dtype != DTV_BF16) return up(sizeof(dtv::WsHeader));
-  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max)).bytes;
+  return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max, D)).bytes;
 }
 
 int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
@@ -626,7 +654,7 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
     REQUIRE(D >= 4 && D <= 128 && D % 4 == 0, DTV_EUNSUPPORTED, "fp32 attention needs D%%4==0, D<=128, got %d", D);
     REQUIRE(P_max + tree->n_cap <= 16384, DTV_EUNSUPPORTED, "fp32 attention supports at most 16384 keys");
   }
-  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max);
+  const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max, D);
   size_t need = dtv_tree_attn_ws_bytes(S, tree->n_cap, Hq, Hkv, D, P_max, dtype);
   REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   dtv::AttnArgs a;
@@ -690,6 +718,7 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
   a.bonus = bonus;
   a.argmax_out = argmax_out;
   a.best = L.best;
+  a.ntick = L.ntick;
   a.tickets = L.tickets;
   a.hdr = L.hdr;
   return launched(dtv::launch_verify_greedy(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));

@@ -163,7 +163,8 @@ struct VerifyArgs {
   int* bonus;
   int* argmax_out;
   unsigned long long* best;  // [S][n_cap]
-  unsigned* tickets;         // [S]
+  unsigned* ntick;           // [S][n_cap] chunks of a node's row done
+  unsigned* tickets;         // [S] nodes of a sequence done
   WsHeader* hdr;
 };
 

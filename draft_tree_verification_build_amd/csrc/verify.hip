@@ -59,7 +59,10 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
     }
   best = block_max(best, sm.redu);
   if (threadIdx.x == 0) atomicMax(&a.best[tb + i], best);
-  if (!last_arrival(&a.tickets[s], static_cast<unsigned>(N * nch), &sm.flag)) return;
+  // two-level tickets: the chunks of a node, then the nodes of a sequence (one counter
+  // taking every chunk of a sequence serialises ~1000 atomics)
+  if (!last_arrival(&a.ntick[tb + i], static_cast<unsigned>(nch), &sm.flag)) return;
+  if (!last_arrival(&a.tickets[s], static_cast<unsigned>(N), &sm.flag)) return;
 
   // ---- the walk, by the last workgroup of sequence s. Everything it needs is loaded in
   //      one parallel pass; acceptance then follows parent links in shared memory.
