@@ -12,10 +12,11 @@
 //   unit so that one's softmax overlaps the other's MFMAs. The ceil(M/32) row groups of a
 //   KV head are spread evenly over the tiles, so ragged row counts do not leave a tile
 //   nearly empty.
-// * K/V are double-buffered in LDS (K row-major, V transposed): the global loads of block
-//   b+1 are issued before block b is computed and land in the other buffer afterwards, one
-//   barrier per 64-key block. Every load is unconditional (clamped to a valid key) so all
-//   of them are in flight together.
+// * K/V are double-buffered in LDS (K row-major, V transposed in fragment order): the
+//   global loads of block b+1 are issued before block b is computed and land in the other
+//   buffer afterwards, one barrier per 64-key block. Every load is unconditional (clamped to
+//   a valid key) so all of them are in flight together; every LDS access is a
+//   conflict-free 16-byte access.
 // * The tree mask and the key-range tail are applied only in blocks that need them, from
 //   one 64-bit visibility word per row and block. The softmax runs in the exp2 domain with
 //   the scale folded into one fma per score and a lazily moved reference maximum.
@@ -41,81 +42,53 @@ union Frag8 {
   uint16_t s[8];
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ---- LDS layout of one 64-key block
+// K and V sit row-major in LDS as in HBM (64 rows of D bf16 each), so the global loads
+// write LDS directly: lane l of a global_load_lds_dwordx4 fills bytes 16 l .. 16 l + 15
+// after the load's LDS base, with no registers and no stores on the way. The 16-byte
+// chunks of a row are XOR-permuted by row, chunk c of row r at position c ^ fk(r) (K) or
+// c ^ fv(r) (V), so that the fragment reads below are free of bank conflicts (LDS: 64 banks
+// of 4 bytes); each load lane fetches the global chunk that belongs at its LDS position.
+//  * K fragments (A operand of S^T = K Q^T) are 16-byte reads: 16 lanes read one chunk
+//    index of 16 consecutive rows, which fk spreads over all 64 banks.
+//  * V fragments (B operand of O += P V) come from ds_read_b64_tr_b16, which hands lane
+//    16 g + i element i % 4 of the 8-byte words addressed by lanes 16 g + 4 j + i / 4,
+//    j = 0..3: the transpose happens in the read. 32 lanes then address 4 consecutive rows
+//    at 4 consecutive chunks, which fv spreads over all 64 banks.
 template <int D>
-struct AttnSmem {
-  static constexpr int KS = D + 8;          // K row stride (elements)
-  static constexpr int VS = kKeyBlock + 4;    // V^T row stride (elements)
-  alignas(16) uint16_t ks[2][kKeyBlock * KS];
-  alignas(16) uint16_t vt[2][D * VS];
-  alignas(16) float alpha[kWaves][32];
-  alignas(16) float ml[kWaves][32][2];
+struct KvLds {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static constexpr int kChunks = D / 8;                               // 16-byte chunks per row
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowShift = D == 128 ? 8 : 7;                  // log2(kRowBytes)
+  static constexpr int kLoads = kKeyBlock * kChunks / 64 / kWaves;    // loads per wave per tensor
+  __device__ static __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// One thread's share of a 64-key K/V block, held in registers between the global loads
-// and the LDS stores: K vectors i (key (t + 256 i) / (D/8), dims 8 * ((t + 256 i) % (D/8)));
-// V keys kg*NV + u of dims 8*dc .. 8*dc+7 (dc = t % (D/8), kg = t / (D/8)).
+// Issues the direct loads of keys kb .. kb+63 into (kd, vd). Rows at or past k_hi read the
+// last valid key instead (they are masked out of the softmax), so every address is valid.
+// ofs[i] / ofs[L + i] hold the in-block byte offsets of this lane's K / V loads; the LDS
+// base of load i of wave w is byte 1024 (w L + i) of the block.
 template <int D>
-struct KvPrefetch {
-  static constexpr int NV = kKeyBlock * D / 8 / kBlock;   // 16-byte vectors per thread (4 or 2)
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;                  // named members keep them in registers
-  __device__ __forceinline__ uint4& k(int i) { return i == 0 ? k0 : i == 1 ? k1 : i == 2 ? k2 : k3; }
-  __device__ __forceinline__ uint4& v(int i) { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
-  __device__ __forceinline__ const uint4& k(int i) const { return i == 0 ? k0 : i == 1 ? k1 : i == 2 ? k2 : k3; }
-  __device__ __forceinline__ const uint4& v(int i) const { return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3; }
-};
-
-__device__ __forceinline__ uint32_t half_of(const uint4& x, int e) {
-  const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// Loads keys kb .. kb+63 (clamped to the last valid key k_hi-1; the extra copies are
-// masked out of the softmax, so they need no zeroing). Every load is unconditional so
-// that all of them are in flight together.
-template <int D>
-__device__ __forceinline__ KvPrefetch<D> kv_fetch(const uint16_t* kbase, const uint16_t* vbase, int kb, int k_hi) {
-  constexpr int NV = KvPrefetch<D>::NV;
-  KvPrefetch<D> r;
-  const int t = threadIdx.x;
+__device__ __forceinline__ void kv_issue(uint16_t* kd, uint16_t* vd, const uint16_t* kbase, const uint16_t* vbase,
+                                         int kb, int k_hi, const int (&ofs)[2 * KvLds<D>::kLoads], int w) {
+  using L = KvLds<D>;
+  const char* kp = reinterpret_cast<const char*>(kbase + static_cast<size_t>(kb) * D);
+  const char* vp = reinterpret_cast<const char*>(vbase + static_cast<size_t>(kb) * D);
+  const int lim = k_hi - 1 - kb;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int vi = t + kBlock * i;
-    const int key = vi / (D / 8), dc = vi % (D / 8);
-    r.k(i) = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(min(kb + key, k_hi - 1)) * D + dc * 8);
-  }
-  const int dc = t % (D / 8), kg = t / (D / 8);
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-    r.v(u) = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(min(kb + kg * NV + u, k_hi - 1)) * D + dc * 8);
-  return r;
-}
-
-// Stores a prefetched block into LDS buffer `buf`: K row-major, V transposed (V^T[d][key]).
-template <int D>
-__device__ __forceinline__ void kv_stage(AttnSmem<D>& sm, int buf, const KvPrefetch<D>& r) {
-  constexpr int KS = AttnSmem<D>::KS;
-  constexpr int VS = AttnSmem<D>::VS;
-  constexpr int NV = KvPrefetch<D>::NV;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int vi = t + kBlock * i;
-    const int key = vi / (D / 8), dc = vi % (D / 8);
-    *reinterpret_cast<uint4*>(&sm.ks[buf][key * KS + dc * 8]) = r.k(i);
-  }
-  const int dc = t % (D / 8), kg = t / (D / 8);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint16_t* dst = &sm.vt[buf][(dc * 8 + e) * VS + kg * NV];
-    if constexpr (NV == 4) {
-      uint2 w;
-      w.x = half_of(r.v(0), e) | (half_of(r.v(1), e) << 16);
-      w.y = half_of(r.v(2), e) | (half_of(r.v(3), e) << 16);
-      *reinterpret_cast<uint2*>(dst) = w;
-    } else {
-      static_assert(NV == 2, "D is 64 or 128");
-      *reinterpret_cast<uint32_t*>(dst) = half_of(r.v(0), e) | (half_of(r.v(1), e) << 16);
-    }
+  for (int i = 0; i < L::kLoads; ++i) {
+    const int ko = (min(ofs[i] >> L::kRowShift, lim) << L::kRowShift) | (ofs[i] & (L::kRowBytes - 1));
+    const int vo = (min(ofs[L::kLoads + i] >> L::kRowShift, lim) << L::kRowShift) |
+                   (ofs[L::kLoads + i] & (L::kRowBytes - 1));
+    const int lds_off = 1024 * (w * L::kLoads + i);
+    __builtin_amdgcn_global_load_lds(kp + ko, (lds_void*)(reinterpret_cast<char*>(kd) + lds_off), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vp + vo, (lds_void*)(reinterpret_cast<char*>(vd) + lds_off), 16, 0, 0);
   }
 }
 
@@ -183,9 +156,15 @@ __device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D 
 
 template <int D>
 __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ AttnSmem<D> sm;
-  constexpr int KS = AttnSmem<D>::KS;
-  constexpr int VS = AttnSmem<D>::VS;
+  using L = KvLds<D>;
+  // Two LDS buffers per tensor, as separate objects: the loop body is instantiated per
+  // buffer, so the compiler can tell the block being read from the one being loaded.
+  __shared__ alignas(16) uint16_t ks0[kKeyBlock * D];
+  __shared__ alignas(16) uint16_t ks1[kKeyBlock * D];
+  __shared__ alignas(16) uint16_t vs0[kKeyBlock * D];
+  __shared__ alignas(16) uint16_t vs1[kKeyBlock * D];
+  __shared__ alignas(16) float alpha_s[kWaves][32];
+  __shared__ alignas(16) float ml_s[kWaves][32][2];
   constexpr int NKS = D / 16;
   constexpr int NT = D / 32;
 
@@ -241,6 +220,29 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < NKS; ++ks) qf[ks].u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * h);
   }
 
+  // ---- per-lane LDS offsets, fixed for the whole kernel
+  int lofs[2 * L::kLoads];   // in-block byte offsets of this lane's K and V loads
+#pragma unroll
+  for (int i = 0; i < L::kLoads; ++i) {
+    const int pos = 64 * (w * L::kLoads + i) + lane;   // chunk position in the block
+    const int row = pos / L::kChunks, c = pos % L::kChunks;
+    lofs[i] = row * L::kRowBytes + ((c ^ L::fk(row)) << 4);
+    lofs[L::kLoads + i] = row * L::kRowBytes + ((c ^ L::fv(row)) << 4);
+  }
+  int kread[NKS];            // K fragment of step ks: row lr, chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) kread[ks] = lr * L::kRowBytes + (((2 * ks + h) ^ L::fk(lr)) << 4);
+  int vread[NT];             // V transpose read of tile nt (see KvLds)
+  {
+    const int gg = lane >> 4, jj = (lane >> 2) & 3, mm = lane & 3;
+    const int row = 4 * (gg >> 1) + jj;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = 4 * nt + 2 * (gg & 1) + (mm >> 1);
+      vread[nt] = row * L::kRowBytes + ((c ^ L::fv(row)) << 4) + 8 * (mm & 1);
+    }
+  }
+
   f32x16 oacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -250,29 +252,27 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kKeyBlock - 1) / kKeyBlock : 0;
-  KvPrefetch<D> pf;
-  if (nblk > 0) {
-    pf = kv_fetch<D>(kbase, vbase, k_lo, k_hi);
-    kv_stage<D>(sm, 0, pf);
-  }
+  if (nblk > 0) kv_issue<D>(ks0, vs0, kbase, vbase, k_lo, k_hi, lofs, w);
   // Nothing may be outstanding at the loop head: otherwise the wait inserted for the
-  // query registers inside the loop also waits for the block prefetch.
+  // query registers inside the loop also waits for the next block's loads.
   drain();
   __syncthreads();
 
-  for (int b = 0; b < nblk; ++b) {
+  // One 64-key block from buffer (kc, vc) while the next one streams into (kn, vn).
+  auto step = [&](int b, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     const int kb = k_lo + b * kKeyBlock;
-    const int cur = b & 1;
     const bool more = b + 1 < nblk;
     // Visibility of this block's keys (tree keys or the range tail only); the ancestor
-    // words are read before the prefetch is issued so that waiting for them does not
-    // wait for the prefetch.
+    // words are read before the next block's loads are issued so that waiting for them
+    // does not wait for those loads.
     const bool need_mask = (kb + kKeyBlock > P) || (kb + kKeyBlock > k_hi);
     uint64_t vis = ~0ull;
     if (need_mask) vis = block_visibility(kb, P, k_hi, anc, ok) >> (4 * h);
-    if (more) pf = kv_fetch<D>(kbase, vbase, kb + kKeyBlock, k_hi);
+    if (more) kv_issue<D>(kn, vn, kbase, vbase, kb + kKeyBlock, k_hi, lofs, w);
 
     if (act) {
+      const char* kcb = reinterpret_cast<const char*>(kc);
+      const char* vcb = reinterpret_cast<const char*>(vc);
       // ---- S^T = K Q^T for two 32-key tiles; lane holds keys kb + kt*32 + (i/4)*8 + 4h + i%4
       f32x16 sc[2];
 #pragma unroll
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           Frag8 kf;
-          kf.u = *reinterpret_cast<const uint4*>(&sm.ks[cur][(kt * 32 + lr) * KS + ks * 16 + 8 * h]);
+          kf.u = *reinterpret_cast<const uint4*>(kcb + kt * 32 * L::kRowBytes + kread[ks]);
           sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, sc[kt], 0, 0, 0);
         }
       }
@@ -315,11 +315,11 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
           m_run = mx;
         }
         // a lane holds O rows (i/4)*8 + 4h + i%4 of the group
-        if (h == 0) sm.alpha[w][lr] = alpha;
+        if (h == 0) alpha_s[w][lr] = alpha;
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[w][q4 * 8 + 4 * h]);
+          const float4 al = *reinterpret_cast<const float4*>(&alpha_s[w][q4 * 8 + 4 * h]);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             oacc[nt][q4 * 4 + 0] *= al.x;
@@ -342,7 +342,8 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
         }
       l_run += sum;
       // ---- O += P V over four 16-key steps; the A operand of step k2 is p values
-      //      8*(k2%2) .. +7 of key tile k2/2
+      //      8*(k2%2) .. +7 of key tile k2/2, i.e. keys 16 k2 + 8 (j/4) + 4h + j%4, which
+      //      is the key order of the two transpose reads (rows 16 k2 + 4h + j and + 8)
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         Frag8 pf8;
@@ -351,25 +352,33 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           Frag8 vf;
-          const uint16_t* vrow = &sm.vt[cur][(nt * 32 + lr) * VS + 16 * k2 + 4 * h];
-          vf.h[0] = *reinterpret_cast<const uint2*>(vrow);
-          vf.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
+          const char* vrow = vcb + 16 * k2 * L::kRowBytes + vread[nt];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 8 * L::kRowBytes));
+          vf.h[0] = __builtin_bit_cast(uint2, lo);
+          vf.h[1] = __builtin_bit_cast(uint2, hi);
           oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf8.v, vf.v, oacc[nt], 0, 0, 0);
         }
       }
     }
-    if (more) kv_stage<D>(sm, cur ^ 1, pf);
+    // the next block has landed (this wave's loads) and is visible (everyone's)
+    drain();
     __syncthreads();
+  };
+
+  for (int b = 0; b < nblk; b += 2) {
+    step(b, ks0, vs0, ks1, vs1);
+    if (b + 1 < nblk) step(b + 1, ks1, vs1, ks0, vs0);
   }
 
   // ---- row statistics in the O layout
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (h == 0) {
-    sm.ml[w][lr][0] = m_run;
-    sm.ml[w][lr][1] = l_tot;
+    ml_s[w][lr][0] = m_run;
+    ml_s[w][lr][1] = l_tot;
   }
   __syncthreads();
-  if (act) o_store<D>(a, oacc, sm.ml[w], s, kv, sp, grp, M, h, lr);
+  if (act) o_store<D>(a, oacc, ml_s[w], s, kv, sp, grp, M, h, lr);
 }
 
 // Merges the key splits of every query row (partials indexed by row): O = sum_q O_q w_q / sum_q l_q w_q
