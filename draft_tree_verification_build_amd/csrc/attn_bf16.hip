@@ -70,26 +70,24 @@ struct KvLds {
   __device__ static __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// Issues the direct loads of keys kb .. kb+63 into (kd, vd). Rows at or past k_hi read the
-// last valid key instead (they are masked out of the softmax), so every address is valid.
-// ofs[i] / ofs[L + i] hold the in-block byte offsets of this lane's K / V loads; the LDS
-// base of load i of wave w is byte 1024 (w L + i) of the block.
+// Issues direct-load pair i (one K and one V load) of keys kb .. kb+63 into (kd, vd). Rows
+// at or past k_hi read the last valid key instead (they are masked out of the softmax), so
+// every address is valid. ofs[i] / ofs[L + i] hold the in-block byte offsets of this lane's
+// K / V loads; the LDS base of load i of wave w is byte 1024 (w L + i) of the block.
 template <int D>
-__device__ __forceinline__ void kv_issue(uint16_t* kd, uint16_t* vd, const uint16_t* kbase, const uint16_t* vbase,
-                                         int kb, int k_hi, const int (&ofs)[2 * KvLds<D>::kLoads], int w) {
+__device__ __forceinline__ void kv_issue_pair(int i, uint16_t* kd, uint16_t* vd, const uint16_t* kbase,
+                                              const uint16_t* vbase, int kb, int k_hi,
+                                              const int (&ofs)[2 * KvLds<D>::kLoads], int w) {
   using L = KvLds<D>;
   const char* kp = reinterpret_cast<const char*>(kbase + static_cast<size_t>(kb) * D);
   const char* vp = reinterpret_cast<const char*>(vbase + static_cast<size_t>(kb) * D);
   const int lim = k_hi - 1 - kb;
-#pragma unroll
-  for (int i = 0; i < L::kLoads; ++i) {
-    const int ko = (min(ofs[i] >> L::kRowShift, lim) << L::kRowShift) | (ofs[i] & (L::kRowBytes - 1));
-    const int vo = (min(ofs[L::kLoads + i] >> L::kRowShift, lim) << L::kRowShift) |
-                   (ofs[L::kLoads + i] & (L::kRowBytes - 1));
-    const int lds_off = 1024 * (w * L::kLoads + i);
-    __builtin_amdgcn_global_load_lds(kp + ko, (lds_void*)(reinterpret_cast<char*>(kd) + lds_off), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + vo, (lds_void*)(reinterpret_cast<char*>(vd) + lds_off), 16, 0, 0);
-  }
+  const int ko = (min(ofs[i] >> L::kRowShift, lim) << L::kRowShift) | (ofs[i] & (L::kRowBytes - 1));
+  const int vo = (min(ofs[L::kLoads + i] >> L::kRowShift, lim) << L::kRowShift) |
+                 (ofs[L::kLoads + i] & (L::kRowBytes - 1));
+  const int lds_off = 1024 * (w * L::kLoads + i);
+  __builtin_amdgcn_global_load_lds(kp + ko, (lds_void*)(reinterpret_cast<char*>(kd) + lds_off), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(vp + vo, (lds_void*)(reinterpret_cast<char*>(vd) + lds_off), 16, 0, 0);
 }
 
 // Visibility of keys kb .. kb+63 to one query row as a 64-bit mask (bit o: key kb + o).
@@ -252,7 +250,10 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const int nblk = (k_hi > k_lo) ? (k_hi - k_lo + kKeyBlock - 1) / kKeyBlock : 0;
-  if (nblk > 0) kv_issue<D>(ks0, vs0, kbase, vbase, k_lo, k_hi, lofs, w);
+  if (nblk > 0) {
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) kv_issue_pair<D>(i, ks0, vs0, kbase, vbase, k_lo, k_hi, lofs, w);
+  }
   // Nothing may be outstanding at the loop head: otherwise the wait inserted for the
   // query registers inside the loop also waits for the next block's loads.
   drain();
@@ -268,24 +269,52 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
     const bool need_mask = (kb + kKeyBlock > P) || (kb + kKeyBlock > k_hi);
     uint64_t vis = ~0ull;
     if (need_mask) vis = block_visibility(kb, P, k_hi, anc, ok) >> (4 * h);
-    if (more) kv_issue<D>(kn, vn, kbase, vbase, kb + kKeyBlock, k_hi, lofs, w);
+    // The next block's loads are spread over the S^T steps so that issuing them overlaps
+    // the MFMAs. After the last block they reload this block into the idle buffer (valid
+    // addresses, never read), which keeps every load unconditional.
+    const int kb_next = more ? kb + kKeyBlock : kb;
+    constexpr int QS = 2 * NKS;             // S^T steps (ks, kt), j = 2 ks + kt
+    constexpr int QPL = QS / L::kLoads;     // steps per load pair
+    constexpr int PS = 4 * NT;              // P V steps (k2, nt), j = NT k2 + nt
+    constexpr int kAhead = 4;               // LDS fragment reads kept in flight
+    const char* kcb = reinterpret_cast<const char*>(kc);
+    const char* vcb = reinterpret_cast<const char*>(vc);
+    auto kfrag = [&](int j) {
+      Frag8 f;
+      f.u = *reinterpret_cast<const uint4*>(kcb + (j & 1) * 32 * L::kRowBytes + kread[j >> 1]);
+      return f;
+    };
+    auto vfrag = [&](int j) {
+      Frag8 f;
+      const char* vrow = vcb + 16 * (j / NT) * L::kRowBytes + vread[j % NT];
+      f.h[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow)));
+      f.h[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 8 * L::kRowBytes)));
+      return f;
+    };
 
     if (act) {
-      const char* kcb = reinterpret_cast<const char*>(kc);
-      const char* vcb = reinterpret_cast<const char*>(vc);
-      // ---- S^T = K Q^T for two 32-key tiles; lane holds keys kb + kt*32 + (i/4)*8 + 4h + i%4
+      // ---- S^T = K Q^T for two 32-key tiles; lane holds keys kb + kt*32 + (i/4)*8 + 4h + i%4.
+      //      Software-pipelined: the K fragment of step j + kAhead is read while step j runs.
       f32x16 sc[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[kt][i] = 0.f;
+      Frag8 kf[QS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          Frag8 kf;
-          kf.u = *reinterpret_cast<const uint4*>(kcb + kt * 32 * L::kRowBytes + kread[ks]);
-          sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, sc[kt], 0, 0, 0);
-        }
+      for (int j = 0; j < kAhead; ++j) kf[j] = kfrag(j);
+#pragma unroll
+      for (int j = 0; j < QS; ++j) {
+        if (j + kAhead < QS) kf[j + kAhead] = kfrag(j + kAhead);
+        if (j % QPL == 0) kv_issue_pair<D>(j / QPL, kn, vn, kbase, vbase, kb_next, k_hi, lofs, w);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j].v, qf[j >> 1].v, sc[j & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // the first V fragments are read while the softmax runs
+      Frag8 vf[PS];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) vf[j] = vfrag(j);
       // ---- masks (tree block, range tail) only where a block needs them
       if (need_mask) {
         const uint32_t v_lo = static_cast<uint32_t>(vis), v_hi = static_cast<uint32_t>(vis >> 32);
@@ -332,34 +361,30 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
       }
       const float mref = (m_run == -INFINITY) ? 0.f : m_run;
       float sum = 0.f;
+      // the A operand of step k2 is p values 8*(k2%2) .. +7 of key tile k2/2, i.e. keys
+      // 16 k2 + 8 (j/4) + 4h + j%4: the key order of the two transpose reads of a V fragment
+      // (rows 16 k2 + 4h + j and 16 k2 + 8 + 4h + j)
+      Frag8 pf8[4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], sl2, -mref));
-          sc[kt][i] = p;
           sum += p;
+          pf8[2 * kt + (i >> 3)].v[i & 7] = static_cast<__bf16>(p);
         }
       l_run += sum;
-      // ---- O += P V over four 16-key steps; the A operand of step k2 is p values
-      //      8*(k2%2) .. +7 of key tile k2/2, i.e. keys 16 k2 + 8 (j/4) + 4h + j%4, which
-      //      is the key order of the two transpose reads (rows 16 k2 + 4h + j and + 8)
+      // ---- O += P V, software-pipelined like S^T
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        Frag8 pf8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf8.v[j] = static_cast<__bf16>(sc[k2 >> 1][8 * (k2 & 1) + j]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          Frag8 vf;
-          const char* vrow = vcb + 16 * k2 * L::kRowBytes + vread[nt];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vrow + 8 * L::kRowBytes));
-          vf.h[0] = __builtin_bit_cast(uint2, lo);
-          vf.h[1] = __builtin_bit_cast(uint2, hi);
-          oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf8.v, vf.v, oacc[nt], 0, 0, 0);
-        }
+      for (int j = 0; j < PS; ++j) {
+        if (j + kAhead < PS) vf[j + kAhead] = vfrag(j + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[j % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf8[j / NT].v, vf[j].v, oacc[j % NT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i) kv_issue_pair<D>(i, kn, vn, kbase, vbase, kb_next, k_hi, lofs, w);
     }
     // the next block has landed (this wave's loads) and is visible (everyone's)
     drain();
