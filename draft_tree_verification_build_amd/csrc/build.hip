@@ -76,7 +76,7 @@ constexpr int kTalonMergeCap = 2048;  // chunks_of(V) * K must not exceed this
 // Phase 1: one workgroup per (sequence, row f < B, chunk). The workgroup that completes a
 // row merges its chunks into the row's Top-K (value, token), count and log-sum-exp.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void talon_rows_kernel(TalonArgs a) {
+__global__ __launch_bounds__(kBlock, 4) void talon_rows_kernel(TalonArgs a) {
   __shared__ RowSmem rs;
   __shared__ MergeSmem<kTalonMergeCap> ms;
   __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * kTalonMaxK) > kCandCap
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void talon_select_kernel(TalonArgs a) {
 constexpr int kSpineMaxK = 65;
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void spine_kernel(SpineArgs a) {
+__global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   __shared__ RowSmem rs;
   __shared__ MergeSmem<kTalonMergeCap> ms;
   __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * 128) > kCandCap ? pow2_at_least(kWaves * 128)

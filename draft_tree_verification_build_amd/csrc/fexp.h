@@ -57,16 +57,20 @@ __device__ __forceinline__ double exp_nonpos(double d, const double* t) {
   return under ? 0.0 : e;
 }
 
-// sum_j exp(x[j] - m) for x[j] <= m (entries of -inf contribute 0), each term as in
-// exp_nonpos. Groups of G terms are written in three passes (reductions, table reads,
-// scaling) so that the group's table reads are in flight together; G bounds the extra
-// registers.
+// sum_j exp(x[j] - m) for x[j] <= m, each term as in exp_nonpos except for how the
+// reduction is rounded: k = rint(d * 64/ln2) is read off fma(d, 64/ln2, 1.5 * 2^52), whose
+// low 32 bits hold k in two's complement, and d is clamped at -745 instead of selecting 0
+// (a term of exp(-745) < 2^-1074 is below every sum, which is at least 1). Entries of -inf
+// contribute that negligible term. Groups of G terms are written in three passes
+// (reductions, table reads, scaling) so that the group's table reads are in flight
+// together; G bounds the extra registers.
 template <int N, int G = 8>
 __device__ __forceinline__ double exp_nonpos_sum(const float (&x)[N], double m, const double* t) {
   static_assert(N % G == 0, "N must be a multiple of G");
   const double kInv = 0x1.71547652b82fep+6;
   const double kL1 = 0x1.62e42fefa0000p-7;
   const double kL2 = 0x1.cf79abc9e3b3ap-46;
+  const double kShift = 0x1.8p52;
   double s = 0.0;
 #pragma unroll
   for (int g0 = 0; g0 < N; g0 += G) {
@@ -74,18 +78,16 @@ __device__ __forceinline__ double exp_nonpos_sum(const float (&x)[N], double m, 
     int n[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const double d = static_cast<double>(x[g0 + j]) - m;
-      const bool under = !(d >= -745.0);
-      const double dc = under ? -745.0 : d;
-      const double k = rint(dc * kInv);
-      n[j] = static_cast<int>(k);
+      const double dc = fmax(static_cast<double>(x[g0 + j]) - m, -745.0);
+      const double kp = fma(dc, kInv, kShift);
+      n[j] = __double2loint(kp);
+      const double k = kp - kShift;
       const double r = fma(-k, kL2, fma(-k, kL1, dc));
       double q = fma(r, 1.0 / 120.0, 1.0 / 24.0);
       q = fma(r, q, 1.0 / 6.0);
       q = fma(r, q, 0.5);
       q = fma(r, q, 1.0);
-      q = fma(r, q, 1.0);
-      p[j] = under ? 0.0 : q;
+      p[j] = fma(r, q, 1.0);
     }
     double tv[G];
 #pragma unroll

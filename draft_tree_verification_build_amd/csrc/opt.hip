@@ -75,7 +75,7 @@ __device__ __forceinline__ double parent_score(const OptArgs& a, int s, int f) {
 // BIG: lists of up to 1024 per chunk (the root layer, K up to n); otherwise K <= 32, which
 // needs far less shared memory and lets several workgroups share a compute unit.
 template <int DT, bool BIG>
-__global__ __launch_bounds__(kBlock) void opt_rows_kernel(OptArgs a) {
+__global__ __launch_bounds__(kBlock, 4) void opt_rows_kernel(OptArgs a) {
   constexpr int kMergeCap = BIG ? kOptMergeCap : 2048;
   constexpr int kSort = BIG ? 4 * 1024 : kCandCap;
   __shared__ RowSmem rs;

@@ -404,12 +404,15 @@ template <int CAP>
 __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx, int nch, int K,
                          float* maxv, int* argmax, double* lse, float* rv, int* ri, RowSmem& sm,
                          MergeSmem<CAP>& ms, int kout = -1) {
-  for (int c = threadIdx.x; c < nch; c += kBlock) {  // one parallel round of loads
+  // one parallel round of loads: the chunk statistics and every list slot (slots past a
+  // chunk's count are read too and ignored, so no load waits for a count)
+  for (int c = threadIdx.x; c < nch; c += kBlock) {
     ms.cnt[c] = ld_cc(&st[c].cnt);
     ms.maxv[c] = ld_cc(&st[c].maxv);
     ms.argmax[c] = ld_cc(&st[c].argmax);
     ms.sumexp[c] = ld_cc(&st[c].sumexp);
   }
+  for (int e = threadIdx.x; e < nch * K; e += kBlock) ms.key[e] = sort_key(ld_cc(&cval[e]), ld_cc(&cidx[e]));
   __syncthreads();
   if (threadIdx.x < 64) {  // wave 0: lane c holds chunk c (nch <= 64)
     const int c = threadIdx.x;
@@ -435,11 +438,6 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     __syncthreads();
     return 0;
   }
-  for (int e = threadIdx.x; e < nch * K; e += kBlock) {
-    const int c = e / K, j = e % K;
-    if (j < ms.cnt[c]) ms.key[e] = sort_key(ld_cc(&cval[e]), ld_cc(&cidx[e]));
-  }
-  __syncthreads();
   const int n = nch * K;
   if (n <= 1024) {  // absent entries count as key 0, below every real key
     for (int e = threadIdx.x; e < n; e += kBlock)
