@@ -310,7 +310,6 @@ VerifyLayout verify_layout(void* ws, int S, int n_cap) {
 struct SampleLayout {
   dtv::WsHeader* hdr;
   dtv::ChunkStat* st;
-  unsigned* rtick;
   double* lse;
   unsigned long long* gbar;
   double* xch;
@@ -325,12 +324,11 @@ SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   SampleLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
   L.st = c.take<dtv::ChunkStat>(rows * nch);
-  L.rtick = c.take<unsigned>(rows);
   L.lse = c.take<double>(rows);
   L.gbar = c.take<unsigned long long>(S);
   // one exchange slot per rejection (at most n_cap - 1) and one for the bonus draw
   L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * 64);
-  L.pbuf = c.take<double>(static_cast<size_t>(S) * 2 * V);
+  L.pbuf = c.take<double>(static_cast<size_t>(S) * 3 * V);   // two residuals and q per sequence
   L.bytes = c.off;
   return L;
 }
@@ -755,7 +753,7 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
   a.bonus = bonus;
   a.hdr = L.hdr;
   a.st = L.st;
-  a.rtick = L.rtick;
+  a.S = S;
   a.lse = L.lse;
   a.gbar = L.gbar;
   a.xch = L.xch;
@@ -769,6 +767,13 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
   int G = (max_blocks < 256 ? max_blocks : 256) / S;
   if (G > kSampleMaxGroup) G = kSampleMaxGroup;
   a.G = G < 1 ? 1 : G;
+  const int lse_slots = dtv::sample_lse_max_blocks(dtype == DTV_BF16 ? 1 : 0);
+  REQUIRE(lse_slots >= 1, DTV_EUNSUPPORTED, "occupancy query failed");
+  const long items = static_cast<long>(S) * tree->n_cap * 2 * a.nch;
+  // every resident workgroup, but no workgroup with more than 64 items
+  long grid = items < lse_slots ? items : lse_slots;
+  if (grid * 64 < items) grid = (items + 63) / 64;
+  a.lse_grid = static_cast<int>(grid);
   return launched(dtv::launch_verify_sample(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }
 

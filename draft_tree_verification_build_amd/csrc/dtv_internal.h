@@ -179,14 +179,15 @@ struct SampleArgs {
   int* path_len;
   int* bonus;
   WsHeader* hdr;
-  ChunkStat* st;             // [S][n_cap][2][nch]
-  unsigned* rtick;           // [S][n_cap][2]
-  double* lse;               // [S][n_cap][2]  (0: target, 1: draft)
+  ChunkStat* st;             // [S][n_cap][2 (0: target, 1: draft)][nch]
+  double* lse;               // [S][n_cap][2]
+  int S;
+  int lse_grid;              // workgroups of the chunk-statistics kernel
   int G;                     // workgroups per sequence in the walk
   unsigned long long* gbar;  // [S] group barrier arrival counters (zeroed by phase 1)
   int max_pass;              // exchange slots per sequence (rejections + 1 bonus draw)
   double* xch;               // [S][max_pass][64] walk exchange slots
-  double* pbuf;              // [S][2][V] residual distributions
+  double* pbuf;              // [S][3][V] residual distributions and q (slices too large for LDS)
 };
 
 struct CompactArgs {
@@ -212,6 +213,7 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st);
 int sample_walk_max_blocks(int dtype);
+int sample_lse_max_blocks(int dtype);
 int launch_compact(const CompactArgs& a, hipStream_t st);
 
 }  // namespace dtv

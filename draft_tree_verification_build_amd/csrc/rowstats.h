@@ -129,6 +129,57 @@ __device__ __forceinline__ void load_chunk(const void* row, int V, int c, float 
   }
 }
 
+// The 16-byte loads of one chunk, held in registers so that a loop over chunks can issue
+// the next chunk's loads before working on the current one (vector path of load_chunk:
+// the row must be 16-byte aligned and hold at least one full vector).
+struct RawChunk {
+  uint4 r0, r1, r2, r3;   // named members keep them in registers
+};
+static_assert(kLoads == 4, "RawChunk holds kLoads vectors");
+
+template <int DT>
+__device__ __forceinline__ void raw_chunk_load(const void* row, int V, int c, RawChunk& rc) {
+  using R = RowT<DT>;
+  const int vfull = V / R::VEC;
+  const int v0 = c * R::CHUNK / R::VEC + static_cast<int>(threadIdx.x);
+  const char* b = static_cast<const char*>(row);
+  rc.r0 = *reinterpret_cast<const uint4*>(b + static_cast<size_t>(min(v0, vfull - 1)) * 16);
+  rc.r1 = *reinterpret_cast<const uint4*>(b + static_cast<size_t>(min(v0 + kBlock, vfull - 1)) * 16);
+  rc.r2 = *reinterpret_cast<const uint4*>(b + static_cast<size_t>(min(v0 + 2 * kBlock, vfull - 1)) * 16);
+  rc.r3 = *reinterpret_cast<const uint4*>(b + static_cast<size_t>(min(v0 + 3 * kBlock, vfull - 1)) * 16);
+}
+
+// Values of a chunk loaded by raw_chunk_load, as load_chunk gives them (-inf past the row
+// end; the one vector straddling the row end re-reads its valid elements).
+template <int DT>
+__device__ __forceinline__ void raw_chunk_decode(const void* row, int V, int c, const RawChunk& rc,
+                                                 float (&x)[RowT<DT>::E]) {
+  using R = RowT<DT>;
+  const int vfull = V / R::VEC;
+  const int v0 = c * R::CHUNK / R::VEC + static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const uint4 q = i == 0 ? rc.r0 : i == 1 ? rc.r1 : i == 2 ? rc.r2 : rc.r3;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    const int vi = v0 + i * kBlock;
+#pragma unroll
+    for (int e = 0; e < R::VEC; ++e) {
+      const float f = DT ? bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu))
+                         : __uint_as_float(w[e]);
+      x[i * R::VEC + e] = vi < vfull ? f : -INFINITY;
+    }
+    if (vi == vfull && vfull * R::VEC < V) {
+#pragma unroll
+      for (int e = 0; e < R::VEC; ++e) {
+        const int ix = vi * R::VEC + e;
+        if (ix < V)
+          x[i * R::VEC + e] = DT ? bf16_to_f32(static_cast<const uint16_t*>(row)[ix])
+                                 : static_cast<const float*>(row)[ix];
+      }
+    }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ int elem_index(int c, int i, int e) {
   using R = RowT<DT>;

@@ -118,11 +118,13 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
 // the walk moves to the first accepted child; when none is accepted (or the node is a
 // leaf) the bonus token is drawn from the current p by inverse CDF with u_res.
 //
-// Work split: one workgroup per (sequence, node, target-or-draft row, chunk) reduces its
-// chunk to (max, float64 sum of exp); the last one of a row merges the row's log-sum-exp;
-// the last one of a sequence walks. In the walk, a first try needs only the two row
-// values at the child's token; each rejection costs one V-wide residual pass over
-// float64 buffers in the workspace; the bonus draw is one V-wide prefix-sum pass.
+// Work split: a grid of resident workgroups reduces every chunk of every node's target and
+// draft rows to (max, float64 sum of exp), loading the next chunk while reducing the
+// current one; the rows' log-sum-exps are merged from those (by a small kernel, or inside
+// the walk for small trees). The walk of a sequence is shared by G workgroups, each owning
+// a slice of the vocabulary: a first try needs only the two row values at the child's
+// token; each rejection costs one residual pass over the slices (kept in shared memory
+// when they fit) and one exchange of slice sums; the bonus draw is one prefix-sum pass.
 
 constexpr int kSampleMaxNodes = 1024;
 
@@ -159,7 +161,12 @@ __device__ __forceinline__ void row_vec(const void* row, int vi, float (&x)[RowT
 // The walk's view of the current distribution p at node v: softmax of the target row
 // (pc null) or the normalised residual pc / zc; q is the softmax of the draft row. A
 // "unit" is a 16-byte vector of VEC consecutive logits when `vec` (rows 16-byte aligned,
-// V a multiple of VEC), else a single entry.
+// V a multiple of VEC), else a single entry. pc and the q cache qc hold this workgroup's
+// entries only, entry j at index j - base; they live in shared memory when the slice
+// fits, else in the workspace, and only this workgroup ever reads what it wrote there.
+// Hence p(j) with pc set and the unit accessors take only entries of this workgroup's
+// slice, while q(j) (any entry: the acceptance test reads the child's token) always
+// evaluates the draft row; the cache holds the same values, computed the same way.
 template <int DT>
 struct WalkDist {
   static constexpr int VEC = RowT<DT>::VEC;
@@ -168,12 +175,15 @@ struct WalkDist {
   double lt, ld;
   const double* pc;
   double zc;
+  double* qc;
+  bool qvalid;
+  int base;
   const double* tab;
   bool vec;
 
   __device__ int width() const { return vec ? VEC : 1; }
   __device__ double p(int j) const {
-    return pc ? ld_cc(pc + j) / zc : exp_nonpos(static_cast<double>(row_value<DT>(trow, j)) - lt, tab);
+    return pc ? pc[j - base] / zc : exp_nonpos(static_cast<double>(row_value<DT>(trow, j)) - lt, tab);
   }
   __device__ double q(int j) const {
     return exp_nonpos(static_cast<double>(row_value<DT>(drow, j)) - ld, tab);
@@ -186,7 +196,7 @@ struct WalkDist {
     }
     if (pc) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) out[e] = ld_cc(pc + static_cast<size_t>(a) * VEC + e) / zc;
+      for (int e = 0; e < VEC; ++e) out[e] = pc[a * VEC + e - base] / zc;
     } else {
       float x[VEC];
       row_vec<DT>(trow, a, x);
@@ -194,15 +204,29 @@ struct WalkDist {
       for (int e = 0; e < VEC; ++e) out[e] = exp_nonpos(static_cast<double>(x[e]) - lt, tab);
     }
   }
+  // q of the entries of unit a; the first pass at a node computes them and fills the cache
   __device__ void q_unit(int a, double (&out)[VEC]) const {
     if (!vec) {
-      out[0] = q(a);
+      if (qvalid) {
+        out[0] = qc[a - base];
+      } else {
+        out[0] = q(a);
+        qc[a - base] = out[0];
+      }
+      return;
+    }
+    if (qvalid) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) out[e] = qc[a * VEC + e - base];
       return;
     }
     float x[VEC];
     row_vec<DT>(drow, a, x);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) out[e] = exp_nonpos(static_cast<double>(x[e]) - ld, tab);
+    for (int e = 0; e < VEC; ++e) {
+      out[e] = exp_nonpos(static_cast<double>(x[e]) - ld, tab);
+      qc[a * VEC + e - base] = out[e];
+    }
   }
 };
 
@@ -214,6 +238,7 @@ struct WalkDist {
 // decisions. A fresh slot per exchange matters on a multi-XCD GPU: re-reading one
 // location that another XCD rewrote can return this XCD's older cached copy.
 constexpr int kXchStride = 64;   // doubles per exchange slot (G <= 32 sums + 2 values)
+constexpr int kWalkSlice = 4096; // entries of a workgroup's slice kept in shared memory
 
 struct WalkGroup {
   int gi, G;
@@ -249,8 +274,8 @@ __device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0,
   return true;
 }
 
-// One rejection: out = max(p - q, 0) over this workgroup's units (st_cc, so the owner's
-// entries are visible to the group after the exchange); returns the block-wide slice sum.
+// One rejection: out = max(p - q, 0) over this workgroup's units (entry j at j - d.base);
+// returns the block-wide slice sum.
 template <int DT>
 __device__ double residual_slice(const WalkDist<DT>& d, double* out, const WalkGroup& g, SampleSmem& sm) {
   constexpr int VEC = WalkDist<DT>::VEC;
@@ -265,7 +290,7 @@ __device__ double residual_slice(const WalkDist<DT>& d, double* out, const WalkG
     for (int e = 0; e < VEC; ++e) {
       if (e < w) {
         const double r = fmax(pv[e] - qv[e], 0.0);
-        st_cc(out + static_cast<size_t>(a) * w + e, r);
+        out[a * w + e - d.base] = r;
         loc += r;
       }
     }
@@ -336,47 +361,161 @@ __device__ __forceinline__ double chunk_lse(const ChunkStat* st, int nch, const 
   return static_cast<double>(M) + log(sum);
 }
 
-// Phase 1: log-sum-exp of every node's target and draft rows, one workgroup per
-// (sequence, node, row, chunk); the last chunk of a row merges.
+// Phase 1: (max, float64 sum of exp) of every chunk of every node's target and draft rows.
+// Work item it = ((s * n_cap + i) * 2 + row kind) * nch + chunk, the index of its ChunkStat.
+// A grid of resident workgroups walks the items with a stride of the grid size; each
+// workgroup issues the loads of its next chunk (and the tree lookups of the one after)
+// before reducing the current chunk, so loading overlaps the float64 exponentials. The
+// statistics are plain stores read after the kernel boundary (by the merge kernel or the
+// walk), so no workgroup waits on another here.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sample_lse_kernel(SampleArgs a) {
   __shared__ RowSmem rs;
+  __shared__ float wmax[2][kWaves];    // per-wave results, double-buffered by item parity
+  __shared__ double wse[2][kWaves];
   using Rw = RowT<DT>;
   row_smem_init(rs);
+  // the walk's group barrier counters start every call at zero
+  if (blockIdx.x == 0)
+    for (int q = threadIdx.x; q < a.S; q += kBlock)
+      __hip_atomic_exchange(&a.gbar[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int nch = a.nch;
   const int cap = a.tree.n_cap;
-  int bid = blockIdx.x;
-  const int c = bid % nch;
-  bid /= nch;
-  const int which = bid % 2;
-  bid /= 2;
-  const int i = bid % cap;
-  const int s = bid / cap;
-  // the walk's group barrier counters start every call at zero
-  if (c == 0 && which == 0 && i == 0 && threadIdx.x == 0)
-    __hip_atomic_exchange(&a.gbar[s], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int N = a.tree.n_nodes[s];
-  if (i >= N) return;
-  if (N > cap) {
-    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+  const int items = a.S * cap * 2 * nch;
+  const int step = static_cast<int>(gridDim.x);
+  const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
+  const int w = threadIdx.x >> 6;
+
+  // Reduces chunk values x of item `it` to its ChunkStat (wave results combined by thread 0).
+  auto reduce = [&](const float (&x)[Rw::E], int it, bool real, int par) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < Rw::E; ++j) m = fmaxf(m, x[j]);
+    const float mw = wave_max(m);
+    double se = 0.0;
+    if (mw != -INFINITY) se = exp_nonpos_sum<Rw::E>(x, static_cast<double>(mw), rs.exptab);
+    se = wave_sum(se);
+    if ((threadIdx.x & 63) == 0) {
+      wmax[par][w] = mw;
+      wse[par][w] = se;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && real) {
+      float M = -INFINITY;
+      for (int q = 0; q < kWaves; ++q) M = fmaxf(M, wmax[par][q]);
+      double S = 0.0;
+      for (int q = 0; q < kWaves; ++q)
+        if (wmax[par][q] != -INFINITY)
+          S += wse[par][q] * exp_nonpos(static_cast<double>(wmax[par][q]) - static_cast<double>(M), rs.exptab);
+      a.st[it].maxv = M;
+      a.st[it].sumexp = S;
+    }
+  };
+  // Tree lookups (node count, row) of this workgroup's items, loaded once: lane j holds
+  // those of its j-th item (the grid gives no workgroup more than 64 items), so the loop
+  // reads them with a lane shuffle instead of waiting on a load per item.
+  struct Meta {
+    int n, r;
+  };
+  int bn, br;
+  {
+    const int itj = static_cast<int>(blockIdx.x) + (static_cast<int>(threadIdx.x) & 63) * step;
+    const int node = min(itj, items - 1) / nch / 2;   // s * cap + i
+    bn = a.tree.n_nodes[node / cap];
+    br = a.tree.row[node];
+  }
+  auto meta = [&](int k) {   // k: the item's position in this workgroup's sequence
+    Meta m;
+    m.n = __shfl(bn, k, 64);
+    m.r = __shfl(br, k, 64);
+    return m;
+  };
+  // Row of item `it`; `real` is false for items past the end or past the sequence's node
+  // count (those load row 0 of their sequence and store nothing).
+  auto row_of = [&](int it, const Meta& m, bool& real) {
+    const int b2 = min(it, items - 1) / nch;
+    const int node = b2 >> 1, s = node / cap, i = node % cap;
+    if (it < items && m.n > cap && threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    real = it < items && i < m.n && m.n <= cap && m.r >= 0 && m.r < a.R;
+    return static_cast<const char*>((b2 & 1) ? a.draft : a.target) +
+           (static_cast<size_t>(s) * a.R + (real ? m.r : 0)) * row_bytes;
+  };
+
+  const bool vec = a.V >= Rw::VEC && row_bytes % 16 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.draft)) & 15u) == 0;
+  int par = 0;
+  if (!vec) {   // unaligned rows: one synchronous chunk at a time
+    for (int it = blockIdx.x, k = 0; it < items; it += step, ++k) {
+      bool real;
+      const char* row = row_of(it, meta(k), real);
+      float x[Rw::E];
+      uint32_t key[Rw::E];
+      load_chunk<DT>(row, a.V, it % nch, x, key);
+      reduce(x, it, real, par);
+      par ^= 1;
+    }
     return;
   }
-  const size_t tb = static_cast<size_t>(s) * cap;
-  const int r = a.tree.row[tb + i];
-  const char* row = static_cast<const char*>(which ? a.draft : a.target) +
-                    (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
-  float x[Rw::E];
-  uint32_t key[Rw::E];
-  load_chunk<DT>(row, a.V, c, x, key);
-  const size_t rr = (tb + i) * 2 + which;
-  chunk_reduce<DT>(x, key, c, a.V, 0, &a.st[rr * nch + c], nullptr, nullptr, nullptr, rs);
-  if (last_arrival(&a.rtick[rr], nch, &rs.flag)) {
-    if (threadIdx.x < 64) {
-      const double l = chunk_lse(a.st + rr * nch, nch, rs.exptab);
-      if (threadIdx.x == 0) a.lse[rr] = l;   // read after the kernel boundary
+  int it = blockIdx.x;
+  bool real0;
+  const char* row0 = row_of(it, meta(0), real0);
+  RawChunk rc;
+  raw_chunk_load<DT>(row0, a.V, min(it, items - 1) % nch, rc);
+  for (int k = 1; it < items; it += step, ++k) {
+    bool real1;
+    const char* row1 = row_of(it + step, meta(k), real1);
+    RawChunk rn;
+    raw_chunk_load<DT>(row1, a.V, min(it + step, items - 1) % nch, rn);
+    float x[Rw::E];
+    raw_chunk_decode<DT>(row0, a.V, it % nch, rc, x);
+    reduce(x, it, real0, par);
+    par ^= 1;
+    rc = rn;
+    row0 = row1;
+    real0 = real1;
+  }
+}
+
+// log-sum-exp of one row from its nch chunk statistics, merged with a running maximum;
+// the statistics are loaded 8 at a time (clamped indices, extra entries ignored) so that
+// their loads are in flight together.
+__device__ double row_lse_from_stats(const ChunkStat* st, int nch, const double* tab) {
+  float M = -INFINITY;
+  double S = 0.0;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float mc[8];
+    double sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = min(c0 + j, nch - 1);
+      mc[j] = st[c].maxv;
+      sc[j] = st[c].sumexp;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c0 + j >= nch || mc[j] == -INFINITY) continue;
+      if (mc[j] > M) {
+        S = S * exp_nonpos(static_cast<double>(M) - static_cast<double>(mc[j]), tab) + sc[j];
+        M = mc[j];
+      } else {
+        S += sc[j] * exp_nonpos(static_cast<double>(mc[j]) - static_cast<double>(M), tab);
+      }
     }
   }
+  return static_cast<double>(M) + log(S);
+}
+
+// Phase 1b (trees of more than kBlock / 2 nodes): the log-sum-exp of every row, one thread
+// per row. Smaller trees skip it: the walk merges its rows itself, one per thread.
+__global__ __launch_bounds__(kBlock) void sample_lse_merge_kernel(SampleArgs a) {
+  __shared__ double tab[64];
+  exp_table_load(tab);
+  __syncthreads();
+  const int rows = a.S * a.tree.n_cap * 2;
+  const int q = blockIdx.x * kBlock + threadIdx.x;
+  if (q >= rows) return;
+  a.lse[q] = row_lse_from_stats(a.st + static_cast<size_t>(q) * a.nch, a.nch, tab);
 }
 
 // Phase 2: the walk of sequence blockIdx.x / G, shared by its G workgroups (the group
@@ -385,6 +524,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   __shared__ SampleSmem sm;
   __shared__ double gvals[kXchStride];
+  __shared__ double slice_buf[3][kWalkSlice];   // residuals (two) and q of this slice
   using Rw = RowT<DT>;
   row_smem_init(sm.rs);
   const int s = blockIdx.x / a.G;
@@ -396,13 +536,24 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   }
   const size_t tb = static_cast<size_t>(s) * cap;
   const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
+  const bool merge_here = 2 * cap <= kBlock;   // else sample_lse_merge_kernel ran
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.par[v] = static_cast<short>(a.tree.parent[tb + v]);
     sm.tok[v] = a.tree.token[tb + v];
-    sm.lset[v] = a.lse[(tb + v) * 2 + 0];
-    sm.lsed[v] = a.lse[(tb + v) * 2 + 1];
+    if (!merge_here) {
+      sm.lset[v] = a.lse[(tb + v) * 2 + 0];
+      sm.lsed[v] = a.lse[(tb + v) * 2 + 1];
+    }
   }
-  __syncthreads();
+  __syncthreads();   // also publishes the exp table
+  if (merge_here) {
+    const int q = threadIdx.x;
+    if (q < 2 * N) {
+      const double l = row_lse_from_stats(a.st + ((tb + (q >> 1)) * 2 + (q & 1)) * a.nch, a.nch, sm.rs.exptab);
+      ((q & 1) ? sm.lsed : sm.lset)[q >> 1] = l;
+    }
+    __syncthreads();
+  }
   const bool vec = (a.V % Rw::VEC) == 0 && (row_bytes % 16) == 0 &&
                    ((reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.draft)) & 15u) == 0;
   WalkGroup grp;
@@ -418,7 +569,22 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   grp.xch = a.xch + static_cast<size_t>(s) * a.max_pass * kXchStride;
   grp.err = &a.hdr->err;
   grp.pass = 0;
-  double* P[2] = {a.pbuf + static_cast<size_t>(s) * 2 * a.V, a.pbuf + (static_cast<size_t>(s) * 2 + 1) * a.V};
+  // residual buffers and q cache: this slice in shared memory when it fits, else the
+  // sequence's rows of the workspace (indexed by entry)
+  const int wdt = vec ? Rw::VEC : 1;
+  const bool in_lds = (grp.u1 - grp.u0) * wdt <= kWalkSlice;
+  const int base = in_lds ? grp.u0 * wdt : 0;
+  double* P[2];
+  double* Q;
+  if (in_lds) {
+    P[0] = slice_buf[0];
+    P[1] = slice_buf[1];
+    Q = slice_buf[2];
+  } else {
+    P[0] = a.pbuf + static_cast<size_t>(s) * 3 * a.V;
+    P[1] = P[0] + a.V;
+    Q = P[1] + a.V;
+  }
   const double inv32 = 1.0 / 4294967296.0;
   const bool lead = grp.gi == 0;
   int v = 0, A = 0;
@@ -442,11 +608,15 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     d.ld = sm.lsed[v];
     d.pc = nullptr;
     d.zc = 1.0;
+    d.qc = Q;
+    d.qvalid = false;
+    d.base = base;
     d.tab = sm.rs.exptab;
     d.vec = vec;
     int cur = -1;
     int accepted = -1;
     double px_next = 0.0;   // p at the next child's token, as published by the last exchange
+    double z_last = 0.0;    // sum of the last residual when it became p (its slice sums are in gvals)
     for (int q = 0; q < nk; ++q) {
       const int ch = sm.kids[q];
       if (threadIdx.x == 0) {
@@ -467,6 +637,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       // and the current p (used if the residual sums to 0).
       const int nxt = (cur == 0) ? 1 : 0;
       const double part = residual_slice<DT>(d, P[nxt], grp, sm);
+      d.qvalid = true;   // residual_slice ends with a block barrier: the cache is complete
       const int xn = (q + 1 < nk) ? sm.tok[sm.kids[q + 1]] : -1;
       const int xu = vec ? xn / Rw::VEC : xn;
       const bool owner = xn >= 0 && xu >= grp.u0 && xu < grp.u1;
@@ -486,6 +657,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       } else {
         px_next = gvals[grp.G + 1];
       }
+      z_last = z;
     }
     if (accepted >= 0) {
       v = accepted;
@@ -493,10 +665,16 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       if (lead && threadIdx.x == 0) a.path[tb + A] = v;
       continue;
     }
-    // bonus: inverse CDF of the current p with u_res[v]; slice masses first
+    // bonus: inverse CDF of the current p with u_res[v]; slice masses first. After a
+    // rejection whose residual became p, they are that exchange's slice sums over z;
+    // otherwise (a leaf, or p kept from before) one pass and an exchange find them.
     const double u = (static_cast<double>(a.u_res[tb + v]) + 0.5) * inv32;
     double mass = 0.0;
-    {
+    if (z_last > 0.0) {
+      __syncthreads();
+      for (int k = threadIdx.x; k < grp.G; k += kBlock) gvals[k] /= z_last;
+      __syncthreads();
+    } else {
       constexpr int VEC = Rw::VEC;
       const int w = d.width();
       double loc = 0.0;
@@ -509,8 +687,8 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
           if (e < w) loc += pv[e];
       }
       mass = block_sum(loc, sm.rs.redd);
+      if (!group_exchange(grp, mass, false, 0.0, 0.0, gvals, &sm.flag)) return;
     }
-    if (!group_exchange(grp, mass, false, 0.0, 0.0, gvals, &sm.flag)) return;
     double total = 0.0;
     for (int k = 0; k < grp.G; ++k) total += gvals[k];
     const double target = u * total;
@@ -540,12 +718,17 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
 }
 
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st) {
-  const dim3 grid(S * a.tree.n_cap * 2 * a.nch);
+  const dim3 grid(a.lse_grid);
   if (dtype == 1)
     hipLaunchKernelGGL(sample_lse_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
     hipLaunchKernelGGL(sample_lse_kernel<0>, grid, dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
+  if (2 * a.tree.n_cap > kBlock) {   // smaller trees merge their rows inside the walk
+    hipLaunchKernelGGL(sample_lse_merge_kernel, dim3((S * a.tree.n_cap * 2 + kBlock - 1) / kBlock), dim3(kBlock),
+                       0, st, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
   // An ordinary launch on the caller's stream: the grid (S * G) is at most the number of
   // workgroups the device holds at once, so every group is resident together once the
   // stream reaches this kernel. (A cooperative launch is avoided: measured on MI355X it
@@ -555,6 +738,23 @@ int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st) 
   else
     hipLaunchKernelGGL(sample_walk_kernel<0>, dim3(S * a.G), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Workgroups of the chunk-statistics kernel that can be resident at once (queried once
+// per device).
+int sample_lse_max_blocks(int dtype) {
+  static int cached[64][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int& c = cached[dev][dtype ? 1 : 0];
+  if (c > 0) return c;
+  int ncu = 0, per = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  const void* fn = dtype ? reinterpret_cast<const void*>(&sample_lse_kernel<1>)
+                         : reinterpret_cast<const void*>(&sample_lse_kernel<0>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kBlock, 0) != hipSuccess || per < 1) return -1;
+  c = ncu * per;
+  return c;
 }
 
 // Workgroups of the walk kernel that can be resident at once (queried once per device).
