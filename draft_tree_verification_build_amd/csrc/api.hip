@@ -311,7 +311,6 @@ struct SampleLayout {
   dtv::WsHeader* hdr;
   dtv::ChunkStat* st;
   double* lse;
-  unsigned long long* gbar;
   double* xch;
   double* pbuf;
   size_t bytes;
@@ -325,7 +324,6 @@ SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   L.hdr = c.take<dtv::WsHeader>(1);
   L.st = c.take<dtv::ChunkStat>(rows * nch);
   L.lse = c.take<double>(rows);
-  L.gbar = c.take<unsigned long long>(S);
   // one exchange slot per rejection (at most n_cap - 1) and one for the bonus draw
   L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * 64);
   L.pbuf = c.take<double>(static_cast<size_t>(S) * 3 * V);   // two residuals and q per sequence
@@ -755,7 +753,6 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
   a.st = L.st;
   a.S = S;
   a.lse = L.lse;
-  a.gbar = L.gbar;
   a.xch = L.xch;
   a.max_pass = tree->n_cap + 1;
   a.pbuf = L.pbuf;

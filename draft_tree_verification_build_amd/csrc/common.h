@@ -199,37 +199,6 @@ __device__ __forceinline__ bool last_arrival(unsigned* counter, unsigned n, int*
   return *flag_lds != 0;
 }
 
-// Barrier over a co-resident group of `n` workgroups on a 64-bit arrival counter that only
-// ever grows: arrival a belongs to barrier instance a / n, which is complete once the
-// counter reaches (a / n + 1) * n. The counter is only ever changed by atomic adds (no
-// reset store races with them); the caller zeroes it before the group's first barrier (in
-// an earlier launch). The wait is bounded: after `limit` polls it writes `timeout_code`
-// into `*err` and returns false (callers then stop their loops).
-__device__ __forceinline__ bool group_barrier(unsigned long long* counter, unsigned n, int* err,
-                                              int timeout_code, int* flag_lds) {
-  drain();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    const unsigned long long a = __hip_atomic_fetch_add(counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long target = (a / n + 1) * n;
-    long polls = 0;
-    const long limit = 40000000;
-    while (ld_cc(counter) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++polls > limit) {
-        atomicExch(err, timeout_code);
-        ok = 0;
-        break;
-      }
-    }
-    acquire_cc();
-    *flag_lds = ok;
-  }
-  __syncthreads();
-  return *flag_lds != 0;
-}
-
 // ---------------------------------------------------------------- error codes in workspaces
 // The first 256 bytes of every workspace hold: int err; unsigned bar[2]; unsigned exit_count.
 struct WsHeader {

@@ -184,9 +184,8 @@ struct SampleArgs {
   int S;
   int lse_grid;              // workgroups of the chunk-statistics kernel
   int G;                     // workgroups per sequence in the walk
-  unsigned long long* gbar;  // [S] group barrier arrival counters (zeroed by phase 1)
   int max_pass;              // exchange slots per sequence (rejections + 1 bonus draw)
-  double* xch;               // [S][max_pass][64] walk exchange slots
+  double* xch;               // [S][max_pass][64] walk exchange slots (emptied by phase 1)
   double* pbuf;              // [S][3][V] residual distributions and q (slices too large for LDS)
 };
 

@@ -231,30 +231,33 @@ struct WalkDist {
 };
 
 // The G workgroups of a sequence share every V-wide pass: workgroup gi owns units
-// [u0, u1). Every exchange (one per pass) publishes into a slot of its own that no
-// workgroup has read before in this launch: per-workgroup slice sums plus two values the
-// owner of the next child's token adds (see the walk). Every workgroup then adds the
-// sums in workgroup order, so all of them see identical totals and take identical
-// decisions. A fresh slot per exchange matters on a multi-XCD GPU: re-reading one
-// location that another XCD rewrote can return this XCD's older cached copy.
+// [u0, u1). Every exchange (one per pass) uses a slot of its own: entry gi receives
+// workgroup gi's slice sum, entries G and G+1 two values from the owner of the next
+// child's token (see the walk). The previous kernel fills every entry with an empty
+// marker (a NaN no sum or probability takes), each entry is written once, and the readers
+// poll the entries they need until none holds the marker, so an exchange costs one store
+// and the polls, with no counter and no fence: the values are the signal. Every
+// workgroup then adds the sums in workgroup order, so all of them see identical totals
+// and take identical decisions.
 constexpr int kXchStride = 64;   // doubles per exchange slot (G <= 32 sums + 2 values)
 constexpr int kWalkSlice = 4096; // entries of a workgroup's slice kept in shared memory
+constexpr unsigned long long kSlotEmpty = 0x7FF8DEAD00000000ull;
+constexpr long kSpinLimit = 2000000;    // polls (each a memory round trip) before a timeout
 
 struct WalkGroup {
   int gi, G;
   int u0, u1;                 // this workgroup's units
-  unsigned long long* bar;    // the group's arrival counter
   double* xch;                // [max_pass][kXchStride] exchange slots
   int max_pass;
   int* err;
   int pass;                   // exchanges so far
 };
 
-// Publishes this workgroup's slice value (and, from the owner, extra values into slot
-// entries G and G+1), waits for the group and copies the slot into sm_vals[0 .. G+2).
-// Returns false on a barrier timeout or when the slots are exhausted.
-__device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0, double e1, double* sm_vals,
-                               int* flag) {
+// Publishes this workgroup's slice value (and, from the owner, e0 / e1 into slot entries G
+// and G+1), waits until the group's G values (and the owner's two when `extra`) are in
+// and copies them into sm_vals. Returns false on a timeout or when the slots are exhausted.
+__device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0, double e1, bool extra,
+                               double* sm_vals, int* flag) {
   if (g.pass >= g.max_pass) {
     if (threadIdx.x == 0) atomicExch(g.err, kErrCapacity);
     return false;
@@ -268,10 +271,30 @@ __device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0,
     }
   }
   ++g.pass;
-  if (!group_barrier(g.bar, static_cast<unsigned>(g.G), g.err, kErrTimeout, flag)) return false;
-  for (int q = threadIdx.x; q < g.G + 2; q += kBlock) sm_vals[q] = ld_cc(&slot[q]);
+  const int nv = g.G + (extra ? 2 : 0);
+  if (threadIdx.x < 64) {   // wave 0: lane k waits for entry k
+    const int k = threadIdx.x;
+    int ok = 1;
+    if (k < nv) {
+      unsigned long long* e = reinterpret_cast<unsigned long long*>(&slot[k]);
+      unsigned long long bits = ld_cc(e);
+      long polls = 0;
+      while (bits == kSlotEmpty) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > kSpinLimit) {
+          ok = 0;
+          break;
+        }
+        bits = ld_cc(e);
+      }
+      sm_vals[k] = __longlong_as_double(static_cast<long long>(bits));
+    }
+    if (!ok) atomicExch(g.err, kErrTimeout);
+    const unsigned long long good = __ballot(ok);
+    if (k == 0) *flag = (good == ~0ull) ? 1 : 0;
+  }
   __syncthreads();
-  return true;
+  return *flag != 0;
 }
 
 // One rejection: out = max(p - q, 0) over this workgroup's units (entry j at j - d.base);
@@ -375,10 +398,13 @@ __global__ __launch_bounds__(kBlock) void sample_lse_kernel(SampleArgs a) {
   __shared__ double wse[2][kWaves];
   using Rw = RowT<DT>;
   row_smem_init(rs);
-  // the walk's group barrier counters start every call at zero
-  if (blockIdx.x == 0)
-    for (int q = threadIdx.x; q < a.S; q += kBlock)
-      __hip_atomic_exchange(&a.gbar[q], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {   // every exchange slot of the walk starts empty
+    unsigned long long* x = reinterpret_cast<unsigned long long*>(a.xch);
+    const size_t n = static_cast<size_t>(a.S) * a.max_pass * kXchStride;
+    for (size_t q = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; q < n;
+         q += static_cast<size_t>(gridDim.x) * kBlock)
+      x[q] = kSlotEmpty;
+  }
   __syncthreads();
   const int nch = a.nch;
   const int cap = a.tree.n_cap;
@@ -564,7 +590,6 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     grp.u0 = static_cast<int>(static_cast<long>(units) * grp.gi / a.G);
     grp.u1 = static_cast<int>(static_cast<long>(units) * (grp.gi + 1) / a.G);
   }
-  grp.bar = a.gbar + s;
   grp.max_pass = a.max_pass;
   grp.xch = a.xch + static_cast<size_t>(s) * a.max_pass * kXchStride;
   grp.err = &a.hdr->err;
@@ -646,7 +671,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
         e1 = d.p(xn);
         e0 = fmax(e1 - d.q(xn), 0.0);   // the entry residual_slice stored for xn
       }
-      if (!group_exchange(grp, part, owner, e0, e1, gvals, &sm.flag)) return;
+      if (!group_exchange(grp, part, owner, e0, e1, xn >= 0, gvals, &sm.flag)) return;
       double z = 0.0;
       for (int k = 0; k < grp.G; ++k) z += gvals[k];
       if (z > 0.0) {
@@ -687,7 +712,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
           if (e < w) loc += pv[e];
       }
       mass = block_sum(loc, sm.rs.redd);
-      if (!group_exchange(grp, mass, false, 0.0, 0.0, gvals, &sm.flag)) return;
+      if (!group_exchange(grp, mass, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
     }
     double total = 0.0;
     for (int k = 0; k < grp.G; ++k) total += gvals[k];
