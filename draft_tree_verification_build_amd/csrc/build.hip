@@ -124,14 +124,23 @@ struct TalonSelSmem {
 };
 
 // Keeps the `room` best candidates (ckey[e] != 0) by (key desc, e asc) and counts them per
-// frontier row into kept[]: the room-th largest key T by radix selection, then every key
-// above T and, of the keys equal to T, those with the lowest e. Requires more than `room`
-// candidates.
+// frontier row into kept[]. Radix selection narrows the boundary to a key prefix: either
+// every key with that prefix is taken (the keys above the prefix and that whole group), or
+// the prefix is the full room-th largest key T and, of the keys equal to T, those with the
+// lowest e are taken. Requires more than `room` candidates.
 __device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int room) {
-  int rem = 0;
-  const unsigned long long T = radix_kth_desc(sm.ckey, n, room, sm.rs, &rem);
+  const RadixCut cut = radix_topk_cut(sm.ckey, n, room, sm.rs);
   for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = 0;
   __syncthreads();
+  if (cut.all_in) {   // every key of the boundary group is taken: no tie order needed
+    for (int e = threadIdx.x; e < n; e += kBlock) {
+      const unsigned long long k = sm.ckey[e];
+      if (k != 0ull && (k & cut.mask) >= cut.prefix) atomicAdd(&sm.kept[e / K], 1);
+    }
+    __syncthreads();
+    return;
+  }
+  const unsigned long long T = cut.prefix;   // the full key: ties at T go by e
   int carry_eq = 0;
   for (int e0 = 0; e0 < n; e0 += kBlock) {
     const int e = e0 + threadIdx.x;
@@ -139,7 +148,7 @@ __device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int r
     const int eq = (k != 0ull && k == T) ? 1 : 0;
     int tot = 0;
     const int before = carry_eq + block_exclusive_scan(eq, sm.scan, &tot);
-    if (k != 0ull && (k > T || (eq && before < rem))) atomicAdd(&sm.kept[e / K], 1);
+    if (k != 0ull && (k > T || (eq && before < cut.rem))) atomicAdd(&sm.kept[e / K], 1);
     carry_eq += tot;
   }
   __syncthreads();

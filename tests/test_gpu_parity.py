@@ -117,6 +117,9 @@ TALON_CASES = [
     ("c2_talon_llama3_8b", 15, {"V": 12, "P": 64, "B": 30, "K": 12, "alpha": 0.2}),
     ("c2_talon_llama3_8b", 16, {"V": 9000, "P": 64, "S": 3, "B": 40, "K": 7}),
     ("c2_talon_llama3_8b", 17, {"V": 1000, "P": 64, "dtype": "f32", "B": 16, "K": 4}),
+    # no gate and a wide second layer (40 frontier rows of 40, 1600 candidates for 60
+    # slots): the radix budget selection past the small-pool path
+    ("c2_talon_llama3_8b", 18, {"V": 2000, "P": 64, "B": 100, "K": 40, "alpha": 0.0}),
 ]
 
 
