@@ -148,8 +148,18 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   // the n-th largest reported score bounds the layer's n-th best score from below
   double lo = -INFINITY;
   if (total >= a.n) {
-    int rem = 0;
-    const unsigned long long k = radix_kth_desc(sm.key, total, a.n, sm.rs, &rem);
+    // the n-th largest key: the smallest key of the boundary group when the radix cut
+    // takes that group whole, else the cut's full key
+    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs);
+    unsigned long long k = cut.prefix;
+    if (cut.all_in) {
+      unsigned long long kmin = ~0ull;
+      for (int e = threadIdx.x; e < total; e += kBlock) {
+        const unsigned long long x = sm.key[e];
+        if ((x & cut.mask) == cut.prefix) kmin = x < kmin ? x : kmin;
+      }
+      k = block_min(kmin, sm.rs.red);
+    }
     const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
     lo = __longlong_as_double(static_cast<long long>(u));
   }
@@ -268,13 +278,15 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   // ---- the layer's n best
   const int kept = C < n ? C : n;
   if (C > n) {
-    int rem = 0;
-    const unsigned long long T = radix_kth_desc(sm.u.in.key, C, n, sm.rs, &rem);
+    // radix cut of the n best: a boundary group taken whole needs no tie order
+    const RadixCut cut = radix_topk_cut(sm.u.in.key, C, n, sm.rs);
+    const unsigned long long T = cut.prefix;
+    const int rem = cut.all_in ? 0 : cut.rem;
     for (int e = threadIdx.x; e < C; e += kBlock) {
       const unsigned long long k = sm.u.in.key[e];
-      if (k > T) {
+      if (cut.all_in ? ((k & cut.mask) >= T) : (k > T)) {
         sm.keep_idx[atomicAdd(&sm.nkept, 1)] = e;
-      } else if (k == T) {
+      } else if (!cut.all_in && k == T) {
         const int t = atomicAdd(&sm.ntie, 1);
         if (t < 1024) {
           sm.tkey[t] = front_key(sm.u.in.c[e]);
