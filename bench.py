@@ -85,6 +85,23 @@ def algorithmic_work(step, wl):
     return out
 
 
+# The kernels each stage launches (a stage's time is the HIP-event time of all of them;
+# rocprofv3 --kernel-trace lists them separately, and their averages add up to it).
+STAGE_KERNELS = {
+    "build": lambda c: {"talon": ["talon_rows_kernel", "talon_select_kernel"],
+                        "spine": ["spine_kernel"],
+                        "opt": ["opt_init_kernel", "opt_rows_kernel", "opt_bound_kernel", "opt_collect_kernel",
+                                "opt_select_kernel", "opt_finalize_kernel"],
+                        "given": ["given_tree_kernel"]}[c.build],
+    "attention": lambda c: (["attn_bf16_kernel", "attn_combine_rows_kernel"] if c.dtype == "bf16"
+                            else ["attn_f32_kernel"]),
+    "verify": lambda c: (["verify_greedy_kernel"] if c.verify == "greedy"
+                         else ["sample_lse_kernel", "sample_lse_merge_kernel (trees of more than 128 nodes)",
+                               "sample_walk_kernel"]),
+    "compact": lambda c: ["compact_kernel"],
+}
+
+
 def csrc_sha256() -> str:
     """Hash of the kernel sources; recorded traffic counts are used only while it matches."""
     import hashlib
@@ -207,6 +224,7 @@ def main():
         roof = {"bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": d["hbm_frac"], "traffic": None}
     roof["kernel"] = dom
+    roof["launches"] = STAGE_KERNELS[dom](cfg)
     roof["traffic"] = recorded_traffic(cfg.name, dom)
 
     out = {
