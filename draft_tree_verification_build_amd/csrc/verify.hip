@@ -47,16 +47,21 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   float x[Rw::E];
   uint32_t key[Rw::E];
   load_chunk<DT>(row, a.V, c, x, key);
+  // this thread's largest value (32-bit order keys, 0 = absent) and, of its entries holding
+  // it, the first in index order (a thread's entries ascend with (ii, e))
+  uint32_t km = 0u;
+#pragma unroll
+  for (int j = 0; j < Rw::E; ++j) km = key[j] > km ? key[j] : km;
+  int jm = 0;
+  float xm = 0.f;
+#pragma unroll
+  for (int j = Rw::E - 1; j >= 0; --j) {
+    const bool hit = key[j] == km;
+    jm = hit ? j : jm;
+    xm = hit ? x[j] : xm;
+  }
   unsigned long long best = 0;
-#pragma unroll
-  for (int ii = 0; ii < kLoads; ++ii)
-#pragma unroll
-    for (int e = 0; e < Rw::VEC; ++e) {
-      const uint32_t k = key[ii * Rw::VEC + e];
-      if (k == 0u) continue;
-      const unsigned long long p = sort_key(x[ii * Rw::VEC + e], elem_index<DT>(c, ii, e));
-      best = p > best ? p : best;
-    }
+  if (km != 0u) best = sort_key(xm, elem_index<DT>(c, jm / Rw::VEC, jm % Rw::VEC));
   best = block_max(best, sm.redu);
   if (threadIdx.x == 0) atomicMax(&a.best[tb + i], best);
   // two-level tickets: the chunks of a node, then the nodes of a sequence (one counter
