@@ -303,6 +303,9 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
       Frag8 kf[QS];
 #pragma unroll
       for (int j = 0; j < kAhead; ++j) kf[j] = kfrag(j);
+      // MFMA phases run at raised wave priority, so that the other workgroup's wave on this
+      // SIMD fills the gaps with its softmax and loads rather than competing for issue
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < QS; ++j) {
         if (j + kAhead < QS) kf[j + kAhead] = kfrag(j + kAhead);
@@ -311,6 +314,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
         sc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j].v, qf[j >> 1].v, sc[j & 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // the first V fragments are read while the softmax runs
       Frag8 vf[PS];
 #pragma unroll
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
         }
       l_run += sum;
       // ---- O += P V, software-pipelined like S^T
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < PS; ++j) {
         if (j + kAhead < PS) vf[j + kAhead] = vfrag(j + kAhead);
@@ -382,6 +387,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
         oacc[j % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf8[j / NT].v, vf[j].v, oacc[j % NT], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int i = 0; i < L::kLoads; ++i) kv_issue_pair<D>(i, kn, vn, kbase, vbase, kb_next, k_hi, lofs, w);
