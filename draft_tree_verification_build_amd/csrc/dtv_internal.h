@@ -83,7 +83,7 @@ struct OptArgs {
   double* lscore;         // [S][max_layers][n] per layer, frontier order
   int* lparent;           // parent's frontier position in the previous layer
   int* ltoken;
-  double* bscore;         // [S][n] best n so far: score desc, layer asc, position asc
+  double* bscore;         // [S][n] the best n so far by (score desc, layer asc, position asc), unordered
   int* blayer;
   int* bpos;
   int* bcount;            // [S]

@@ -212,11 +212,13 @@ __global__ __launch_bounds__(kBlock) void opt_collect_kernel(OptArgs a) {
 
 // ------------------------------------------------------------------ 4. exact selection
 //
-// One workgroup per sequence. The layer keeps its n best gathered candidates: radix
-// selection of the n-th best score key, and of the candidates tied with it the first in
-// frontier order. The kept candidates are sorted by frontier key (their positions in the
-// next frontier) and then by (score desc, position asc); the new best-n list merges that
-// with the old one by binary-search ranks.
+// One workgroup per sequence. The layer keeps its n best gathered candidates (radix cut of
+// the score keys; candidates tied at a full key go in frontier order). Their positions in
+// the next frontier, (parent position, logit desc, token), come from grouping them by
+// parent (count, scan, scatter) and counting, within a group, the members before each one
+// (a bitonic sort when one group is large, as at the root layer). The best n so far are a
+// second radix cut over the old best list and this layer's nodes, by (score desc, layer
+// asc, position asc); that list is kept unordered.
 
 struct OptKept {
   unsigned long long key;   // frontier key, then unused
@@ -229,6 +231,8 @@ struct OptBest {
   int layer, pos;
 };
 
+constexpr int kOptBucketMax = 128;   // largest parent group ranked by counting
+
 struct OptSelectSmem {
   union {
     struct {
@@ -236,18 +240,27 @@ struct OptSelectSmem {
       unsigned long long key[kOptLdsCand];   // their score keys
     } in;
     struct {
-      OptKept k[1024];      // kept candidates
-      OptBest old[1024];    // previous best list
-      OptBest merged[1024];
-    } out;
+      OptKept k[1024];      // kept candidates (frontier numbering by bitonic sort)
+    } srt;
+    struct {
+      unsigned long long key[2048];   // score keys of the old best list and this layer
+      double score[2048];
+      int info[2048];                 // (layer << 16) | position
+    } best;
   } u;
-  unsigned long long tkey[1024];   // candidates tied at the n-th best score: frontier keys
+  unsigned long long tkey[1024];   // entries tied at a cut: tie-order keys
   int tidx[1024];
   int keep_idx[1024];              // indices of the kept candidates
+  unsigned long long fkey[1024];   // frontier keys of the kept candidates
+  int cntp[1024];                  // kept candidates per parent
+  int basep[1024];                 // first frontier position of each parent's group
+  int memb[1024];                  // kept candidates grouped by parent
+  int kslot[1024];                 // a kept candidate's slot in its parent's group
+  double kscore[1024];             // a kept candidate's score, by frontier position
   int scan[kWaves];
   double red[kWaves];
   RadixSmem rs;
-  int ntie, nkept;
+  int ntie, nkept, nout;
 };
 
 __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
@@ -314,92 +327,144 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     for (int e = threadIdx.x; e < C; e += kBlock) sm.keep_idx[e] = e;
   }
   __syncthreads();
-  // ---- frontier order: sort the kept candidates by frontier key
-  OptKept mine[4];
-  const int P2 = pow2_at_least(kept > 0 ? kept : 1);
+  // ---- frontier order (parent position asc, logit desc, token asc) numbers the next
+  //      frontier. Kept candidates are grouped by parent (count, scan, scatter); within a
+  //      group, a candidate's position is the count of its group's members before it. A
+  //      group larger than kOptBucketMax (the root layer) is numbered by a bitonic sort.
+  const int l0 = a.layer - 1;
+  const size_t lb = (static_cast<size_t>(s) * a.max_layers + l0) * n;
+  for (int f = threadIdx.x; f < a.W; f += kBlock) sm.cntp[f] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kept; i += kBlock) {
+    const OptCand cd = sm.u.in.c[sm.keep_idx[i]];
+    sm.fkey[i] = front_key(cd);
+    sm.kslot[i] = atomicAdd(&sm.cntp[cd.fj >> 22], 1);
+  }
+  __syncthreads();
+  {
+    int mb = 0;
+    for (int f = threadIdx.x; f < a.W; f += kBlock) mb = max(mb, sm.cntp[f]);
+    mb = block_max(mb, sm.scan);
+    if (mb > kOptBucketMax) {
+      // one large group: sort all kept candidates by frontier key
+      const int P2 = pow2_at_least(kept > 0 ? kept : 1);   // <= 1024
+      OptKept mine[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = threadIdx.x + q * kBlock;
-    if (i < P2) {
-      if (i < kept) {
-        const OptCand cd = sm.u.in.c[sm.keep_idx[i]];
-        mine[q].key = front_key(cd);
-        mine[q].score = cd.score;
-      } else {
-        mine[q].key = ~0ull;
-        mine[q].score = -INFINITY;
+      for (int q = 0; q < 4; ++q) {
+        const int i = threadIdx.x + q * kBlock;
+        mine[q].key = i < kept ? sm.fkey[i] : ~0ull;
+        mine[q].score = i < kept ? sm.u.in.c[sm.keep_idx[i]].score : -INFINITY;
+        mine[q].pos = i;
+      }
+      __syncthreads();   // the sort area overlaps the candidates
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = threadIdx.x + q * kBlock;
+        if (i < P2) sm.u.srt.k[i] = mine[q];
+      }
+      __syncthreads();
+      bitonic_sort(sm.u.srt.k, P2, [](const OptKept& x, const OptKept& y) { return x.key < y.key; });
+      for (int r = threadIdx.x; r < kept; r += kBlock) {
+        const OptKept k = sm.u.srt.k[r];
+        a.lscore[lb + r] = k.score;
+        a.lparent[lb + r] = static_cast<int>(k.key >> 54);
+        a.ltoken[lb + r] = static_cast<int>(k.key & 0x3FFFFFull);
+        sm.kscore[r] = k.score;
+      }
+    } else {
+      int carry = 0;
+      for (int f0 = 0; f0 < a.W; f0 += kBlock) {
+        const int f = f0 + threadIdx.x;
+        int tot = 0;
+        const int ex = block_exclusive_scan(f < a.W ? sm.cntp[f] : 0, sm.scan, &tot);
+        if (f < a.W) sm.basep[f] = carry + ex;
+        carry += tot;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < kept; i += kBlock) {
+        const int f = static_cast<int>(sm.fkey[i] >> 54);
+        sm.memb[sm.basep[f] + sm.kslot[i]] = i;
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < kept; i += kBlock) {
+        const unsigned long long me = sm.fkey[i];
+        const int f = static_cast<int>(me >> 54);
+        const int b0 = sm.basep[f], bn = sm.cntp[f];
+        int r = b0;
+        for (int q = 0; q < bn; ++q) r += sm.fkey[sm.memb[b0 + q]] < me ? 1 : 0;
+        const double sc = sm.u.in.c[sm.keep_idx[i]].score;
+        a.lscore[lb + r] = sc;
+        a.lparent[lb + r] = f;
+        a.ltoken[lb + r] = static_cast<int>(me & 0x3FFFFFull);
+        sm.kscore[r] = sc;
       }
     }
   }
   __syncthreads();   // the candidate area is reused from here on
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = threadIdx.x + q * kBlock;
-    if (i < P2) sm.u.out.k[i] = mine[q];
-  }
-  __syncthreads();
-  bitonic_sort(sm.u.out.k, P2, [](const OptKept& x, const OptKept& y) { return x.key < y.key; });
-  const int l0 = a.layer - 1;
-  const size_t lb = (static_cast<size_t>(s) * a.max_layers + l0) * n;
-  for (int i = threadIdx.x; i < kept; i += kBlock) {
-    const OptKept k = sm.u.out.k[i];
-    a.lscore[lb + i] = k.score;
-    a.lparent[lb + i] = static_cast<int>(k.key >> 54);
-    a.ltoken[lb + i] = static_cast<int>(k.key & 0x3FFFFFull);
-    sm.u.out.k[i].pos = i;
-  }
-  __syncthreads();
-  // ---- this layer's nodes by (score desc, position asc); the old best list from global
-  bitonic_sort(sm.u.out.k, P2, [](const OptKept& x, const OptKept& y) {
-    if (x.score != y.score) return x.score > y.score;
-    return x.pos < y.pos;
-  });
+  // ---- the best n so far by (score desc, layer asc, position asc): the old best list
+  //      and this layer's nodes, cut by radix selection (the list is kept unordered)
   const int nb = a.bcount[s];
   const size_t bb = static_cast<size_t>(s) * n;
 #pragma unroll 4
   for (int e = threadIdx.x; e < nb; e += kBlock) {
-    OptBest o;
-    o.score = a.bscore[bb + e];
-    o.layer = a.blayer[bb + e];
-    o.pos = a.bpos[bb + e];
-    sm.u.out.old[e] = o;
+    const double sc = a.bscore[bb + e];
+    sm.u.best.score[e] = sc;
+    sm.u.best.key[e] = dkey(sc);
+    sm.u.best.info[e] = (a.blayer[bb + e] << 16) | a.bpos[bb + e];
+  }
+  for (int r = threadIdx.x; r < kept; r += kBlock) {
+    const double sc = sm.kscore[r];
+    sm.u.best.score[nb + r] = sc;
+    sm.u.best.key[nb + r] = dkey(sc);
+    sm.u.best.info[nb + r] = (a.layer << 16) | r;
+  }
+  if (threadIdx.x == 0) {
+    sm.ntie = 0;
+    sm.nout = 0;
   }
   __syncthreads();
-  // ---- merge: rank = old entries before + this layer's entries before (both sorted)
-  for (int e = threadIdx.x; e < nb + kept; e += kBlock) {
-    OptBest me;
-    int r;
-    if (e < nb) {   // old entry: this layer's entries before it have a strictly higher score
-      me = sm.u.out.old[e];
-      int lo = 0, hi = kept;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.u.out.k[mid].score > me.score) lo = mid + 1; else hi = mid;
-      }
-      r = e + lo;
-    } else {        // this layer's entry: old entries with a score >= mine come first
-      const int i = e - nb;
-      me.score = sm.u.out.k[i].score;
-      me.layer = a.layer;
-      me.pos = sm.u.out.k[i].pos;
-      int lo = 0, hi = nb;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.u.out.old[mid].score >= me.score) lo = mid + 1; else hi = mid;
-      }
-      r = i + lo;
-    }
-    if (r < n) sm.u.out.merged[r] = me;
-  }
-  __syncthreads();
-  const int nnew = (nb + kept) < n ? (nb + kept) : n;
+  const int M2 = nb + kept;
+  const int nnew = M2 < n ? M2 : n;
   double part = 0.0;
-  for (int e = threadIdx.x; e < nnew; e += kBlock) {
-    const OptBest m = sm.u.out.merged[e];
-    a.bscore[bb + e] = m.score;
-    a.blayer[bb + e] = m.layer;
-    a.bpos[bb + e] = m.pos;
-    part += exp(m.score);
+  auto emit = [&](int e) {
+    const int o = atomicAdd(&sm.nout, 1);
+    const double sc = sm.u.best.score[e];
+    a.bscore[bb + o] = sc;
+    a.blayer[bb + o] = sm.u.best.info[e] >> 16;
+    a.bpos[bb + o] = sm.u.best.info[e] & 0xFFFF;
+    part += exp(sc);
+  };
+  if (M2 <= n) {
+    for (int e = threadIdx.x; e < M2; e += kBlock) emit(e);
+  } else {
+    const RadixCut cut = radix_topk_cut(sm.u.best.key, M2, n, sm.rs);
+    for (int e = threadIdx.x; e < M2; e += kBlock) {
+      const unsigned long long k = sm.u.best.key[e];
+      if (cut.all_in ? ((k & cut.mask) >= cut.prefix) : (k > cut.prefix)) {
+        emit(e);
+      } else if (!cut.all_in && k == cut.prefix) {
+        const int t = atomicAdd(&sm.ntie, 1);
+        if (t < 1024) {
+          sm.tkey[t] = static_cast<unsigned long long>(sm.u.best.info[e]);
+          sm.tidx[t] = e;
+        }
+      }
+    }
+    __syncthreads();
+    if (sm.ntie > 1024) {   // more than 1024 entries share the n-th best score: refuse
+      if (threadIdx.x == 0) {
+        atomicExch(&a.hdr->err, kErrCapacity);
+        a.done[s] = 1;
+      }
+      return;
+    }
+    const int nt = sm.ntie;
+    for (int t = threadIdx.x; t < nt; t += kBlock) {
+      const unsigned long long me = sm.tkey[t];
+      int before = 0;
+      for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      if (before < cut.rem) emit(sm.tidx[t]);
+    }
   }
   const double E = block_sum(part, sm.red);
   if (threadIdx.x == 0) {
@@ -414,9 +479,11 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
 // ------------------------------------------------------------------ 5. the final tree
 
 struct OptFinalSmem {
+  unsigned bits[64 * 1024 / 32];   // presence of (layer, position), bit (layer-1)*1024 + position
+  int wpre[64 * 1024 / 32];        // chosen nodes in earlier words
   int lp[1024];      // (layer << 16) | position of each chosen node, sorted
   short par[1025];
-  int flag;
+  int scan[kWaves];
 };
 
 __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
@@ -425,11 +492,38 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
   const int n = a.n;
   const int nb = a.bcount[s];
   const size_t bb = static_cast<size_t>(s) * n;
-  const int P2 = pow2_at_least(nb > 0 ? nb : 1);
-  for (int e = threadIdx.x; e < P2; e += kBlock)
-    sm.lp[e] = (e < nb) ? ((a.blayer[bb + e] << 16) | a.bpos[bb + e]) : 0x7FFFFFFF;
+  // the chosen nodes by (layer, position): a presence bitmap over (layer, position) and
+  // prefix counts of its words give every node its rank (the keys are distinct)
+  const int nwords = a.max_layers * 32;
+  for (int w = threadIdx.x; w < nwords; w += kBlock) sm.bits[w] = 0u;
   __syncthreads();
-  bitonic_sort(sm.lp, P2, [](int x, int y) { return x < y; });   // by (layer, position)
+  for (int e = threadIdx.x; e < nb; e += kBlock) {
+    const int b = (a.blayer[bb + e] - 1) * 1024 + a.bpos[bb + e];
+    atomicOr(&sm.bits[b >> 5], 1u << (b & 31));
+  }
+  __syncthreads();
+  {
+    const int per = (nwords + kBlock - 1) / kBlock;   // contiguous words per thread
+    const int w0 = threadIdx.x * per;
+    int loc = 0;
+    for (int q = 0; q < per; ++q)
+      if (w0 + q < nwords) loc += __popc(sm.bits[w0 + q]);
+    int tot = 0;
+    int run = block_exclusive_scan(loc, sm.scan, &tot);
+    for (int q = 0; q < per; ++q)
+      if (w0 + q < nwords) {
+        sm.wpre[w0 + q] = run;
+        run += __popc(sm.bits[w0 + q]);
+      }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nb; e += kBlock) {
+    const int layer = a.blayer[bb + e], pos = a.bpos[bb + e];
+    const int b = (layer - 1) * 1024 + pos;
+    const int r = sm.wpre[b >> 5] + __popc(sm.bits[b >> 5] & ((1u << (b & 31)) - 1u));
+    sm.lp[r] = (layer << 16) | pos;
+  }
+  __syncthreads();
   const size_t tb = static_cast<size_t>(s) * a.tree.n_cap;
   const int words = a.tree.words;
   if (threadIdx.x == 0) {
