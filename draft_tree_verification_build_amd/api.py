@@ -70,9 +70,13 @@ class Workspace:
         return buf
 
     def status(self, key, stream=None) -> int:
-        """Synchronise and return (and clear) the device status of one workspace."""
+        """Synchronise and return the device status of one workspace; a workspace that
+        reports an error is zero-filled again, as the library requires before its reuse."""
         buf = self._bufs[key]
-        return _lib.load().dtv_ws_status(buf.data_ptr(), _stream(stream))
+        rc = _lib.load().dtv_ws_status(buf.data_ptr(), _stream(stream))
+        if rc != 0:
+            buf.zero_()
+        return rc
 
 
 class Tree:

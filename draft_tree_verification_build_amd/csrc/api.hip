@@ -291,18 +291,14 @@ AttnLayout attn_layout(void* ws, int S, int Hkv, int D, const AttnPlan& p) {
 
 struct VerifyLayout {
   dtv::WsHeader* hdr;
-  unsigned long long* best;
-  unsigned* ntick;
-  unsigned* tickets;
+  unsigned long long* cbest;
   size_t bytes;
 };
-VerifyLayout verify_layout(void* ws, int S, int n_cap) {
+VerifyLayout verify_layout(void* ws, int S, int n_cap, int nch) {
   Carver c(ws);
   VerifyLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
-  L.best = c.take<unsigned long long>(static_cast<size_t>(S) * n_cap);
-  L.ntick = c.take<unsigned>(static_cast<size_t>(S) * n_cap);
-  L.tickets = c.take<unsigned>(S);
+  L.cbest = c.take<unsigned long long>(static_cast<size_t>(S) * n_cap * nch);
   L.bytes = c.off;
   return L;
 }
@@ -690,7 +686,7 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
 
 size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype) {
   if (S < 1 || n_cap < 1 || V < 1 || !dtype_ok(dtype)) return 0;
-  return verify_layout(nullptr, S, n_cap).bytes;
+  return verify_layout(nullptr, S, n_cap, nch_of(V, dtype)).bytes;
 }
 
 int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype, int32_t R,
@@ -701,7 +697,7 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
   REQUIRE(target && path && path_len && bonus, DTV_EINVAL, "target, path, path_len or bonus is NULL");
   REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
   REQUIRE(S >= 1 && R >= 1 && V >= 1, DTV_EINVAL, "S=%d R=%d V=%d", S, R, V);
-  const VerifyLayout L = verify_layout(ws, S, tree->n_cap);
+  const VerifyLayout L = verify_layout(ws, S, tree->n_cap, nch_of(V, dtype));
   REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
   dtv::VerifyArgs a;
   a.tree = tree_args(tree);
@@ -713,9 +709,7 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
   a.path_len = path_len;
   a.bonus = bonus;
   a.argmax_out = argmax_out;
-  a.best = L.best;
-  a.ntick = L.ntick;
-  a.tickets = L.tickets;
+  a.cbest = L.cbest;
   a.hdr = L.hdr;
   return launched(dtv::launch_verify_greedy(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
 }

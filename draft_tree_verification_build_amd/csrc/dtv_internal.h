@@ -162,9 +162,7 @@ struct VerifyArgs {
   int* path_len;
   int* bonus;
   int* argmax_out;
-  unsigned long long* best;  // [S][n_cap]
-  unsigned* ntick;           // [S][n_cap] chunks of a node's row done
-  unsigned* tickets;         // [S] nodes of a sequence done
+  unsigned long long* cbest;  // [S][n_cap][nch] chunk argmax keys (0: not yet reported)
   WsHeader* hdr;
 };
 

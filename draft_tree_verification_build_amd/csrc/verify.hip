@@ -1,12 +1,15 @@
 // Greedy verification on gfx950 (OPT-Tree summary, section 2; GOOSE page, section 2C).
 //
 // One workgroup per (sequence, node, chunk of the node's target row) finds the chunk's
-// largest value and its lowest index and folds it into the node's 64-bit best key with
-// one atomic max ((value key << 32) | ~index, so larger value wins, then lower index).
-// The workgroup that completes a sequence last walks its tree: node c matches when its
+// largest value and its lowest index and publishes them as one 64-bit key
+// ((value key << 32) | ~index: larger value wins, then lower index) in a slot of its own
+// (an agent-scope store; a slot is never 0 once written, and the workspace keeps every slot
+// 0 between calls). The sequence's last workgroup in launch order walks: it polls the slots
+// of the sequence's nodes until every chunk has reported, reduces each node's chunks to its
+// argmax, clears the slots for the next call, and walks the tree: node c matches when its
 // token equals the argmax at its parent; a node is accepted when every node on its root
-// path matches (checked by following parent links in shared memory); the deepest accepted
-// node, lowest slot first, ends the path.
+// path matches (parent links in shared memory); the deepest accepted node, lowest slot
+// first, ends the path. No workgroup waits on a counter or a fence.
 #include "dtv_internal.h"
 #include "rowstats.h"
 
@@ -14,6 +17,7 @@ namespace dtv {
 
 constexpr int kVerifyMaxNodes = 1024;
 constexpr int kVerifyMaxWords = 16;
+constexpr long kGreedySpinLimit = 2000000;   // poll rounds (each a memory round trip) before a timeout
 
 struct VerifySmem {
   int a[kVerifyMaxNodes];       // target argmax at every node
@@ -35,55 +39,76 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   const int rest = blockIdx.x % (cap * nch);
   const int i = rest / nch, c = rest % nch;
   const int N = a.tree.n_nodes[s];
-  if (i >= N) return;
-  if (N > cap) {  // n_nodes is device data: refuse rather than read past the tree
-    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+  if (N > cap || N < 1) {  // n_nodes is device data: refuse rather than read past the tree
+    if (threadIdx.x == 0 && i == 0 && c == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
   }
   const size_t tb = static_cast<size_t>(s) * cap;
-  const int r = a.tree.row[tb + i];
-  const char* row = static_cast<const char*>(a.target) +
-                    (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
-  float x[Rw::E];
-  uint32_t key[Rw::E];
-  load_chunk<DT>(row, a.V, c, x, key);
-  // this thread's largest value (32-bit order keys, 0 = absent) and, of its entries holding
-  // it, the first in index order (a thread's entries ascend with (ii, e))
-  uint32_t km = 0u;
+  unsigned long long* slots = a.cbest + tb * nch;   // [node][chunk]
+  if (i < N) {
+    const int r = a.tree.row[tb + i];
+    const char* row = static_cast<const char*>(a.target) +
+                      (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
+    float x[Rw::E];
+    uint32_t key[Rw::E];
+    load_chunk<DT>(row, a.V, c, x, key);
+    // this thread's largest value (32-bit order keys, 0 = absent) and, of its entries
+    // holding it, the first in index order (a thread's entries ascend with (ii, e))
+    uint32_t km = 0u;
 #pragma unroll
-  for (int j = 0; j < Rw::E; ++j) km = key[j] > km ? key[j] : km;
-  int jm = 0;
-  float xm = 0.f;
+    for (int j = 0; j < Rw::E; ++j) km = key[j] > km ? key[j] : km;
+    int jm = 0;
+    float xm = 0.f;
 #pragma unroll
-  for (int j = Rw::E - 1; j >= 0; --j) {
-    const bool hit = key[j] == km;
-    jm = hit ? j : jm;
-    xm = hit ? x[j] : xm;
+    for (int j = Rw::E - 1; j >= 0; --j) {
+      const bool hit = key[j] == km;
+      jm = hit ? j : jm;
+      xm = hit ? x[j] : xm;
+    }
+    unsigned long long best = 0;
+    if (km != 0u) best = sort_key(xm, elem_index<DT>(c, jm / Rw::VEC, jm % Rw::VEC));
+    best = block_max(best, sm.redu);
+    // every chunk holds an element (c < nch), and a key from an element is never 0
+    if (threadIdx.x == 0) st_cc(&slots[static_cast<size_t>(i) * nch + c], best);
   }
-  unsigned long long best = 0;
-  if (km != 0u) best = sort_key(xm, elem_index<DT>(c, jm / Rw::VEC, jm % Rw::VEC));
-  best = block_max(best, sm.redu);
-  if (threadIdx.x == 0) atomicMax(&a.best[tb + i], best);
-  // two-level tickets: the chunks of a node, then the nodes of a sequence (one counter
-  // taking every chunk of a sequence serialises ~1000 atomics)
-  if (!last_arrival(&a.ntick[tb + i], static_cast<unsigned>(nch), &sm.flag)) return;
-  if (!last_arrival(&a.tickets[s], static_cast<unsigned>(N), &sm.flag)) return;
+  if (i != cap - 1 || c != nch - 1) return;
 
-  // ---- the walk, by the last workgroup of sequence s. Everything it needs is loaded in
-  //      one parallel pass; acceptance then follows parent links in shared memory.
+  // ---- the walk, by the sequence's last workgroup: wait for every chunk of every node and
+  //      reduce them (each thread owns nodes v = t, t + kBlock, ...; a node's chunk slots
+  //      are read 8 at a time, all in flight), then load the tree in one parallel pass
+  int ok = 1;
   for (int v = threadIdx.x; v < N; v += kBlock) {
-    const unsigned long long b = __hip_atomic_load(&a.best[tb + v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int p = a.tree.parent[tb + v];
-    const int tok = a.tree.token[tb + v];
-    const int d = a.tree.depth[tb + v];
-    a.best[tb + v] = 0ull;  // ready for the next call
-    const int am = sort_key_index(b);
+    unsigned long long* sv = slots + static_cast<size_t>(v) * nch;
+    unsigned long long bmax = 0;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      unsigned long long b[8];
+      long polls = 0;
+      for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          b[q] = ld_cc(&sv[min(c0 + q, nch - 1)]);
+          all = all && b[q] != 0ull;
+        }
+        if (all) break;
+        if (++polls > kGreedySpinLimit) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) bmax = b[q] > bmax ? b[q] : bmax;
+    }
+    for (int cc = 0; cc < nch; ++cc) sv[cc] = 0ull;   // ready for the next call
+    const int am = sort_key_index(bmax);
     sm.a[v] = am;
-    sm.tok[v] = tok;
-    sm.par[v] = static_cast<short>(v == 0 ? -1 : p);
-    sm.dep[v] = static_cast<short>(d);
+    sm.tok[v] = a.tree.token[tb + v];
+    sm.par[v] = static_cast<short>(v == 0 ? -1 : a.tree.parent[tb + v]);
+    sm.dep[v] = static_cast<short>(a.tree.depth[tb + v]);
     if (a.argmax_out) a.argmax_out[tb + v] = am;
   }
+  if (!ok) atomicExch(&a.hdr->err, kErrTimeout);
   __syncthreads();
   // a node is bad when its token is not the target argmax at its parent (or its parent
   // link is not an earlier slot, which also bounds every walk below)

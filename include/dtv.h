@@ -18,7 +18,9 @@
  * - Argument errors are detected on the host before any launch and returned as a
  *   negative dtv_status; a launch failure returns DTV_EHIP. Errors found by a kernel
  *   (capacity exceeded on the device, a bounded wait that ran out) are recorded in the
- *   workspace and read with dtv_ws_status(), which synchronises the stream.
+ *   workspace and read with dtv_ws_status(), which synchronises the stream. A
+ *   workspace whose status is an error must be zero-filled again before its next use
+ *   (an interrupted call can leave its per-call state set).
  *   dtv_last_error() returns a message for the last failing call of the thread.
  * - Logit tables are `[S][R][V]`, row-major, of the given dtype; a node's rows are
  *   addressed through the tree's `row` array. Stored values are compared exactly;
