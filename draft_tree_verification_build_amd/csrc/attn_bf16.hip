@@ -425,20 +425,29 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   const int c4 = threadIdx.x % TPR;
   const int kv = head % a.Hkv;
   const int s = head / a.Hkv;
-  const int N = a.n_nodes[s];
-  if (N > a.n_cap || rr >= a.g * N) return;
   const size_t pr0 = static_cast<size_t>(head) * a.n_split * rows_per_head + rr;
+  // the first eight splits' O rows, every (m, l) and the node count are loaded together
+  // (rows past g * N hold stale partials in valid workspace memory and are not stored)
+  float4 o[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int qq = min(u, a.n_split - 1);
+    o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
+  }
   float w[NS];
   const float L = attn_split_weights<NS>(a.part_ml + pr0 * 2, static_cast<size_t>(rows_per_head) * 2, a.n_split, w);
+  const int N = a.n_nodes[s];
+  if (N > a.n_cap || rr >= a.g * N) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int q0 = 0; q0 < NS; q0 += 8) {
     if (q0 >= a.n_split) break;
-    float4 o[8];
+    if (q0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int qq = min(q0 + u, a.n_split - 1);
-      o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
+      for (int u = 0; u < 8; ++u) {
+        const int qq = min(q0 + u, a.n_split - 1);
+        o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {

@@ -15,11 +15,16 @@ constexpr int kCompactRowBytes = 512;     // D * esize <= 512 (D <= 128 fp32)
 
 __global__ __launch_bounds__(kBlock) void compact_kernel(CompactArgs a) {
   __shared__ uint4 stage[kCompactRows * kCompactRowBytes / 16];
+  __shared__ int spath[kBlock];
   const int which = blockIdx.x & 1;
   const int kv = (blockIdx.x >> 1) % a.Hkv;
   const int s = (blockIdx.x >> 1) / a.Hkv;
+  // the first kBlock path entries are read together with the path length and P (valid
+  // memory whatever the length), so the row loads wait for one round trip, not two
+  if (threadIdx.x < a.n_cap) spath[threadIdx.x] = a.path[static_cast<size_t>(s) * a.n_cap + threadIdx.x];
   const int L = a.path_len[s];
   const int P = a.P[s];
+  __syncthreads();
   if (L < 1 || L > a.n_cap || P < 0 || P + a.n_cap > a.P_cap) {
     // inconsistent device inputs: leave the cache alone and mark the sequence
     if (which == 0 && kv == 0 && threadIdx.x == 0) a.P_new[s] = -1;
@@ -34,7 +39,7 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(CompactArgs a) {
     const int nb = (L - k0) < kCompactRows ? (L - k0) : kCompactRows;
     for (int e = threadIdx.x; e < nb * vec_per_row; e += kBlock) {
       const int rr = e / vec_per_row, cc = e % vec_per_row;
-      const int src = P + path[k0 + rr];
+      const int src = P + (k0 + rr < kBlock ? spath[k0 + rr] : path[k0 + rr]);
       stage[rr * (kCompactRowBytes / 16) + cc] =
           reinterpret_cast<const uint4*>(base + static_cast<size_t>(src) * row_bytes)[cc];
     }
