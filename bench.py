@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2_talon_llama3_8b")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--launch", choices=["graph", "eager"], default="eager",
+                    help="replay the step as a captured HIP graph, or launch its kernels one by one")
     ap.add_argument("--event-every", type=int, default=16,
                     help="record per-stage events on every n-th timed step")
     ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps for cpu_baseline (0: skip)")
@@ -182,9 +184,29 @@ def main():
         print(f"device status after warmup: {st}", file=sys.stderr)
         return 1
 
-    # Whole-step timing. Every `event_every`-th step of the same timed loop also records HIP
-    # events on the launch stream around each stage; a record between two kernels adds a gap of
-    # a few microseconds, so sampling keeps that cost inside the timed region at about 1%.
+    # Optionally one step captured as a HIP graph (the step makes no host round trip and no
+    # allocation once warm), replayed on the launch stream. Measured on MI355X, replay only
+    # pays off where the host's launch work is the bound (c1: 35 -> 27.5 us per step); for
+    # the larger steps it adds about 0.7 us per kernel (c2: 68.4 -> 72.9 us), so eager
+    # launches are the default.
+    graph = None
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        st = step.ws_status()
+        if any(v != 0 for v in st.values()):
+            print(f"device status after graph replays: {st}", file=sys.stderr)
+            return 1
+    run_step = graph.replay if graph is not None else step.run
+
+    # Whole-step timing. Every `event_every`-th step of the same timed loop runs its stages as
+    # separate launches with HIP events on the launch stream around each stage; a record
+    # between two kernels adds a gap of a few microseconds, so sampling keeps that cost inside
+    # the timed region at about 1%.
     every = max(1, args.event_every)
     sampled = list(range(0, args.steps, every))
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for k in sampled}
@@ -193,7 +215,7 @@ def main():
     for k in range(args.steps):
         e = ev.get(k)
         if e is None:
-            step.run()
+            run_step()
             continue
         e[0].record(stream)
         for j, fn in enumerate(fns):
@@ -237,7 +259,7 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "seed": seed, "S": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "P": cfg.P, "V": cfg.V, "N": cfg.N, "build": cfg.build,
-                   "verify": cfg.verify},
+                   "verify": cfg.verify, "launch": args.launch},
         "tree_tokens_per_s": tree_tokens * steps_s,
         "roofline": roof,
         "stages": stage_report,
