@@ -611,7 +611,12 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
     if (Kc < 2) Kc = 2;
     if (Kc > K) Kc = K;
     a.Kc = static_cast<int>(Kc);
-    if (dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st)) return launched(-1);
+    a.Kw = layer == 1 ? dtv::opt_root_wave_quota(V, n, dtype == DTV_BF16 ? 1 : 0) : 0;
+    if (a.Kw > 0) {   // the root layer in one launch
+      if (dtv::launch_opt_root(a, dtype == DTV_BF16 ? 1 : 0, st)) return launched(-1);
+    } else if (dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st)) {
+      return launched(-1);
+    }
     long kept = W * per_row;
     if (kept > n) kept = n;
     W = kept;

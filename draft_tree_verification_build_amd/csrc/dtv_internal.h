@@ -67,6 +67,7 @@ struct OptArgs {
   double delta;
   // per layer (set by the host before each layer's launches)
   int layer, W, Wcap, K, Kc;   // K: entries a row reports; Kc: per chunk (nch * Kc >= K)
+  int Kw;                      // root layer in one launch: lane maxima per full wave (0: not used)
   WsHeader* hdr;
   ChunkStat* st;          // [S][Wcap][nch]
   float* cval;            // [S][Wcap][nch][Kmax]
@@ -203,6 +204,8 @@ int launch_talon(const TalonArgs& a, int dtype, hipStream_t st);
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st);
 int launch_opt_init(const OptArgs& a, hipStream_t st);
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
+int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st);
+int opt_root_wave_quota(int V, int n, int dtype);
 int launch_opt_finalize(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);

@@ -106,6 +106,268 @@ __global__ __launch_bounds__(kBlock, 4) void opt_rows_kernel(OptArgs a) {
   if (threadIdx.x == 0) st_cc(&a.rcnt[rf], n);
 }
 
+// ------------------------------------------------------------------ 1'. the root layer in one launch
+//
+// Layer 1 expands the root alone: its frontier is the root row's n best entries by (logit
+// desc, token asc), each scored logit - lse, and the best list is that frontier. One launch
+// does all of it. Each chunk workgroup reduces its chunk (max, float64 sum of exp) and, in
+// every wave whose lanes all hold in-range elements, takes the Kw-th largest of the 64 lane
+// maxima: that wave holds at least Kw elements at or above it, so the minimum over such
+// waves bounds the row's n-th largest key from below once their count times Kw reaches n.
+// The last chunk workgroup to finish forms the log-sum-exp, re-reads the row gathering every
+// element at or above the bound (somewhat more than n) and ranks them exactly through value
+// buckets: an entry's rank is the number of entries in higher buckets plus the members of
+// its own bucket with a larger sort key ((value key, index) keys are unique). Entries ranked
+// below n are the layer.
+
+constexpr int kRootCand = 4096;      // gathered elements at or above the bound
+constexpr int kRootBuckets = 1024;
+
+struct OptRootSmem {
+  RowSmem rs;
+  unsigned long long cand[kRootCand];
+  int kbs[kRootCand];          // (bucket << 16) | place within the bucket
+  unsigned long long mkey[kRootCand];   // keys of the gathered entries grouped by bucket
+  double ksc[1024];            // score of the entry at each rank
+  int bcnt[kRootBuckets];      // entries per bucket
+  int bbase[kRootBuckets];     // entries in higher buckets
+  float cmax[kMergeMaxChunks];
+  double csum[kMergeMaxChunks];
+  uint32_t ctau[kMergeMaxChunks];
+  uint32_t wtau[kWaves];
+  unsigned long long red64[kWaves];
+  int scan[kWaves];
+  double red[kWaves];
+  int ncand;
+  uint32_t lokey;
+  double lse;
+};
+
+// Appends this thread's elements of chunk c at or above the bound: one shared-memory atomic
+// per wave, placed by the lanes' prefix counts.
+template <int DT>
+__device__ __forceinline__ void root_gather(const float (&xv)[RowT<DT>::E], int c, int V, uint32_t lok,
+                                            OptRootSmem& sm) {
+  using Rw = RowT<DT>;
+  static_assert(Rw::E <= 32, "one predicate bit per element");
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+    for (int e = 0; e < Rw::VEC; ++e) {
+      const int j = i * Rw::VEC + e;
+      const uint32_t k = f32_key(xv[j]) >> (32 - Rw::KEYBITS);
+      if (elem_index<DT>(c, i, e) < V && k != 0u && k >= lok) bits |= 1u << j;
+    }
+  const int lane = threadIdx.x & 63;
+  const int cnt = __popc(bits);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  int base = 0;
+  if (lane == 63) base = atomicAdd(&sm.ncand, incl);
+  base = __shfl(base, 63, 64);
+  int pos = base + incl - cnt;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+#pragma unroll
+    for (int e = 0; e < Rw::VEC; ++e) {
+      const int j = i * Rw::VEC + e;
+      if ((bits >> j) & 1u) {
+        if (pos < kRootCand) sm.cand[pos] = sort_key(xv[j], elem_index<DT>(c, i, e));
+        ++pos;
+      }
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void opt_root_kernel(OptArgs a) {
+  __shared__ OptRootSmem sm;
+  using Rw = RowT<DT>;
+  const int c = blockIdx.x % a.nch;
+  const int s = blockIdx.x / a.nch;
+  row_smem_init(sm.rs);
+  __syncthreads();
+  const char* row = static_cast<const char*>(a.draft) +
+                    static_cast<size_t>(s) * a.R * static_cast<size_t>(a.V) * Rw::ESIZE;   // row 0: the root
+  const size_t cb = static_cast<size_t>(s) * a.Wcap * a.nch;   // chunk statistics of (s, f = 0)
+  {
+    float x[Rw::E];
+    uint32_t key[Rw::E];
+    load_chunk<DT>(row, a.V, c, x, key);
+    chunk_reduce<DT>(x, key, c, a.V, 0, &a.st[cb + c], nullptr, nullptr, sm.cand, sm.rs);
+    // the Kw-th largest lane maximum of every full wave
+    const int w = threadIdx.x >> 6;
+    uint32_t lmk = 0u;
+#pragma unroll
+    for (int j = 0; j < Rw::E; ++j) lmk = key[j] > lmk ? key[j] : lmk;
+    const long last = static_cast<long>(c) * Rw::CHUNK +
+                      static_cast<long>((kLoads - 1) * kBlock + 64 * w + 63) * Rw::VEC + Rw::VEC - 1;
+    uint32_t tau = 0xFFFFFFFFu;
+    if (last < a.V) {   // wave-uniform: every lane holds in-range elements only
+      unsigned long long lo = 1ull, hi = static_cast<unsigned long long>(wave_max(lmk)) + 1ull;
+      if (__popcll(__ballot(lmk >= 1u)) >= a.Kw) {
+        while (hi - lo > 1ull) {
+          const unsigned long long mid = lo + ((hi - lo) >> 1);
+          if (__popcll(__ballot(lmk >= mid)) >= a.Kw) lo = mid; else hi = mid;
+        }
+        tau = static_cast<uint32_t>(lo);
+      } else {
+        tau = 1u;   // keys of 0 (absent) in a full wave: no bound from it
+      }
+    }
+    if ((threadIdx.x & 63) == 0) sm.wtau[w] = tau;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t t = 0xFFFFFFFFu;
+      for (int q = 0; q < kWaves; ++q) t = sm.wtau[q] < t ? sm.wtau[q] : t;
+      st_cc(&a.st[cb + c].pad, static_cast<int>(t));
+    }
+  }
+  if (!last_arrival(&a.tickets[static_cast<size_t>(s) * a.Wcap], a.nch, &sm.rs.flag)) return;
+
+  // ---- the last chunk workgroup: the first four chunks of the row are requested before the
+  //      chunk statistics, so that both round trips overlap
+  const int vfull = a.V / Rw::VEC;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && vfull > 0;
+  RawChunk rq[4];
+  if (vec_ok) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw_chunk_load<DT>(row, a.V, u < a.nch ? u : a.nch - 1, rq[u]);
+  }
+  for (int q = threadIdx.x; q < a.nch; q += kBlock) {
+    sm.cmax[q] = ld_cc(&a.st[cb + q].maxv);
+    sm.csum[q] = ld_cc(&a.st[cb + q].sumexp);
+    sm.ctau[q] = static_cast<uint32_t>(ld_cc(&a.st[cb + q].pad));
+  }
+  for (int b = threadIdx.x; b < kRootBuckets; b += kBlock) sm.bcnt[b] = 0;
+  if (threadIdx.x == 0) sm.ncand = 0;
+  __syncthreads();
+  // log-sum-exp (as the row merge forms it) and the bound
+  if (threadIdx.x < 64) {   // lane q holds chunk q (nch <= 64)
+    const int q = threadIdx.x;
+    const float mc = q < a.nch ? sm.cmax[q] : -INFINITY;
+    const float M = wave_max(mc);
+    double term = 0.0;
+    if (q < a.nch && mc != -INFINITY)
+      term = sm.csum[q] * exp_nonpos(static_cast<double>(mc) - static_cast<double>(M), sm.rs.exptab);
+    const double S = wave_sum(term);
+    const uint32_t lk = wave_min(q < a.nch ? sm.ctau[q] : 0xFFFFFFFFu);
+    if (q == 0) {
+      sm.lse = static_cast<double>(M) + log(S);
+      sm.lokey = lk;
+    }
+  }
+  __syncthreads();
+  const uint32_t lok = sm.lokey;
+  // ---- every element at or above the bound, four chunks' loads in flight at a time
+  if (vec_ok) {
+    for (int c0 = 0; c0 < a.nch; c0 += 4) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw_chunk_load<DT>(row, a.V, c0 + u < a.nch ? c0 + u : a.nch - 1, rq[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c0 + u < a.nch) {
+          float xv[Rw::E];
+          raw_chunk_decode<DT>(row, a.V, c0 + u, rq[u], xv);
+          root_gather<DT>(xv, c0 + u, a.V, lok, sm);
+        }
+      }
+    }
+  } else {
+    for (int c0 = 0; c0 < a.nch; ++c0) {
+      float xv[Rw::E];
+      uint32_t kv[Rw::E];
+      load_chunk<DT>(row, a.V, c0, xv, kv);
+      root_gather<DT>(xv, c0, a.V, lok, sm);
+    }
+  }
+  __syncthreads();
+  const int C = sm.ncand;
+  const int n = a.n;
+  if (C > kRootCand) {   // far more entries tie at the bound than the buffer holds: refuse
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrCapacity);
+      a.done[s] = 1;
+    }
+    return;
+  }
+  const int kept = C < n ? C : n;
+  // ---- exact ranks: buckets of the value-key range, largest values first
+  unsigned long long vmax = 0ull, vmin = ~0ull;
+  for (int e = threadIdx.x; e < C; e += kBlock) {
+    const unsigned long long v = sm.cand[e] >> 32;
+    vmax = v > vmax ? v : vmax;
+    vmin = v < vmin ? v : vmin;
+  }
+  vmax = block_max(vmax, sm.red64);
+  vmin = block_min(vmin, sm.red64);
+  const unsigned long long range = vmax - vmin + 1ull;
+  for (int e = threadIdx.x; e < C; e += kBlock) {
+    const unsigned long long v = sm.cand[e] >> 32;
+    const int b = static_cast<int>(((vmax - v) * kRootBuckets) / range);
+    sm.kbs[e] = (b << 16) | atomicAdd(&sm.bcnt[b], 1);
+  }
+  __syncthreads();
+  {
+    constexpr int per = kRootBuckets / kBlock;
+    const int b0 = threadIdx.x * per;
+    int loc = 0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) loc += sm.bcnt[b0 + q];
+    int tot = 0;
+    int run = block_exclusive_scan(loc, sm.scan, &tot);
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+      sm.bbase[b0 + q] = run;
+      run += sm.bcnt[b0 + q];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < C; e += kBlock) {
+    const int kb = sm.kbs[e];
+    sm.mkey[sm.bbase[kb >> 16] + (kb & 0xFFFF)] = sm.cand[e];
+  }
+  __syncthreads();
+  const double lse = sm.lse;
+  const size_t lb = static_cast<size_t>(s) * a.max_layers * n;   // layer 1 of sequence s
+  const size_t bb = static_cast<size_t>(s) * n;
+  for (int e = threadIdx.x; e < C; e += kBlock) {
+    const unsigned long long me = sm.cand[e];
+    const int b = sm.kbs[e] >> 16;
+    const int b0 = sm.bbase[b], bn = sm.bcnt[b];
+    if (b0 >= n) continue;   // the whole bucket ranks at or past n
+    int r = b0;
+    for (int q = 0; q < bn; ++q) r += sm.mkey[b0 + q] > me ? 1 : 0;
+    if (r >= n) continue;
+    const double sc = 0.0 + (static_cast<double>(sort_key_value(me)) - lse);
+    a.lscore[lb + r] = sc;
+    a.lparent[lb + r] = 0;
+    a.ltoken[lb + r] = sort_key_index(me);
+    a.bscore[bb + r] = sc;
+    a.blayer[bb + r] = 1;
+    a.bpos[bb + r] = r;
+    sm.ksc[r] = sc;
+  }
+  __syncthreads();
+  // E_1 = sum of exp(score) over the best list, each thread over ranks t, t + kBlock, ...
+  double part = 0.0;
+  for (int r = threadIdx.x; r < kept; r += kBlock) part += exp(sm.ksc[r]);
+  const double E = block_sum(part, sm.red);
+  if (threadIdx.x == 0) {
+    a.bcount[s] = kept;
+    const double gain = E - a.Eprev[s];
+    a.Eprev[s] = E;
+    a.nlayers[s] = 1;
+    if (gain < a.delta || 1 >= a.max_layers) a.done[s] = 1;
+  }
+}
+
 // ------------------------------------------------------------------ 2. lower bound
 
 struct OptBoundSmem {
@@ -611,6 +873,34 @@ int launch_opt_layer(OptArgs a, int dtype, hipStream_t st) {
     hipLaunchKernelGGL(opt_collect_kernel<0>, rows, dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL(opt_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Lane maxima per full wave for the one-launch root layer (0: that path does not apply):
+// a wave is full when its 64 lanes hold in-range elements only, and the bound needs
+// (full waves) * Kw >= n with Kw <= 64.
+int opt_root_wave_quota(int V, int n, int dtype) {
+  const int vec = dtype == 1 ? RowT<1>::VEC : RowT<0>::VEC;
+  const int chunk = dtype == 1 ? RowT<1>::CHUNK : RowT<0>::CHUNK;
+  const int nch = (V + chunk - 1) / chunk;
+  if (nch > kMergeMaxChunks || n > 1023) return 0;
+  long full = 0;
+  for (int c = 0; c < nch; ++c)
+    for (int w = 0; w < kWaves; ++w) {
+      const long last = static_cast<long>(c) * chunk + static_cast<long>((kLoads - 1) * kBlock + 64 * w + 63) * vec + vec - 1;
+      if (last < V) ++full;
+    }
+  if (full == 0) return 0;
+  const long kw = (n + full - 1) / full;
+  return kw <= 64 ? static_cast<int>(kw) : 0;
+}
+
+int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st) {
+  const dim3 grid(a.S * a.nch);
+  if (dtype == 1)
+    hipLaunchKernelGGL(opt_root_kernel<1>, grid, dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(opt_root_kernel<0>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -426,6 +426,9 @@ OPT_CASES = [
     ("c4_opt_llama2_7b", 43, {"P": 16, "V": 3, "n": 20, "max_layers": 4, "delta": 0.0}),
     ("c4_opt_llama2_7b", 44, {"P": 16, "V": 3000, "n": 40, "max_layers": 3, "dtype": "f32", "S": 2}),
     ("c4_opt_llama2_7b", 45, {"P": 16, "V": 9000, "n": 200, "max_layers": 6, "delta": 0.05, "draft_sigma": 2.0}),
+    # root layer in one launch with fp32 rows, and with heavy bf16 ties at the n-th value
+    ("c4_opt_llama2_7b", 46, {"P": 16, "V": 20000, "n": 300, "max_layers": 3, "dtype": "f32"}),
+    ("c4_opt_llama2_7b", 47, {"P": 16, "V": 32000, "n": 512, "max_layers": 2, "draft_sigma": 0.05, "S": 2}),
 ]
 
 
