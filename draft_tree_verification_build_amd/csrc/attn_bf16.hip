@@ -426,11 +426,12 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   const int kv = head % a.Hkv;
   const int s = head / a.Hkv;
   const size_t pr0 = static_cast<size_t>(head) * a.n_split * rows_per_head + rr;
-  // the first eight splits' O rows, every (m, l) and the node count are loaded together
-  // (rows past g * N hold stale partials in valid workspace memory and are not stored)
-  float4 o[8];
+  // every split's O row, every (m, l) and the node count are loaded together, one round
+  // trip (rows past g * N hold stale partials in valid workspace memory and are not stored;
+  // splits past n_split re-read the last one and get weight 0)
+  float4 o[NS];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < NS; ++u) {
     const int qq = min(u, a.n_split - 1);
     o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
   }
@@ -440,23 +441,12 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   if (N > a.n_cap || rr >= a.g * N) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int q0 = 0; q0 < NS; q0 += 8) {
-    if (q0 >= a.n_split) break;
-    if (q0 > 0) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int qq = min(q0 + u, a.n_split - 1);
-        o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float sc = w[q0 + u];   // 0 past n_split
-      acc.x += o[u].x * sc;
-      acc.y += o[u].y * sc;
-      acc.z += o[u].z * sc;
-      acc.w += o[u].w * sc;
-    }
+  for (int u = 0; u < NS; ++u) {
+    const float sc = w[u];   // 0 past n_split
+    acc.x += o[u].x * sc;
+    acc.y += o[u].y * sc;
+    acc.z += o[u].z * sc;
+    acc.w += o[u].w * sc;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   __bf16* orow = static_cast<__bf16*>(a.o) +
@@ -478,15 +468,20 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.n_split > 1) {
     const int rpb = kBlock / (a.D / 4);
     const dim3 blocks(a.S * a.Hkv * ((a.mcap + rpb - 1) / rpb));
-    const bool few = a.n_split <= 8;
+    // one register per split of a row's partials: 8, 16 or 32 loads in flight per thread
+    const int ns = a.n_split <= 8 ? 8 : (a.n_split <= 16 ? 16 : kAttnMaxSplit);
     if (a.D == 128) {
-      if (few)
+      if (ns == 8)
         hipLaunchKernelGGL((attn_combine_rows_kernel<128, 8>), blocks, dim3(kBlock), 0, st, a);
+      else if (ns == 16)
+        hipLaunchKernelGGL((attn_combine_rows_kernel<128, 16>), blocks, dim3(kBlock), 0, st, a);
       else
         hipLaunchKernelGGL((attn_combine_rows_kernel<128, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
     } else {
-      if (few)
+      if (ns == 8)
         hipLaunchKernelGGL((attn_combine_rows_kernel<64, 8>), blocks, dim3(kBlock), 0, st, a);
+      else if (ns == 16)
+        hipLaunchKernelGGL((attn_combine_rows_kernel<64, 16>), blocks, dim3(kBlock), 0, st, a);
       else
         hipLaunchKernelGGL((attn_combine_rows_kernel<64, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
     }

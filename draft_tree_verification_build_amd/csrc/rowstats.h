@@ -435,9 +435,13 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
 // Shared staging area of row_merge: CAP entries of all chunk lists together.
 constexpr int kMergeMaxChunks = 64;
 
+constexpr int kMergeFast = 64;   // candidates of the thresholded merge (one per lane of a wave)
+
 template <int CAP>
 struct MergeSmem {
   unsigned long long key[CAP];  // sort keys of every chunk's list, list c at c*K
+  unsigned long long cand[kMergeFast];   // entries at or above the threshold (fast path)
+  int ncand;
   int cnt[kMergeMaxChunks];
   float maxv[kMergeMaxChunks];
   int argmax[kMergeMaxChunks];
@@ -446,10 +450,15 @@ struct MergeSmem {
 
 // Merges the ChunkStats and sorted top-K lists of the `nch` chunks of one row (written by
 // other workgroups with st_cc). The lists are first copied into shared memory (one
-// parallel pass of coherent loads); each entry's rank in the merged order is then the
-// count of entries of all lists that precede it (binary search in the sorted lists).
-// Outputs (wave 0): maxv, argmax, lse; all threads: the top kout (default K) entries
-// (value, index) into rv/ri, all written with st_cc. Requires nch <= 64 and nch * K <= CAP.
+// parallel pass of coherent loads). The last wave forms the log-sum-exp while the others
+// rank the entries. When the merged list is no longer than a chunk list (kout <= K), only
+// entries at or above T0 = the largest last entry of a full list can be among the top (that
+// list alone holds K entries at or above T0); wave 0 gathers those (usually a few more than
+// K) and ranks them among themselves. Otherwise, or when more than 64 entries reach T0,
+// every entry's rank is the count of entries of all lists that precede it (counting for
+// <= 1024 entries, else binary search in the sorted lists).
+// Outputs: maxv, argmax, lse (last wave); the top kout (default K) entries (value, index)
+// into rv/ri, all written with st_cc. Requires nch <= 64 and nch * K <= CAP.
 // Returns min(kout, entries).
 template <int CAP>
 __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx, int nch, int K,
@@ -464,9 +473,12 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     ms.sumexp[c] = ld_cc(&st[c].sumexp);
   }
   for (int e = threadIdx.x; e < nch * K; e += kBlock) ms.key[e] = sort_key(ld_cc(&cval[e]), ld_cc(&cidx[e]));
+  if (threadIdx.x == 0) ms.ncand = 0;
   __syncthreads();
-  if (threadIdx.x < 64) {  // wave 0: lane c holds chunk c (nch <= 64)
-    const int c = threadIdx.x;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  if (w == kWaves - 1) {  // the last wave: lane c holds chunk c (nch <= 64)
+    const int c = lane;
     const float mc = c < nch ? ms.maxv[c] : -INFINITY;
     const float M = wave_max(mc);
     // chunks are in index order: the first chunk reaching the maximum has the lowest index
@@ -490,6 +502,46 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     return 0;
   }
   const int n = nch * K;
+  bool fast = false;
+  if (want <= K && n <= 1024) {
+    // T0 = the largest K-th entry of a full list; every wave forms it (no barrier needed)
+    unsigned long long t0 = 0ull;
+    if (lane < nch && ms.cnt[lane] >= K) t0 = ms.key[lane * K + K - 1];
+    t0 = wave_max(t0);
+    if (w == 0) {
+      int base = 0;
+      for (int e0 = 0; e0 < n; e0 += 64) {
+        const int e = e0 + lane;
+        const int c = e / K, j = e % K;
+        const unsigned long long k = e < n ? ms.key[e] : 0ull;
+        const bool in = e < n && j < ms.cnt[c] && k >= t0;
+        const unsigned long long m = __ballot(in);
+        const int pos = base + lanes_below(m);
+        if (in && pos < kMergeFast) ms.cand[pos] = k;
+        base += __popcll(m);
+      }
+      fast = base <= kMergeFast;
+      if (fast) {
+        __builtin_amdgcn_wave_barrier();
+        if (lane < base) {
+          const unsigned long long me = ms.cand[lane];
+          int rank = 0;
+          for (int q = 0; q < base; ++q) rank += ms.cand[q] > me ? 1 : 0;
+          if (rank < kk) {
+            st_cc(&rv[rank], sort_key_value(me));
+            st_cc(&ri[rank], sort_key_index(me));
+          }
+        }
+      }
+      if (lane == 0) ms.ncand = fast ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (want <= K && n <= 1024 && ms.ncand != 0) {
+    __syncthreads();   // every wave has read ncand before the next merge may reset it
+    return kk;
+  }
+  // ---- general path: every entry's rank among all lists
   if (n <= 1024) {  // absent entries count as key 0, below every real key
     for (int e = threadIdx.x; e < n; e += kBlock)
       if ((e % K) >= ms.cnt[e / K]) ms.key[e] = 0ull;
