@@ -94,8 +94,8 @@ def algorithmic_work(step, wl):
 STAGE_KERNELS = {
     "build": lambda c: {"talon": ["talon_rows_kernel", "talon_select_kernel"],
                         "spine": ["spine_kernel"],
-                        "opt": ["opt_init_kernel", "opt_rows_kernel", "opt_bound_kernel", "opt_collect_kernel",
-                                "opt_select_kernel", "opt_finalize_kernel"],
+                        "opt": ["opt_init_kernel", "opt_root_kernel", "opt_rows_kernel", "opt_bound_kernel",
+                                "opt_collect_kernel", "opt_select_kernel", "opt_finalize_kernel"],
                         "given": ["given_tree_kernel"]}[c.build],
     "attention": lambda c: (["attn_bf16_kernel", "attn_combine_rows_kernel"] if c.dtype == "bf16"
                             else ["attn_f32_kernel"]),
