@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--launch", choices=["graph", "eager"], default="eager",
                     help="replay the step as a captured HIP graph, or launch its kernels one by one")
+    ap.add_argument("--separate-compact", action="store_true",
+                    help="compact the KV cache in its own launch instead of inside the verification")
     ap.add_argument("--event-every", type=int, default=16,
                     help="record per-stage events on every n-th timed step")
     ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps for cpu_baseline (0: skip)")
@@ -86,6 +88,7 @@ def algorithmic_work(step, wl):
         out["attention"]["flops"] += 4.0 * cfg.Hq * cfg.D * (N * P + vis)
         out["verify"]["bytes"] += N * row * (1 if cfg.verify == "greedy" else 2)
         out["compact"]["bytes"] += 4 * int(plen[s]) * cfg.Hkv * cfg.D * esz
+    out["verify_compact"] = {"bytes": out["verify"]["bytes"] + out["compact"]["bytes"]}
     return out
 
 
@@ -103,6 +106,9 @@ STAGE_KERNELS = {
                          else ["sample_lse_kernel", "sample_lse_merge_kernel (trees of more than 128 nodes)",
                                "sample_walk_kernel"]),
     "compact": lambda c: ["compact_kernel"],
+    "verify_compact": lambda c: (["verify_greedy_kernel (compacts the cache)"] if c.verify == "greedy"
+                                 else ["sample_lse_kernel", "sample_lse_merge_kernel (trees of more than 128 nodes)",
+                                       "sample_walk_kernel (compacts the cache)"]),
 }
 
 
@@ -171,10 +177,10 @@ def main():
         del src, dst
     wl = make_workload(args.config, seed)
     cfg = wl.cfg
-    step = DraftTreeStep(wl, "cuda")
+    step = DraftTreeStep(wl, "cuda", fuse_compact=not args.separate_compact)
     stream = torch.cuda.current_stream()
-    stages = ["build", "attention", "verify", "compact"]
-    fns = [step.build, step.attention, step.verify, step.compact]
+    stages = [name for name, _ in step.stages()]
+    fns = [fn for _, fn in step.stages()]
 
     for _ in range(args.warmup):
         step.run()
@@ -259,7 +265,8 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "seed": seed, "S": cfg.S, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "P": cfg.P, "V": cfg.V, "N": cfg.N, "build": cfg.build,
-                   "verify": cfg.verify, "launch": args.launch},
+                   "verify": cfg.verify, "launch": args.launch,
+                   "compaction": "separate" if args.separate_compact else "in verification"},
         "tree_tokens_per_s": tree_tokens * steps_s,
         "roofline": roof,
         "stages": stage_report,

@@ -21,6 +21,16 @@ class DtvTree(ctypes.Structure):
 
 PTREE = ctypes.POINTER(DtvTree)
 
+
+class DtvKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k", c_vp), ("v", c_vp), ("P", c_vp), ("P_new", c_vp),
+        ("P_cap", c_i32), ("Hkv", c_i32), ("D", c_i32),
+    ]
+
+
+PKV = ctypes.POINTER(DtvKvCache)
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "dtv_status_str": (c_char_p, [c_int]),
@@ -46,6 +56,10 @@ SIGNATURES = {
     "dtv_tree_verify_greedy_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_verify_greedy": (c_int, [PTREE, c_i32, c_vp, c_int, c_i32, c_i32, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_size, c_vp]),
+    "dtv_tree_verify_greedy_compact": (c_int, [PTREE, c_i32, c_vp, c_int, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                               c_vp, PKV, c_vp, c_size, c_vp]),
+    "dtv_tree_verify_sample_compact": (c_int, [PTREE, c_i32, c_vp, c_vp, c_int, c_i32, c_i32, c_vp, c_vp,
+                                               c_vp, c_vp, c_vp, PKV, c_vp, c_size, c_vp]),
     "dtv_tree_verify_sample_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_verify_sample": (c_int, [PTREE, c_i32, c_vp, c_vp, c_int, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_size, c_vp]),

@@ -190,8 +190,21 @@ def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor
     return o
 
 
-def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None, stream=None):
-    """target [S][R][V]. Returns (path [S][n_cap], path_len [S], bonus [S], argmax [S][n_cap])."""
+def _kv_cache(kv):
+    """(k, v, P, P_new) torch tensors -> the C description of a cache to compact."""
+    k, v, P, P_new = kv
+    S, Hkv, P_cap, D = k.shape
+    if v.shape != k.shape or _dtype_code(v) != _dtype_code(k):
+        raise TypeError("k and v must share shape and dtype")
+    c = _lib.DtvKvCache(_ptr(k), _ptr(v), _ptr(P), _ptr(P_new), P_cap, Hkv, D)
+    return c
+
+
+def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None, stream=None, kv=None):
+    """target [S][R][V]. Returns (path [S][n_cap], path_len [S], bonus [S], argmax [S][n_cap]).
+
+    kv = (k, v, P, P_new): compact that cache along the path in the same launch
+    (dtv_tree_verify_greedy_compact); P_new must be its own tensor."""
     S, R, V = target.shape
     dt = _dtype_code(target)
     dev = target.device
@@ -203,15 +216,23 @@ def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None
     path, plen, bonus, amax = out
     lib = _lib.load()
     buf = ws.get("verify_greedy", lib.dtv_tree_verify_greedy_ws_bytes(S, tree.n_cap, V, dt))
-    _call("dtv_tree_verify_greedy", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
-          _ptr(bonus), _ptr(amax), buf.data_ptr(), buf.numel(), _stream(stream))
+    if kv is None:
+        _call("dtv_tree_verify_greedy", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
+              _ptr(bonus), _ptr(amax), buf.data_ptr(), buf.numel(), _stream(stream))
+    else:
+        c = _kv_cache(kv)
+        _call("dtv_tree_verify_greedy_compact", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
+              _ptr(bonus), _ptr(amax), ctypes.byref(c), buf.data_ptr(), buf.numel(), _stream(stream))
     return out
 
 
 def tree_verify_sample(tree: Tree, target: torch.Tensor, draft: torch.Tensor, u_acc: torch.Tensor,
-                       u_res: torch.Tensor, ws: Workspace, out=None, stream=None):
+                       u_res: torch.Tensor, ws: Workspace, out=None, stream=None, kv=None):
     """target, draft [S][R][V]; u_acc, u_res [S][n_cap] (uint32 bits in an int32 tensor).
-    Returns (path [S][n_cap], path_len [S], bonus [S])."""
+    Returns (path [S][n_cap], path_len [S], bonus [S]).
+
+    kv = (k, v, P, P_new): compact that cache along the path in the same launch
+    (dtv_tree_verify_sample_compact); P_new must be its own tensor."""
     S, R, V = target.shape
     dt = _dtype_code(target)
     if _dtype_code(draft) != dt:
@@ -224,8 +245,14 @@ def tree_verify_sample(tree: Tree, target: torch.Tensor, draft: torch.Tensor, u_
     path, plen, bonus = out[:3]
     lib = _lib.load()
     buf = ws.get("verify_sample", lib.dtv_tree_verify_sample_ws_bytes(S, tree.n_cap, V, dt))
-    _call("dtv_tree_verify_sample", tree.c, S, _ptr(target), _ptr(draft), dt, R, V, _ptr(u_acc), _ptr(u_res),
-          _ptr(path), _ptr(plen), _ptr(bonus), buf.data_ptr(), buf.numel(), _stream(stream))
+    if kv is None:
+        _call("dtv_tree_verify_sample", tree.c, S, _ptr(target), _ptr(draft), dt, R, V, _ptr(u_acc),
+              _ptr(u_res), _ptr(path), _ptr(plen), _ptr(bonus), buf.data_ptr(), buf.numel(), _stream(stream))
+    else:
+        c = _kv_cache(kv)
+        _call("dtv_tree_verify_sample_compact", tree.c, S, _ptr(target), _ptr(draft), dt, R, V, _ptr(u_acc),
+              _ptr(u_res), _ptr(path), _ptr(plen), _ptr(bonus), ctypes.byref(c), buf.data_ptr(), buf.numel(),
+              _stream(stream))
     return out
 
 

@@ -694,9 +694,33 @@ size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int 
   return verify_layout(nullptr, S, n_cap, nch_of(V, dtype)).bytes;
 }
 
-int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype, int32_t R,
-                           int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
-                           int32_t* argmax_out, void* ws, size_t ws_bytes, void* stream) {
+// The compaction view of a fused verification (kv null: no compaction). A status code.
+static int kv_view(const dtv_kv_cache* kv, int dtype, const dtv_tree* tree, dtv::KvCompactView* out) {
+  memset(out, 0, sizeof(*out));
+  if (kv == nullptr) return DTV_OK;
+  REQUIRE(kv->k && kv->v && kv->P && kv->P_new, DTV_EINVAL, "kv: k, v, P or P_new is NULL");
+  REQUIRE(static_cast<const void*>(kv->P) != static_cast<const void*>(kv->P_new), DTV_EINVAL,
+          "kv: P_new must not alias P in a fused verification");
+  REQUIRE(kv->Hkv >= 1 && kv->P_cap >= tree->n_cap, DTV_EINVAL, "kv: Hkv=%d P_cap=%d n_cap=%d", kv->Hkv,
+          kv->P_cap, tree->n_cap);
+  const int es = esize_of(dtype);
+  REQUIRE(kv->D >= 1 && (kv->D * es) % 16 == 0 && kv->D * es <= 512, DTV_EUNSUPPORTED,
+          "kv: row of D=%d elements must be a multiple of 16 bytes and at most 512", kv->D);
+  out->k = static_cast<char*>(kv->k);
+  out->v = static_cast<char*>(kv->v);
+  out->P = kv->P;
+  out->P_new = kv->P_new;
+  out->P_cap = kv->P_cap;
+  out->Hkv = kv->Hkv;
+  out->D = kv->D;
+  out->esize = es;
+  return DTV_OK;
+}
+
+static int verify_greedy_impl(const dtv_tree* tree, int32_t S, const void* target, int dtype, int32_t R,
+                              int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                              int32_t* argmax_out, const dtv_kv_cache* kv, void* ws, size_t ws_bytes,
+                              void* stream) {
   int rc = check_tree(tree);
   if (rc) return rc;
   REQUIRE(target && path && path_len && bonus, DTV_EINVAL, "target, path, path_len or bonus is NULL");
@@ -716,7 +740,25 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
   a.argmax_out = argmax_out;
   a.cbest = L.cbest;
   a.hdr = L.hdr;
+  rc = kv_view(kv, dtype, tree, &a.kvc);
+  if (rc) return rc;
   return launched(dtv::launch_verify_greedy(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype, int32_t R,
+                           int32_t V, int32_t* path, int32_t* path_len, int32_t* bonus,
+                           int32_t* argmax_out, void* ws, size_t ws_bytes, void* stream) {
+  return verify_greedy_impl(tree, S, target, dtype, R, V, path, path_len, bonus, argmax_out, nullptr, ws,
+                            ws_bytes, stream);
+}
+
+int dtv_tree_verify_greedy_compact(const dtv_tree* tree, int32_t S, const void* target, int dtype,
+                                   int32_t R, int32_t V, int32_t* path, int32_t* path_len,
+                                   int32_t* bonus, int32_t* argmax_out, const dtv_kv_cache* kv,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(kv != nullptr, DTV_EINVAL, "kv is NULL");
+  return verify_greedy_impl(tree, S, target, dtype, R, V, path, path_len, bonus, argmax_out, kv, ws,
+                            ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- rejection sampling
@@ -726,9 +768,10 @@ size_t dtv_tree_verify_sample_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int 
   return sample_layout(nullptr, S, n_cap, V, dtype).bytes;
 }
 
-int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, const void* draft, int dtype,
-                           int32_t R, int32_t V, const uint32_t* u_acc, const uint32_t* u_res, int32_t* path,
-                           int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+static int verify_sample_impl(const dtv_tree* tree, int32_t S, const void* target, const void* draft,
+                              int dtype, int32_t R, int32_t V, const uint32_t* u_acc, const uint32_t* u_res,
+                              int32_t* path, int32_t* path_len, int32_t* bonus, const dtv_kv_cache* kv,
+                              void* ws, size_t ws_bytes, void* stream) {
   int rc = check_tree(tree);
   if (rc) return rc;
   REQUIRE(target && draft && u_acc && u_res && path && path_len && bonus, DTV_EINVAL, "a pointer is NULL");
@@ -770,7 +813,26 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
   long grid = items < lse_slots ? items : lse_slots;
   if (grid * 64 < items) grid = (items + 63) / 64;
   a.lse_grid = static_cast<int>(grid);
+  rc = kv_view(kv, dtype, tree, &a.kvc);
+  if (rc) return rc;
   return launched(dtv::launch_verify_sample(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, const void* draft, int dtype,
+                           int32_t R, int32_t V, const uint32_t* u_acc, const uint32_t* u_res, int32_t* path,
+                           int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes, void* stream) {
+  return verify_sample_impl(tree, S, target, draft, dtype, R, V, u_acc, u_res, path, path_len, bonus, nullptr,
+                            ws, ws_bytes, stream);
+}
+
+int dtv_tree_verify_sample_compact(const dtv_tree* tree, int32_t S, const void* target,
+                                   const void* draft, int dtype, int32_t R, int32_t V,
+                                   const uint32_t* u_acc, const uint32_t* u_res, int32_t* path,
+                                   int32_t* path_len, int32_t* bonus, const dtv_kv_cache* kv,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(kv != nullptr, DTV_EINVAL, "kv is NULL");
+  return verify_sample_impl(tree, S, target, draft, dtype, R, V, u_acc, u_res, path, path_len, bonus, kv,
+                            ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- compaction

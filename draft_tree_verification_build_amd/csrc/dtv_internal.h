@@ -155,6 +155,15 @@ struct AttnArgs {
   WsHeader* hdr;
 };
 
+// A KV cache that a verification compacts along its path in the same launch (k null: none).
+struct KvCompactView {
+  char* k;
+  char* v;
+  const int* P;
+  int* P_new;
+  int P_cap, Hkv, D, esize;
+};
+
 struct VerifyArgs {
   TreeArgs tree;
   const void* target;
@@ -165,6 +174,7 @@ struct VerifyArgs {
   int* argmax_out;
   unsigned long long* cbest;  // [S][n_cap][nch] chunk argmax keys (0: not yet reported)
   WsHeader* hdr;
+  KvCompactView kvc;
 };
 
 struct SampleArgs {
@@ -186,6 +196,7 @@ struct SampleArgs {
   int max_pass;              // exchange slots per sequence (rejections + 1 bonus draw)
   double* xch;               // [S][max_pass][64] walk exchange slots (emptied by phase 1)
   double* pbuf;              // [S][3][V] residual distributions and q (slices too large for LDS)
+  KvCompactView kvc;
 };
 
 struct CompactArgs {

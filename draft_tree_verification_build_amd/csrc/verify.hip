@@ -19,6 +19,48 @@ constexpr int kVerifyMaxNodes = 1024;
 constexpr int kVerifyMaxWords = 16;
 constexpr long kGreedySpinLimit = 2000000;   // poll rounds (each a memory round trip) before a timeout
 
+// ------------------------------------------------------------------ compaction by the walk
+//
+// KV compaction of sequence s along its accepted path (spath[k], k < L, in shared memory),
+// concept page, "The protocol", step 4: cache[P + k] <- cache[P + spath[k]] for the (KV
+// head, tensor) pairs pair0, pair0 + pstep, ... Each pair is memory of its own, and within
+// a pair the rows are taken in increasing k, in batches whose reads all precede their
+// writes; a node at depth k has slot >= k, so no later source row is an earlier
+// destination. Every thread of the workgroup calls it. Returns false, touching nothing,
+// when P and the tree do not fit the cache.
+__device__ bool walk_compact(const KvCompactView& c, int s, int n_cap, const int* spath, int L, int pair0,
+                             int pstep) {
+  const int P = c.P[s];
+  if (L < 1 || L > n_cap || P < 0 || P + n_cap > c.P_cap) return false;
+  const int vpr = c.D * c.esize / 16;   // 16-byte vectors per row
+  const size_t row_bytes = static_cast<size_t>(c.D) * c.esize;
+  const int npairs = pair0 < 2 * c.Hkv ? (2 * c.Hkv - pair0 + pstep - 1) / pstep : 0;
+  const int per_pair = L * vpr;
+  const int total = npairs * per_pair;
+  constexpr int kPer = 4;   // vectors per thread and batch, all loaded before any store
+  for (int b0 = 0; b0 < total; b0 += kBlock * kPer) {
+    uint4 val[kPer];
+    char* dst[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int v = min(b0 + q * kBlock + static_cast<int>(threadIdx.x), total - 1);
+      const int pi = v / per_pair, rem = v % per_pair;
+      const int k = rem / vpr, ch = rem % vpr;
+      const int pair = pair0 + pi * pstep;
+      char* base = ((pair & 1) ? c.v : c.k) +
+                   (static_cast<size_t>(s) * c.Hkv + (pair >> 1)) * c.P_cap * row_bytes;
+      val[q] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(P + spath[k]) * row_bytes + ch * 16);
+      dst[q] = base + static_cast<size_t>(P + k) * row_bytes + ch * 16;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (b0 + q * kBlock + static_cast<int>(threadIdx.x) < total) *reinterpret_cast<uint4*>(dst[q]) = val[q];
+    __syncthreads();
+  }
+  return true;
+}
+
 struct VerifySmem {
   int a[kVerifyMaxNodes];       // target argmax at every node
   short par[kVerifyMaxNodes];   // parent slot
@@ -133,9 +175,17 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   const int vstar = 0xFFFFF - static_cast<int>(pick & 0xFFFFFull);
   const int A = static_cast<int>(pick >> 20);
   if (threadIdx.x == 0) {
-    for (int u = vstar; u >= 0; u = sm.par[u]) a.path[tb + sm.dep[u]] = u;
+    for (int u = vstar; u >= 0; u = sm.par[u]) {
+      a.path[tb + sm.dep[u]] = u;
+      sm.tok[sm.dep[u]] = u;   // the path, for the compaction (tokens are no longer read)
+    }
     a.path_len[s] = A + 1;
     a.bonus[s] = sm.a[vstar];
+  }
+  if (a.kvc.k != nullptr) {
+    __syncthreads();
+    const bool done = walk_compact(a.kvc, s, cap, sm.tok, A + 1, 0, 1);
+    if (threadIdx.x == 0) a.kvc.P_new[s] = done ? a.kvc.P[s] + A + 1 : -1;
   }
 }
 
@@ -165,6 +215,7 @@ struct SampleSmem {
   double lset[kSampleMaxNodes];
   double lsed[kSampleMaxNodes];
   int kids[kSampleMaxNodes];
+  int spath[kSampleMaxNodes];   // the accepted path so far (every workgroup of the group)
   double wsum[kWaves];
   int iwsum[kWaves];
   int flag;
@@ -644,6 +695,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   const bool lead = grp.gi == 0;
   int v = 0, A = 0;
   if (lead && threadIdx.x == 0) a.path[tb] = 0;
+  if (threadIdx.x == 0) sm.spath[0] = 0;
   for (;;) {
     // children of v in slot order
     const int seg = (N + kBlock - 1) / kBlock;
@@ -718,6 +770,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       v = accepted;
       ++A;
       if (lead && threadIdx.x == 0) a.path[tb + A] = v;
+      if (threadIdx.x == 0) sm.spath[A] = v;
       continue;
     }
     // bonus: inverse CDF of the current p with u_res[v]; slice masses first. After a
@@ -770,6 +823,11 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     break;
   }
   if (lead && threadIdx.x == 0) a.path_len[s] = A + 1;
+  if (a.kvc.k != nullptr) {   // the group's workgroups share the (head, tensor) pairs
+    __syncthreads();
+    const bool done = walk_compact(a.kvc, s, cap, sm.spath, A + 1, grp.gi, grp.G);
+    if (lead && threadIdx.x == 0) a.kvc.P_new[s] = done ? a.kvc.P[s] + A + 1 : -1;
+  }
 }
 
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st) {

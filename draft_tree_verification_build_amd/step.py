@@ -2,7 +2,8 @@
 
 ``DraftTreeStep`` uploads the inputs of a synthetic workload once (any object with the
 fields of ``workloads.Workload``), allocates every output and workspace, and then runs
-the four stages through libdtv on one stream with no host synchronisation. The step is
+the four stages through libdtv on one stream with no host synchronisation; with
+``fuse_compact`` (the default) the verification launch also compacts the cache. The step is
 re-runnable: the build, attention and verification read only inputs; the compaction
 writes the new prefix length to a separate ``P_new`` and moves cache rows inside the
 tree block, which changes attention outputs of later repetitions but not their work.
@@ -27,8 +28,9 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 class DraftTreeStep:
-    def __init__(self, wl, device="cuda"):
+    def __init__(self, wl, device="cuda", fuse_compact=True):
         cfg = wl.cfg
+        self.fuse_compact = fuse_compact
         self.cfg = cfg
         self.device = torch.device(device)
         dev = self.device
@@ -87,15 +89,29 @@ class DraftTreeStep:
             api.tree_verify_sample(self.tree, self.target, self.draft, self.u_acc, self.u_res, self.ws,
                                    out=self.verify_out, stream=stream)
 
+    def verify_compact(self, stream=None):
+        """Verification that compacts the KV cache along its path in the same launch."""
+        kv = (self.k, self.v, self.P, self.P_new)
+        if self.cfg.verify == "greedy":
+            api.tree_verify_greedy(self.tree, self.target, self.ws, out=self.verify_out, stream=stream, kv=kv)
+        else:
+            api.tree_verify_sample(self.tree, self.target, self.draft, self.u_acc, self.u_res, self.ws,
+                                   out=self.verify_out, stream=stream, kv=kv)
+
     def compact(self, stream=None):
         path, plen = self.verify_out[0], self.verify_out[1]
         api.kv_compact(self.k, self.v, self.P, path, plen, P_new=self.P_new, stream=stream)
 
+    def stages(self):
+        """(name, callable) of every launch group of a step, in order."""
+        if self.fuse_compact:
+            return [("build", self.build), ("attention", self.attention), ("verify_compact", self.verify_compact)]
+        return [("build", self.build), ("attention", self.attention), ("verify", self.verify),
+                ("compact", self.compact)]
+
     def run(self, stream=None):
-        self.build(stream)
-        self.attention(stream)
-        self.verify(stream)
-        self.compact(stream)
+        for _, fn in self.stages():
+            fn(stream)
 
     def ws_status(self) -> dict:
         """Synchronise and collect the device status of every workspace used so far."""

@@ -233,6 +233,37 @@ int dtv_kv_compact(void* k, void* v, const int32_t* P, int32_t* P_new, int32_t P
                    int32_t Hkv, int32_t D, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Verification and KV compaction in one launch (concept page, "The protocol", steps 3-4).
+ *
+ * The same results as dtv_tree_verify_greedy / dtv_tree_verify_sample followed by
+ * dtv_kv_compact on their path: the workgroups that finish a sequence's walk copy the
+ * accepted rows of every KV head in place (rows of one head and tensor in increasing
+ * path order, every read of a batch before its writes), then set P_new[s] = P[s] +
+ * path_len[s] (-1 when P[s] and the tree do not fit P_cap; the cache is then untouched).
+ * `kv` describes the cache as in dtv_kv_compact: k, v `[S][Hkv][P_cap][D]` in the
+ * verification's dtype, P `[S]`, P_new `[S]`, which must not alias P (other workgroups of
+ * the sequence may still read P). Workspace: the size of the verification alone.
+ * DTV_EINVAL for a NULL or inconsistent kv, otherwise the errors of the verification.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  const int32_t* P;
+  int32_t* P_new;
+  int32_t P_cap, Hkv, D;
+} dtv_kv_cache;
+
+int dtv_tree_verify_greedy_compact(const dtv_tree* tree, int32_t S, const void* target, int dtype,
+                                   int32_t R, int32_t V, int32_t* path, int32_t* path_len,
+                                   int32_t* bonus, int32_t* argmax_out, const dtv_kv_cache* kv,
+                                   void* ws, size_t ws_bytes, void* stream);
+int dtv_tree_verify_sample_compact(const dtv_tree* tree, int32_t S, const void* target,
+                                   const void* draft, int dtype, int32_t R, int32_t V,
+                                   const uint32_t* u_acc, const uint32_t* u_res, int32_t* path,
+                                   int32_t* path_len, int32_t* bonus, const dtv_kv_cache* kv,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Draft-efficiency bookkeeping (TALON page, section 5.3). Host only.
  *
  * accepted_h[t] = A_t accepted draft tokens of verification pass t (t < n_passes),

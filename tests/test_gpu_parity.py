@@ -472,3 +472,49 @@ def test_step_end_to_end_c4():
     assert int(step.P_new[0]) == r["P_new"]
     kk = step.k.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(kk[0], r["k"])
+
+
+@pytest.mark.parametrize("name,seed,ov", [
+    ("c1_tiny", 1, {}),
+    ("c2_talon_llama3_8b", 2, {}),
+    ("c3_goose_spine", 3, {"P": 64}),
+    ("c4_opt_llama2_7b", 4, {"P": 64}),
+    ("c5_batched_llama2_70b", 5, {"P": 256}),
+])
+def test_verify_compact_fused_matches_separate(name, seed, ov):
+    """Verification that compacts in the same launch gives exactly the separate launches' path,
+    bonus, P_new and cache (the separate compaction is itself checked against the oracle)."""
+    need_gpu()
+    wl = make_workload(name, seed, **ov)
+    sep = DraftTreeStep(wl, DEV, fuse_compact=False)
+    sep.run()
+    fus = DraftTreeStep(wl, DEV, fuse_compact=True)
+    fus.run()
+    torch.cuda.synchronize()
+    for st in (sep, fus):
+        assert all(v == 0 for v in st.ws_status().values())
+    for a, b in zip(sep.verify_out[:3], fus.verify_out[:3]):
+        assert torch.equal(a, b)
+    assert torch.equal(sep.P_new, fus.P_new)
+    assert torch.equal(sep.k, fus.k) and torch.equal(sep.v, fus.v)
+
+
+def test_verify_compact_refuses_overfull_cache():
+    """P[s] + n_cap beyond P_cap: P_new[s] = -1 and that sequence's cache rows stay as they were."""
+    need_gpu()
+    wl = make_workload("c5_batched_llama2_70b", 5, P=256)
+    step = DraftTreeStep(wl, DEV)
+    step.build()
+    step.attention()
+    k0, v0 = step.k.clone(), step.v.clone()
+    P_bad = step.P.clone()
+    P_cap = step.k.shape[2]
+    P_bad[1] = P_cap - step.tree.n_cap + 1
+    dtv.tree_verify_sample(step.tree, step.target, step.draft, step.u_acc, step.u_res, step.ws,
+                           out=step.verify_out, kv=(step.k, step.v, P_bad, step.P_new))
+    torch.cuda.synchronize()
+    assert int(step.P_new[1]) == -1
+    assert torch.equal(step.k[1], k0[1]) and torch.equal(step.v[1], v0[1])
+    plen = step.verify_out[1]
+    for s in (0, 2):
+        assert int(step.P_new[s]) == int(step.P[s]) + int(plen[s])
