@@ -374,6 +374,8 @@ struct OptBoundSmem {
   unsigned long long key[8192];
   int off[1024];
   int cnt[1024];
+  double ps[1024];    // parent score of each frontier row
+  double lse[1024];   // its log-sum-exp
   int wsum[kWaves];
   RadixSmem rs;
 };
@@ -383,27 +385,35 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   const int s = blockIdx.x;
   if (a.done[s]) return;
   // the reported candidates: the top-m of every row (m = K), packed row after row
+  // per row: list length (scanned to offsets), parent score and log-sum-exp, read once
   int carry = 0;
   for (int f0 = 0; f0 < a.W; f0 += kBlock) {
     const int f = f0 + threadIdx.x;
-    const int cnt = (f < a.W) ? a.rcnt[static_cast<size_t>(s) * a.Wcap + f] : 0;
+    const int fc = f < a.W ? f : a.W - 1;
+    const size_t rf = static_cast<size_t>(s) * a.Wcap + fc;
+    const int cnt = (f < a.W) ? a.rcnt[rf] : 0;
+    const double ps = parent_score(a, s, fc);
+    const double lse = a.rlse[rf];
     int tot = 0;
     const int ex = block_exclusive_scan(cnt, sm.wsum, &tot);
     if (f < a.W) {
       sm.off[f] = carry + ex;
       sm.cnt[f] = cnt;
+      sm.ps[f] = ps;
+      sm.lse[f] = lse;
     }
     carry += tot;
   }
   const int total = carry;
   __syncthreads();   // offsets of every row before the keys are placed
-  // every load is unconditional (all addresses are in the workspace), so an unrolled
-  // thread keeps them all in flight
-#pragma unroll 8
-  for (int e = threadIdx.x; e < a.W * a.K; e += kBlock) {
-    const int f = e / a.K, j = e % a.K;
-    const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
-    const double sc = parent_score(a, s, f) + (static_cast<double>(a.rv[rf * a.K + j]) - a.rlse[rf]);
+  // the score of an entry is formed exactly as the collection forms it; its list value
+  // loads are unconditional (all addresses are in the workspace) and in flight together
+  const int nent = a.W * a.K;
+#pragma unroll 16
+  for (int e = threadIdx.x; e < nent; e += kBlock) {
+    const int f = e / a.K, j = e - f * a.K;
+    const float x = a.rv[(static_cast<size_t>(s) * a.Wcap + f) * a.K + j];
+    const double sc = sm.ps[f] + (static_cast<double>(x) - sm.lse[f]);
     if (j < sm.cnt[f]) sm.key[sm.off[f] + j] = dkey(sc);
   }
   __syncthreads();

@@ -5,10 +5,16 @@
 
 namespace dtv {
 
+constexpr int kRadixBits = 11;                  // digit width of a pass
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kRadixPer = kRadixBins / kBlock;  // bins owned by a thread in the scan
+
 struct RadixSmem {
-  int hist[256];
+  int hist[kRadixBins];   // counts of the pass; zero between passes
   int digit, rem, cnt;
+  int scan[kWaves];
   unsigned long long red[kWaves];
+  unsigned long long red2[kWaves];
 };
 
 // Result of radix_topk_cut: the keys k with (k & mask) > prefix are all among the top k;
@@ -21,14 +27,17 @@ struct RadixCut {
 };
 
 // The cut of the top k (k >= 1) of the nonzero keys key[0 .. n) (zero marks an absent
-// entry; at least k keys present), by most-significant-byte-first radix selection that
-// starts at the highest byte where the present keys differ: each pass histograms the next
-// byte of the keys sharing the prefix so far and extends the prefix by the byte at which
-// the count from the top reaches the number still to take. It stops as soon as the group
-// of keys sharing the prefix lies entirely within the top k (then no lower byte matters).
+// entry; at least k keys present), by most-significant-digit-first radix selection with
+// 11-bit digits that starts at the highest bit where the present keys differ: each pass
+// histograms the next digit of the keys sharing the prefix so far (2048 bins, so keys
+// packed in a narrow range still spread over many bins and the shared-memory atomics
+// rarely collide) and extends the prefix by the digit at which the count from the top
+// reaches the number still to take. It stops as soon as the group of keys sharing the
+// prefix lies entirely within the top k (then no lower digit matters), or when the whole
+// key is resolved. A pass clears the bins it has read, ready for the next one.
 // Every thread of the block must call it; all get the same result.
 __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs) {
-  static_assert(kBlock == 256, "one histogram bin per thread");
+  static_assert(kRadixBins % kBlock == 0, "whole bins per thread");
   unsigned long long kmax = 0ull, kmin = ~0ull;
   for (int e = threadIdx.x; e < n; e += kBlock) {
     const unsigned long long x = key[e];
@@ -37,63 +46,73 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
       kmin = x < kmin ? x : kmin;
     }
   }
-  kmax = block_max(kmax, rs.red);
-  kmin = block_min(kmin, rs.red);
+  kmax = wave_max(kmax);
+  kmin = wave_min(kmin);
+  if ((threadIdx.x & 63) == 0) {
+    rs.red[threadIdx.x >> 6] = kmax;
+    rs.red2[threadIdx.x >> 6] = kmin;
+  }
+#pragma unroll
+  for (int q = 0; q < kRadixPer; ++q) rs.hist[threadIdx.x * kRadixPer + q] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    kmax = rs.red[q] > kmax ? rs.red[q] : kmax;
+    kmin = rs.red2[q] < kmin ? rs.red2[q] : kmin;
+  }
   const unsigned long long diff = kmax ^ kmin;
-  int top = 0;
-  for (int b = 7; b >= 0; --b)
-    if ((diff >> (8 * b)) & 0xFFull) {
-      top = b;
-      break;
-    }
+  // bits above the highest differing one are shared by every present key
+  int unresolved = diff ? 64 - __clzll(static_cast<long long>(diff)) : kRadixBits;
   RadixCut cut;
-  cut.mask = top == 7 ? 0ull : (~0ull << (8 * (top + 1)));
+  cut.mask = unresolved >= 64 ? 0ull : (~0ull << unresolved);
   cut.prefix = kmax & cut.mask;
   cut.rem = k;
   cut.all_in = false;
-  for (int shift = 8 * top; shift >= 0; shift -= 8) {
-    rs.hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kBlock) {
+  const int t = threadIdx.x;
+  while (unresolved > 0) {
+    const int w = unresolved < kRadixBits ? unresolved : kRadixBits;
+    const int shift = unresolved - w;
+    const unsigned dmask = (1u << w) - 1u;
+    for (int e = t; e < n; e += kBlock) {
       const unsigned long long x = key[e];
-      if (x != 0ull && (x & cut.mask) == cut.prefix) atomicAdd(&rs.hist[(x >> shift) & 255u], 1);
+      if (x != 0ull && (x & cut.mask) == cut.prefix) atomicAdd(&rs.hist[(x >> shift) & dmask], 1);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l owns digits 255-4l .. 252-4l; find the digit whose cumulative count from
-      // the top first reaches rem
-      const int l = threadIdx.x;
-      const int c0 = rs.hist[255 - 4 * l], c1 = rs.hist[254 - 4 * l];
-      const int c2 = rs.hist[253 - 4 * l], c3 = rs.hist[252 - 4 * l];
-      const int mine = c0 + c1 + c2 + c3;
-      int inc = mine;
+    // thread t owns the kRadixPer digits just below kRadixBins - kRadixPer t, largest first;
+    // it reads and clears them, and the thread whose range takes the count from the top
+    // past rem records the digit
+    int c[kRadixPer];
+    int mine = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(inc, o, 64);
-        if (l >= o) inc += y;
-      }
-      const int above = inc - mine;
-      if (above < cut.rem && cut.rem <= inc) {
-        int acc = above, d = 255 - 4 * l;
-        const int cs[4] = {c0, c1, c2, c3};
-        for (int q = 0; q < 4; ++q) {
-          if (acc + cs[q] >= cut.rem) {
-            d = 255 - 4 * l - q;
-            break;
-          }
-          acc += cs[q];
+    for (int q = 0; q < kRadixPer; ++q) {
+      const int d = kRadixBins - 1 - kRadixPer * t - q;
+      c[q] = rs.hist[d];
+      rs.hist[d] = 0;
+      mine += c[q];
+    }
+    int tot = 0;
+    const int above = block_exclusive_scan(mine, rs.scan, &tot);
+    if (above < cut.rem && cut.rem <= above + mine) {
+      int acc = above;
+#pragma unroll
+      for (int q = 0; q < kRadixPer; ++q) {
+        if (acc + c[q] >= cut.rem) {
+          rs.digit = kRadixBins - 1 - kRadixPer * t - q;
+          rs.rem = cut.rem - acc;
+          rs.cnt = c[q];
+          break;
         }
-        rs.digit = d;
-        rs.rem = cut.rem - acc;
-        rs.cnt = rs.hist[d];
+        acc += c[q];
       }
     }
     __syncthreads();
     cut.prefix |= static_cast<unsigned long long>(rs.digit) << shift;
-    cut.mask |= 0xFFull << shift;
+    cut.mask |= static_cast<unsigned long long>(dmask) << shift;
     cut.rem = rs.rem;
     const int cnt = rs.cnt;
-    __syncthreads();
+    unresolved = shift;
+    // (the next pass writes the result only after its own barriers, which every thread
+    // reaches after these reads)
     if (cnt == cut.rem) {   // the whole group is taken
       cut.all_in = true;
       break;
