@@ -181,6 +181,22 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   const int g = a.g;
   const int M = g * N;
   const int P = a.P[s];
+  // Query rows come from the planned tiling (n_cap nodes), so their loads are issued with
+  // the node count and prefix length rather than after them: a row past the sequence's
+  // nodes reads a valid slot and is never stored.
+  constexpr int NKS0 = D / 16;
+  Frag8 qf[NKS0];
+  const int Gp = (g * a.n_cap + 31) / 32;   // groups of the planned tiling
+  {
+    const int w0 = threadIdx.x >> 6, lane0 = threadIdx.x & 63;
+    const int grp0 = tm * Gp / a.n_mtiles + w0;
+    const int r0 = grp0 * 32 + (lane0 & 31);
+    const int node0 = min(r0 / g, a.n_cap - 1);
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((static_cast<size_t>(s) * a.n_cap + node0) * a.Hq + kv * g + r0 % g) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS0; ++ks) qf[ks].u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * (lane0 >> 5));
+  }
   if (N > a.n_cap || P < 0 || P + N > a.P_cap) {
     if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
@@ -208,12 +224,11 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + kvoff;
   const uint64_t* anc = a.anc + (static_cast<size_t>(s) * a.n_cap + node) * a.words;
 
-  Frag8 qf[NKS];
-  {
+  if (G != Gp) {
+    // fewer nodes than planned changes the tiling: this wave's rows are reloaded (a padding
+    // row past M reads row 0's query, valid memory, and its output is never stored)
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((static_cast<size_t>(s) * a.n_cap + node) * a.Hq + kv * g + (ok ? r % g : 0)) * D;
-    // Unconditional loads: a padding row (past M) reads row 0's query, which is valid
-    // memory; its scores stay finite and its output is never stored.
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks].u = *reinterpret_cast<const uint4*>(qrow + ks * 16 + 8 * h);
   }

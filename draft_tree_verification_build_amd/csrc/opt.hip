@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kBlock, 4) void opt_rows_kernel(OptArgs a) {
   bid /= a.nch;
   const int f = bid % a.W;
   const int s = bid / a.W;
-  if (ld_cc(&a.done[s])) return;
+  // the stop flag was set by an earlier launch: a plain load sees it (a stopped sequence
+  // must not stream its rows, so the chunk waits for it)
+  if (a.done[s]) return;
   row_smem_init(rs);
   __syncthreads();
   const char* row = static_cast<const char*>(a.draft) +
@@ -451,13 +453,16 @@ __global__ __launch_bounds__(kBlock) void opt_collect_kernel(OptArgs a) {
   bid /= a.nch;
   const int f = bid % a.W;
   const int s = bid / a.W;
-  if (a.done[s]) return;
+  // the stop flag, the bound and the row's values in one round of loads (valid memory
+  // whether or not the sequence has stopped)
+  const int done = a.done[s];
   const double lo = a.lo[s];
   const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
   const double base = parent_score(a, s, f);
   const double lse = a.rlse[rf];
-  // a chunk whose largest logit cannot reach lo has no candidate: skip reading it
   const float cmax = a.st[rf * a.nch + c].maxv;
+  if (done) return;
+  // a chunk whose largest logit cannot reach lo has no candidate: skip reading it
   if (!(base + (static_cast<double>(cmax) - lse) >= lo)) return;
   const char* row = static_cast<const char*>(a.draft) +
                     (static_cast<size_t>(s) * a.R + row_of(a, f)) * static_cast<size_t>(a.V) * Rw::ESIZE;

@@ -80,15 +80,18 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   const int s = blockIdx.x / (cap * nch);
   const int rest = blockIdx.x % (cap * nch);
   const int i = rest / nch, c = rest % nch;
+  const size_t tb = static_cast<size_t>(s) * cap;
+  // the node count and this node's row in one round of loads (slot i < n_cap is valid
+  // memory; its row is used only when i < N)
   const int N = a.tree.n_nodes[s];
+  const int r_slot = a.tree.row[tb + i];
   if (N > cap || N < 1) {  // n_nodes is device data: refuse rather than read past the tree
     if (threadIdx.x == 0 && i == 0 && c == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
   }
-  const size_t tb = static_cast<size_t>(s) * cap;
   unsigned long long* slots = a.cbest + tb * nch;   // [node][chunk]
   if (i < N) {
-    const int r = a.tree.row[tb + i];
+    const int r = r_slot;
     const char* row = static_cast<const char*>(a.target) +
                       (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
     float x[Rw::E];
