@@ -82,8 +82,6 @@ __global__ __launch_bounds__(kBlock, 4) void talon_rows_kernel(TalonArgs a) {
   __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * kTalonMaxK) > kCandCap
                                             ? pow2_at_least(kWaves * kTalonMaxK) : kCandCap];
   using Rw = RowT<DT>;
-  row_smem_init(rs);
-  __syncthreads();
   const int nch = a.nch;
   const int K = a.K;
   const int c = blockIdx.x % nch;
@@ -91,9 +89,13 @@ __global__ __launch_bounds__(kBlock, 4) void talon_rows_kernel(TalonArgs a) {
   const int s = rf / a.B, f = rf % a.B;  // row f of sequence s is draft row f (rows keyed by slot)
   const char* row = static_cast<const char*>(a.draft) +
                     (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
+  // the exp table and the chunk in one round trip
+  row_smem_issue(rs);
   float x[Rw::E];
   uint32_t key[Rw::E];
   load_chunk<DT>(row, a.V, c, x, key);
+  drain();
+  __syncthreads();
   const size_t ci = static_cast<size_t>(rf) * nch + c;
   chunk_reduce<DT>(x, key, c, a.V, K, &a.st[ci], a.cval + ci * K, a.cidx + ci * K, sortbuf, rs);
   if (last_arrival(&a.tickets[rf], nch, &rs.flag)) {
@@ -307,8 +309,6 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   __shared__ unsigned long long sortbuf[pow2_at_least(kWaves * 128) > kCandCap ? pow2_at_least(kWaves * 128)
                                                                               : kCandCap];
   using Rw = RowT<DT>;
-  row_smem_init(rs);
-  __syncthreads();
   const int nch = a.nch;
   const int K = a.K;
   const int cap = a.tree.n_cap;
@@ -319,6 +319,15 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   const int s = bid / a.F;
   const size_t tb = static_cast<size_t>(s) * cap;
   const int words = a.tree.words;
+  const char* row = static_cast<const char*>(a.draft) +
+                    (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
+  // the exp table and the fork row's chunk in one round trip
+  row_smem_issue(rs);
+  float x[Rw::E];
+  uint32_t key[Rw::E];
+  load_chunk<DT>(row, a.V, c, x, key);
+  drain();
+  __syncthreads();
 
   if (f == 0 && c == 0) {  // root and spine chain of sequence s
     for (int k = threadIdx.x; k <= a.n_spine; k += kBlock) {
@@ -343,11 +352,6 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   const int wf = a.width[f];
   if (wf <= 0) return;
   const int kf = wf + 1 < a.V ? wf + 1 : a.V;   // one spare for the skipped spine token
-  const char* row = static_cast<const char*>(a.draft) +
-                    (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
-  float x[Rw::E];
-  uint32_t key[Rw::E];
-  load_chunk<DT>(row, a.V, c, x, key);
   const size_t rf = static_cast<size_t>(s) * a.F + f;
   const size_t ci = rf * nch + c;
   chunk_reduce<DT>(x, key, c, a.V, kf, &a.st[ci], a.cval + ci * K, a.cidx + ci * K, sortbuf, rs);

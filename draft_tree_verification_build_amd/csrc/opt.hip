@@ -90,13 +90,15 @@ __global__ __launch_bounds__(kBlock, 4) void opt_rows_kernel(OptArgs a) {
   // the stop flag was set by an earlier launch: a plain load sees it (a stopped sequence
   // must not stream its rows, so the chunk waits for it)
   if (a.done[s]) return;
-  row_smem_init(rs);
-  __syncthreads();
   const char* row = static_cast<const char*>(a.draft) +
                     (static_cast<size_t>(s) * a.R + row_of(a, f)) * static_cast<size_t>(a.V) * Rw::ESIZE;
+  // the exp table and the chunk in one round trip
+  row_smem_issue(rs);
   float x[Rw::E];
   uint32_t key[Rw::E];
   load_chunk<DT>(row, a.V, c, x, key);
+  drain();
+  __syncthreads();
   const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
   const size_t ci = rf * a.nch + c;
   // each chunk reports its top Kc (nch * Kc >= K): the row's merged K are then the best of
@@ -191,15 +193,17 @@ __global__ __launch_bounds__(kBlock) void opt_root_kernel(OptArgs a) {
   using Rw = RowT<DT>;
   const int c = blockIdx.x % a.nch;
   const int s = blockIdx.x / a.nch;
-  row_smem_init(sm.rs);
-  __syncthreads();
   const char* row = static_cast<const char*>(a.draft) +
                     static_cast<size_t>(s) * a.R * static_cast<size_t>(a.V) * Rw::ESIZE;   // row 0: the root
   const size_t cb = static_cast<size_t>(s) * a.Wcap * a.nch;   // chunk statistics of (s, f = 0)
   {
+    // the exp table and the chunk in one round trip
+    row_smem_issue(sm.rs);
     float x[Rw::E];
     uint32_t key[Rw::E];
     load_chunk<DT>(row, a.V, c, x, key);
+    drain();
+    __syncthreads();
     chunk_reduce<DT>(x, key, c, a.V, 0, &a.st[cb + c], nullptr, nullptr, sm.cand, sm.rs);
     // the Kw-th largest lane maximum of every full wave
     const int w = threadIdx.x >> 6;

@@ -56,6 +56,20 @@ struct RowSmem {
 // Must run in every thread at kernel start, followed by __syncthreads().
 __device__ __forceinline__ void row_smem_init(RowSmem& sm) { exp_table_load(sm.exptab); }
 
+// The same without registers, so that the table shares the round trip of the loads that
+// follow it: wave 0 copies the table straight into shared memory with two direct loads
+// (lane l moves bytes 4l .. 4l+3 of each 256-byte half). Every thread must then wait for its
+// loads (drain) and pass __syncthreads() before the table is read.
+__device__ __forceinline__ void row_smem_issue(RowSmem& sm) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  if (threadIdx.x < 64) {
+    const char* src = reinterpret_cast<const char*>(kExp2_64) + 4 * threadIdx.x;
+    char* dst = reinterpret_cast<char*>(sm.exptab);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + 256, (lds_void_t*)(dst + 256), 4, 0, 0);
+  }
+}
+
 constexpr int kCandCap = 512;   // candidate slots of the small-K selection (sortbuf entries)
 
 // Loads chunk `c` of `row` into registers. Out-of-range elements get key 0 and -inf.
