@@ -254,11 +254,15 @@ AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int D) {
   const double bytes_per_block = 11.0e6;
   int max_split = (T + min_keys - 1) / min_keys;
   if (max_split > dtv::kAttnMaxSplit) max_split = dtv::kAttnMaxSplit;
+  // measured on MI355X: a workgroup streaming more than 48 blocks (3072 keys) loses more
+  // than the extra round and partials cost (c5, 8257 keys: 2 splits 260 us, 3 splits 236 us)
+  const int max_kps = 48 * 64;
   int best_kps = (T + 63) / 64 * 64;
   double best_cost = 1e300;
   for (int want = 1; want <= max_split; ++want) {
     int kps = (T + want - 1) / want;
     kps = (kps + 63) / 64 * 64;
+    if (kps > max_kps && want < max_split) continue;
     const int ns = (T + kps - 1) / kps;
     const long rounds = (tiles * ns + slots - 1) / slots;
     const double cost = static_cast<double>(rounds) * (kps / 64) + (ns > 1 ? ns * partial_bytes / bytes_per_block : 0.0);
