@@ -412,15 +412,24 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   }
   const int total = carry;
   __syncthreads();   // offsets of every row before the keys are placed
-  // the score of an entry is formed exactly as the collection forms it; its list value
-  // loads are unconditional (all addresses are in the workspace) and in flight together
-  const int nent = a.W * a.K;
-#pragma unroll 16
-  for (int e = threadIdx.x; e < nent; e += kBlock) {
-    const int f = e / a.K, j = e - f * a.K;
-    const float x = a.rv[(static_cast<size_t>(s) * a.Wcap + f) * a.K + j];
-    const double sc = sm.ps[f] + (static_cast<double>(x) - sm.lse[f]);
-    if (j < sm.cnt[f]) sm.key[sm.off[f] + j] = dkey(sc);
+  // the score of an entry is formed exactly as the collection forms it. A thread takes
+  // whole rows: their list values are loaded unconditionally (all addresses are in the
+  // workspace), eight at a time in flight, and placed after the row's earlier entries
+  const int K = a.K;
+  for (int f = threadIdx.x; f < a.W; f += kBlock) {
+    const float* rv = a.rv + (static_cast<size_t>(s) * a.Wcap + f) * K;
+    const double ps = sm.ps[f], lse = sm.lse[f];
+    const int cnt = sm.cnt[f], off = sm.off[f];
+    for (int j0 = 0; j0 < K; j0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = rv[min(j0 + u, K - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < cnt) sm.key[off + j] = dkey(ps + (static_cast<double>(x[u]) - lse));
+      }
+    }
   }
   __syncthreads();
   // the n-th largest reported score bounds the layer's n-th best score from below
