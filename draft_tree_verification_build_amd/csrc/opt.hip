@@ -432,23 +432,17 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
     }
   }
   __syncthreads();
-  // the n-th largest reported score bounds the layer's n-th best score from below
+  // the n-th largest reported score bounds the layer's n-th best score from below, and so
+  // does anything below it: one radix pass finds the 11-bit digit bucket that holds the
+  // n-th largest key, and the bucket's lowest key is the bound (a few more candidates pass
+  // it than pass the exact n-th score, for a fraction of the selection's passes)
   double lo = -INFINITY;
   if (total >= a.n) {
-    // the n-th largest key: the smallest key of the boundary group when the radix cut
-    // takes that group whole, else the cut's full key
-    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs);
-    unsigned long long k = cut.prefix;
-    if (cut.all_in) {
-      unsigned long long kmin = ~0ull;
-      for (int e = threadIdx.x; e < total; e += kBlock) {
-        const unsigned long long x = sm.key[e];
-        if ((x & cut.mask) == cut.prefix) kmin = x < kmin ? x : kmin;
-      }
-      k = block_min(kmin, sm.rs.red);
-    }
+    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs, 1);
+    const unsigned long long k = cut.prefix;
     const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
     lo = __longlong_as_double(static_cast<long long>(u));
+    if (lo != lo) lo = -INFINITY;   // a bucket floor past -inf (the n-th score is -inf)
   }
   if (threadIdx.x == 0) {
     a.lo[s] = lo;

@@ -35,8 +35,11 @@ struct RadixCut {
 // reaches the number still to take. It stops as soon as the group of keys sharing the
 // prefix lies entirely within the top k (then no lower digit matters), or when the whole
 // key is resolved. A pass clears the bins it has read, ready for the next one.
-// Every thread of the block must call it; all get the same result.
-__device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs) {
+// With max_passes, the selection stops after that many passes; the cut is then a prefix
+// whose group holds the k-th largest key, so prefix (lower bits zero) still bounds that key
+// from below. Every thread of the block must call it; all get the same result.
+__device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs,
+                                                   int max_passes = 64) {
   static_assert(kRadixBins % kBlock == 0, "whole bins per thread");
   unsigned long long kmax = 0ull, kmin = ~0ull;
   for (int e = threadIdx.x; e < n; e += kBlock) {
@@ -69,7 +72,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
   cut.rem = k;
   cut.all_in = false;
   const int t = threadIdx.x;
-  while (unresolved > 0) {
+  for (int pass = 0; unresolved > 0 && pass < max_passes; ++pass) {
     const int w = unresolved < kRadixBits ? unresolved : kRadixBits;
     const int shift = unresolved - w;
     const unsigned dmask = (1u << w) - 1u;
