@@ -516,6 +516,7 @@ struct OptBest {
 };
 
 constexpr int kOptBucketMax = 128;   // largest parent group ranked by counting
+constexpr int kOptGroupMax = 64;     // boundary groups ranked directly instead of more radix passes
 
 struct OptSelectSmem {
   union {
@@ -534,6 +535,7 @@ struct OptSelectSmem {
   } u;
   unsigned long long tkey[1024];   // entries tied at a cut: tie-order keys
   int tidx[1024];
+  unsigned long long gkey[kOptGroupMax];   // a small boundary group's score keys
   int keep_idx[1024];              // indices of the kept candidates
   unsigned long long fkey[1024];   // frontier keys of the kept candidates
   int cntp[1024];                  // kept candidates per parent
@@ -575,19 +577,22 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   // ---- the layer's n best
   const int kept = C < n ? C : n;
   if (C > n) {
-    // radix cut of the n best: a boundary group taken whole needs no tie order
-    const RadixCut cut = radix_topk_cut(sm.u.in.key, C, n, sm.rs);
+    // radix cut of the n best: a boundary group taken whole needs no tie order; a small
+    // one (or the keys tied at the n-th full key) is ranked by (score desc, frontier order)
+    const RadixCut cut = radix_topk_cut(sm.u.in.key, C, n, sm.rs, 64, kOptGroupMax);
     const unsigned long long T = cut.prefix;
     const int rem = cut.all_in ? 0 : cut.rem;
     for (int e = threadIdx.x; e < C; e += kBlock) {
       const unsigned long long k = sm.u.in.key[e];
-      if (cut.all_in ? ((k & cut.mask) >= T) : (k > T)) {
+      const unsigned long long km = k & cut.mask;
+      if (cut.all_in ? (km >= T) : (km > T)) {
         sm.keep_idx[atomicAdd(&sm.nkept, 1)] = e;
-      } else if (!cut.all_in && k == T) {
+      } else if (!cut.all_in && km == T) {
         const int t = atomicAdd(&sm.ntie, 1);
         if (t < 1024) {
           sm.tkey[t] = front_key(sm.u.in.c[e]);
           sm.tidx[t] = e;
+          if (t < kOptGroupMax) sm.gkey[t] = k;
         }
       }
     }
@@ -604,7 +609,15 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     for (int t = threadIdx.x; t < nt; t += kBlock) {
       const unsigned long long me = sm.tkey[t];
       int before = 0;
-      for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      if (cut.group) {   // full score key desc, then frontier order
+        const unsigned long long mk = sm.gkey[t];
+        for (int t2 = 0; t2 < nt; ++t2) {
+          const unsigned long long ok2 = sm.gkey[t2];
+          before += (ok2 > mk || (ok2 == mk && sm.tkey[t2] < me)) ? 1 : 0;
+        }
+      } else {           // all at the same full key: frontier order
+        for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      }
       if (before < rem) sm.keep_idx[above + before] = sm.tidx[t];
     }
   } else {
@@ -721,16 +734,18 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   if (M2 <= n) {
     for (int e = threadIdx.x; e < M2; e += kBlock) emit(e);
   } else {
-    const RadixCut cut = radix_topk_cut(sm.u.best.key, M2, n, sm.rs);
+    const RadixCut cut = radix_topk_cut(sm.u.best.key, M2, n, sm.rs, 64, kOptGroupMax);
     for (int e = threadIdx.x; e < M2; e += kBlock) {
       const unsigned long long k = sm.u.best.key[e];
-      if (cut.all_in ? ((k & cut.mask) >= cut.prefix) : (k > cut.prefix)) {
+      const unsigned long long km = k & cut.mask;
+      if (cut.all_in ? (km >= cut.prefix) : (km > cut.prefix)) {
         emit(e);
-      } else if (!cut.all_in && k == cut.prefix) {
+      } else if (!cut.all_in && km == cut.prefix) {
         const int t = atomicAdd(&sm.ntie, 1);
         if (t < 1024) {
           sm.tkey[t] = static_cast<unsigned long long>(sm.u.best.info[e]);
           sm.tidx[t] = e;
+          if (t < kOptGroupMax) sm.gkey[t] = k;
         }
       }
     }
@@ -746,7 +761,15 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     for (int t = threadIdx.x; t < nt; t += kBlock) {
       const unsigned long long me = sm.tkey[t];
       int before = 0;
-      for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      if (cut.group) {   // full score key desc, then (layer, position)
+        const unsigned long long mk = sm.gkey[t];
+        for (int t2 = 0; t2 < nt; ++t2) {
+          const unsigned long long ok2 = sm.gkey[t2];
+          before += (ok2 > mk || (ok2 == mk && sm.tkey[t2] < me)) ? 1 : 0;
+        }
+      } else {
+        for (int t2 = 0; t2 < nt; ++t2) before += sm.tkey[t2] < me ? 1 : 0;
+      }
       if (before < cut.rem) emit(sm.tidx[t]);
     }
   }

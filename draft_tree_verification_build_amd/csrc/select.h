@@ -24,6 +24,7 @@ struct RadixCut {
   unsigned long long prefix, mask;
   int rem;
   bool all_in;
+  bool group;   // stopped at a small group: its `rem` best by (full key desc, tie order) are in
 };
 
 // The cut of the top k (k >= 1) of the nonzero keys key[0 .. n) (zero marks an absent
@@ -37,9 +38,12 @@ struct RadixCut {
 // key is resolved. A pass clears the bins it has read, ready for the next one.
 // With max_passes, the selection stops after that many passes; the cut is then a prefix
 // whose group holds the k-th largest key, so prefix (lower bits zero) still bounds that key
-// from below. Every thread of the block must call it; all get the same result.
+// from below. With group_max > 0 it also stops once the group that holds the k-th largest
+// key has at most group_max members and is not taken whole (group set): the caller then
+// ranks those members by full key (and its tie order) itself, which costs less than the
+// remaining passes. Every thread of the block must call it; all get the same result.
 __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs,
-                                                   int max_passes = 64) {
+                                                   int max_passes = 64, int group_max = 0) {
   static_assert(kRadixBins % kBlock == 0, "whole bins per thread");
   unsigned long long kmax = 0ull, kmin = ~0ull;
   for (int e = threadIdx.x; e < n; e += kBlock) {
@@ -71,6 +75,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
   cut.prefix = kmax & cut.mask;
   cut.rem = k;
   cut.all_in = false;
+  cut.group = false;
   const int t = threadIdx.x;
   for (int pass = 0; unresolved > 0 && pass < max_passes; ++pass) {
     const int w = unresolved < kRadixBits ? unresolved : kRadixBits;
@@ -118,6 +123,10 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
     // reaches after these reads)
     if (cnt == cut.rem) {   // the whole group is taken
       cut.all_in = true;
+      break;
+    }
+    if (cnt <= group_max && unresolved > 0) {   // a small group: ranked by the caller
+      cut.group = true;
       break;
     }
   }
