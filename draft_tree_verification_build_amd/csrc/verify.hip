@@ -4,9 +4,10 @@
 // largest value and its lowest index and publishes them as one 64-bit key
 // ((value key << 32) | ~index: larger value wins, then lower index) in a slot of its own
 // (an agent-scope store; a slot is never 0 once written, and the workspace keeps every slot
-// 0 between calls). The sequence's last workgroup in launch order walks: it polls the slots
-// of the sequence's nodes until every chunk has reported, reduces each node's chunks to its
-// argmax, clears the slots for the next call, and walks the tree: node c matches when its
+// 0 between calls). The sequence's last workgroup in launch order walks: it loads the tree,
+// polls the slots of the sequence's nodes (all of them at once, spread over its threads)
+// until every chunk has reported, reduces each node's chunks to its argmax, clears the
+// slots for the next call, and walks the tree: node c matches when its
 // token equals the argmax at its parent; a node is accepted when every node on its root
 // path matches (parent links in shared memory); the deepest accepted node, lowest slot
 // first, ends the path. No workgroup waits on a counter or a fence.
@@ -67,6 +68,7 @@ struct VerifySmem {
   short dep[kVerifyMaxNodes];   // depth
   int tok[kVerifyMaxNodes];     // drafted token
   unsigned char bad[kVerifyMaxNodes];   // 1: token differs from the argmax at the parent
+  unsigned long long best[kVerifyMaxNodes];   // largest chunk key of every node
   unsigned long long redu[kWaves];
   int flag;
 };
@@ -118,39 +120,51 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   }
   if (i != cap - 1 || c != nch - 1) return;
 
-  // ---- the walk, by the sequence's last workgroup: wait for every chunk of every node and
-  //      reduce them (each thread owns nodes v = t, t + kBlock, ...; a node's chunk slots
-  //      are read 8 at a time, all in flight), then load the tree in one parallel pass
-  int ok = 1;
+  // ---- the walk, by the sequence's last workgroup. The tree is loaded first, so that its
+  //      loads are in flight with the first polls; every thread then polls its share of
+  //      the N * nch chunk slots (node-major), up to 8 at once, until all have reported,
+  //      folds them into its node's maximum in shared memory and clears them for the next
+  //      call.
   for (int v = threadIdx.x; v < N; v += kBlock) {
-    unsigned long long* sv = slots + static_cast<size_t>(v) * nch;
-    unsigned long long bmax = 0;
-    for (int c0 = 0; c0 < nch; c0 += 8) {
-      unsigned long long b[8];
-      long polls = 0;
-      for (;;) {
-        bool all = true;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          b[q] = ld_cc(&sv[min(c0 + q, nch - 1)]);
-          all = all && b[q] != 0ull;
-        }
-        if (all) break;
-        if (++polls > kGreedySpinLimit) {
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) bmax = b[q] > bmax ? b[q] : bmax;
-    }
-    for (int cc = 0; cc < nch; ++cc) sv[cc] = 0ull;   // ready for the next call
-    const int am = sort_key_index(bmax);
-    sm.a[v] = am;
+    sm.best[v] = 0ull;
     sm.tok[v] = a.tree.token[tb + v];
     sm.par[v] = static_cast<short>(v == 0 ? -1 : a.tree.parent[tb + v]);
     sm.dep[v] = static_cast<short>(a.tree.depth[tb + v]);
+  }
+  __syncthreads();
+  int ok = 1;
+  const int total = N * nch;
+  for (int j0 = 0; j0 < total; j0 += kBlock * 8) {
+    unsigned long long b[8];
+    long polls = 0;
+    for (;;) {
+      bool all = true;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q * kBlock + static_cast<int>(threadIdx.x);
+        b[q] = j < total ? ld_cc(&slots[j]) : 1ull;
+        all = all && b[q] != 0ull;
+      }
+      if (all) break;
+      if (++polls > kGreedySpinLimit) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q * kBlock + static_cast<int>(threadIdx.x);
+      if (j < total) {
+        atomicMax(&sm.best[j / nch], b[q]);
+        slots[j] = 0ull;   // ready for the next call
+      }
+    }
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < N; v += kBlock) {
+    const int am = sort_key_index(sm.best[v]);
+    sm.a[v] = am;
     if (a.argmax_out) a.argmax_out[tb + v] = am;
   }
   if (!ok) atomicExch(&a.hdr->err, kErrTimeout);
