@@ -204,6 +204,16 @@ def test_attention_large_sampled(name, ov, pairs):
     _attn_check(make_workload(name, 5, **ov), pairs_per_seq=pairs)
 
 
+def test_attention_ragged_prefix_large():
+    """A large launch (8 sequences, 8257-key cache, several key splits) with per-sequence
+    prefix lengths that leave a split empty or one or two blocks long, or end one key into a
+    block."""
+    need_gpu()
+    wl = make_workload("c5_batched_llama2_70b", 23, V=64)
+    wl.P = np.array([8192, 0, 1, 4160, 4161, 4100, 8000, 63], dtype=np.int32)
+    _attn_check(wl, pairs_per_seq=24)
+
+
 def _upload_oracle_tree(otree, S=1):
     tree = _given_tree(otree.parent, otree.token, otree.N, S)
     ws = dtv.Workspace(DEV)
