@@ -70,10 +70,11 @@ struct KvLds {
   __device__ static __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// Issues direct-load pair i (one K and one V load) of keys kb .. kb+63 into (kd, vd). Rows
-// at or past k_hi read the last valid key instead (they are masked out of the softmax), so
-// every address is valid. ofs[i] / ofs[L + i] hold the in-block byte offsets of this lane's
-// K / V loads; the LDS base of load i of wave w is byte 1024 (w L + i) of the block.
+// Issues direct-load pair i (one K and one V load) of keys kb .. kb+63 into (kd, vd)
+// (requires kb < k_hi). A lane whose row is at or past k_hi reads the last 16 bytes of row
+// k_hi - 1 instead: finite data of a key the softmax masks out, and a valid address.
+// ofs[i] / ofs[L + i] hold the in-block byte offsets of this lane's K / V loads (multiples
+// of 16); the LDS base of load i of wave w is byte 1024 (w L + i) of the block.
 template <int D>
 __device__ __forceinline__ void kv_issue_pair(int i, uint16_t* kd, uint16_t* vd, const uint16_t* kbase,
                                               const uint16_t* vbase, int kb, int k_hi,
@@ -81,10 +82,12 @@ __device__ __forceinline__ void kv_issue_pair(int i, uint16_t* kd, uint16_t* vd,
   using L = KvLds<D>;
   const char* kp = reinterpret_cast<const char*>(kbase + static_cast<size_t>(kb) * D);
   const char* vp = reinterpret_cast<const char*>(vbase + static_cast<size_t>(kb) * D);
-  const int lim = k_hi - 1 - kb;
-  const int ko = (min(ofs[i] >> L::kRowShift, lim) << L::kRowShift) | (ofs[i] & (L::kRowBytes - 1));
-  const int vo = (min(ofs[L::kLoads + i] >> L::kRowShift, lim) << L::kRowShift) |
-                 (ofs[L::kLoads + i] & (L::kRowBytes - 1));
+  // One unsigned min per load against the offset of the last 16-byte chunk of row
+  // k_hi - 1 - kb; the offset stays a 32-bit value over a wave-uniform base, which the load
+  // can take as scalar base + vector offset.
+  const uint32_t cap = static_cast<uint32_t>(k_hi - 1 - kb) * L::kRowBytes + (L::kRowBytes - 16);
+  const uint32_t ko = min(static_cast<uint32_t>(ofs[i]), cap);
+  const uint32_t vo = min(static_cast<uint32_t>(ofs[L::kLoads + i]), cap);
   const int lds_off = 1024 * (w * L::kLoads + i);
   __builtin_amdgcn_global_load_lds(kp + ko, (lds_void*)(reinterpret_cast<char*>(kd) + lds_off), 16, 0, 0);
   __builtin_amdgcn_global_load_lds(vp + vo, (lds_void*)(reinterpret_cast<char*>(vd) + lds_off), 16, 0, 0);
