@@ -155,7 +155,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(no multi-GPU path in this build)", file=sys.stderr)
+              "(the draft-tree step has no multi-GPU path)", file=sys.stderr)
         return 2
     import numpy as np
     import torch
