@@ -48,7 +48,10 @@ class DraftTreeStep:
             parent = torch.from_numpy(np.asarray(wl.parent, dtype=np.int32)).to(dev)
             token = torch.from_numpy(np.asarray(wl.token, dtype=np.int32)).to(dev)
             self.tree = api.Tree(self.S, self.N, dev, parent=parent, token=token)
-            self.tree.n_nodes.fill_(self.N)
+            if wl.n_nodes is None:
+                self.tree.n_nodes.fill_(self.N)
+            else:   # a ragged batch: each request's own tree size
+                self.tree.n_nodes.copy_(torch.from_numpy(np.asarray(wl.n_nodes, dtype=np.int32)))
         else:
             self.tree = api.Tree(self.S, self.N, dev)
         if cfg.build == "spine":

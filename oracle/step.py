@@ -22,7 +22,8 @@ def build_tree(wl, s: int) -> build.Tree:
     cfg = wl.cfg
     draft = lambda r: decode(wl.draft[s, r], cfg.dtype)
     if cfg.build == "given":
-        return build.given_tree(wl.parent[s], wl.token[s])
+        n = cfg.N if getattr(wl, "n_nodes", None) is None else int(wl.n_nodes[s])
+        return build.given_tree(wl.parent[s][:n], wl.token[s][:n])
     if cfg.build == "talon":
         return build.talon(draft, cfg.B, cfg.K, cfg.alpha)
     if cfg.build == "spine":

@@ -204,6 +204,16 @@ def test_attention_large_sampled(name, ov, pairs):
     _attn_check(make_workload(name, 5, **ov), pairs_per_seq=pairs)
 
 
+@pytest.mark.parametrize("seed,ov,pairs", [
+    (6, {"V": 64}, 24),
+    (62, {"S": 6, "P": 300, "P_min": 0, "B_min": 0, "V": 64}, None),
+])
+def test_attention_ragged_serving(seed, ov, pairs):
+    """Ragged batch: per-request prefix lengths and tree sizes in one launch."""
+    need_gpu()
+    _attn_check(make_workload("c6_ragged_serving", seed, **ov), pairs_per_seq=pairs)
+
+
 def test_attention_ragged_prefix_large():
     """A large launch (8 sequences, 8257-key cache, several key splits) with per-sequence
     prefix lengths that leave a split empty or one or two blocks long, or end one key into a
@@ -399,6 +409,9 @@ def test_verify_sample_opt_tree():
 @pytest.mark.parametrize("name,seed,ov", [
     ("c3_goose_spine", 3, {}),
     ("c5_batched_llama2_70b", 5, {}),
+    # ragged batches: every request has its own prefix length and tree size
+    ("c6_ragged_serving", 6, {}),
+    ("c6_ragged_serving", 61, {"S": 5, "P": 700, "P_min": 0, "B_min": 0, "V": 3000}),
 ])
 def test_step_end_to_end_all_sequences(name, seed, ov):
     need_gpu()

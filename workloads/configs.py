@@ -23,6 +23,7 @@ ST_DRAFT, ST_TNOISE, ST_PARENT, ST_TOKEN = 5, 6, 7, 8
 ST_UACC, ST_URES, ST_SPINE_COIN, ST_SPINE_SUB = 9, 10, 11, 12
 ST_TARGET = 13  # independent target rows
 ST_PLANT = 14   # coins of the planted-token variant
+ST_RAGGED = 15  # per-request prefix lengths and tree sizes of a ragged batch
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -78,6 +79,8 @@ class Config:
     target_sigma: float = 0.0
     noise_sigma: float = 0.0
     target_from: str = ""  # "draft+noise" | "independent" | "target->draft"
+    P_min: int = -1       # ragged batch (given trees): per-request prefix uniform in [P_min, P]
+    B_min: int = -1       # ragged batch (given trees): per-request draft nodes uniform in [B_min, B]
 
     @property
     def g(self) -> int:
@@ -121,10 +124,15 @@ CONFIGS = {
         name="c5_batched_llama2_70b", S=8, Hq=64, Hkv=8, D=128, dtype="bf16", P=8192, V=32000,
         build="given", verify="sample", B=64, max_depth=10,
         target_sigma=3.0, noise_sigma=1.5, target_from="target->draft"),
+    # large-batch ragged serving: every request has its own prefix length and tree size
+    "c6_ragged_serving": Config(
+        name="c6_ragged_serving", S=16, Hq=32, Hkv=8, D=128, dtype="bf16", P=4096, V=32000,
+        build="given", verify="sample", B=64, max_depth=10, P_min=256, B_min=8,
+        target_sigma=3.0, noise_sigma=1.5, target_from="target->draft"),
 }
 
 CONFIG_ORDER = ["c1_tiny", "c2_talon_llama3_8b", "c3_goose_spine",
-                "c4_opt_llama2_7b", "c5_batched_llama2_70b"]
+                "c4_opt_llama2_7b", "c5_batched_llama2_70b", "c6_ragged_serving"]
 
 
 def config_by_name(name: str, **overrides) -> Config:
@@ -148,6 +156,7 @@ class Workload:
     widths: Optional[np.ndarray] = None   # [n_forks] int32
     u_acc: Optional[np.ndarray] = None    # [S][N] uint32
     u_res: Optional[np.ndarray] = None    # [S][N] uint32
+    n_nodes: Optional[np.ndarray] = None  # [S] int32 nodes of each request's tree (None: all N)
 
 
 def _random_parents(seed, s, N, max_depth):
@@ -187,7 +196,16 @@ def make_workload(cfg: Config | str, seed: int, planted: float = 0.0, **override
         cfg = dataclasses.replace(cfg, **overrides)
     S, N, R, V, D = cfg.S, cfg.N, cfg.rows, cfg.V, cfg.D
     dt = cfg.dtype
-    P = np.full(S, cfg.P, dtype=np.int32)
+    ragged = cfg.P_min >= 0 or cfg.B_min >= 0
+    if ragged and cfg.build != "given":
+        raise ValueError("ragged batches are defined for given trees")
+    if ragged:
+        rr = _rng(seed, ST_RAGGED, 0)
+        P = rr.integers(max(cfg.P_min, 0), cfg.P + 1, size=S).astype(np.int32)
+        n_nodes = 1 + rr.integers(max(cfg.B_min, 0), cfg.B + 1, size=S).astype(np.int32)
+    else:
+        P = np.full(S, cfg.P, dtype=np.int32)
+        n_nodes = None
     P_cap = cfg.P + N
     store = np.uint16 if dt == "bf16" else np.float32
 
@@ -195,11 +213,12 @@ def make_workload(cfg: Config | str, seed: int, planted: float = 0.0, **override
     k = np.zeros((S, cfg.Hkv, P_cap, D), dtype=store)
     v = np.zeros((S, cfg.Hkv, P_cap, D), dtype=store)
     for s in range(S):
+        Ps = int(P[s])   # the tree's keys and values sit at Ps + slot
         for h in range(cfg.Hkv):
-            k[s, h, :cfg.P] = _normal(seed, ST_KPRE, (s, h), (cfg.P, D), 1.0, dt)
-            v[s, h, :cfg.P] = _normal(seed, ST_VPRE, (s, h), (cfg.P, D), 1.0, dt)
-            k[s, h, cfg.P:cfg.P + N] = _normal(seed, ST_KTREE, (s, h), (N, D), 1.0, dt)
-            v[s, h, cfg.P:cfg.P + N] = _normal(seed, ST_VTREE, (s, h), (N, D), 1.0, dt)
+            k[s, h, :Ps] = _normal(seed, ST_KPRE, (s, h), (Ps, D), 1.0, dt)
+            v[s, h, :Ps] = _normal(seed, ST_VPRE, (s, h), (Ps, D), 1.0, dt)
+            k[s, h, Ps:Ps + N] = _normal(seed, ST_KTREE, (s, h), (N, D), 1.0, dt)
+            v[s, h, Ps:Ps + N] = _normal(seed, ST_VTREE, (s, h), (N, D), 1.0, dt)
 
     draft = np.zeros((S, R, V), dtype=store)
     target = np.zeros((S, R, V), dtype=store)
@@ -221,20 +240,23 @@ def make_workload(cfg: Config | str, seed: int, planted: float = 0.0, **override
                     t32 = _as_f32(d, dt) + np.float32(cfg.noise_sigma) * noise
                     target[s, r] = f32_to_bf16_bits(t32) if dt == "bf16" else t32
 
-    wl = Workload(cfg=cfg, seed=seed, P=P, P_cap=P_cap, q=q, k=k, v=v, draft=draft, target=target)
+    wl = Workload(cfg=cfg, seed=seed, P=P, P_cap=P_cap, q=q, k=k, v=v, draft=draft, target=target,
+                  n_nodes=n_nodes)
 
     if cfg.build == "given":
         parents, tokens = [], []
         for s in range(S):
-            par = _random_parents(seed, s, N, cfg.max_depth)
+            Ns = N if n_nodes is None else int(n_nodes[s])
+            par = _random_parents(seed, s, Ns, cfg.max_depth)
             tok = _gumbel_tokens(seed, s, par, _as_f32(draft[s], dt))
             if planted > 0.0:
-                coin = _rng(seed, ST_PLANT, s).random(N)
-                for i in range(1, N):
+                coin = _rng(seed, ST_PLANT, s).random(Ns)
+                for i in range(1, Ns):
                     if coin[i] < planted:
                         tok[i] = int(np.argmax(_as_f32(target[s, par[i]], dt)))
-            parents.append(par)
-            tokens.append(tok)
+            # slots past a request's tree are unused (parent -1, token -1)
+            parents.append(np.concatenate([par, np.full(N - Ns, -1, dtype=par.dtype)]))
+            tokens.append(np.concatenate([tok, np.full(N - Ns, -1, dtype=tok.dtype)]))
         wl.parent = np.stack(parents).astype(np.int32)
         wl.token = np.stack(tokens).astype(np.int32)
 
