@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--event-every", type=int, default=16,
                     help="record per-stage events on every n-th timed step")
     ap.add_argument("--cpu-steps", type=int, default=4, help="oracle steps for cpu_baseline (0: skip)")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="also run a decoding loop of this many steps on one growing KV cache and add "
+                         "its rates and bookkeeping to the line as `decode` (0: skip)")
+    ap.add_argument("--gamma", type=float, default=0.1,
+                    help="draft-to-target cost ratio for the decoding loop's Speedup = E[A]/(1 + gamma eta)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before timing, run one device-to-device copy of this many MiB (a reference "
                          "kernel of known traffic for HBM byte counters); not part of any timing")
@@ -272,10 +277,42 @@ def main():
         "stages": stage_report,
         "stage_samples": len(sampled),
     }
+    if args.decode_steps > 0:
+        out["decode"] = decode_loop(args.config, seed, args.decode_steps, args.gamma)
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_steps)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def decode_loop(config: str, seed: int, steps: int, gamma: float) -> dict:
+    """A decoding loop of ``steps`` draft-tree steps on one KV cache that grows by each
+    step's accepted path. Every step's inputs are generated and uploaded before timing, and
+    step 0 (which allocates the workspaces) runs untimed; the timed region holds steps
+    1 .. steps-1, the writes of each step's tree keys and values after the current prefix,
+    and the host's read of the accepted lengths after every step. E[A], eta and Speedup
+    cover all steps."""
+    import numpy as np
+    import torch
+    from draft_tree_verification_build_amd.decode import DraftTreeDecoder
+    from workloads import make_step_inputs
+    inputs = lambda t: make_step_inputs(config, seed, t)
+    dec = DraftTreeDecoder(inputs, steps, "cuda")
+    ups = [dec.upload(t) for t in range(steps)]
+    dec.step(0, ups[0])   # untimed: the first step allocates the workspaces
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(1, steps):
+        dec.step(t, ups[t])
+    wall = time.perf_counter() - t0
+    books = dec.bookkeeping(gamma)
+    timed = steps - 1
+    emitted = float(sum(int(r["A"].sum()) + len(r["A"]) for r in dec.log[1:]))
+    return {"steps": steps, "timed_steps": timed, "ms_per_step": wall * 1e3 / timed, "steps_per_s": timed / wall,
+            "emitted_tokens_per_s": emitted / wall, "sequences": len(books),
+            "E_A": float(np.mean([b["E_A"] for b in books])), "eta": float(np.mean([b["eta"] for b in books])),
+            "gamma": gamma, "speedup": float(np.mean([b["speedup"] for b in books])),
+            "P_final": [int(p) for p in dec.P_host]}
 
 
 if __name__ == "__main__":

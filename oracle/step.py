@@ -80,3 +80,52 @@ def step_bookkeeping(results, gamma: float) -> dict:
     """Bookkeeping over the sequences of one step, each counted as a verification pass."""
     return bookkeeping.bookkeeping([r["verify"]["A"] for r in results],
                                    sum(r["tree"].layers for r in results), gamma)
+
+
+def decode_capacity(cfg, steps: int) -> int:
+    """Cache rows per (sequence, KV head) for ``steps`` steps: each step appends at most N
+    rows (path plus the next tree block), after a prefix of at most cfg.P."""
+    return cfg.P + (steps + 1) * cfg.N
+
+
+def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None) -> dict:
+    """A decoding loop of ``steps`` draft-tree steps on one KV cache (scope row f2).
+
+    ``inputs(t)`` gives step t's workload: step 0 with the prefix and the first tree in its
+    cache; later steps with only their tree's keys and values (slots 0..N-1), which are
+    written at each sequence's current prefix length P_t. Each step is ``run_step`` on the
+    cache as it stands; its compaction leaves the accepted path's rows at P_t .. P_t + A_t
+    and P_{t+1} = P_t + A_t + 1 (the bonus token becomes the next step's root and is not
+    written). Returns the per-step results, the final cache and prefix lengths, and per
+    sequence the bookkeeping of the TALON page, section 5.3, over the loop (N_v = steps
+    verification passes, N_d = the draft layers the builds spent, L = sum of A_t + 1).
+    """
+    import dataclasses
+    wl0 = inputs(0)
+    cfg = wl0.cfg
+    N, S = cfg.N, cfg.S
+    cap = decode_capacity(cfg, steps)
+    shape = (S, cfg.Hkv, cap, cfg.D)
+    k = np.zeros(shape, dtype=wl0.k.dtype)
+    v = np.zeros(shape, dtype=wl0.v.dtype)
+    k[:, :, :wl0.k.shape[2]] = wl0.k
+    v[:, :, :wl0.v.shape[2]] = wl0.v
+    P = np.asarray(wl0.P, dtype=np.int64).copy()
+    log = []
+    for t in range(steps):
+        wl = wl0 if t == 0 else inputs(t)
+        if t > 0:
+            for s in range(S):
+                k[s, :, P[s]:P[s] + N] = wl.k[s, :, :N]
+                v[s, :, P[s]:P[s] + N] = wl.v[s, :, :N]
+        view = dataclasses.replace(wl, P=P.astype(np.int32), P_cap=cap, k=k, v=v)
+        res = run_step(view, attn_pairs=attn_pairs, with_attention=with_attention)
+        for s in range(S):
+            k[s] = res[s]["k"]
+            v[s] = res[s]["v"]
+            P[s] = res[s]["P_new"]
+        log.append(res)
+    books = [bookkeeping.bookkeeping([log[t][s]["verify"]["A"] for t in range(steps)],
+                                     sum(log[t][s]["tree"].layers for t in range(steps)), 1.0)
+             for s in range(S)]
+    return {"steps": log, "k": k, "v": v, "P": P, "bookkeeping": books}

@@ -1,0 +1,56 @@
+"""The device decoding loop (several draft-tree steps on one growing KV cache) equals the
+oracle's loop: per step and sequence the accepted length, path and bonus token exactly,
+the final prefix lengths, the whole final cache bit for bit, and the bookkeeping."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from draft_tree_verification_build_amd.decode import DraftTreeDecoder
+from oracle import step as ostep
+from tests.gpu_common import need_gpu
+from workloads import make_step_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,seed,ov,steps", [
+    ("c1_tiny", 1, {}, 6),
+    ("c2_talon_llama3_8b", 2, {"P": 64, "V": 3000}, 3),
+    ("c3_goose_spine", 3, {"P": 64, "V": 2000}, 3),
+    ("c4_opt_llama2_7b", 4, {"P": 64, "V": 2000, "n": 64, "max_layers": 4}, 3),
+    ("c5_batched_llama2_70b", 5, {"S": 3, "P": 200, "V": 500}, 4),
+    ("c6_ragged_serving", 6, {"S": 4, "P": 300, "V": 400}, 4),
+])
+def test_decode_loop_matches_oracle(name, seed, ov, steps):
+    need_gpu()
+    inputs = lambda t: make_step_inputs(name, seed, t, planted=0.7, **ov)
+    dec = DraftTreeDecoder(inputs, steps, DEV)
+    log = dec.run()
+    ref = ostep.run_decode(inputs, steps)
+    S = dec.S
+    for t in range(steps):
+        for s in range(S):
+            r = ref["steps"][t][s]["verify"]
+            A = int(log[t]["A"][s])
+            assert A == r["A"], (t, s)
+            assert list(log[t]["path"][s, :A + 1]) == r["path"], (t, s)
+            assert int(log[t]["bonus"][s]) == r["bonus"], (t, s)
+    np.testing.assert_array_equal(dec.P_host, ref["P"])
+    k, v = _bits(dec.k), _bits(dec.v)
+    for s in range(S):
+        p = int(ref["P"][s])
+        np.testing.assert_array_equal(k[s, :, :p], ref["k"][s, :, :p])
+        np.testing.assert_array_equal(v[s, :, :p], ref["v"][s, :, :p])
+    books = dec.bookkeeping(1.0)
+    for s in range(S):
+        for key in ("E_A", "eta", "speedup"):
+            assert books[s][key] == pytest.approx(ref["bookkeeping"][s][key], rel=1e-12, abs=1e-12), key

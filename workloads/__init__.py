@@ -11,7 +11,8 @@ Every array is drawn from ``np.random.default_rng(SeedSequence([seed, stream, id
 so that any single row can be regenerated on its own. Normals are drawn in float32,
 scaled, and stored as bf16 (round to nearest even) for the bf16 configurations.
 """
-from .configs import CONFIGS, config_by_name, Workload, make_workload, bf16_bits_to_f32, f32_to_bf16_bits
+from .configs import (CONFIGS, config_by_name, Workload, make_workload, make_step_inputs, step_seed,
+                      bf16_bits_to_f32, f32_to_bf16_bits)
 
-__all__ = ["CONFIGS", "config_by_name", "Workload", "make_workload",
+__all__ = ["CONFIGS", "config_by_name", "Workload", "make_workload", "make_step_inputs", "step_seed",
            "bf16_bits_to_f32", "f32_to_bf16_bits"]

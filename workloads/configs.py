@@ -283,3 +283,24 @@ def make_workload(cfg: Config | str, seed: int, planted: float = 0.0, **override
         wl.u_res = np.stack([_rng(seed, ST_URES, s).integers(0, 2**32, size=N, dtype=np.uint64)
                              .astype(np.uint32) for s in range(S)])
     return wl
+
+
+def step_seed(seed: int, t: int) -> int:
+    """Seed of step t of a decoding loop started with ``seed`` (step 0 uses ``seed``)."""
+    return seed if t == 0 else seed * 100003 + t
+
+
+def make_step_inputs(cfg: Config | str, seed: int, t: int, planted: float = 0.0, **overrides) -> Workload:
+    """Inputs of step t of a synthetic decoding loop.
+
+    Step 0 is ``make_workload(cfg, seed)``: the prefix and the first tree. A later step's
+    cache is the loop's state, so its workload carries no prefix: its k and v hold only that
+    step's tree keys and values, at slots 0..N-1, which the loop writes after the current
+    prefix. Queries, logits, tree and uniforms are the step's own (seed ``step_seed``).
+    """
+    if t == 0:
+        return make_workload(cfg, seed, planted=planted, **overrides)
+    ov = dict(overrides)
+    ov["P"] = 0
+    ov["P_min"] = -1
+    return make_workload(cfg, step_seed(seed, t), planted=planted, **ov)
