@@ -295,16 +295,44 @@ def decode_loop(config: str, seed: int, steps: int, gamma: float) -> dict:
     import numpy as np
     import torch
     from draft_tree_verification_build_amd.decode import DraftTreeDecoder
-    from workloads import make_step_inputs
-    inputs = lambda t: make_step_inputs(config, seed, t)
+    from draft_tree_verification_build_amd import goose
+    from workloads import config_by_name, make_step_inputs
+    cfg = config_by_name(config)
+    adaptive = cfg.build == "spine"   # GOOSE: each step's topology from the spine acceptance so far
+    policy = goose.SpineTopology(cfg.N - 1) if adaptive else None
+    topo = {0: policy.plan()} if adaptive else {}
+
+    def inputs(t):
+        if not adaptive:
+            return make_step_inputs(config, seed, t)
+        L, w = topo[t]
+        return make_step_inputs(config, seed, t, n_spine=L, n_forks=len(w), spine_widths=tuple(w))
+
     dec = DraftTreeDecoder(inputs, steps, "cuda")
-    ups = [dec.upload(t) for t in range(steps)]
-    dec.step(0, ups[0])   # untimed: the first step allocates the workspaces
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(1, steps):
-        dec.step(t, ups[t])
-    wall = time.perf_counter() - t0
+
+    def observe(t, rec):
+        L = topo[t][0]
+        policy.observe([goose.spine_accepted(rec["path"][s][:int(rec["A"][s]) + 1], L) for s in range(dec.S)], L)
+        topo[t + 1] = policy.plan()
+
+    if adaptive:   # topologies depend on results: inputs are made and uploaded step by step, untimed
+        wall = 0.0
+        for t in range(steps):
+            up = dec.upload(t)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            rec = dec.step(t, up)
+            if t > 0:
+                wall += time.perf_counter() - t0
+            observe(t, rec)
+    else:
+        ups = [dec.upload(t) for t in range(steps)]
+        dec.step(0, ups[0])   # untimed: the first step allocates the workspaces
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(1, steps):
+            dec.step(t, ups[t])
+        wall = time.perf_counter() - t0
     books = dec.bookkeeping(gamma)
     timed = steps - 1
     emitted = float(sum(int(r["A"].sum()) + len(r["A"]) for r in dec.log[1:]))
@@ -312,7 +340,9 @@ def decode_loop(config: str, seed: int, steps: int, gamma: float) -> dict:
             "emitted_tokens_per_s": emitted / wall, "sequences": len(books),
             "E_A": float(np.mean([b["E_A"] for b in books])), "eta": float(np.mean([b["eta"] for b in books])),
             "gamma": gamma, "speedup": float(np.mean([b["speedup"] for b in books])),
-            "P_final": [int(p) for p in dec.P_host]}
+            "P_final": [int(p) for p in dec.P_host],
+            **({"topology": "GOOSE adaptive", "spine_lengths": [int(topo[t][0]) for t in range(steps)]}
+               if adaptive else {})}
 
 
 if __name__ == "__main__":

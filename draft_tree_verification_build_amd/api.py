@@ -60,13 +60,20 @@ class Workspace:
     def __init__(self, device):
         self.device = torch.device(device)
         self._bufs: dict = {}
+        self._sizes: dict = {}
 
-    def get(self, key, nbytes: int) -> torch.Tensor:
+    def get(self, key, nbytes: int, sizes=None) -> torch.Tensor:
+        """The buffer for one kind of call. The library keeps a workspace consistent from
+        call to call only while the call's sizes stay the same (the layout of its per-call
+        state follows them), so a buffer is zero-filled again when ``sizes`` change."""
         nbytes = max(int(nbytes), 256)
         buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
             buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
             self._bufs[key] = buf
+        elif sizes is not None and self._sizes.get(key) != sizes:
+            buf.zero_()
+        self._sizes[key] = sizes
         return buf
 
     def status(self, key, stream=None) -> int:
@@ -124,7 +131,7 @@ def row_stats(table: torch.Tensor, K: int, ws: Workspace, row_idx: torch.Tensor 
     topk = torch.empty((R, max(K, 1)), dtype=torch.int32, device=dev)
     lib = _lib.load()
     nb = lib.dtv_row_stats_ws_bytes(R, V, K, dt)
-    buf = ws.get("row_stats", nb)
+    buf = ws.get("row_stats", nb, (R, V, K, dt))
     _call("dtv_row_stats", _ptr(table), dt, R, V, _ptr(row_idx), K, _ptr(maxv), _ptr(amax), _ptr(lse),
           _ptr(topk) if K > 0 else None, buf.data_ptr(), buf.numel(), _stream(stream))
     return maxv, amax, lse, topk[:, :K]
@@ -132,7 +139,7 @@ def row_stats(table: torch.Tensor, K: int, ws: Workspace, row_idx: torch.Tensor 
 
 def tree_build_given(tree: Tree, ws: Workspace, stream=None) -> None:
     lib = _lib.load()
-    buf = ws.get("given", lib.dtv_tree_build_given_ws_bytes(tree.S))
+    buf = ws.get("given", lib.dtv_tree_build_given_ws_bytes(tree.S), (tree.S, tree.n_cap))
     _call("dtv_tree_build_given", tree.c, tree.S, buf.data_ptr(), buf.numel(), _stream(stream))
 
 
@@ -142,7 +149,7 @@ def tree_build_talon(tree: Tree, draft: torch.Tensor, B: int, K: int, alpha: flo
     S, R, V = draft.shape
     dt = _dtype_code(draft)
     lib = _lib.load()
-    buf = ws.get("talon", lib.dtv_tree_build_talon_ws_bytes(S, B, K, V, dt))
+    buf = ws.get("talon", lib.dtv_tree_build_talon_ws_bytes(S, B, K, V, dt), (S, B, K, R, V, dt, tree.n_cap))
     _call("dtv_tree_build_talon", tree.c, S, _ptr(draft), dt, R, V, B, K, float(alpha),
           buf.data_ptr(), buf.numel(), _stream(stream))
 
@@ -156,7 +163,8 @@ def tree_build_spine(tree: Tree, spine: torch.Tensor, widths, draft: torch.Tenso
     w = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
     dt = _dtype_code(draft)
     lib = _lib.load()
-    buf = ws.get("spine", lib.dtv_tree_build_spine_ws_bytes(S, int(w.size), int(w.max(initial=0)), V, dt))
+    buf = ws.get("spine", lib.dtv_tree_build_spine_ws_bytes(S, int(w.size), int(w.max(initial=0)), V, dt),
+                 (S, n_spine, tuple(int(x) for x in w), R, V, dt, tree.n_cap))
     _call("dtv_tree_build_spine", tree.c, S, _ptr(spine), n_spine, w.ctypes.data, int(w.size), _ptr(draft), dt,
           R, V, buf.data_ptr(), buf.numel(), _stream(stream))
 
@@ -167,7 +175,7 @@ def tree_build_opt(tree: Tree, draft: torch.Tensor, n: int, delta: float, max_la
     S, R, V = draft.shape
     dt = _dtype_code(draft)
     lib = _lib.load()
-    buf = ws.get("opt", lib.dtv_tree_build_opt_ws_bytes(S, n, V, max_layers, dt))
+    buf = ws.get("opt", lib.dtv_tree_build_opt_ws_bytes(S, n, V, max_layers, dt), (S, n, R, V, max_layers, dt, tree.n_cap))
     _call("dtv_tree_build_opt", tree.c, S, _ptr(draft), dt, R, V, int(n), float(delta), int(max_layers),
           buf.data_ptr(), buf.numel(), _stream(stream))
 
@@ -184,6 +192,8 @@ def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     lib = _lib.load()
+    # attention keeps no state between calls (its status word sits first, its partials are
+    # rewritten by every call), so its buffer is reused whatever the sizes
     buf = ws.get("attn", lib.dtv_tree_attn_ws_bytes(S, n_cap, Hq, Hkv, D, P_max, dt))
     _call("dtv_tree_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(P), P_cap, int(P_max), tree.c, S, Hq, Hkv,
           D, dt, float(scale), _ptr(o), buf.data_ptr(), buf.numel(), _stream(stream))
@@ -215,7 +225,7 @@ def tree_verify_greedy(tree: Tree, target: torch.Tensor, ws: Workspace, out=None
                torch.zeros((S, tree.n_cap), dtype=torch.int32, device=dev))
     path, plen, bonus, amax = out
     lib = _lib.load()
-    buf = ws.get("verify_greedy", lib.dtv_tree_verify_greedy_ws_bytes(S, tree.n_cap, V, dt))
+    buf = ws.get("verify_greedy", lib.dtv_tree_verify_greedy_ws_bytes(S, tree.n_cap, V, dt), (S, tree.n_cap, R, V, dt))
     if kv is None:
         _call("dtv_tree_verify_greedy", tree.c, S, _ptr(target), dt, R, V, _ptr(path), _ptr(plen),
               _ptr(bonus), _ptr(amax), buf.data_ptr(), buf.numel(), _stream(stream))
@@ -244,7 +254,7 @@ def tree_verify_sample(tree: Tree, target: torch.Tensor, draft: torch.Tensor, u_
                torch.zeros(S, dtype=torch.int32, device=dev))
     path, plen, bonus = out[:3]
     lib = _lib.load()
-    buf = ws.get("verify_sample", lib.dtv_tree_verify_sample_ws_bytes(S, tree.n_cap, V, dt))
+    buf = ws.get("verify_sample", lib.dtv_tree_verify_sample_ws_bytes(S, tree.n_cap, V, dt), (S, tree.n_cap, R, V, dt))
     if kv is None:
         _call("dtv_tree_verify_sample", tree.c, S, _ptr(target), _ptr(draft), dt, R, V, _ptr(u_acc),
               _ptr(u_res), _ptr(path), _ptr(plen), _ptr(bonus), buf.data_ptr(), buf.numel(), _stream(stream))

@@ -12,9 +12,12 @@
  *   and returns; nothing is synchronised.
  * - The caller owns every buffer. The library allocates nothing; calls that need scratch
  *   take a caller-provided workspace `ws` of `ws_bytes` bytes, sized by the matching
- *   `*_ws_bytes` query and zero-filled by the caller once after allocation (the
- *   library keeps it consistent afterwards). One workspace must not be used by two
- *   calls that may run at the same time.
+ *   `*_ws_bytes` query and zero-filled by the caller once after allocation. The library
+ *   keeps it consistent from one call to the next as long as the calls' sizes (batch,
+ *   capacity, rows, vocabulary, widths or budgets) stay the same: the layout of a call's
+ *   per-call state follows its sizes, so a workspace reused by a call with other sizes
+ *   must be zero-filled again first (dtv_tree_attn keeps no state and is exempt). One
+ *   workspace must not be used by two calls that may run at the same time.
  * - Argument errors are detected on the host before any launch and returned as a
  *   negative dtv_status; a launch failure returns DTV_EHIP. Errors found by a kernel
  *   (capacity exceeded on the device, a bounded wait that ran out) are recorded in the

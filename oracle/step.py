@@ -88,7 +88,7 @@ def decode_capacity(cfg, steps: int) -> int:
     return cfg.P + (steps + 1) * cfg.N
 
 
-def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None) -> dict:
+def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None, after_step=None) -> dict:
     """A decoding loop of ``steps`` draft-tree steps on one KV cache (scope row f2).
 
     ``inputs(t)`` gives step t's workload: step 0 with the prefix and the first tree in its
@@ -99,6 +99,8 @@ def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None) -> dic
     written). Returns the per-step results, the final cache and prefix lengths, and per
     sequence the bookkeeping of the TALON page, section 5.3, over the loop (N_v = steps
     verification passes, N_d = the draft layers the builds spent, L = sum of A_t + 1).
+    ``after_step(t, results)``, if given, sees every step's results before step t + 1's
+    inputs are asked for (an adaptive drafting policy observes the step there).
     """
     import dataclasses
     wl0 = inputs(0)
@@ -125,6 +127,8 @@ def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None) -> dic
             v[s] = res[s]["v"]
             P[s] = res[s]["P_new"]
         log.append(res)
+        if after_step is not None:
+            after_step(t, res)
     books = [bookkeeping.bookkeeping([log[t][s]["verify"]["A"] for t in range(steps)],
                                      sum(log[t][s]["tree"].layers for t in range(steps)), 1.0)
              for s in range(S)]

@@ -114,3 +114,19 @@ def test_bookkeeping_rejects_bad_counts(lib):
     out = np.zeros(4)
     assert lib.dtv_bookkeeping(a.ctypes.data, 2, 3, 0.1, out.ctypes.data) == -1
     assert lib.dtv_bookkeeping(a.ctypes.data, 0, 3, 0.1, out.ctypes.data) == -1
+
+
+def test_workspace_refills_when_call_sizes_change():
+    """A workspace keeps its per-call state only for calls of the same sizes; the binding
+    zero-fills a reused buffer when a call's sizes change (and not otherwise)."""
+    import torch
+    from draft_tree_verification_build_amd.api import Workspace
+    ws = Workspace("cpu")
+    b = ws.get("spine", 512, (1, 24, (4, 4)))
+    b.fill_(7)
+    assert int(ws.get("spine", 512, (1, 24, (4, 4)))[0]) == 7      # same sizes: kept
+    assert int(ws.get("spine", 256, (1, 30, (3, 2))).sum()) == 0    # other sizes: zero-filled
+    b = ws.get("attn", 512)
+    b.fill_(5)
+    assert int(ws.get("attn", 512)[0]) == 5                         # no sizes given: kept
+    assert isinstance(b, torch.Tensor)

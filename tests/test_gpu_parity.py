@@ -318,6 +318,9 @@ SPINE_CASES = [
     ("c3_goose_spine", 35, {"P": 16, "V": 5000, "n_spine": 10, "n_forks": 11, "fork_width": 9, "S": 2}),
     ("c3_goose_spine", 36, {"P": 16, "V": 900, "dtype": "f32", "n_spine": 5, "n_forks": 3, "fork_width": 2}),
     ("c3_goose_spine", 37, {"P": 16, "V": 64, "n_spine": 70, "n_forks": 71, "fork_width": 1}),
+    # widths falling linearly with depth, zero at the deepest forks (the adaptive topology)
+    ("c3_goose_spine", 38, {"P": 16, "V": 3000, "n_spine": 12, "n_forks": 12,
+                            "spine_widths": (5, 4, 3, 2, 1, 1, 0, 0, 0, 0, 0, 0)}),
 ]
 
 

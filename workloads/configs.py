@@ -79,6 +79,7 @@ class Config:
     target_sigma: float = 0.0
     noise_sigma: float = 0.0
     target_from: str = ""  # "draft+noise" | "independent" | "target->draft"
+    spine_widths: tuple = ()  # GOOSE: per-fork branch widths (forks 0..len-1), instead of n_forks x fork_width
     P_min: int = -1       # ragged batch (given trees): per-request prefix uniform in [P_min, P]
     B_min: int = -1       # ragged batch (given trees): per-request draft nodes uniform in [B_min, B]
 
@@ -90,6 +91,8 @@ class Config:
     def N(self) -> int:
         """Node capacity per sequence, root included."""
         if self.build == "spine":
+            if self.spine_widths:
+                return 1 + self.n_spine + int(sum(self.spine_widths))
             return 1 + self.n_spine + self.n_forks * self.fork_width
         if self.build == "opt":
             return 1 + self.n
@@ -275,7 +278,10 @@ def make_workload(cfg: Config | str, seed: int, planted: float = 0.0, **override
                     sp[kk] = int(sub[kk]) + (1 if sub[kk] >= best else 0)
             spines.append(sp)
         wl.spine = np.stack(spines)
-        wl.widths = np.full(cfg.n_forks, cfg.fork_width, dtype=np.int32)
+        if cfg.spine_widths:
+            wl.widths = np.asarray(cfg.spine_widths, dtype=np.int32)
+        else:
+            wl.widths = np.full(cfg.n_forks, cfg.fork_width, dtype=np.int32)
 
     if cfg.verify == "sample":
         wl.u_acc = np.stack([_rng(seed, ST_UACC, s).integers(0, 2**32, size=N, dtype=np.uint64)
