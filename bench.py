@@ -342,7 +342,10 @@ def decode_loop(config: str, seed: int, steps: int, gamma: float) -> dict:
             "gamma": gamma, "speedup": float(np.mean([b["speedup"] for b in books])),
             "P_final": [int(p) for p in dec.P_host],
             **({"topology": "GOOSE adaptive", "spine_lengths": [int(topo[t][0]) for t in range(steps)]}
-               if adaptive else {})}
+               if adaptive else {}),
+            **({"E_A_predicted": float(np.mean([r["E_A_predicted"].mean() for r in dec.log])),
+                "A_realised": float(np.mean([r["A"].mean() for r in dec.log]))}
+               if cfg.build == "opt" else {})}
 
 
 if __name__ == "__main__":

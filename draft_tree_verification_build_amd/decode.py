@@ -109,6 +109,12 @@ class DraftTreeDecoder:
             raise RuntimeError(f"step {t}: the cache cannot hold the step (P_new {P_new})")
         rec = {"A": (plen_h - 1).astype(np.int64), "path": res[4 * S:].reshape(S, -1), "bonus": bonus_h,
                "layers": res[3 * S:4 * S], "P": self.P_host.copy()}
+        if cfg.build == "opt":
+            # OPT-Tree's own forecast: the expected number of accepted draft tokens, the sum
+            # of the draft path probabilities exp(score) over the tree's non-root nodes
+            sc = tree.score.cpu().numpy()
+            nn = tree.n_nodes.cpu().numpy()
+            rec["E_A_predicted"] = np.array([float(np.exp(sc[s, 1:int(nn[s])]).sum()) for s in range(S)])
         self.P_host = P_new
         self.P.copy_(self.P_new)
         self.log.append(rec)

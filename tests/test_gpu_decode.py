@@ -52,6 +52,12 @@ def test_decode_loop_matches_oracle(name, seed, ov, steps):
         p = int(ref["P"][s])
         np.testing.assert_array_equal(k[s, :, :p], ref["k"][s, :, :p])
         np.testing.assert_array_equal(v[s, :, :p], ref["v"][s, :, :p])
+    if dec.cfg.build == "opt":   # OPT-Tree's forecast E[A] = sum of exp(score) over the tree
+        for t in range(steps):
+            for s in range(S):
+                tr = ref["steps"][t][s]["tree"]
+                want = float(np.exp(np.asarray(tr.score[1:tr.N], dtype=np.float64)).sum())
+                assert log[t]["E_A_predicted"][s] == pytest.approx(want, rel=1e-9)
     books = dec.bookkeeping(1.0)
     for s in range(S):
         for key in ("E_A", "eta", "speedup"):
