@@ -89,7 +89,7 @@ def decode_capacity(cfg, steps: int) -> int:
 
 
 def run_decode(inputs, steps: int, with_attention=False, attn_pairs=None, after_step=None) -> dict:
-    """A decoding loop of ``steps`` draft-tree steps on one KV cache (scope row f2).
+    """A decoding loop of ``steps`` draft-tree steps on one KV cache.
 
     ``inputs(t)`` gives step t's workload: step 0 with the prefix and the first tree in its
     cache; later steps with only their tree's keys and values (slots 0..N-1), which are
