@@ -130,3 +130,15 @@ def test_workspace_refills_when_call_sizes_change():
     b.fill_(5)
     assert int(ws.get("attn", 512)[0]) == 5                         # no sizes given: kept
     assert isinstance(b, torch.Tensor)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs the step on one GPU; asked for more it exits with status 2 and says so,
+    before touching the GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "4"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
