@@ -234,6 +234,10 @@ def main():
             e[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    st = step.ws_status()
+    if any(v != 0 for v in st.values()):
+        print(f"device status after the timed steps: {st}", file=sys.stderr)
+        return 1
     stage_ms = {name: float(np.mean([ev[k][j].elapsed_time(ev[k][j + 1]) for k in sampled]))
                 for j, name in enumerate(stages)}
 

@@ -63,6 +63,7 @@ SIGNATURES = {
     "dtv_tree_verify_sample_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_verify_sample": (c_int, [PTREE, c_i32, c_vp, c_vp, c_int, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_size, c_vp]),
+    "dtv_tree_verify_sample_plan": (c_int, [c_i32, c_i32, c_i32, c_int, c_i32, c_i32, c_vp]),
     "dtv_kv_compact": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                c_i32, c_int, c_vp]),
     "dtv_bookkeeping": (c_int, [c_vp, c_i32, c_i64, c_f64, c_vp]),

@@ -76,6 +76,19 @@ class Workspace:
         self._sizes[key] = sizes
         return buf
 
+    def status_words(self) -> dict:
+        """Device views of every buffer's status word (the first int32), for a caller that
+        reads them together with its own results in one copy instead of one call each."""
+        return {k: b[:4].view(torch.int32) for k, b in self._bufs.items()}
+
+    def check(self, stream=None) -> None:
+        """Raise DtvError for the first buffer whose device status is an error (the
+        buffer is zero-filled again, as its reuse requires)."""
+        for k in list(self._bufs):
+            rc = self.status(k, stream)
+            if rc != 0:
+                raise DtvError(f"device status of the {k!r} workspace", rc)
+
     def status(self, key, stream=None) -> int:
         """Synchronise and return the device status of one workspace; a workspace that
         reports an error is zero-filled again, as the library requires before its reuse."""

@@ -315,7 +315,6 @@ struct SampleLayout {
   double* pbuf;
   size_t bytes;
 };
-constexpr int kSampleMaxGroup = 32;   // workgroups per sequence in the walk
 SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   const int nch = nch_of(V, dtype);
   const size_t rows = static_cast<size_t>(S) * n_cap * 2;
@@ -325,15 +324,70 @@ SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
   L.st = c.take<dtv::ChunkStat>(rows * nch);
   L.lse = c.take<double>(rows);
   // one exchange slot per rejection (at most n_cap - 1) and one for the bonus draw
-  L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * 64);
+  L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * dtv::kXchStride);
   L.pbuf = c.take<double>(static_cast<size_t>(S) * 3 * V);   // two residuals and q per sequence
   L.bytes = c.off;
   return L;
 }
 
+// How the rejection-sampling walk divides its work, checked against every buffer it uses.
+// `resident` = walk workgroups the device holds at once; `vec` = rows walked in 16-byte
+// units. The walk of a sequence runs in G workgroups; workgroup gi owns units
+// [units*gi/G, units*(gi+1)/G), so no slice exceeds ceil(units/G) units. A slice of at most
+// kWalkSlice entries keeps its two residuals and q in shared memory (entries indexed from
+// the slice's first), a larger one in the sequence's 3*V workspace entries (indexed by
+// entry < V). Exchange slots: one per rejection (at most n_cap - 1) and one for the bonus
+// draw, each holding G sums and two values.
+struct WalkPlan {
+  int G, units, slice_units, slice_entries, in_lds, xch_slots;
+  long pbuf_entries;
+};
+int walk_plan(int S, int n_cap, int V, int dtype, int resident, int vec, WalkPlan* p) {
+  REQUIRE(S >= 1 && n_cap >= 1 && V >= 1 && dtype_ok(dtype), DTV_EINVAL, "S=%d n_cap=%d V=%d dtype=%d", S,
+          n_cap, V, dtype);
+  REQUIRE(n_cap <= dtv::kSampleMaxNodes, DTV_EUNSUPPORTED, "n_cap=%d exceeds the walk's %d slots", n_cap,
+          dtv::kSampleMaxNodes);
+  REQUIRE(resident >= S, DTV_EUNSUPPORTED, "S=%d sequences exceed the %d co-resident walk workgroups", S,
+          resident);
+  const int VEC = dtype == DTV_BF16 ? 8 : 4;
+  REQUIRE(!vec || V % VEC == 0, DTV_EINVAL, "16-byte units need V=%d to be a multiple of %d", V, VEC);
+  int G = (resident < 256 ? resident : 256) / S;
+  if (G > dtv::kSampleMaxGroup) G = dtv::kSampleMaxGroup;
+  if (G < 1) G = 1;
+  p->G = G;
+  p->units = vec ? V / VEC : V;
+  p->slice_units = (p->units + G - 1) / G;
+  p->slice_entries = p->slice_units * (vec ? VEC : 1);
+  p->in_lds = p->slice_entries <= dtv::kWalkSlice ? 1 : 0;
+  p->xch_slots = n_cap + 1;
+  p->pbuf_entries = 3L * V;
+  // the bounds the kernel relies on
+  REQUIRE(G + 2 <= dtv::kXchStride, DTV_EUNSUPPORTED, "G=%d exceeds an exchange slot", G);
+  REQUIRE(static_cast<long>(p->units) * (vec ? VEC : 1) <= V, DTV_EUNSUPPORTED, "units exceed the row");
+  REQUIRE(p->in_lds || static_cast<long>(p->slice_entries) <= V, DTV_EUNSUPPORTED,
+          "a slice of %d entries exceeds the %d-entry workspace rows", p->slice_entries, V);
+  return DTV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dtv_tree_verify_sample_plan(int32_t S, int32_t n_cap, int32_t V, int dtype, int32_t resident_blocks,
+                                int32_t vec, int64_t* plan_h) {
+  REQUIRE(plan_h != nullptr, DTV_EINVAL, "plan_h is NULL");
+  WalkPlan p;
+  const int rc = walk_plan(S, n_cap, V, dtype, resident_blocks, vec, &p);
+  if (rc) return rc;
+  plan_h[0] = p.G;
+  plan_h[1] = p.units;
+  plan_h[2] = p.slice_units;
+  plan_h[3] = p.slice_entries;
+  plan_h[4] = p.in_lds;
+  plan_h[5] = p.xch_slots;
+  plan_h[6] = p.pbuf_entries;
+  return DTV_OK;
+}
 
 const char* dtv_status_str(int status) {
   switch (status) {
@@ -368,6 +422,9 @@ int dtv_ws_status(const void* ws, void* stream) {
     case dtv::kErrCapacity: return fail(DTV_ECAPACITY, "a kernel ran out of capacity");
     case dtv::kErrTimeout: return fail(DTV_EDEVICE, "a bounded grid-wide wait timed out");
     case dtv::kErrBadTree: return fail(DTV_EDEVICE, "a parent is not an earlier slot");
+    case dtv::kErrBadRow:
+      return fail(DTV_EDEVICE, "a node's row lies outside the logit table (0 <= row < R), its token outside "
+                               "the vocabulary (0 <= token < V) or its depth outside the tree");
     default: return fail(DTV_EDEVICE, "device error %d", err);
   }
 }
@@ -805,11 +862,15 @@ static int verify_sample_impl(const dtv_tree* tree, int32_t S, const void* targe
   // the walk's groups must all be resident at once: about one workgroup per compute unit
   // in total (far below what the device holds), at most kSampleMaxGroup per sequence
   const int max_blocks = dtv::sample_walk_max_blocks(dtype == DTV_BF16 ? 1 : 0);
-  REQUIRE(max_blocks >= S, DTV_EUNSUPPORTED, "S=%d sequences exceed the %d co-resident walk workgroups",
-          S, max_blocks);
-  int G = (max_blocks < 256 ? max_blocks : 256) / S;
-  if (G > kSampleMaxGroup) G = kSampleMaxGroup;
-  a.G = G < 1 ? 1 : G;
+  REQUIRE(max_blocks >= 1, DTV_EHIP, "occupancy query failed");
+  const int VEC = dtype == DTV_BF16 ? 8 : 4;
+  const int vec = (V % VEC == 0) &&
+                  ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft)) & 15u) == 0;
+  WalkPlan plan;
+  rc = walk_plan(S, tree->n_cap, V, dtype, max_blocks, vec, &plan);
+  if (rc) return rc;
+  a.G = plan.G;
+  a.vec = vec;
   const int lse_slots = dtv::sample_lse_max_blocks(dtype == DTV_BF16 ? 1 : 0);
   REQUIRE(lse_slots >= 1, DTV_EUNSUPPORTED, "occupancy query failed");
   const long items = static_cast<long>(S) * tree->n_cap * 2 * a.nch;

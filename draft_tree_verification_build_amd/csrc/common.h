@@ -209,6 +209,8 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 
-enum : int { kErrNone = 0, kErrCapacity = 1, kErrTimeout = 2, kErrBadTree = 3 };
+// kErrBadRow: a node's row lies outside its logit table (row < 0 or row >= R), or a drafted
+// token outside the vocabulary where a kernel would read the logit at that token.
+enum : int { kErrNone = 0, kErrCapacity = 1, kErrTimeout = 2, kErrBadTree = 3, kErrBadRow = 4 };
 
 }  // namespace dtv

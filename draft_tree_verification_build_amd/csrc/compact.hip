@@ -58,9 +58,11 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(CompactArgs a) {
   if (which == 0 && kv == 0 && threadIdx.x == 0 && a.P_new != a.P) a.P_new[s] = P + L;
 }
 
+// P_new aliasing P: the new length is added after the copies. compact_kernel marks a
+// sequence it refused with P[s] = -1 (a negative P is refused too), and that mark stays.
 __global__ void compact_update_p(const int* path_len, int* P, int S) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < S) P[s] += path_len[s];
+  if (s < S && P[s] >= 0) P[s] += path_len[s];
 }
 
 int launch_compact(const CompactArgs& a, hipStream_t st) {

@@ -177,6 +177,13 @@ struct VerifyArgs {
   KvCompactView kvc;
 };
 
+// Sizes of the rejection-sampling walk, shared by the host plan (api.hip) and the kernels.
+constexpr int kSampleMaxNodes = 1024;   // tree slots the walk keeps in shared memory
+constexpr int kSampleMaxGroup = 32;     // workgroups per sequence in the walk
+constexpr int kXchStride = 64;          // doubles per exchange slot (G slice sums + 2 values)
+constexpr int kWalkSlice = 4096;        // slice entries kept in shared memory (else the workspace)
+static_assert(kSampleMaxGroup + 2 <= kXchStride, "an exchange slot holds G sums and two values");
+
 struct SampleArgs {
   TreeArgs tree;
   const void* target;
@@ -193,6 +200,7 @@ struct SampleArgs {
   int S;
   int lse_grid;              // workgroups of the chunk-statistics kernel
   int G;                     // workgroups per sequence in the walk
+  int vec;                   // 1: rows are walked in 16-byte units (aligned, V a multiple of 8 / 4)
   int max_pass;              // exchange slots per sequence (rejections + 1 bonus draw)
   double* xch;               // [S][max_pass][64] walk exchange slots (emptied by phase 1)
   double* pbuf;              // [S][3][V] residual distributions and q (slices too large for LDS)

@@ -92,7 +92,14 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
     return;
   }
   unsigned long long* slots = a.cbest + tb * nch;   // [node][chunk]
-  if (i < N) {
+  if (i < N && (r_slot < 0 || r_slot >= a.R)) {
+    // a row outside the table is never read: the chunk reports the smallest non-empty key,
+    // so the walker's polls end, and the walker refuses the tree
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrBadRow);
+      st_cc(&slots[static_cast<size_t>(i) * nch + c], 1ull);
+    }
+  } else if (i < N) {
     const int r = r_slot;
     const char* row = static_cast<const char*>(a.target) +
                       (static_cast<size_t>(s) * a.R + r) * static_cast<size_t>(a.V) * Rw::ESIZE;
@@ -125,11 +132,17 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   //      the N * nch chunk slots (node-major), up to 8 at once, until all have reported,
   //      folds them into its node's maximum in shared memory and clears them for the next
   //      call.
+  if (threadIdx.x == 0) sm.flag = 0;
+  __syncthreads();
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.best[v] = 0ull;
     sm.tok[v] = a.tree.token[tb + v];
     sm.par[v] = static_cast<short>(v == 0 ? -1 : a.tree.parent[tb + v]);
     sm.dep[v] = static_cast<short>(a.tree.depth[tb + v]);
+    const int r = a.tree.row[tb + v];
+    const int dv = sm.dep[v];
+    // the path is written at the nodes' depths: they must lie inside the tree
+    if (r < 0 || r >= a.R || dv < 0 || dv >= N || (v == 0 && dv != 0)) sm.flag = 1;
   }
   __syncthreads();
   int ok = 1;
@@ -162,6 +175,15 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
     }
   }
   __syncthreads();
+  if (sm.flag) {   // a row outside the table or a depth outside the tree: no path
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrBadRow);
+      a.path_len[s] = 0;
+      a.bonus[s] = -1;
+      if (a.kvc.k != nullptr) a.kvc.P_new[s] = -1;
+    }
+    return;
+  }
   for (int v = threadIdx.x; v < N; v += kBlock) {
     const int am = sort_key_index(sm.best[v]);
     sm.a[v] = am;
@@ -222,8 +244,6 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
 // a slice of the vocabulary: a first try needs only the two row values at the child's
 // token; each rejection costs one residual pass over the slices (kept in shared memory
 // when they fit) and one exchange of slice sums; the bonus draw is one prefix-sum pass.
-
-constexpr int kSampleMaxNodes = 1024;
 
 struct SampleSmem {
   RowSmem rs;
@@ -337,8 +357,6 @@ struct WalkDist {
 // and the polls, with no counter and no fence: the values are the signal. Every
 // workgroup then adds the sums in workgroup order, so all of them see identical totals
 // and take identical decisions.
-constexpr int kXchStride = 64;   // doubles per exchange slot (G <= 32 sums + 2 values)
-constexpr int kWalkSlice = 4096; // entries of a workgroup's slice kept in shared memory
 constexpr unsigned long long kSlotEmpty = 0x7FF8DEAD00000000ull;
 constexpr long kSpinLimit = 2000000;    // polls (each a memory round trip) before a timeout
 
@@ -561,7 +579,10 @@ __global__ __launch_bounds__(kBlock) void sample_lse_kernel(SampleArgs a) {
     const int b2 = min(it, items - 1) / nch;
     const int node = b2 >> 1, s = node / cap, i = node % cap;
     if (it < items && m.n > cap && threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
-    real = it < items && i < m.n && m.n <= cap && m.r >= 0 && m.r < a.R;
+    const bool in_tree = it < items && i < m.n && m.n <= cap;
+    real = in_tree && m.r >= 0 && m.r < a.R;
+    // a row outside the table is never read; the walk refuses the tree
+    if (in_tree && !real && threadIdx.x == 0) atomicExch(&a.hdr->err, kErrBadRow);
     return static_cast<const char*>((b2 & 1) ? a.draft : a.target) +
            (static_cast<size_t>(s) * a.R + (real ? m.r : 0)) * row_bytes;
   };
@@ -661,6 +682,8 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   const size_t tb = static_cast<size_t>(s) * cap;
   const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
   const bool merge_here = 2 * cap <= kBlock;   // else sample_lse_merge_kernel ran
+  if (threadIdx.x == 0) sm.flag = 0;
+  __syncthreads();
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.par[v] = static_cast<short>(a.tree.parent[tb + v]);
     sm.tok[v] = a.tree.token[tb + v];
@@ -668,8 +691,21 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       sm.lset[v] = a.lse[(tb + v) * 2 + 0];
       sm.lsed[v] = a.lse[(tb + v) * 2 + 1];
     }
+    // rows are read at every node the walk may visit, tokens at every child tried: both
+    // must lie inside the tables
+    const int r = a.tree.row[tb + v];
+    if (r < 0 || r >= a.R || (v > 0 && (sm.tok[v] < 0 || sm.tok[v] >= a.V))) sm.flag = 1;
   }
   __syncthreads();   // also publishes the exp table
+  if (sm.flag) {   // every workgroup of the group sees the same tree and leaves here
+    if (blockIdx.x % a.G == 0 && threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrBadRow);
+      a.path_len[s] = 0;
+      a.bonus[s] = -1;
+      if (a.kvc.k != nullptr) a.kvc.P_new[s] = -1;
+    }
+    return;
+  }
   if (merge_here) {
     const int q = threadIdx.x;
     if (q < 2 * N) {
@@ -678,8 +714,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     }
     __syncthreads();
   }
-  const bool vec = (a.V % Rw::VEC) == 0 && (row_bytes % 16) == 0 &&
-                   ((reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.draft)) & 15u) == 0;
+  const bool vec = a.vec != 0;   // decided by the host plan (rows aligned, V a multiple of VEC)
   WalkGroup grp;
   grp.gi = blockIdx.x % a.G;
   grp.G = a.G;

@@ -100,9 +100,14 @@ class DraftTreeDecoder:
         else:
             path, plen, bonus = api.tree_verify_sample(tree, d["target"], d["draft"], d["u_acc"], d["u_res"],
                                                        ws, stream=stream, kv=kv)[:3]
-        # the step's results in one read: path length, bonus, new prefix, layers, path
+        # the step's results in one read: path length, bonus, new prefix, layers, path and the
+        # status word of every workspace (a kernel that refused or timed out records it there)
         S = self.S
-        res = torch.cat([plen, bonus, self.P_new, tree.layers, path.reshape(-1)]).cpu().numpy()
+        words = ws.status_words()
+        res = torch.cat([plen, bonus, self.P_new, tree.layers, path.reshape(-1), *words.values()]).cpu().numpy()
+        if (res[len(res) - len(words):] != 0).any():
+            ws.check(stream)   # raises with the library's message
+        res = res[:len(res) - len(words)]
         plen_h, bonus_h = res[:S], res[S:2 * S]
         P_new = res[2 * S:3 * S].astype(np.int64)
         if (P_new < 0).any():

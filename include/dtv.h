@@ -198,7 +198,10 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
  * the accepted node v* is the deepest node whose whole root path matches (lowest slot
  * among equals). Outputs per sequence: path[s][0..A] = slots root .. v* (by depth),
  * path_len[s] = A + 1, bonus[s] = a[v*]; optional argmax_out[s][n_cap] = a.
- * `target` is `[S][R][V]`.
+ * `target` is `[S][R][V]` with R > row[v] for every node (for an OPT-Tree tree, whose rows
+ * reach max_layers * n, R >= 1 + max_layers * n). A node whose row lies outside [0, R), or
+ * whose depth lies outside [0, n_nodes), is never read: the sequence gets path_len = 0 and
+ * bonus = -1, and dtv_ws_status reports DTV_EDEVICE.
  */
 size_t dtv_tree_verify_greedy_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype);
 int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, int dtype,
@@ -217,6 +220,11 @@ int dtv_tree_verify_greedy(const dtv_tree* tree, int32_t S, const void* target, 
  * leaf, the bonus token is the smallest k with sum_{j<=k} p_j > u * sum p (ascending
  * float64 prefix sums, u from u_res[s][v]). Outputs as dtv_tree_verify_greedy. Decisions
  * are taken in float64; the result depends only on the inputs and the uniforms.
+ * Both tables need R > row[v] for every node (OPT-Tree trees: R >= 1 + max_layers * n), and
+ * every drafted token must lie in [0, V). A tree that breaks either is never read past
+ * its tables: the sequence gets path_len = 0 and bonus = -1, and dtv_ws_status reports
+ * DTV_EDEVICE. Sizes the walk cannot hold (more sequences than walk workgroups fit on the
+ * device at once, more than 1024 slots) are refused with DTV_EUNSUPPORTED before launch.
  */
 size_t dtv_tree_verify_sample_ws_bytes(int32_t S, int32_t n_cap, int32_t V, int dtype);
 int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, const void* draft,
@@ -224,12 +232,28 @@ int dtv_tree_verify_sample(const dtv_tree* tree, int32_t S, const void* target, 
                            int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* How dtv_tree_verify_sample divides the walk of each sequence, for S sequences of n_cap
+ * slots, vocabulary V and dtype, when the device holds `resident_blocks` walk workgroups at
+ * once and rows are walked in 16-byte units (`vec` = 1: rows 16-byte aligned and V a
+ * multiple of 8 bf16 / 4 fp32 values) or entry by entry (`vec` = 0). Host only, no device
+ * call. Writes plan_h[0..7) = { G workgroups per sequence, units per row, units of the
+ * largest slice, entries of the largest slice, 1 if a slice fits the workgroup's shared
+ * memory (else it uses the workspace), exchange slots per sequence, workspace entries of
+ * residuals and q per sequence }. Returns the status the verification would return for
+ * these sizes (DTV_EUNSUPPORTED when S > resident_blocks or n_cap > 1024).
+ */
+int dtv_tree_verify_sample_plan(int32_t S, int32_t n_cap, int32_t V, int dtype, int32_t resident_blocks,
+                                int32_t vec, int64_t* plan_h);
+
 /* ---------------------------------------------------------------------------------
  * KV compaction (concept page, "The protocol", step 4: append the accepted tokens).
  *
  * For every sequence and KV head: cache[P + k] <- cache[P + path[k]] for k < path_len,
  * for both k and v (in place, all reads before any write), and P_new[s] = P[s] +
- * path_len[s]. P_new may alias P. Layout as in dtv_tree_attn; path `[S][n_cap]`.
+ * path_len[s]. P_new may alias P. Layout as in dtv_tree_attn; path `[S][n_cap]`. A
+ * sequence whose path_len lies outside 1..n_cap, or whose P[s] is negative or leaves fewer
+ * than n_cap rows of the cache, is left untouched and gets P_new[s] = -1 (also when P_new
+ * aliases P).
  */
 int dtv_kv_compact(void* k, void* v, const int32_t* P, int32_t* P_new, int32_t P_cap,
                    const int32_t* path, const int32_t* path_len, int32_t n_cap, int32_t S,

@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mask import ancestors
+from .mask import ancestor_matrix, ancestors
 
 
 def node_head(q_ih: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray, P: int,
@@ -53,4 +53,35 @@ def tree_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: int, parent,
         if i not in anc:
             anc[i] = ancestors(parent, i)
         o[i, h] = node_head(q[i, h], k[h // g], v[h // g], P, anc[i], scale)
+    return o
+
+
+def tree_attention_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: int, parent,
+                         scale: float | None = None) -> np.ndarray:
+    """All outputs of one sequence, the same definition with one matrix product per KV head.
+
+    For KV head kv the query rows of its g heads meet every key of the prefix and of the
+    tree block at once: scores = q k^T * scale, tree keys that are not an ancestor-or-self
+    of the query's node are excluded (their weight is exactly 0), then a softmax over each
+    row and a product with v. q [N][Hq][D], k and v [Hkv][P_cap][D], float64; returns
+    o [N][Hq][D]. This is the per-row definition of ``tree_attention`` evaluated for all
+    rows at once, for full-size checks that the per-row loop would take minutes over.
+    """
+    N, Hq, D = q.shape
+    Hkv = k.shape[0]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    visible = np.ones((N, P + N), dtype=bool)
+    visible[:, P:] = ancestor_matrix(parent)          # row i: prefix, then anc(i) in the tree block
+    o = np.empty((N, Hq, D))
+    for kv in range(Hkv):
+        qg = q[:, kv * g:(kv + 1) * g, :].reshape(N * g, D)   # row n*g + h' = (node n, head kv*g + h')
+        s = (qg @ k[kv, :P + N].T) * scale                       # [N*g][P+N]
+        s = np.where(np.repeat(visible, g, axis=0), s, -np.inf)
+        w = np.exp(s - np.max(s, axis=1, keepdims=True))
+        w = w / np.sum(w, axis=1, keepdims=True)
+        o[:, kv * g:(kv + 1) * g, :] = (w @ v[kv, :P + N]).reshape(N, g, D)
     return o

@@ -142,3 +142,50 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _plan(lib, S, n_cap, V, dtype, resident, vec):
+    out = np.zeros(7, dtype=np.int64)
+    rc = lib.dtv_tree_verify_sample_plan(S, n_cap, V, dtype, resident, vec, out.ctypes.data)
+    return rc, out
+
+
+@pytest.mark.parametrize("S,n_cap,V,dtype,resident,vec", [
+    (8, 65, 32000, 1, 256, 1), (1, 513, 32000, 1, 256, 1), (16, 65, 32000, 1, 256, 1),
+    (3, 201, 5000, 1, 256, 1), (4, 41, 64, 1, 256, 1), (2, 65, 1000, 0, 256, 1),
+    (1, 17, 1000, 0, 256, 1), (8, 65, 32001, 1, 256, 0), (1, 65, 128256, 1, 256, 1),
+    (1, 65, 128256, 1, 256, 0), (1, 1024, 4194304, 1, 64, 1), (256, 65, 32000, 1, 256, 1),
+    (5, 65, 300, 1, 7, 0), (1, 3, 1, 0, 1, 0),
+])
+def test_sample_walk_plan_fits_its_buffers(lib, S, n_cap, V, dtype, resident, vec):
+    """The walk's division of each vocabulary row over G workgroups stays inside the buffers
+    the kernel indexes: G*S workgroups co-resident, slices inside shared memory or inside the
+    3*V workspace entries, exchange slots for every rejection plus the bonus draw, and G sums
+    plus two values per exchange slot."""
+    rc, p = _plan(lib, S, n_cap, V, dtype, resident, vec)
+    assert rc == 0, lib.dtv_last_error()
+    G, units, su, se, in_lds, xch, pbuf = (int(x) for x in p)
+    VEC = 8 if dtype == 1 else 4
+    assert 1 <= G <= 32 and G * S <= resident and G + 2 <= 64
+    assert units == (V // VEC if vec else V)
+    # the kernel's slices [units*gi/G, units*(gi+1)/G): none larger than the plan's
+    sizes = [units * (g + 1) // G - units * g // G for g in range(G)]
+    assert sum(sizes) == units and max(sizes) <= su
+    assert se == su * (VEC if vec else 1)
+    assert in_lds == (se <= 4096)
+    if not in_lds:
+        assert se <= V and pbuf == 3 * V     # entries index the workspace rows, j < V
+    assert xch >= n_cap                      # at most n_cap - 1 rejections and one bonus draw
+
+
+@pytest.mark.parametrize("S,n_cap,V,dtype,resident,vec,code", [
+    (9, 65, 32000, 1, 8, 1, -2),      # more sequences than co-resident walk workgroups
+    (1, 1025, 32000, 1, 256, 1, -2),  # more slots than the walk keeps in shared memory
+    (1, 65, 32001, 1, 256, 1, -1),    # 16-byte units need V a multiple of 8 (bf16)
+    (1, 65, 1001, 0, 256, 1, -1),     # ... and of 4 (fp32)
+    (0, 65, 32000, 1, 256, 1, -1),
+    (1, 65, 32000, 5, 256, 1, -1),
+])
+def test_sample_walk_plan_refusals(lib, S, n_cap, V, dtype, resident, vec, code):
+    rc, _ = _plan(lib, S, n_cap, V, dtype, resident, vec)
+    assert rc == code, (rc, lib.dtv_last_error())

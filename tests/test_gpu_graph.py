@@ -71,3 +71,49 @@ def test_graph_replay_matches_eager(name, seed, ov):
         step.run()        # eager work between replays
         _assert_same(_outputs(step), want, f"eager step after replay {r}")
     assert all(v == 0 for v in step.ws_status().values())
+
+
+def test_graph_replay_matches_oracle_c2():
+    """The headline step (TALON tree on the Llama-3-8B shape) captured as a HIP graph: every
+    replay against the float64 oracle directly, not only against the eager step: tree arrays
+    and masks, path and bonus, new prefix length and compacted cache bit-exact, attention
+    outputs (every row) within 2e-2."""
+    need_gpu()
+    import numpy as np
+    from oracle import step as ostep
+    from tests.gpu_common import assert_tree_equal, tree_to_numpy
+    from tests.test_gpu_parity import attn_compare, attn_reference
+    wl = make_workload("c2_talon_llama3_8b", 2)
+    step = DraftTreeStep(wl, DEV)
+    k0, v0 = step.k.clone(), step.v.clone()
+    step.run()            # warm: workspaces allocated outside the capture
+    assert all(v == 0 for v in step.ws_status().values())
+    res = ostep.run_step(wl, with_attention=False)[0]
+    graph = torch.cuda.CUDAGraph()
+    step.k.copy_(k0)
+    step.v.copy_(v0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step.run()
+    refs = None
+    for r in range(3):
+        step.k.copy_(k0)
+        step.v.copy_(v0)
+        step.o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(v == 0 for v in step.ws_status().values())
+        g = tree_to_numpy(step.tree)
+        assert_tree_equal(g, 0, res["tree"], step.tree.words)
+        if refs is None:
+            refs = attn_reference(wl, g)
+        attn_compare(step.o.float().cpu().numpy(), refs, 2e-2, f"c2 graph replay {r}")
+        path, plen, bonus, _ = [t.cpu() for t in step.verify_out]
+        A = int(plen[0]) - 1
+        assert A == res["verify"]["A"] and list(path[0, :A + 1].numpy()) == res["verify"]["path"]
+        assert int(bonus[0]) == res["verify"]["bonus"]
+        assert int(step.P_new[0]) == res["P_new"]
+        kk = step.k.view(torch.int16).cpu().numpy().view(np.uint16)
+        vv = step.v.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(kk[0], res["k"])
+        np.testing.assert_array_equal(vv[0], res["v"])

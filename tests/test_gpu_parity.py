@@ -145,7 +145,38 @@ def test_talon_build(name, seed, ov):
         np.testing.assert_array_equal(g[key], g2[key])
 
 
-def _attn_check(wl, pairs_per_seq=None, tol=2e-2):
+def attn_reference(wl, g):
+    """The float64 oracle's outputs of every sequence, all rows (one product per KV head)."""
+    cfg = wl.cfg
+    refs = []
+    for s in range(cfg.S):
+        N = int(g["n_nodes"][s])
+        q = orows.decode(wl.q[s], cfg.dtype).reshape(wl.q.shape[1:])
+        k = orows.decode(wl.k[s], cfg.dtype).reshape(wl.k.shape[1:])
+        v = orows.decode(wl.v[s], cfg.dtype).reshape(wl.v.shape[1:])
+        refs.append(oattn.tree_attention_dense(q[:N], k, v, int(wl.P[s]), list(g["parent"][s, :N])))
+    return refs
+
+
+def attn_compare(o, refs, tol, label):
+    """Every (sequence, node, head) row of the GPU output against the oracle; returns the
+    worst absolute error and prints it with the number of rows compared."""
+    worst, rows = 0.0, 0
+    for s, ref in enumerate(refs):
+        N = ref.shape[0]
+        err = np.abs(o[s, :N].astype(np.float64) - ref)
+        assert np.isfinite(err).all(), (label, s)
+        e = float(err.max())
+        if e > worst:
+            worst = e
+        rows += N * ref.shape[1]
+    print(f"attention parity {label}: worst max-abs error {worst:.3e} over {rows} rows")
+    assert worst <= tol, (label, worst)
+    return worst
+
+
+def _attn_check(wl, tol=2e-2, label=None):
+    """Build the tree and run tree attention on the GPU, then compare every output row."""
     cfg = wl.cfg
     step = DraftTreeStep(wl, DEV)
     step.build()
@@ -153,25 +184,7 @@ def _attn_check(wl, pairs_per_seq=None, tol=2e-2):
     torch.cuda.synchronize()
     o = step.o.float().cpu().numpy()
     g = tree_to_numpy(step.tree)
-    rng = np.random.default_rng(99)
-    worst = 0.0
-    for s in range(cfg.S):
-        N = int(g["n_nodes"][s])
-        parent = list(g["parent"][s, :N])
-        q = orows.decode(wl.q[s], cfg.dtype).reshape(wl.q.shape[1:])
-        k = orows.decode(wl.k[s], cfg.dtype).reshape(wl.k.shape[1:])
-        v = orows.decode(wl.v[s], cfg.dtype).reshape(wl.v.shape[1:])
-        pairs = None
-        if pairs_per_seq is not None:
-            pairs = [(int(rng.integers(0, N)), int(rng.integers(0, cfg.Hq))) for _ in range(pairs_per_seq)]
-            pairs += [(N - 1, cfg.Hq - 1), (0, 0)]
-        ref = oattn.tree_attention(q[:N], k, v, int(wl.P[s]), parent, pairs=pairs)
-        sel = pairs if pairs is not None else [(i, h) for i in range(N) for h in range(cfg.Hq)]
-        for i, h in sel:
-            err = float(np.max(np.abs(o[s, i, h] - ref[i, h])))
-            worst = max(worst, err)
-    assert worst <= tol, worst
-    return worst
+    return attn_compare(o, attn_reference(wl, g), tol, label or cfg.name)
 
 
 def test_attention_c1_fp32():
@@ -191,37 +204,39 @@ def test_attention_edges(P, B):
     _attn_check(make_workload("c5_batched_llama2_70b", 21, S=2, P=P, B=B, V=64, max_depth=B))
 
 
-@pytest.mark.parametrize("name,ov,pairs", [
-    ("c5_batched_llama2_70b", {"V": 64}, 24),
-    ("c5_batched_llama2_70b", {"V": 64, "Hq": 8, "Hkv": 8, "D": 64}, 40),
-    # 512 packed rows per KV head at head_dim 64 (two-group-per-wave kernel, D=64)
-    ("c5_batched_llama2_70b", {"V": 64, "S": 2, "Hq": 32, "Hkv": 4, "D": 64, "B": 63}, 40),
+@pytest.mark.parametrize("name,ov", [
+    ("c5_batched_llama2_70b", {"V": 64}),
+    ("c5_batched_llama2_70b", {"V": 64, "Hq": 8, "Hkv": 8, "D": 64}),
+    # 512 packed rows per KV head at head_dim 64
+    ("c5_batched_llama2_70b", {"V": 64, "S": 2, "Hq": 32, "Hkv": 4, "D": 64, "B": 63}),
     # 328 rows = 11 row groups over two tiles (5 + 6): a wave with a single group
-    ("c5_batched_llama2_70b", {"V": 64, "S": 3, "P": 1000, "B": 40}, 40),
+    ("c5_batched_llama2_70b", {"V": 64, "S": 3, "P": 1000, "B": 40}),
 ])
-def test_attention_large_sampled(name, ov, pairs):
+def test_attention_large_full(name, ov):
+    """Full-size launches (c5: 8 sequences x 8 KV heads, 17 row groups of 32 per KV head,
+    three key splits of the 8257-key cache and their merge): every output row."""
     need_gpu()
-    _attn_check(make_workload(name, 5, **ov), pairs_per_seq=pairs)
+    _attn_check(make_workload(name, 5, **ov), label=f"{name} {ov}")
 
 
-@pytest.mark.parametrize("seed,ov,pairs", [
-    (6, {"V": 64}, 24),
-    (62, {"S": 6, "P": 300, "P_min": 0, "B_min": 0, "V": 64}, None),
+@pytest.mark.parametrize("seed,ov", [
+    (6, {"V": 64}),
+    (62, {"S": 6, "P": 300, "P_min": 0, "B_min": 0, "V": 64}),
 ])
-def test_attention_ragged_serving(seed, ov, pairs):
-    """Ragged batch: per-request prefix lengths and tree sizes in one launch."""
+def test_attention_ragged_serving(seed, ov):
+    """Ragged batch: per-request prefix lengths and tree sizes in one launch (every row)."""
     need_gpu()
-    _attn_check(make_workload("c6_ragged_serving", seed, **ov), pairs_per_seq=pairs)
+    _attn_check(make_workload("c6_ragged_serving", seed, **ov), label=f"c6_ragged_serving {ov}")
 
 
 def test_attention_ragged_prefix_large():
     """A large launch (8 sequences, 8257-key cache, several key splits) with per-sequence
     prefix lengths that leave a split empty or one or two blocks long, or end one key into a
-    block."""
+    block (every row)."""
     need_gpu()
     wl = make_workload("c5_batched_llama2_70b", 23, V=64)
     wl.P = np.array([8192, 0, 1, 4160, 4161, 4100, 8000, 63], dtype=np.int32)
-    _attn_check(wl, pairs_per_seq=24)
+    _attn_check(wl, label="c5 ragged prefixes")
 
 
 def _upload_oracle_tree(otree, S=1):
@@ -440,9 +455,9 @@ def test_step_end_to_end_all_sequences(name, seed, ov):
         np.testing.assert_array_equal(vv[s], r["v"])
 
 
-def test_attention_c3_sampled():
+def test_attention_c3_full():
     need_gpu()
-    _attn_check(make_workload("c3_goose_spine", 3), pairs_per_seq=40)
+    _attn_check(make_workload("c3_goose_spine", 3, V=64))
 
 
 OPT_CASES = [
@@ -476,9 +491,10 @@ def test_opt_build(name, seed, ov):
             assert int(g["layers"][s]) == ot.layers
 
 
-def test_attention_c4_sampled():
+def test_attention_c4_full():
+    """The 512-node OPT-Tree tree (9 mask words, 32 KV heads x 17 row groups): every row."""
     need_gpu()
-    _attn_check(make_workload("c4_opt_llama2_7b", 4), pairs_per_seq=40)
+    _attn_check(make_workload("c4_opt_llama2_7b", 4))
 
 
 def test_step_end_to_end_c4():
@@ -544,3 +560,89 @@ def test_verify_compact_refuses_overfull_cache():
     plen = step.verify_out[1]
     for s in (0, 2):
         assert int(step.P_new[s]) == int(step.P[s]) + int(plen[s])
+
+
+def test_verify_refuses_rows_and_tokens_outside_the_tables():
+    """A node whose row lies past the logit tables (R too small for the tree), or, for
+    rejection sampling, a drafted token past the vocabulary, is never read: that sequence
+    gets path_len 0 and bonus -1, the workspace reports DTV_EDEVICE, and the other
+    sequences still match the oracle. After the tree is repaired the same workspaces give
+    the oracle's results again."""
+    need_gpu()
+    wl = make_workload("c5_batched_llama2_70b", 5, P=16, V=300, S=3)
+    cfg = wl.cfg
+    otrees = [ostep.build_tree(wl, s) for s in range(cfg.S)]
+    tgt = to_device(wl.target, cfg.dtype, DEV)
+    drf = to_device(wl.draft, cfg.dtype, DEV)
+    ua = torch.from_numpy(wl.u_acc.view(np.int32)).to(DEV)
+    ur = torch.from_numpy(wl.u_res.view(np.int32)).to(DEV)
+    R = wl.target.shape[1]
+    ws = dtv.Workspace(DEV)
+
+    def refs(s):
+        t = otrees[s]
+        dec_t = lambda r: orows.decode(wl.target[s, r], cfg.dtype)
+        dec_d = lambda r: orows.decode(wl.draft[s, r], cfg.dtype)
+        return (overify.greedy(t.parent, t.token, t.row, dec_t),
+                overify.sample(t.parent, t.token, t.row, dec_t, dec_d, wl.u_acc[s], wl.u_res[s]))
+
+    def check_ok(s, out, ref):
+        A = int(out[1][s]) - 1
+        assert A == ref["A"] and list(out[0][s, :A + 1].cpu().numpy()) == ref["path"]
+        assert int(out[2][s]) == ref["bonus"]
+
+    for bad in ("row", "token"):
+        tree = _upload_tree_with_rows(otrees, cfg.N)
+        if bad == "row":
+            tree.row[1, cfg.N - 1] = R
+        else:
+            tree.token[1, cfg.N - 1] = cfg.V
+        torch.cuda.synchronize()
+        outs = {}
+        if bad == "row":   # greedy never reads a logit at a drafted token
+            outs["verify_greedy"] = dtv.tree_verify_greedy(tree, tgt, ws)
+        outs["verify_sample"] = dtv.tree_verify_sample(tree, tgt, drf, ua, ur, ws)
+        for key, out in outs.items():
+            assert ws.status(key) == -6, key
+            assert int(out[1][1]) == 0 and int(out[2][1]) == -1, key
+            for s in (0, 2):
+                check_ok(s, out, refs(s)[0 if key == "verify_greedy" else 1])
+    # repaired: the same workspaces give the oracle's results for every sequence
+    tree = _upload_tree_with_rows(otrees, cfg.N)
+    g = dtv.tree_verify_greedy(tree, tgt, ws)
+    smp = dtv.tree_verify_sample(tree, tgt, drf, ua, ur, ws)
+    assert ws.status("verify_greedy") == 0 and ws.status("verify_sample") == 0
+    for s in range(cfg.S):
+        rg, rs = refs(s)
+        check_ok(s, g, rg)
+        check_ok(s, smp, rs)
+
+
+def test_kv_compact_aliased_refusal_keeps_its_mark():
+    """dtv_kv_compact with P_new aliasing P: a sequence it refuses (too little cache left)
+    keeps P = -1 and its rows; the others move their paths and advance P."""
+    need_gpu()
+    rng = np.random.default_rng(4)
+    S, Hkv, D, N = 3, 2, 128, 20
+    P_cap = 100
+    x = f32_to_bf16_bits(rng.standard_normal((S, Hkv, P_cap, D), dtype=np.float32))
+    y = f32_to_bf16_bits(rng.standard_normal((S, Hkv, P_cap, D), dtype=np.float32))
+    k = to_device(x, "bf16", DEV)
+    v = to_device(y, "bf16", DEV)
+    P0 = [30, P_cap - N + 1, 50]
+    paths = [[0, 2, 7], [0, 1], [0, 3, 4, 19]]
+    path = np.full((S, N), -1, dtype=np.int32)
+    for s, p in enumerate(paths):
+        path[s, :len(p)] = p
+    P = torch.tensor(P0, dtype=torch.int32, device=DEV)
+    dtv.kv_compact(k, v, P, torch.tensor(path, device=DEV),
+                   torch.tensor([len(p) for p in paths], dtype=torch.int32, device=DEV), P_new=P)
+    torch.cuda.synchronize()
+    Ph = P.cpu().tolist()
+    assert Ph == [P0[0] + 3, -1, P0[2] + 4]
+    kk = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(kk[1], x[1])
+    for s in (0, 2):
+        k2, _, Pn = ocompact.kv_compact(x[s], y[s], P0[s], paths[s])
+        np.testing.assert_array_equal(kk[s], k2)
+        assert Pn == Ph[s]

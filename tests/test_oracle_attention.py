@@ -89,3 +89,43 @@ def test_relabelling_nodes_permutes_outputs():
     v2[:, P:P + 4] = v[:, P + np.array(perm)]
     o2 = attention.tree_attention(q2, k2, v2, P, parent2)
     np.testing.assert_allclose(o2, o[perm], rtol=1e-13, atol=1e-13)
+
+
+# The all-rows form used by the full-size GPU checks: the same pins, plus agreement with
+# the per-row form on random trees with grouped-query heads and a ragged prefix.
+
+def test_dense_chain_equals_causal_attention():
+    rng = np.random.default_rng(20)
+    for P, N, Hq, Hkv, D in ((0, 5, 2, 2, 8), (37, 17, 4, 2, 16), (64, 65, 2, 1, 8)):
+        q = _rand(rng, N, Hq, D)
+        k = _rand(rng, Hkv, P + N + 3, D)
+        v = _rand(rng, Hkv, P + N + 3, D)
+        o = attention.tree_attention_dense(q, k, v, P, [-1] + list(range(N - 1)))
+        g = Hq // Hkv
+        allowed = np.arange(P + N)[None, :] <= (P + np.arange(N))[:, None]
+        ref = _sdpa(np.transpose(q, (1, 0, 2)).copy(), np.repeat(k[:, :P + N], g, axis=0),
+                    np.repeat(v[:, :P + N], g, axis=0), allowed, 1.0 / np.sqrt(D))
+        np.testing.assert_allclose(o, np.transpose(ref, (1, 0, 2)), rtol=1e-12, atol=1e-12)
+
+
+def test_dense_star_sees_prefix_root_and_self():
+    rng = np.random.default_rng(21)
+    P, N, H, D = 20, 9, 3, 8
+    q, k, v = _rand(rng, N, H, D), _rand(rng, H, P + N, D), _rand(rng, H, P + N, D)
+    o = attention.tree_attention_dense(q, k, v, P, [-1] + [0] * (N - 1))
+    allowed = np.zeros((N, P + N), dtype=bool)
+    allowed[:, :P + 1] = True
+    allowed[np.arange(N), P + np.arange(N)] = True
+    ref = _sdpa(np.transpose(q, (1, 0, 2)).copy(), k, v, allowed, 1.0 / np.sqrt(D))
+    np.testing.assert_allclose(o, np.transpose(ref, (1, 0, 2)), rtol=1e-12, atol=1e-12)
+
+
+def test_dense_gqa_equals_repeated_mha_and_per_row_form():
+    rng = np.random.default_rng(22)
+    for P, N, Hq, Hkv, D in ((15, 11, 8, 2, 8), (0, 30, 4, 4, 16), (130, 70, 16, 2, 8)):
+        parent = [-1] + [int(rng.integers(0, i)) for i in range(1, N)]
+        q, k, v = _rand(rng, N, Hq, D), _rand(rng, Hkv, P + N + 5, D), _rand(rng, Hkv, P + N + 5, D)
+        o1 = attention.tree_attention_dense(q, k, v, P, parent)
+        o2 = attention.tree_attention_dense(q, np.repeat(k, Hq // Hkv, 0), np.repeat(v, Hq // Hkv, 0), P, parent)
+        np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(o1, attention.tree_attention(q, k, v, P, parent), rtol=1e-12, atol=1e-12)
