@@ -4,9 +4,9 @@ The computation lives in libdtv.so (HIP kernels behind the C ABI of include/dtv.
 ``api`` marshals torch device tensors into those calls.
 """
 from .api import (BF16, F32, DtvError, Tree, Workspace, bookkeeping, kv_compact, row_stats,
-                  tree_attn, tree_build_given, tree_build_opt, tree_build_spine, tree_build_talon, tree_verify_greedy,
+                  tree_attn, tree_attn_noalloc, tree_build_given, tree_build_opt, tree_build_spine, tree_build_talon, tree_verify_greedy,
                   tree_verify_sample)
 
 __all__ = ["BF16", "F32", "DtvError", "Tree", "Workspace", "bookkeeping", "kv_compact", "row_stats",
-           "tree_attn", "tree_build_given", "tree_build_opt", "tree_build_spine", "tree_build_talon", "tree_verify_greedy",
+           "tree_attn", "tree_attn_noalloc", "tree_build_given", "tree_build_opt", "tree_build_spine", "tree_build_talon", "tree_verify_greedy",
            "tree_verify_sample"]

@@ -53,6 +53,8 @@ SIGNATURES = {
     "dtv_tree_attn_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_attn": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, PTREE, c_i32, c_i32, c_i32,
                               c_i32, c_int, c_f32, c_vp, c_vp, c_size, c_vp]),
+    "dtv_tree_attn_noalloc": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, PTREE, c_i32, c_i32, c_i32,
+                                      c_i32, c_int, c_f32, c_vp, c_vp]),
     "dtv_tree_verify_greedy_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_verify_greedy": (c_int, [PTREE, c_i32, c_vp, c_int, c_i32, c_i32, c_vp, c_vp, c_vp,
                                        c_vp, c_vp, c_size, c_vp]),

@@ -213,6 +213,20 @@ def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor
     return o
 
 
+def tree_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, P_max: int,
+                      tree: Tree, o: torch.Tensor, scale: float | None = None, stream=None) -> torch.Tensor:
+    """tree_attn without a workspace (dtv_tree_attn_noalloc): the key-split partials live in
+    the library's static per-GPU array; ``o`` must be given (the call allocates nothing)."""
+    S, n_cap, Hq, D = q.shape
+    Hkv, P_cap = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _call("dtv_tree_attn_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(P), P_cap, int(P_max), tree.c, S, Hq, Hkv,
+          D, dt, float(scale), _ptr(o), _stream(stream))
+    return o
+
+
 def _kv_cache(kv):
     """(k, v, P, P_new) torch tensors -> the C description of a cache to compact."""
     k, v, P, P_new = kv

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dtv.h"
 #include "dtv_internal.h"
 #include "rowstats.h"
@@ -694,9 +696,17 @@ size_t dtv_tree_attn_ws_bytes(int32_t S, int32_t n_cap, int32_t Hq, int32_t Hkv,
   return attn_layout(nullptr, S, Hkv, D, attn_plan(S, n_cap, Hq, Hkv, P_max, D)).bytes;
 }
 
-int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
-                  int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
-                  int dtype, float scale, void* o, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The checks, workspace layout and launches of tree attention, on a workspace `ws` of
+// `ws_bytes` (a caller's buffer, or the no-allocation variant's static array). `ws_cap`
+// (0: none) is the most any size may need from a fixed workspace; larger sizes are refused
+// with DTV_ECAPACITY before launch. With `check_only` the call stops after the argument
+// checks (ws may then be NULL) and launches nothing.
+static int attn_impl(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                     int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                     int dtype, float scale, void* o, void* ws, size_t ws_bytes, size_t ws_cap,
+                     bool check_only, void* stream) {
   int rc = check_tree(tree);
   if (rc) return rc;
   REQUIRE(q && k && v && P && o, DTV_EINVAL, "q, k, v, P or o is NULL");
@@ -714,6 +724,11 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
   }
   const AttnPlan plan = attn_plan(S, tree->n_cap, Hq, Hkv, P_max, D);
   size_t need = dtv_tree_attn_ws_bytes(S, tree->n_cap, Hq, Hkv, D, P_max, dtype);
+  REQUIRE(ws_cap == 0 || need <= ws_cap, DTV_ECAPACITY,
+          "these sizes need %zu bytes of key-split partials and status, more than the %zu-byte static scratch "
+          "array; call dtv_tree_attn with a workspace",
+          need, ws_cap);
+  if (check_only) return DTV_OK;
   REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   dtv::AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -746,6 +761,59 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
     a.hdr = static_cast<dtv::WsHeader*>(ws);
   }
   return launched(dtv::launch_attn(a, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- attention without a workspace
+//
+// The scratch of dtv_tree_attn_noalloc: the 256-byte status header and the key-split
+// partials, in a static array that every GPU the library runs on holds until the process
+// ends. Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in): the device address of each GPU's copy comes from hipGetSymbolAddress, called
+// once per device with that device current, and is the only address used.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on its first use).
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DTV_EHIP, "no current device (or device index %d beyond %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(DTV_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DTV_OK;
+}
+
+extern "C" {
+
+int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                  int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                  int dtype, float scale, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return attn_impl(q, k, v, P, P_cap, P_max, tree, S, Hq, Hkv, D, dtype, scale, o, ws, ws_bytes, 0, false, stream);
+}
+
+int dtv_tree_attn_noalloc(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                          int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                          int dtype, float scale, void* o, void* stream) {
+  // every argument check, the array's capacity included, before any device call
+  int rc = attn_impl(q, k, v, P, P_cap, P_max, tree, S, Hq, Hkv, D, dtype, scale, o, nullptr, 0,
+                     kNoAllocScratchBytes, true, stream);
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return attn_impl(q, k, v, P, P_cap, P_max, tree, S, Hq, Hkv, D, dtype, scale, o, ws, kNoAllocScratchBytes,
+                   kNoAllocScratchBytes, false, stream);
 }
 
 // ---------------------------------------------------------------- greedy verification

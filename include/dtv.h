@@ -191,6 +191,26 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
                   int32_t D, int dtype, float scale, void* o, void* ws, size_t ws_bytes,
                   void* stream);
 
+/* Tree attention for callers that cannot allocate: code under HIP graph capture, serving
+ * loops and harnesses that forbid allocation. The same computation and results as
+ * dtv_tree_attn (the same launches and key-split plan, so bit-identical outputs), with no
+ * workspace argument: the key-split partials and the status word live in a static device
+ * array of 64 MiB (67108864 bytes) that each GPU the library runs on holds until the
+ * process ends. Sizes whose partials would need more (dtv_tree_attn_ws_bytes > 64 MiB, for
+ * example 16 sequences of 4096-key caches with 65-node trees and 32/8 heads) are refused
+ * with DTV_ECAPACITY before any device call. The call allocates nothing: it calls no
+ * hipMalloc or hipFree; its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress) once. Every call on one GPU shares that GPU's array, which
+ * keeps the last call's partials: nothing in it must start at zero (every partial a call
+ * reads, that call writes first), but calls that may overlap on one GPU (concurrent streams
+ * or threads) race on it and must be ordered by the caller. Device-side refusals
+ * (n_nodes[s] > n_cap, or P[s] + n_nodes[s] > P_cap) leave those rows of o unwritten and
+ * are not reported (dtv_tree_attn reports them through its workspace).
+ */
+int dtv_tree_attn_noalloc(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
+                          int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv,
+                          int32_t D, int dtype, float scale, void* o, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * Greedy verification (OPT-Tree summary, section 2; GOOSE page, section 2C).
  *
