@@ -57,9 +57,10 @@ def algorithmic_work(step, wl):
 
     Build: every draft row the builder expands, read once. Attention: prefix K/V once per
     KV head, tree K/V, Q in and O out; flops 4*Hq*D per visible (query, key) pair. Verify:
-    greedy reads each node's target row once; sampling reads each node's target and draft
-    rows once (residual passes come on top). Compaction: K and V rows of the path, read and
-    written once.
+    greedy reads each node's target row once; rejection sampling reads, at each node the
+    walk visits (the accepted path), its target row and, when it has children, its draft
+    row (residual passes re-read those rows). Compaction: K and V rows of the path, read
+    and written once.
     """
     import numpy as np
     cfg = wl.cfg
@@ -69,6 +70,8 @@ def algorithmic_work(step, wl):
     layers = step.tree.layers.cpu().numpy()
     anc = step.tree.anc.cpu().numpy().view(np.uint64)
     plen = step.verify_out[1].cpu().numpy()
+    paths = step.verify_out[0].cpu().numpy()
+    parents = step.tree.parent.cpu().numpy()
     out = {"build": {"bytes": 0.0}, "attention": {"bytes": 0.0, "flops": 0.0},
            "verify": {"bytes": 0.0}, "compact": {"bytes": 0.0}}
     row = cfg.V * esz
@@ -91,9 +94,39 @@ def algorithmic_work(step, wl):
         out["attention"]["bytes"] += (2 * P * cfg.Hkv * cfg.D + 2 * N * cfg.Hkv * cfg.D
                                       + 2 * N * cfg.Hq * cfg.D) * esz
         out["attention"]["flops"] += 4.0 * cfg.Hq * cfg.D * (N * P + vis)
-        out["verify"]["bytes"] += N * row * (1 if cfg.verify == "greedy" else 2)
+        if cfg.verify == "greedy":   # every node's argmax decides which paths match
+            out["verify"]["bytes"] += N * row
+        else:   # p and q are needed only where the walk goes: the nodes of the accepted path
+            internal = set(int(x) for x in parents[s, 1:N])
+            for v in paths[s, :int(plen[s])]:
+                out["verify"]["bytes"] += row * (2 if int(v) in internal else 1)
         out["compact"]["bytes"] += 4 * int(plen[s]) * cfg.Hkv * cfg.D * esz
     out["verify_compact"] = {"bytes": out["verify"]["bytes"] + out["compact"]["bytes"]}
+    return out
+
+
+def kernel_work(step, wl, work):
+    """Algorithmic bytes (and flops) of one launch of each kernel of the step, from the
+    stage figures: the kernel that streams a stage's rows or keys carries its work, the
+    stage's small follow-up kernels (selections, merges of partials) carry none."""
+    cfg = wl.cfg
+    out = {}
+    if cfg.build == "talon":
+        out["talon_rows_kernel"] = dict(work["build"])
+    elif cfg.build == "spine":
+        out["spine_kernel"] = dict(work["build"])
+    elif cfg.build == "opt":
+        out["opt_rows_kernel+opt_root_kernel"] = dict(work["build"])
+    else:
+        out["given_tree_kernel"] = dict(work["build"])
+    att = "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
+    out[att] = dict(work["attention"])
+    if cfg.verify == "greedy":
+        out["verify_greedy_kernel"] = dict(work["verify_compact"] if step.fuse_compact else work["verify"])
+    else:
+        out["sample_walk_kernel"] = dict(work["verify_compact"] if step.fuse_compact else work["verify"])
+    if not step.fuse_compact:
+        out["compact_kernel"] = dict(work["compact"])
     return out
 
 
@@ -107,14 +140,22 @@ STAGE_KERNELS = {
                         "given": ["given_tree_kernel"]}[c.build],
     "attention": lambda c: (["attn_bf16_kernel", "attn_combine_rows_kernel"] if c.dtype == "bf16"
                             else ["attn_f32_kernel"]),
-    "verify": lambda c: (["verify_greedy_kernel"] if c.verify == "greedy"
-                         else ["sample_lse_kernel", "sample_lse_merge_kernel (trees of more than 128 nodes)",
-                               "sample_walk_kernel"]),
+    "verify": lambda c: (["verify_greedy_kernel"] if c.verify == "greedy" else ["sample_walk_kernel"]),
     "compact": lambda c: ["compact_kernel"],
     "verify_compact": lambda c: (["verify_greedy_kernel (compacts the cache)"] if c.verify == "greedy"
-                                 else ["sample_lse_kernel", "sample_lse_merge_kernel (trees of more than 128 nodes)",
-                                       "sample_walk_kernel (compacts the cache)"]),
+                                 else ["sample_walk_kernel (compacts the cache)"]),
 }
+
+
+def kernel_stage(kernel: str, fused: bool) -> str:
+    """The stage (launch group of DraftTreeStep) a kernel belongs to."""
+    if kernel.startswith(("talon_", "spine_", "opt_", "given_")):
+        return "build"
+    if kernel.startswith("attn_"):
+        return "attention"
+    if kernel.startswith(("verify_", "sample_")):
+        return "verify_compact" if fused else "verify"
+    return "compact"
 
 
 def csrc_sha256() -> str:
@@ -143,17 +184,35 @@ def recorded_traffic(workload: str, stage: str):
     return rec.get(stage)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wl, steps: int):
+    """The oracle on the host: `steps` whole steps with one thread, then with every core this
+    process may run on (numpy's BLAS threads; the oracle's loops stay in one thread)."""
     from threadpoolctl import threadpool_limits
     from oracle import step as ostep
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            ostep.run_step(wl)
-        dt = time.perf_counter() - t0
-    return {"value": steps / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    ncores = len(os.sched_getaffinity(0))
+    legs = {}
+    for label, limit in (("one_thread", 1), ("all_cores", ncores)):
+        with threadpool_limits(limits=limit):
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                ostep.run_step(wl)
+            legs[label] = steps / (time.perf_counter() - t0)
+    return {"value": legs["all_cores"], "unit": "steps/s", "cores": ncores, "kind": "oracle",
             "sample": f"{steps} whole oracle steps (build, attention, verify, compact) of the same "
-                      f"workload, float64 numpy, one thread"}
+                      f"workload, float64 numpy, per leg",
+            "one_thread": {"value": legs["one_thread"], "cores": 1}, "cpu_model": cpu_model()}
 
 
 def main():
@@ -218,15 +277,26 @@ def main():
     # separate launches with HIP events on the launch stream around each stage; a record
     # between two kernels adds a gap of a few microseconds, so sampling keeps that cost inside
     # the timed region at about 1%.
-    every = max(1, args.event_every)
+    # Every `every`-th step also carries HIP events: steps k = 0, every, ... around each
+    # stage (torch events on the launch stream); steps k = every/2, every + every/2, ...
+    # around each kernel (the library's own events, recorded on the stream it launches on).
+    from draft_tree_verification_build_amd import api
+    every = max(2, args.event_every)
     sampled = list(range(0, args.steps, every))
+    ktimed = set(range(every // 2, args.steps, every))
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for k in sampled}
+    api.kernel_timing(False, reset=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         e = ev.get(k)
         if e is None:
-            run_step()
+            if k in ktimed:
+                api.kernel_timing(True)
+                step.run()
+                api.kernel_timing(False)
+            else:
+                run_step()
             continue
         e[0].record(stream)
         for j, fn in enumerate(fns):
@@ -234,6 +304,7 @@ def main():
             e[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ktimes = api.kernel_times()
     st = step.ws_status()
     if any(v != 0 for v in st.values()):
         print(f"device status after the timed steps: {st}", file=sys.stderr)
@@ -256,17 +327,59 @@ def main():
             peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
             rep.update({"flops": w["flops"], "TFLOP/s": tf, "mfma_frac": tf / peak})
         stage_report[name] = rep
-    dom = max(stages, key=lambda n: stage_ms[n])
-    d = stage_report[dom]
-    if dom == "attention" and d["flops"] / max(d["bytes"], 1) > (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": d["TFLOP/s"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": d["mfma_frac"], "traffic": None}
+    # Per kernel: mean event time per launch and per step; the dominant kernel (most time per
+    # step) gives `roofline`: its algorithmic bytes (or flops) per launch over its mean launch
+    # time, against 8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA.
+    nk = max(1, len(ktimed))
+    kwork = kernel_work(step, wl, work)
+    kernels = {}
+    for name, (tot, cnt) in ktimes.items():
+        kernels[name] = {"launches_per_step": cnt / nk, "ms_per_launch": tot / cnt, "ms_per_step": tot / nk}
+    for key, w in kwork.items():   # a work entry may cover several kernels ("a+b")
+        parts = [kernels[n] for n in key.split("+") if n in kernels]
+        if not parts:
+            continue
+        launches = sum(p["launches_per_step"] for p in parts)
+        ms_launch = sum(p["ms_per_step"] for p in parts) / launches
+        for n in key.split("+"):
+            if n in kernels:
+                kernels[n]["work_of"] = key
+        per = {"bytes": w["bytes"] / launches}
+        if "flops" in w:
+            per["flops"] = w["flops"] / launches
+        kernels[key] = {**kernels.get(key, {}), "launches_per_step": launches, "ms_per_launch": ms_launch,
+                        "ms_per_step": ms_launch * launches, **{f"{k}_per_launch": v for k, v in per.items()}}
+    scored = {n: k for n, k in kernels.items() if "bytes_per_launch" in k}
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"]) if kernels else None
+    if dom is not None and "bytes_per_launch" not in kernels[dom]:
+        # the most expensive kernel moves no algorithmic data (a selection or a merge of
+        # partials): the roofline goes to the most expensive kernel that streams data, and
+        # the line names both
+        slowest = dom
+        dom = max(scored, key=lambda n: scored[n]["ms_per_step"])
     else:
-        roof = {"bound": "hbm", "achieved": d["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["hbm_frac"], "traffic": None}
-    roof["kernel"] = dom
-    roof["launches"] = STAGE_KERNELS[dom](cfg)
+        slowest = dom
+    kd = kernels[dom]
+    t = kd["ms_per_launch"] * 1e-3
+    gbs = kd["bytes_per_launch"] / t / 1e9
+    flops = kd.get("flops_per_launch")
+    ridge = (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if flops is not None and flops / max(kd["bytes_per_launch"], 1) > ridge and cfg.dtype == "bf16":
+        tf = flops / t / 1e12
+        roof = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
     roof["traffic"] = recorded_traffic(cfg.name, dom)
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = kd["ms_per_launch"]
+    roof["bytes_per_launch"] = kd["bytes_per_launch"]
+    if flops is not None:
+        roof["flops_per_launch"] = flops
+    if slowest != dom:
+        roof["slowest_kernel"] = slowest
+    stage = kernel_stage(dom.split("+")[0], step.fuse_compact)
+    roof["stage"] = {"name": stage, **stage_report[stage]}
 
     out = {
         "metric": METRIC, "value": steps_s, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -280,6 +393,8 @@ def main():
         "roofline": roof,
         "stages": stage_report,
         "stage_samples": len(sampled),
+        "kernels": kernels,
+        "kernel_samples": nk,
     }
     if args.decode_steps > 0:
         out["decode"] = decode_loop(args.config, seed, args.decode_steps, args.gamma)

@@ -68,6 +68,8 @@ SIGNATURES = {
     "dtv_tree_verify_sample_plan": (c_int, [c_i32, c_i32, c_i32, c_int, c_i32, c_i32, c_vp]),
     "dtv_kv_compact": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                c_i32, c_int, c_vp]),
+    "dtv_kernel_timing": (c_int, [c_int, c_int]),
+    "dtv_kernel_times": (c_int, [c_i32, c_vp, c_i32, c_vp, c_vp]),
     "dtv_bookkeeping": (c_int, [c_vp, c_i32, c_i64, c_f64, c_vp]),
 }
 

@@ -304,6 +304,29 @@ def kv_compact(k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, path: torch.Te
     return P_new
 
 
+def kernel_timing(enable: bool, reset: bool = False) -> None:
+    """Turn the library's per-launch event timing on or off (optionally dropping the totals)."""
+    _call("dtv_kernel_timing", int(bool(enable)), int(bool(reset)))
+
+
+def kernel_times() -> dict:
+    """{kernel name: (total ms, timed launches)} over the launches timed so far."""
+    import numpy as np
+    lib = _lib.load()
+    n = lib.dtv_kernel_times(0, None, 0, None, None)
+    if n < 0:
+        raise DtvError("dtv_kernel_times", n)
+    nb = 96
+    names = ctypes.create_string_buffer(max(n, 1) * nb)
+    ms = np.zeros(max(n, 1), dtype=np.float64)
+    cnt = np.zeros(max(n, 1), dtype=np.int64)
+    n = lib.dtv_kernel_times(n, names, nb, ms.ctypes.data, cnt.ctypes.data)
+    if n < 0:
+        raise DtvError("dtv_kernel_times", n)
+    raw = names.raw
+    return {raw[i * nb:(i + 1) * nb].split(b"\0", 1)[0].decode(): (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
 def bookkeeping(accepted, draft_steps: int, gamma: float) -> dict:
     """Host-side E[A], eta and Speedup from logged counts."""
     import numpy as np

@@ -311,23 +311,23 @@ VerifyLayout verify_layout(void* ws, int S, int n_cap, int nch) {
 
 struct SampleLayout {
   dtv::WsHeader* hdr;
-  dtv::ChunkStat* st;
-  double* lse;
   double* xch;
   double* pbuf;
+  unsigned* done;
   size_t bytes;
 };
+// Exchange slots of the walk per sequence: one per visited node (its normalisers), one per
+// rejection, one for a bonus draw whose slice masses are not known from an earlier exchange.
+int sample_max_pass(int n_cap) { return 2 * n_cap + 1; }
+
 SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
-  const int nch = nch_of(V, dtype);
-  const size_t rows = static_cast<size_t>(S) * n_cap * 2;
+  (void)dtype;
   Carver c(ws);
   SampleLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
-  L.st = c.take<dtv::ChunkStat>(rows * nch);
-  L.lse = c.take<double>(rows);
-  // one exchange slot per rejection (at most n_cap - 1) and one for the bonus draw
-  L.xch = c.take<double>(static_cast<size_t>(S) * (n_cap + 1) * dtv::kXchStride);
+  L.xch = c.take<double>(static_cast<size_t>(S) * sample_max_pass(n_cap) * dtv::kXchStride);
   L.pbuf = c.take<double>(static_cast<size_t>(S) * 3 * V);   // two residuals and q per sequence
+  L.done = c.take<unsigned>(S);
   L.bytes = c.off;
   return L;
 }
@@ -338,8 +338,8 @@ SampleLayout sample_layout(void* ws, int S, int n_cap, int V, int dtype) {
 // [units*gi/G, units*(gi+1)/G), so no slice exceeds ceil(units/G) units. A slice of at most
 // kWalkSlice entries keeps its two residuals and q in shared memory (entries indexed from
 // the slice's first), a larger one in the sequence's 3*V workspace entries (indexed by
-// entry < V). Exchange slots: one per rejection (at most n_cap - 1) and one for the bonus
-// draw, each holding G sums and two values.
+// entry < V). Exchange slots: one per visited node (at most n_cap), one per rejection (at
+// most n_cap - 1) and one for a bonus draw, each holding 4 values per workgroup.
 struct WalkPlan {
   int G, units, slice_units, slice_entries, in_lds, xch_slots;
   long pbuf_entries;
@@ -361,10 +361,11 @@ int walk_plan(int S, int n_cap, int V, int dtype, int resident, int vec, WalkPla
   p->slice_units = (p->units + G - 1) / G;
   p->slice_entries = p->slice_units * (vec ? VEC : 1);
   p->in_lds = p->slice_entries <= dtv::kWalkSlice ? 1 : 0;
-  p->xch_slots = n_cap + 1;
+  p->xch_slots = sample_max_pass(n_cap);
   p->pbuf_entries = 3L * V;
   // the bounds the kernel relies on
-  REQUIRE(G + 2 <= dtv::kXchStride, DTV_EUNSUPPORTED, "G=%d exceeds an exchange slot", G);
+  REQUIRE(4 * G <= dtv::kXchStride && G + 2 <= dtv::kXchStride, DTV_EUNSUPPORTED, "G=%d exceeds an exchange slot",
+          G);
   REQUIRE(static_cast<long>(p->units) * (vec ? VEC : 1) <= V, DTV_EUNSUPPORTED, "units exceed the row");
   REQUIRE(p->in_lds || static_cast<long>(p->slice_entries) <= V, DTV_EUNSUPPORTED,
           "a slice of %d entries exceeds the %d-entry workspace rows", p->slice_entries, V);
@@ -921,12 +922,11 @@ static int verify_sample_impl(const dtv_tree* tree, int32_t S, const void* targe
   a.path_len = path_len;
   a.bonus = bonus;
   a.hdr = L.hdr;
-  a.st = L.st;
   a.S = S;
-  a.lse = L.lse;
   a.xch = L.xch;
-  a.max_pass = tree->n_cap + 1;
+  a.max_pass = sample_max_pass(tree->n_cap);
   a.pbuf = L.pbuf;
+  a.done = L.done;
   // the walk's groups must all be resident at once: about one workgroup per compute unit
   // in total (far below what the device holds), at most kSampleMaxGroup per sequence
   const int max_blocks = dtv::sample_walk_max_blocks(dtype == DTV_BF16 ? 1 : 0);
@@ -939,13 +939,6 @@ static int verify_sample_impl(const dtv_tree* tree, int32_t S, const void* targe
   if (rc) return rc;
   a.G = plan.G;
   a.vec = vec;
-  const int lse_slots = dtv::sample_lse_max_blocks(dtype == DTV_BF16 ? 1 : 0);
-  REQUIRE(lse_slots >= 1, DTV_EUNSUPPORTED, "occupancy query failed");
-  const long items = static_cast<long>(S) * tree->n_cap * 2 * a.nch;
-  // every resident workgroup, but no workgroup with more than 64 items
-  long grid = items < lse_slots ? items : lse_slots;
-  if (grid * 64 < items) grid = (items + 63) / 64;
-  a.lse_grid = static_cast<int>(grid);
   rc = kv_view(kv, dtype, tree, &a.kvc);
   if (rc) return rc;
   return launched(dtv::launch_verify_sample(a, S, dtype == DTV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)));

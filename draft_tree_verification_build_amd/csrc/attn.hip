@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void attn_f32_kernel(AttnArgs a) {
 
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st) {
   if (dtype == 1) return launch_attn_bf16(a, st);
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.S * a.n_cap * a.Hq), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(attn_f32_kernel, dim3(a.S * a.n_cap * a.Hq), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -479,9 +479,9 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const int units = a.S * a.Hkv * a.n_split;
   const int grid = ((units + kNumXcd - 1) / kNumXcd) * kNumXcd * a.n_mtiles;
   if (a.D == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(attn_bf16_kernel<128>, dim3(grid), dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(attn_bf16_kernel<64>, dim3(grid), dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.n_split > 1) {
     const int rpb = kBlock / (a.D / 4);
@@ -490,18 +490,18 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
     const int ns = a.n_split <= 8 ? 8 : (a.n_split <= 16 ? 16 : kAttnMaxSplit);
     if (a.D == 128) {
       if (ns == 8)
-        hipLaunchKernelGGL((attn_combine_rows_kernel<128, 8>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 8>), blocks, dim3(kBlock), 0, st, a);
       else if (ns == 16)
-        hipLaunchKernelGGL((attn_combine_rows_kernel<128, 16>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 16>), blocks, dim3(kBlock), 0, st, a);
       else
-        hipLaunchKernelGGL((attn_combine_rows_kernel<128, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<128, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
     } else {
       if (ns == 8)
-        hipLaunchKernelGGL((attn_combine_rows_kernel<64, 8>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<64, 8>), blocks, dim3(kBlock), 0, st, a);
       else if (ns == 16)
-        hipLaunchKernelGGL((attn_combine_rows_kernel<64, 16>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<64, 16>), blocks, dim3(kBlock), 0, st, a);
       else
-        hipLaunchKernelGGL((attn_combine_rows_kernel<64, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
+        DTV_LAUNCH((attn_combine_rows_kernel<64, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
     }
     if (hipGetLastError() != hipSuccess) return -1;
   }

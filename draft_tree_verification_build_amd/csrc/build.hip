@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void given_tree_kernel(TreeArgs t, WsHeader
 }
 
 int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st) {
-  hipLaunchKernelGGL(given_tree_kernel, dim3(S), dim3(kBlock), 0, st, t, hdr);
+  DTV_LAUNCH(given_tree_kernel, dim3(S), dim3(kBlock), 0, st, t, hdr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -389,20 +389,20 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
   const dim3 grid(a.S * a.F * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(spine_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(spine_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(spine_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(spine_kernel<0>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_talon(const TalonArgs& a, int dtype, hipStream_t st) {
   const dim3 grid(a.S * a.B * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(talon_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(talon_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

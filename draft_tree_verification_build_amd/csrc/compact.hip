@@ -66,10 +66,10 @@ __global__ void compact_update_p(const int* path_len, int* P, int S) {
 }
 
 int launch_compact(const CompactArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(compact_kernel, dim3(a.S * a.Hkv * 2), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(compact_kernel, dim3(a.S * a.Hkv * 2), dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.P_new == a.P) {
-    hipLaunchKernelGGL(compact_update_p, dim3((a.S + 255) / 256), dim3(256), 0, st, a.path_len,
+    DTV_LAUNCH(compact_update_p, dim3((a.S + 255) / 256), dim3(256), 0, st, a.path_len,
                        a.P_new, a.S);
     if (hipGetLastError() != hipSuccess) return -1;
   }

@@ -9,6 +9,30 @@
 
 namespace dtv {
 
+// Kernel timing (dtv_kernel_timing, timing.hip). While timing is on, a LaunchTimer brackets
+// one launch with two HIP events recorded on the launch's stream; their elapsed time is
+// folded into the kernel's totals when the caller reads them. While it is off, it does
+// nothing.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char* kernel, hipStream_t stream);
+  ~LaunchTimer();
+  LaunchTimer(const LaunchTimer&) = delete;
+  LaunchTimer& operator=(const LaunchTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t begin_ = nullptr;
+};
+
+// Every kernel of the library is launched through this macro, so that timing sees it.
+#define DTV_LAUNCH(kernel, grid, block, smem, stream, ...)                      \
+  do {                                                                          \
+    ::dtv::LaunchTimer dtv_launch_timer_(#kernel, stream);                      \
+    hipLaunchKernelGGL(kernel, grid, block, smem, stream, __VA_ARGS__);         \
+  } while (0)
+
 struct ChunkStat;
 
 struct TreeArgs {
@@ -180,7 +204,7 @@ struct VerifyArgs {
 // Sizes of the rejection-sampling walk, shared by the host plan (api.hip) and the kernels.
 constexpr int kSampleMaxNodes = 1024;   // tree slots the walk keeps in shared memory
 constexpr int kSampleMaxGroup = 32;     // workgroups per sequence in the walk
-constexpr int kXchStride = 64;          // doubles per exchange slot (G slice sums + 2 values)
+constexpr int kXchStride = 4 * kSampleMaxGroup;   // entries per exchange slot (4 values per workgroup)
 constexpr int kWalkSlice = 4096;        // slice entries kept in shared memory (else the workspace)
 static_assert(kSampleMaxGroup + 2 <= kXchStride, "an exchange slot holds G sums and two values");
 
@@ -195,15 +219,13 @@ struct SampleArgs {
   int* path_len;
   int* bonus;
   WsHeader* hdr;
-  ChunkStat* st;             // [S][n_cap][2 (0: target, 1: draft)][nch]
-  double* lse;               // [S][n_cap][2]
   int S;
-  int lse_grid;              // workgroups of the chunk-statistics kernel
   int G;                     // workgroups per sequence in the walk
   int vec;                   // 1: rows are walked in 16-byte units (aligned, V a multiple of 8 / 4)
-  int max_pass;              // exchange slots per sequence (rejections + 1 bonus draw)
-  double* xch;               // [S][max_pass][64] walk exchange slots (emptied by phase 1)
+  int max_pass;              // exchange slots per sequence (visited nodes + rejections + 1)
+  double* xch;               // [S][max_pass][kXchStride] exchange slots (all zero between calls)
   double* pbuf;              // [S][3][V] residual distributions and q (slices too large for LDS)
+  unsigned* done;            // [S] workgroups that finished the walk (zero between calls)
   KvCompactView kvc;
 };
 
@@ -232,7 +254,6 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st);
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st);
 int sample_walk_max_blocks(int dtype);
-int sample_lse_max_blocks(int dtype);
 int launch_compact(const CompactArgs& a, hipStream_t st);
 
 }  // namespace dtv

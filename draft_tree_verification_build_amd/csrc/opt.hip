@@ -890,7 +890,7 @@ __global__ void opt_init_kernel(OptArgs a) {
 // ------------------------------------------------------------------ launches
 
 int launch_opt_init(const OptArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(opt_init_kernel, dim3((a.S + 255) / 256), dim3(256), 0, st, a);
+  DTV_LAUNCH(opt_init_kernel, dim3((a.S + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -900,24 +900,24 @@ int launch_opt_layer(OptArgs a, int dtype, hipStream_t st) {
   const bool big = a.Kc > 32;
   if (dtype == 1) {
     if (big)
-      hipLaunchKernelGGL((opt_rows_kernel<1, true>), rows, dim3(kBlock), 0, st, a);
+      DTV_LAUNCH((opt_rows_kernel<1, true>), rows, dim3(kBlock), 0, st, a);
     else
-      hipLaunchKernelGGL((opt_rows_kernel<1, false>), rows, dim3(kBlock), 0, st, a);
+      DTV_LAUNCH((opt_rows_kernel<1, false>), rows, dim3(kBlock), 0, st, a);
   } else {
     if (big)
-      hipLaunchKernelGGL((opt_rows_kernel<0, true>), rows, dim3(kBlock), 0, st, a);
+      DTV_LAUNCH((opt_rows_kernel<0, true>), rows, dim3(kBlock), 0, st, a);
     else
-      hipLaunchKernelGGL((opt_rows_kernel<0, false>), rows, dim3(kBlock), 0, st, a);
+      DTV_LAUNCH((opt_rows_kernel<0, false>), rows, dim3(kBlock), 0, st, a);
   }
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(opt_bound_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_bound_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (dtype == 1)
-    hipLaunchKernelGGL(opt_collect_kernel<1>, rows, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(opt_collect_kernel<1>, rows, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(opt_collect_kernel<0>, rows, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(opt_collect_kernel<0>, rows, dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL(opt_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -943,14 +943,14 @@ int opt_root_wave_quota(int V, int n, int dtype) {
 int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st) {
   const dim3 grid(a.S * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(opt_root_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(opt_root_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(opt_root_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(opt_root_kernel<0>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_opt_finalize(const OptArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(opt_finalize_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_finalize_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

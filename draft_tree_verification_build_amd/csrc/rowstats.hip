@@ -38,9 +38,9 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(RowStatsArgs a) {
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st) {
   const dim3 grid(a.R * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(row_stats_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(row_stats_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(row_stats_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(row_stats_kernel<0>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -237,22 +237,23 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
 // the walk moves to the first accepted child; when none is accepted (or the node is a
 // leaf) the bonus token is drawn from the current p by inverse CDF with u_res.
 //
-// Work split: a grid of resident workgroups reduces every chunk of every node's target and
-// draft rows to (max, float64 sum of exp), loading the next chunk while reducing the
-// current one; the rows' log-sum-exps are merged from those (by a small kernel, or inside
-// the walk for small trees). The walk of a sequence is shared by G workgroups, each owning
-// a slice of the vocabulary: a first try needs only the two row values at the child's
-// token; each rejection costs one residual pass over the slices (kept in shared memory
-// when they fit) and one exchange of slice sums; the bonus draw is one prefix-sum pass.
+// Work split: one launch. The walk of a sequence is shared by G workgroups, each owning a
+// slice of the vocabulary. p and q are needed only at the nodes the walk visits (about
+// A + 1 per sequence), so their normalisers are computed there, not for every node of the
+// tree: on arriving at a node, every workgroup reduces its slice of the node's target and
+// draft rows to (max, float64 sum of exp) and the group exchanges those. A first try then
+// needs only the two row values at the child's token; each rejection costs one residual
+// pass over the slices (kept in shared memory when they fit) and one exchange of slice
+// sums; the bonus draw is one prefix-sum pass in the workgroup that holds the target mass.
 
 struct SampleSmem {
   RowSmem rs;
   short par[kSampleMaxNodes];
   int tok[kSampleMaxNodes];
-  double lset[kSampleMaxNodes];
-  double lsed[kSampleMaxNodes];
   int kids[kSampleMaxNodes];
   int spath[kSampleMaxNodes];   // the accepted path so far (every workgroup of the group)
+  double lsev[4 * kSampleMaxGroup];   // the node's slice statistics of every workgroup
+  double wpair[kWaves][4];            // per-wave (max, sum) pairs of the two rows
   double wsum[kWaves];
   int iwsum[kWaves];
   int flag;
@@ -349,68 +350,194 @@ struct WalkDist {
 };
 
 // The G workgroups of a sequence share every V-wide pass: workgroup gi owns units
-// [u0, u1). Every exchange (one per pass) uses a slot of its own: entry gi receives
-// workgroup gi's slice sum, entries G and G+1 two values from the owner of the next
-// child's token (see the walk). The previous kernel fills every entry with an empty
-// marker (a NaN no sum or probability takes), each entry is written once, and the readers
-// poll the entries they need until none holds the marker, so an exchange costs one store
-// and the polls, with no counter and no fence: the values are the signal. Every
-// workgroup then adds the sums in workgroup order, so all of them see identical totals
-// and take identical decisions.
-constexpr unsigned long long kSlotEmpty = 0x7FF8DEAD00000000ull;
+// [u0, u1). Every exchange uses a slot of its own: entries n gi .. n gi + n-1 receive
+// workgroup gi's n values, entries n G and n G + 1 two values from the owner of the next
+// child's token (see the walk). A value is stored as the complement of its bits, so that
+// an entry of all zero bits, which no stored value takes, means "not yet written": the
+// workspace starts zero-filled, and the last workgroup of a sequence to finish its walk
+// zeroes the slots the walk used, ready for the next call. Each entry is written once per
+// call, and the readers poll the entries they need until none is zero, so an exchange
+// costs one store and the polls, with no counter and no fence: the values are the signal.
+// Every workgroup then combines the values in workgroup order, so all of them see
+// identical totals and take identical decisions.
 constexpr long kSpinLimit = 2000000;    // polls (each a memory round trip) before a timeout
+
+__device__ __forceinline__ unsigned long long xch_encode(double v) {
+  return ~static_cast<unsigned long long>(__double_as_longlong(v));
+}
+__device__ __forceinline__ double xch_decode(unsigned long long b) {
+  return __longlong_as_double(static_cast<long long>(~b));
+}
 
 struct WalkGroup {
   int gi, G;
   int u0, u1;                 // this workgroup's units
-  double* xch;                // [max_pass][kXchStride] exchange slots
+  unsigned long long* xch;    // [max_pass][kXchStride] exchange slots
   int max_pass;
   int* err;
   int pass;                   // exchanges so far
 };
 
-// Publishes this workgroup's slice value (and, from the owner, e0 / e1 into slot entries G
-// and G+1), waits until the group's G values (and the owner's two when `extra`) are in
-// and copies them into sm_vals. Returns false on a timeout or when the slots are exhausted.
-__device__ bool group_exchange(WalkGroup& g, double mine, bool owner, double e0, double e1, bool extra,
-                               double* sm_vals, int* flag) {
+// Publishes this workgroup's n values (thread 0's `mine`; from the owner also e0 / e1 into
+// entries n G and n G + 1), waits until the group's n G values (and the owner's two when
+// `extra`) are in and copies them into sm_vals. Returns false on a timeout or when the
+// slots are exhausted.
+__device__ bool group_exchange(WalkGroup& g, const double* mine, int n, bool owner, double e0, double e1,
+                               bool extra, double* sm_vals, int* flag) {
   if (g.pass >= g.max_pass) {
     if (threadIdx.x == 0) atomicExch(g.err, kErrCapacity);
     return false;
   }
-  double* slot = g.xch + static_cast<size_t>(g.pass) * kXchStride;
+  unsigned long long* slot = g.xch + static_cast<size_t>(g.pass) * kXchStride;
   if (threadIdx.x == 0) {
-    st_cc(&slot[g.gi], mine);
+    for (int j = 0; j < n; ++j) st_cc(&slot[g.gi * n + j], xch_encode(mine[j]));
     if (owner) {
-      st_cc(&slot[g.G], e0);
-      st_cc(&slot[g.G + 1], e1);
+      st_cc(&slot[n * g.G], xch_encode(e0));
+      st_cc(&slot[n * g.G + 1], xch_encode(e1));
     }
   }
   ++g.pass;
-  const int nv = g.G + (extra ? 2 : 0);
-  if (threadIdx.x < 64) {   // wave 0: lane k waits for entry k
-    const int k = threadIdx.x;
+  const int nv = n * g.G + (extra ? 2 : 0);
+  if (threadIdx.x < 64) {   // wave 0: lane k waits for entries k, k + 64, ...
     int ok = 1;
-    if (k < nv) {
-      unsigned long long* e = reinterpret_cast<unsigned long long*>(&slot[k]);
-      unsigned long long bits = ld_cc(e);
+    for (int k = threadIdx.x; k < nv && ok; k += 64) {
+      unsigned long long bits = ld_cc(&slot[k]);
       long polls = 0;
-      while (bits == kSlotEmpty) {
+      while (bits == 0ull) {
         __builtin_amdgcn_s_sleep(1);
         if (++polls > kSpinLimit) {
           ok = 0;
           break;
         }
-        bits = ld_cc(e);
+        bits = ld_cc(&slot[k]);
       }
-      sm_vals[k] = __longlong_as_double(static_cast<long long>(bits));
+      sm_vals[k] = xch_decode(bits);
     }
     if (!ok) atomicExch(g.err, kErrTimeout);
     const unsigned long long good = __ballot(ok);
-    if (k == 0) *flag = (good == ~0ull) ? 1 : 0;
+    if (threadIdx.x == 0) *flag = (good == ~0ull) ? 1 : 0;
   }
   __syncthreads();
   return *flag != 0;
+}
+
+// (max, float64 sum of exp(x - max)) of this workgroup's units of nr <= 2 rows, in one pass
+// over memory: every thread loads its units of both rows together, the block takes each
+// row's maximum (one barrier), then every thread sums exp(x - max) over its values and the
+// block sums those (a second barrier). A slice larger than kStatUnits units per thread is
+// folded batch by batch, rescaling the running sum when a later batch raises the maximum.
+// Thread 0 receives the pairs in out[2 r], out[2 r + 1] (max -inf and sum 0 for an empty
+// slice or r >= nr).
+constexpr int kStatUnits = 2;   // units per thread and batch
+
+template <int DT>
+__device__ void slice_stats(const void* row0, const void* row1, int nr, const WalkGroup& g, bool vec,
+                            const double* tab, double (*wred)[4], double* out) {
+  constexpr int VEC = RowT<DT>::VEC;
+  const int w = vec ? VEC : 1;
+  const void* rows[2] = {row0, row1};
+  const int wv = threadIdx.x >> 6;
+  double M[2] = {-INFINITY, -INFINITY}, S[2] = {0.0, 0.0};
+  for (int b0 = g.u0; b0 < g.u1; b0 += kBlock * kStatUnits) {   // block-uniform batches
+    float x[2][kStatUnits][VEC];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < kStatUnits; ++q) {
+        const int a = b0 + q * kBlock + static_cast<int>(threadIdx.x);
+        const bool in = r < nr && a < g.u1;
+        if (vec) {
+          if (in) {
+            row_vec<DT>(rows[r], a, x[r][q]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) x[r][q][e] = -INFINITY;
+          }
+        } else {
+          x[r][q][0] = in ? row_value<DT>(rows[r], a) : -INFINITY;
+        }
+      }
+    float tm[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      tm[r] = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kStatUnits; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (e < w) tm[r] = fmaxf(tm[r], x[r][q][e]);
+      tm[r] = wave_max(tm[r]);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      wred[wv][0] = tm[0];
+      wred[wv][1] = tm[1];
+    }
+    __syncthreads();
+    double bm[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float m = wred[0][r];
+#pragma unroll
+      for (int q = 1; q < kWaves; ++q) m = fmaxf(m, static_cast<float>(wred[q][r]));
+      bm[r] = fmax(M[r], static_cast<double>(m));   // the running maximum after this batch
+    }
+    double ts[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      ts[r] = 0.0;
+      if (bm[r] != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < kStatUnits; ++q)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            if (e < w) ts[r] += exp_nonpos(static_cast<double>(x[r][q][e]) - bm[r], tab);
+      }
+      ts[r] = wave_sum(ts[r]);
+    }
+    if ((threadIdx.x & 63) == 0) {   // (the sums go to entries 2 and 3, the maxima stay in 0 and 1)
+      wred[wv][2] = ts[0];
+      wred[wv][3] = ts[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      double bs = 0.0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) bs += wred[q][2 + r];
+      if (bm[r] != -INFINITY) {
+        S[r] = (M[r] == -INFINITY ? 0.0 : S[r] * exp_nonpos(M[r] - bm[r], tab)) + bs;
+        M[r] = bm[r];
+      }
+    }
+    if (b0 + kBlock * kStatUnits < g.u1) __syncthreads();   // read before the next batch writes it
+  }
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      out[2 * r] = M[r];
+      out[2 * r + 1] = S[r];
+    }
+  }
+}
+
+// log sum exp of the target (lanes 0..31) and draft (lanes 32..63) rows from the (max, sum)
+// pairs of the G slices, vals[4 k .. 4 k + 3] = (target max, target sum, draft max, draft
+// sum) of slice k: lane l merges slice l % 32 of its row, the wave combines them. Every
+// wave of every workgroup computes it the same way, so all see the same bits.
+__device__ __forceinline__ void merged_lse2(const double* vals, int G, const double* tab, double& lt, double& ld) {
+  const int lane = threadIdx.x & 63;
+  const int k = lane & 31, r = lane >> 5;
+  const double m = k < G ? vals[4 * k + 2 * r] : -INFINITY;
+  const double sm = k < G ? vals[4 * k + 2 * r + 1] : 0.0;
+  double M = m;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+  double t = m == -INFINITY ? 0.0 : sm * exp_nonpos(m - M, tab);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  const double l = M + log(t);
+  lt = __shfl(l, 0, 64);
+  ld = __shfl(l, 32, 64);
 }
 
 // One rejection: out = max(p - q, 0) over this workgroup's units (entry j at j - d.base);
@@ -487,184 +614,8 @@ __device__ int slice_inverse_cdf(const WalkDist<DT>& d, const WalkGroup& g, doub
   return sm.pick;
 }
 
-// log-sum-exp of a row from its chunk statistics (nch <= 64), by wave 0; the result is
-// valid in lane 0.
-__device__ __forceinline__ double chunk_lse(const ChunkStat* st, int nch, const double* tab) {
-  const int c = threadIdx.x;
-  const float mc = c < nch ? ld_cc(&st[c].maxv) : -INFINITY;
-  const double sc = c < nch ? ld_cc(&st[c].sumexp) : 0.0;
-  const float M = wave_max(mc);
-  const double term = (c < nch && mc != -INFINITY)
-                          ? sc * exp_nonpos(static_cast<double>(mc) - static_cast<double>(M), tab) : 0.0;
-  const double sum = wave_sum(term);
-  return static_cast<double>(M) + log(sum);
-}
-
-// Phase 1: (max, float64 sum of exp) of every chunk of every node's target and draft rows.
-// Work item it = ((s * n_cap + i) * 2 + row kind) * nch + chunk, the index of its ChunkStat.
-// A grid of resident workgroups walks the items with a stride of the grid size; each
-// workgroup issues the loads of its next chunk (and the tree lookups of the one after)
-// before reducing the current chunk, so loading overlaps the float64 exponentials. The
-// statistics are plain stores read after the kernel boundary (by the merge kernel or the
-// walk), so no workgroup waits on another here.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void sample_lse_kernel(SampleArgs a) {
-  __shared__ RowSmem rs;
-  __shared__ float wmax[2][kWaves];    // per-wave results, double-buffered by item parity
-  __shared__ double wse[2][kWaves];
-  using Rw = RowT<DT>;
-  row_smem_init(rs);
-  {   // every exchange slot of the walk starts empty
-    unsigned long long* x = reinterpret_cast<unsigned long long*>(a.xch);
-    const size_t n = static_cast<size_t>(a.S) * a.max_pass * kXchStride;
-    for (size_t q = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; q < n;
-         q += static_cast<size_t>(gridDim.x) * kBlock)
-      x[q] = kSlotEmpty;
-  }
-  __syncthreads();
-  const int nch = a.nch;
-  const int cap = a.tree.n_cap;
-  const int items = a.S * cap * 2 * nch;
-  const int step = static_cast<int>(gridDim.x);
-  const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
-  const int w = threadIdx.x >> 6;
-
-  // Reduces chunk values x of item `it` to its ChunkStat (wave results combined by thread 0).
-  auto reduce = [&](const float (&x)[Rw::E], int it, bool real, int par) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < Rw::E; ++j) m = fmaxf(m, x[j]);
-    const float mw = wave_max(m);
-    double se = 0.0;
-    if (mw != -INFINITY) se = exp_nonpos_sum<Rw::E>(x, static_cast<double>(mw), rs.exptab);
-    se = wave_sum(se);
-    if ((threadIdx.x & 63) == 0) {
-      wmax[par][w] = mw;
-      wse[par][w] = se;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && real) {
-      float M = -INFINITY;
-      for (int q = 0; q < kWaves; ++q) M = fmaxf(M, wmax[par][q]);
-      double S = 0.0;
-      for (int q = 0; q < kWaves; ++q)
-        if (wmax[par][q] != -INFINITY)
-          S += wse[par][q] * exp_nonpos(static_cast<double>(wmax[par][q]) - static_cast<double>(M), rs.exptab);
-      a.st[it].maxv = M;
-      a.st[it].sumexp = S;
-    }
-  };
-  // Tree lookups (node count, row) of this workgroup's items, loaded once: lane j holds
-  // those of its j-th item (the grid gives no workgroup more than 64 items), so the loop
-  // reads them with a lane shuffle instead of waiting on a load per item.
-  struct Meta {
-    int n, r;
-  };
-  int bn, br;
-  {
-    const int itj = static_cast<int>(blockIdx.x) + (static_cast<int>(threadIdx.x) & 63) * step;
-    const int node = min(itj, items - 1) / nch / 2;   // s * cap + i
-    bn = a.tree.n_nodes[node / cap];
-    br = a.tree.row[node];
-  }
-  auto meta = [&](int k) {   // k: the item's position in this workgroup's sequence
-    Meta m;
-    m.n = __shfl(bn, k, 64);
-    m.r = __shfl(br, k, 64);
-    return m;
-  };
-  // Row of item `it`; `real` is false for items past the end or past the sequence's node
-  // count (those load row 0 of their sequence and store nothing).
-  auto row_of = [&](int it, const Meta& m, bool& real) {
-    const int b2 = min(it, items - 1) / nch;
-    const int node = b2 >> 1, s = node / cap, i = node % cap;
-    if (it < items && m.n > cap && threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
-    const bool in_tree = it < items && i < m.n && m.n <= cap;
-    real = in_tree && m.r >= 0 && m.r < a.R;
-    // a row outside the table is never read; the walk refuses the tree
-    if (in_tree && !real && threadIdx.x == 0) atomicExch(&a.hdr->err, kErrBadRow);
-    return static_cast<const char*>((b2 & 1) ? a.draft : a.target) +
-           (static_cast<size_t>(s) * a.R + (real ? m.r : 0)) * row_bytes;
-  };
-
-  const bool vec = a.V >= Rw::VEC && row_bytes % 16 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(a.target) | reinterpret_cast<uintptr_t>(a.draft)) & 15u) == 0;
-  int par = 0;
-  if (!vec) {   // unaligned rows: one synchronous chunk at a time
-    for (int it = blockIdx.x, k = 0; it < items; it += step, ++k) {
-      bool real;
-      const char* row = row_of(it, meta(k), real);
-      float x[Rw::E];
-      uint32_t key[Rw::E];
-      load_chunk<DT>(row, a.V, it % nch, x, key);
-      reduce(x, it, real, par);
-      par ^= 1;
-    }
-    return;
-  }
-  int it = blockIdx.x;
-  bool real0;
-  const char* row0 = row_of(it, meta(0), real0);
-  RawChunk rc;
-  raw_chunk_load<DT>(row0, a.V, min(it, items - 1) % nch, rc);
-  for (int k = 1; it < items; it += step, ++k) {
-    bool real1;
-    const char* row1 = row_of(it + step, meta(k), real1);
-    RawChunk rn;
-    raw_chunk_load<DT>(row1, a.V, min(it + step, items - 1) % nch, rn);
-    float x[Rw::E];
-    raw_chunk_decode<DT>(row0, a.V, it % nch, rc, x);
-    reduce(x, it, real0, par);
-    par ^= 1;
-    rc = rn;
-    row0 = row1;
-    real0 = real1;
-  }
-}
-
-// log-sum-exp of one row from its nch chunk statistics, merged with a running maximum;
-// the statistics are loaded 8 at a time (clamped indices, extra entries ignored) so that
-// their loads are in flight together.
-__device__ double row_lse_from_stats(const ChunkStat* st, int nch, const double* tab) {
-  float M = -INFINITY;
-  double S = 0.0;
-  for (int c0 = 0; c0 < nch; c0 += 8) {
-    float mc[8];
-    double sc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = min(c0 + j, nch - 1);
-      mc[j] = st[c].maxv;
-      sc[j] = st[c].sumexp;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (c0 + j >= nch || mc[j] == -INFINITY) continue;
-      if (mc[j] > M) {
-        S = S * exp_nonpos(static_cast<double>(M) - static_cast<double>(mc[j]), tab) + sc[j];
-        M = mc[j];
-      } else {
-        S += sc[j] * exp_nonpos(static_cast<double>(mc[j]) - static_cast<double>(M), tab);
-      }
-    }
-  }
-  return static_cast<double>(M) + log(S);
-}
-
-// Phase 1b (trees of more than kBlock / 2 nodes): the log-sum-exp of every row, one thread
-// per row. Smaller trees skip it: the walk merges its rows itself, one per thread.
-__global__ __launch_bounds__(kBlock) void sample_lse_merge_kernel(SampleArgs a) {
-  __shared__ double tab[64];
-  exp_table_load(tab);
-  __syncthreads();
-  const int rows = a.S * a.tree.n_cap * 2;
-  const int q = blockIdx.x * kBlock + threadIdx.x;
-  if (q >= rows) return;
-  a.lse[q] = row_lse_from_stats(a.st + static_cast<size_t>(q) * a.nch, a.nch, tab);
-}
-
-// Phase 2: the walk of sequence blockIdx.x / G, shared by its G workgroups (the group
-// barrier needs them all resident: the launch keeps the grid within what the device holds).
+// The walk of sequence blockIdx.x / G, shared by its G workgroups (the exchanges need them
+// all resident: the launch keeps the grid within what the device holds).
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   __shared__ SampleSmem sm;
@@ -675,22 +626,17 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   const int s = blockIdx.x / a.G;
   const int cap = a.tree.n_cap;
   const int N = a.tree.n_nodes[s];
-  if (N < 1 || N > cap) {   // every workgroup of the group leaves: no barrier is entered
+  if (N < 1 || N > cap) {   // every workgroup of the group leaves: no exchange is entered
     if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
   }
   const size_t tb = static_cast<size_t>(s) * cap;
   const size_t row_bytes = static_cast<size_t>(a.V) * Rw::ESIZE;
-  const bool merge_here = 2 * cap <= kBlock;   // else sample_lse_merge_kernel ran
   if (threadIdx.x == 0) sm.flag = 0;
   __syncthreads();
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.par[v] = static_cast<short>(a.tree.parent[tb + v]);
     sm.tok[v] = a.tree.token[tb + v];
-    if (!merge_here) {
-      sm.lset[v] = a.lse[(tb + v) * 2 + 0];
-      sm.lsed[v] = a.lse[(tb + v) * 2 + 1];
-    }
     // rows are read at every node the walk may visit, tokens at every child tried: both
     // must lie inside the tables
     const int r = a.tree.row[tb + v];
@@ -706,14 +652,6 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     }
     return;
   }
-  if (merge_here) {
-    const int q = threadIdx.x;
-    if (q < 2 * N) {
-      const double l = row_lse_from_stats(a.st + ((tb + (q >> 1)) * 2 + (q & 1)) * a.nch, a.nch, sm.rs.exptab);
-      ((q & 1) ? sm.lsed : sm.lset)[q >> 1] = l;
-    }
-    __syncthreads();
-  }
   const bool vec = a.vec != 0;   // decided by the host plan (rows aligned, V a multiple of VEC)
   WalkGroup grp;
   grp.gi = blockIdx.x % a.G;
@@ -724,7 +662,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     grp.u1 = static_cast<int>(static_cast<long>(units) * (grp.gi + 1) / a.G);
   }
   grp.max_pass = a.max_pass;
-  grp.xch = a.xch + static_cast<size_t>(s) * a.max_pass * kXchStride;
+  grp.xch = reinterpret_cast<unsigned long long*>(a.xch) + static_cast<size_t>(s) * a.max_pass * kXchStride;
   grp.err = &a.hdr->err;
   grp.pass = 0;
   // residual buffers and q cache: this slice in shared memory when it fits, else the
@@ -763,8 +701,27 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     WalkDist<DT> d;
     d.trow = static_cast<const char*>(a.target) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
     d.drow = static_cast<const char*>(a.draft) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
-    d.lt = sm.lset[v];
-    d.ld = sm.lsed[v];
+    // The node's normalisers: every workgroup reduces its slice of the target row (and of
+    // the draft row when children are tried) and the group exchanges the four values.
+    // thread 0 starts the loads the first acceptance test needs (the child's logits in both
+    // rows and its uniform), so that they complete during the pass and the exchange
+    float t_first = 0.f, d_first = 0.f;
+    uint32_t u_first = 0u;
+    if (threadIdx.x == 0 && nk > 0) {
+      const int x = sm.tok[sm.kids[0]];
+      t_first = row_value<DT>(d.trow, x);
+      d_first = row_value<DT>(d.drow, x);
+      u_first = a.u_acc[tb + sm.kids[0]];
+    }
+    {
+      double st[4];
+      slice_stats<DT>(d.trow, d.drow, nk > 0 ? 2 : 1, grp, vec, sm.rs.exptab, sm.wpair, st);
+      if (!group_exchange(grp, st, 4, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
+      for (int k = threadIdx.x; k < 4 * grp.G; k += kBlock) sm.lsev[k] = gvals[k];
+      merged_lse2(gvals, grp.G, sm.rs.exptab, d.lt, d.ld);
+      if (nk == 0) d.ld = 0.0;
+      __syncthreads();   // the copy is complete before gvals is reused
+    }
     d.pc = nullptr;
     d.zc = 1.0;
     d.qc = Q;
@@ -779,10 +736,11 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     for (int q = 0; q < nk; ++q) {
       const int ch = sm.kids[q];
       if (threadIdx.x == 0) {
-        const int x = sm.tok[ch];
-        const double px = (q == 0) ? d.p(x) : px_next;   // the first try reads the target row
-        const double qx = d.q(x);
-        const double u = (static_cast<double>(a.u_acc[tb + ch]) + 0.5) * inv32;
+        // p and q at the child's token: the first try from the prefetched logits, a later
+        // one from the value the last exchange published and the prefetched draft logit
+        const double px = (q == 0) ? exp_nonpos(static_cast<double>(t_first) - d.lt, d.tab) : px_next;
+        const double qx = exp_nonpos(static_cast<double>(d_first) - d.ld, d.tab);
+        const double u = (static_cast<double>(u_first) + 0.5) * inv32;
         sm.accept = (qx > 0.0) ? (u < px / qx ? 1 : 0) : (px > 0.0 ? 1 : 0);
       }
       __syncthreads();
@@ -800,12 +758,16 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       const int xn = (q + 1 < nk) ? sm.tok[sm.kids[q + 1]] : -1;
       const int xu = vec ? xn / Rw::VEC : xn;
       const bool owner = xn >= 0 && xu >= grp.u0 && xu < grp.u1;
+      if (xn >= 0 && threadIdx.x == 0) {   // the next try's draft logit and uniform, during the exchange
+        d_first = row_value<DT>(d.drow, xn);
+        u_first = a.u_acc[tb + sm.kids[q + 1]];
+      }
       double e0 = 0.0, e1 = 0.0;
       if (owner && threadIdx.x == 0) {
         e1 = d.p(xn);
         e0 = fmax(e1 - d.q(xn), 0.0);   // the entry residual_slice stored for xn
       }
-      if (!group_exchange(grp, part, owner, e0, e1, xn >= 0, gvals, &sm.flag)) return;
+      if (!group_exchange(grp, &part, 1, owner, e0, e1, xn >= 0, gvals, &sm.flag)) return;
       double z = 0.0;
       for (int k = 0; k < grp.G; ++k) z += gvals[k];
       if (z > 0.0) {
@@ -826,13 +788,19 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
       continue;
     }
     // bonus: inverse CDF of the current p with u_res[v]; slice masses first. After a
-    // rejection whose residual became p, they are that exchange's slice sums over z;
-    // otherwise (a leaf, or p kept from before) one pass and an exchange find them.
+    // rejection whose residual became p, they are that exchange's slice sums over z; while
+    // p is still the target's softmax (a leaf, or residuals that summed to 0 every time),
+    // they follow from the node's slice statistics, m_g and s_g: s_g exp(m_g - lt); else one
+    // pass and an exchange find them.
     const double u = (static_cast<double>(a.u_res[tb + v]) + 0.5) * inv32;
-    double mass = 0.0;
     if (z_last > 0.0) {
       __syncthreads();
       for (int k = threadIdx.x; k < grp.G; k += kBlock) gvals[k] /= z_last;
+      __syncthreads();
+    } else if (d.pc == nullptr) {
+      __syncthreads();
+      for (int k = threadIdx.x; k < grp.G; k += kBlock)
+        gvals[k] = sm.lsev[4 * k] == -INFINITY ? 0.0 : sm.lsev[4 * k + 1] * exp_nonpos(sm.lsev[4 * k] - d.lt, d.tab);
       __syncthreads();
     } else {
       constexpr int VEC = Rw::VEC;
@@ -846,8 +814,8 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
         for (int e = 0; e < VEC; ++e)
           if (e < w) loc += pv[e];
       }
-      mass = block_sum(loc, sm.rs.redd);
-      if (!group_exchange(grp, mass, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
+      const double mass = block_sum(loc, sm.rs.redd);
+      if (!group_exchange(grp, &mass, 1, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
     }
     double total = 0.0;
     for (int k = 0; k < grp.G; ++k) total += gvals[k];
@@ -880,46 +848,24 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     const bool done = walk_compact(a.kvc, s, cap, sm.spath, A + 1, grp.gi, grp.G);
     if (lead && threadIdx.x == 0) a.kvc.P_new[s] = done ? a.kvc.P[s] + A + 1 : -1;
   }
+  // The last workgroup of the group to finish empties the exchange slots the walk used (every
+  // workgroup arrives only after its last read of them), ready for the next call.
+  if (last_arrival(&a.done[s], static_cast<unsigned>(grp.G), &sm.flag)) {
+    const size_t used = static_cast<size_t>(grp.pass) * kXchStride;
+    for (size_t k = threadIdx.x; k < used; k += kBlock) grp.xch[k] = 0ull;
+  }
 }
 
 int launch_verify_sample(const SampleArgs& a, int S, int dtype, hipStream_t st) {
-  const dim3 grid(a.lse_grid);
-  if (dtype == 1)
-    hipLaunchKernelGGL(sample_lse_kernel<1>, grid, dim3(kBlock), 0, st, a);
-  else
-    hipLaunchKernelGGL(sample_lse_kernel<0>, grid, dim3(kBlock), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return -1;
-  if (2 * a.tree.n_cap > kBlock) {   // smaller trees merge their rows inside the walk
-    hipLaunchKernelGGL(sample_lse_merge_kernel, dim3((S * a.tree.n_cap * 2 + kBlock - 1) / kBlock), dim3(kBlock),
-                       0, st, a);
-    if (hipGetLastError() != hipSuccess) return -1;
-  }
   // An ordinary launch on the caller's stream: the grid (S * G) is at most the number of
   // workgroups the device holds at once, so every group is resident together once the
   // stream reaches this kernel. (A cooperative launch is avoided: measured on MI355X it
   // let consecutive walks share the group barrier and time out now and then.)
   if (dtype == 1)
-    hipLaunchKernelGGL(sample_walk_kernel<1>, dim3(S * a.G), dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(sample_walk_kernel<1>, dim3(S * a.G), dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(sample_walk_kernel<0>, dim3(S * a.G), dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(sample_walk_kernel<0>, dim3(S * a.G), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// Workgroups of the chunk-statistics kernel that can be resident at once (queried once
-// per device).
-int sample_lse_max_blocks(int dtype) {
-  static int cached[64][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  int& c = cached[dev][dtype ? 1 : 0];
-  if (c > 0) return c;
-  int ncu = 0, per = 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const void* fn = dtype ? reinterpret_cast<const void*>(&sample_lse_kernel<1>)
-                         : reinterpret_cast<const void*>(&sample_lse_kernel<0>);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kBlock, 0) != hipSuccess || per < 1) return -1;
-  c = ncu * per;
-  return c;
 }
 
 // Workgroups of the walk kernel that can be resident at once (queried once per device).
@@ -941,9 +887,9 @@ int sample_walk_max_blocks(int dtype) {
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st) {
   const dim3 grid(S * a.tree.n_cap * a.nch);
   if (dtype == 1)
-    hipLaunchKernelGGL(verify_greedy_kernel<1>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(verify_greedy_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else
-    hipLaunchKernelGGL(verify_greedy_kernel<0>, grid, dim3(kBlock), 0, st, a);
+    DTV_LAUNCH(verify_greedy_kernel<0>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

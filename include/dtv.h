@@ -311,6 +311,23 @@ int dtv_tree_verify_sample_compact(const dtv_tree* tree, int32_t S, const void* 
                                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Kernel timing, for measurement (not part of the pages' method).
+ *
+ * dtv_kernel_timing(enable, reset): with enable = 1, every later launch of the library
+ * (any thread, any stream) is bracketed by two HIP events recorded on its stream, which
+ * adds a few microseconds between kernels; with enable = 0 launches are not timed. With
+ * reset = 1 the totals (and any launches not yet read) are dropped first. Host call;
+ * returns DTV_OK or DTV_EHIP.
+ * dtv_kernel_times(cap, names_h, name_bytes, total_ms_h, launches_h): waits for every timed
+ * launch so far, then writes, for up to cap kernels, the kernel's name (without template
+ * arguments, NUL-terminated in name_bytes bytes at names_h + i * name_bytes), the summed
+ * event time in milliseconds and the number of timed launches. Any output may be NULL.
+ * Returns the number of distinct kernels timed (which may exceed cap), or DTV_EHIP.
+ */
+int dtv_kernel_timing(int enable, int reset);
+int dtv_kernel_times(int32_t cap, char* names_h, int32_t name_bytes, double* total_ms_h, int64_t* launches_h);
+
+/* ---------------------------------------------------------------------------------
  * Draft-efficiency bookkeeping (TALON page, section 5.3). Host only.
  *
  * accepted_h[t] = A_t accepted draft tokens of verification pass t (t < n_passes),

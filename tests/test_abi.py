@@ -175,7 +175,9 @@ def test_sample_walk_plan_fits_its_buffers(lib, S, n_cap, V, dtype, resident, ve
     assert in_lds == (se <= 4096)
     if not in_lds:
         assert se <= V and pbuf == 3 * V     # entries index the workspace rows, j < V
-    assert xch >= n_cap                      # at most n_cap - 1 rejections and one bonus draw
+    # one slot per visited node (at most n_cap), per rejection (at most n_cap - 1) and one
+    # for a bonus draw
+    assert xch >= 2 * n_cap
 
 
 @pytest.mark.parametrize("S,n_cap,V,dtype,resident,vec,code", [
