@@ -64,7 +64,27 @@ def given_tree(parent, token) -> Tree:
     return t
 
 
-def talon(draft: RowFn, B: int, K: int, alpha: float) -> Tree:
+def _boundary_margin(ranked, k: int, score, group) -> float:
+    """Smallest score gap between a kept and a dropped candidate of different groups, when
+    `ranked` (best first) keeps its first k: the decision that two rows' normalisers could
+    flip. Candidates of one group (one parent row) differ by their logits alone, exactly,
+    so their order is not a cross-row decision. inf when no such pair exists."""
+    kept_min, drop_max = {}, {}
+    for i, c in enumerate(ranked):
+        g, sc = group(c), score(c)
+        if i < k:
+            kept_min[g] = min(kept_min.get(g, math.inf), sc)
+        else:
+            drop_max[g] = max(drop_max.get(g, -math.inf), sc)
+    m = math.inf
+    for ga, lo in kept_min.items():
+        for gb, hi in drop_max.items():
+            if ga != gb:
+                m = min(m, lo - hi)
+    return m
+
+
+def talon(draft: RowFn, B: int, K: int, alpha: float, margins: list | None = None) -> Tree:
     """TALON budget-driven hybrid expansion (TALON page, sections 5.1 and 5.2).
 
     * Budget (5.1): B is the largest number of draft nodes; the root is extra (slot 0).
@@ -85,6 +105,12 @@ def talon(draft: RowFn, B: int, K: int, alpha: float) -> Tree:
     * The loop ends when B nodes exist; the anchor always passes, so every layer adds
       at least one node.
     * Rows are keyed by slot: node i expands with draft row i.
+
+    With ``margins`` (a list), every cross-row decision appends (kind, margin): for the
+    gate, |log s(c) - (log alpha + log anchor)| of every candidate whose parent differs
+    from the anchor's; for the budget cut, the smallest score gap between a kept and a
+    dropped candidate of different parents. Margins are in log units (relative
+    differences of the path probabilities); they are reported, not used.
     """
     if B < 1 or K < 1 or not (0.0 <= alpha <= 1.0):
         raise ValueError("need B >= 1, K >= 1 and 0 <= alpha <= 1")
@@ -108,8 +134,16 @@ def talon(draft: RowFn, B: int, K: int, alpha: float) -> Tree:
         anchor = max(c[0] for c in pool)
         kept = [c for c in pool if c[0] >= log_alpha + anchor]
         room = B - (t.N - 1)
+        if margins is not None and alpha > 0.0:
+            a_par = next(c[1] for c in pool if c[0] == anchor)
+            for c in pool:
+                if c[1] != a_par:
+                    margins.append(("talon_gate", abs(c[0] - (log_alpha + anchor))))
         if len(kept) > room:
-            kept = sorted(kept, key=lambda c: (-c[0], c[1], c[2]))[:room]
+            ranked = sorted(kept, key=lambda c: (-c[0], c[1], c[2]))
+            if margins is not None:
+                margins.append(("talon_cap", _boundary_margin(ranked, room, lambda c: c[0], lambda c: c[1])))
+            kept = ranked[:room]
         kept.sort(key=lambda c: (c[1], c[2]))
         prev = []
         for s, v, r, tok in kept:
@@ -149,7 +183,7 @@ def spine(draft: RowFn, spine_tokens, widths) -> Tree:
     return t
 
 
-def opt_tree(draft: RowFn, n: int, delta: float, max_layers: int) -> Tree:
+def opt_tree(draft: RowFn, n: int, delta: float, max_layers: int, margins: list | None = None) -> Tree:
     """OPT-Tree greedy construction (OPT-Tree summary, section 3).
 
     * A node's score is the product of draft probabilities along its parent path, kept
@@ -169,6 +203,11 @@ def opt_tree(draft: RowFn, n: int, delta: float, max_layers: int) -> Tree:
       frontier order.
     * Row identity: the node at frontier position p of layer l uses row
       1 + (l-1)*n + p of the tables (the root uses row 0).
+
+    With ``margins`` (a list), every cross-row decision appends (kind, margin): the layer's
+    selection and the best-n set (smallest score gap between a kept and a dropped
+    candidate of different parents, log units) and the stop test (|E_l - E_{l-1} - delta|).
+    They are reported, not used.
     """
     if n < 1 or max_layers < 1:
         raise ValueError("need n >= 1 and max_layers >= 1")
@@ -190,16 +229,24 @@ def opt_tree(draft: RowFn, n: int, delta: float, max_layers: int) -> Tree:
                 pool.append((s_v + lp[tok], pos, r, int(tok)))
         layers += 1
         rows_read += len(frontier)
-        best = sorted(pool, key=lambda c: (-c[0], c[1], c[2]))[:n]
+        ranked = sorted(pool, key=lambda c: (-c[0], c[1], c[2]))
+        if margins is not None and len(ranked) > n:
+            margins.append(("opt_layer", _boundary_margin(ranked, n, lambda c: c[0], lambda c: c[1])))
+        best = ranked[:n]
         best.sort(key=lambda c: (c[1], c[2]))
         new_frontier = []
         for p_new, (s, pos, r, tok) in enumerate(best):
             nodes.append((s, layer, p_new, frontier[pos], r, tok, 1 + (layer - 1) * n + p_new))
             new_frontier.append(len(nodes) - 1)
         frontier = new_frontier
-        top = sorted(nodes, key=lambda c: (-c[0], c[1], c[2]))[:n]
+        allr = sorted(nodes, key=lambda c: (-c[0], c[1], c[2]))
+        if margins is not None and len(allr) > n:
+            margins.append(("opt_best", _boundary_margin(allr, n, lambda c: c[0], lambda c: (c[1], c[3]))))
+        top = allr[:n]
         E_l = float(sum(math.exp(c[0]) for c in top))
         expected.append(E_l)
+        if margins is not None and layer < max_layers:
+            margins.append(("opt_stop", abs((E_l - E_prev) - delta)))
         if E_l - E_prev < delta:
             break
         E_prev = E_l

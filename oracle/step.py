@@ -18,26 +18,29 @@ from . import attention, bookkeeping, build, compact, mask, verify
 from .rows import decode
 
 
-def build_tree(wl, s: int) -> build.Tree:
+def build_tree(wl, s: int, margins: list | None = None) -> build.Tree:
+    """Sequence s's tree; ``margins`` (a list) receives the build's cross-row decision margins."""
     cfg = wl.cfg
     draft = lambda r: decode(wl.draft[s, r], cfg.dtype)
     if cfg.build == "given":
         n = cfg.N if getattr(wl, "n_nodes", None) is None else int(wl.n_nodes[s])
         return build.given_tree(wl.parent[s][:n], wl.token[s][:n])
     if cfg.build == "talon":
-        return build.talon(draft, cfg.B, cfg.K, cfg.alpha)
+        return build.talon(draft, cfg.B, cfg.K, cfg.alpha, margins=margins)
     if cfg.build == "spine":
         return build.spine(draft, wl.spine[s], wl.widths)
     if cfg.build == "opt":
-        return build.opt_tree(draft, cfg.n, cfg.delta, cfg.max_layers)
+        return build.opt_tree(draft, cfg.n, cfg.delta, cfg.max_layers, margins=margins)
     raise ValueError(cfg.build)
 
 
-def run_step(wl, attn_pairs=None, sequences=None, with_attention=True, timings=None) -> list:
+def run_step(wl, attn_pairs=None, sequences=None, with_attention=True, timings=None, margins=None) -> list:
     """Per sequence: tree, mask words, attention output, verification and compaction.
 
     ``attn_pairs`` restricts attention to the listed (node, head) pairs; ``sequences``
-    restricts the step to some sequences. ``timings`` (a dict) receives seconds per stage.
+    restricts the step to some sequences. ``timings`` (a dict) receives seconds per stage;
+    ``margins`` (a list) receives every cross-row decision margin of the build and the
+    verification.
     """
     cfg = wl.cfg
     out = []
@@ -45,7 +48,7 @@ def run_step(wl, attn_pairs=None, sequences=None, with_attention=True, timings=N
     tm = timings if timings is not None else {}
     for s in seqs:
         t0 = time.perf_counter()
-        tree = build_tree(wl, s)
+        tree = build_tree(wl, s, margins=margins)
         anc = mask.ancestor_matrix(tree.parent)
         words = (cfg.N + 63) // 64
         anc_words = mask.pack_words(anc, words)
@@ -64,7 +67,7 @@ def run_step(wl, attn_pairs=None, sequences=None, with_attention=True, timings=N
             ver = verify.greedy(tree.parent, tree.token, tree.row, target)
         else:
             ver = verify.sample(tree.parent, tree.token, tree.row, target, draft,
-                                wl.u_acc[s], wl.u_res[s])
+                                wl.u_acc[s], wl.u_res[s], margins=margins)
         t3 = time.perf_counter()
         k2, v2, P_new = compact.kv_compact(wl.k[s], wl.v[s], P, ver["path"])
         t4 = time.perf_counter()

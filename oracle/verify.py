@@ -51,7 +51,7 @@ def inverse_cdf(p: np.ndarray, u32) -> int:
     return int(np.argmax(c > uniform(u32) * c[-1]))
 
 
-def sample(parent, token, row, target, draft, u_acc, u_res) -> dict:
+def sample(parent, token, row, target, draft, u_acc, u_res, margins: list | None = None) -> dict:
     """Rejection-sampling verification (concept page, "The protocol", steps 3-4).
 
     The chain rule of the page: accept a drafted token x with probability
@@ -66,6 +66,11 @@ def sample(parent, token, row, target, draft, u_acc, u_res) -> dict:
       is 0 the current p is kept;
     * on acceptance the walk moves to c; when no child is accepted, or v is a leaf, the
       bonus is drawn from the current p by inverse CDF with u_res[v].
+
+    With ``margins`` (a list), every decision that depends on the rows' normalisers
+    appends (kind, relative margin): each acceptance test |u - p/q| / (p/q), and the bonus
+    draw's distance from the nearer boundary of the drawn entry's cumulative interval,
+    over the total mass. They are reported, not used.
     """
     N = len(parent)
     children = [[] for _ in range(N)]
@@ -89,6 +94,8 @@ def sample(parent, token, row, target, draft, u_acc, u_res) -> dict:
                     ratio = np.inf
                     ok = p[x] > 0.0
                 decisions.append((c, u, ratio))
+                if margins is not None and np.isfinite(ratio) and ratio > 0.0:
+                    margins.append(("sample_accept", abs(u - ratio) / ratio))
                 if ok:
                     accepted = c
                     break
@@ -98,6 +105,11 @@ def sample(parent, token, row, target, draft, u_acc, u_res) -> dict:
                     p = r / z
         if accepted is None:
             bonus = inverse_cdf(p, u_res[v])
+            if margins is not None:
+                c = np.cumsum(p)
+                tgt = uniform(u_res[v]) * c[-1]
+                lo = c[bonus - 1] if bonus > 0 else 0.0
+                margins.append(("sample_bonus", min(tgt - lo, c[bonus] - tgt) / c[-1]))
             break
         v = accepted
         path.append(v)
