@@ -31,6 +31,16 @@ class DtvKvCache(ctypes.Structure):
 
 PKV = ctypes.POINTER(DtvKvCache)
 
+
+class DtvBuildParams(ctypes.Structure):
+    _fields_ = [
+        ("mode", c_i32), ("B", c_i32), ("K", c_i32), ("alpha", c_f64),
+        ("n", c_i32), ("delta", c_f64), ("max_layers", c_i32),
+    ]
+
+
+PBP = ctypes.POINTER(DtvBuildParams)
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "dtv_status_str": (c_char_p, [c_int]),
@@ -50,6 +60,10 @@ SIGNATURES = {
     "dtv_tree_build_opt_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_build_opt": (c_int, [PTREE, c_i32, c_vp, c_int, c_i32, c_i32, c_i32, c_f64, c_i32,
                                    c_vp, c_size, c_vp]),
+    "dtv_tree_build_layered_ws_bytes": (c_size, [PBP, c_i32, c_i32, c_int]),
+    "dtv_tree_build_begin": (c_int, [PTREE, c_i32, PBP, c_vp, c_int, c_i32, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "dtv_tree_build_step": (c_int, [PTREE, c_i32, PBP, c_i32, c_vp, c_i32, c_int, c_i32, c_vp, c_vp, c_vp, c_size,
+                                    c_vp]),
     "dtv_tree_attn_ws_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_int]),
     "dtv_tree_attn": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, PTREE, c_i32, c_i32, c_i32,
                               c_i32, c_int, c_f32, c_vp, c_vp, c_size, c_vp]),

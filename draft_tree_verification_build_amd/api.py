@@ -193,6 +193,44 @@ def tree_build_opt(tree: Tree, draft: torch.Tensor, n: int, delta: float, max_la
           buf.data_ptr(), buf.numel(), _stream(stream))
 
 
+BUILD_TALON, BUILD_OPT = 1, 2
+
+
+def build_params(mode: str, B: int = 0, K: int = 0, alpha: float = 0.0, n: int = 0, delta: float = 0.0,
+                 max_layers: int = 0) -> _lib.DtvBuildParams:
+    """The parameters of a layered build: mode "talon" (B, K, alpha) or "opt" (n, delta, max_layers)."""
+    code = {"talon": BUILD_TALON, "opt": BUILD_OPT}[mode]
+    return _lib.DtvBuildParams(code, int(B), int(K), float(alpha), int(n), float(delta), int(max_layers))
+
+
+def _layered_ws(ws: Workspace, tree: Tree, params, S: int, V: int, dt: int):
+    lib = _lib.load()
+    nb = lib.dtv_tree_build_layered_ws_bytes(ctypes.byref(params), S, V, dt)
+    key = (params.mode, params.B, params.K, params.n, params.max_layers, S, V, dt, tree.n_cap)
+    return ws.get("layered", nb, key)
+
+
+def tree_build_begin(tree: Tree, params, root: torch.Tensor, ws: Workspace, W: torch.Tensor, done: torch.Tensor,
+                     stream=None) -> None:
+    """Layer 1 of a layered build from each sequence's root row (root [S][V]); writes the next
+    frontier's width W [S] and done [S] (int32, device)."""
+    S, V = root.shape
+    dt = _dtype_code(root)
+    buf = _layered_ws(ws, tree, params, S, V, dt)
+    _call("dtv_tree_build_begin", tree.c, S, ctypes.byref(params), _ptr(root), dt, V, _ptr(W), _ptr(done),
+          buf.data_ptr(), buf.numel(), _stream(stream))
+
+
+def tree_build_step(tree: Tree, params, layer: int, frontier: torch.Tensor, ws: Workspace, W: torch.Tensor,
+                    done: torch.Tensor, stream=None) -> None:
+    """Layer `layer` (>= 2) of a layered build from its frontier's rows (frontier [S][W_cap][V])."""
+    S, W_cap, V = frontier.shape
+    dt = _dtype_code(frontier)
+    buf = _layered_ws(ws, tree, params, S, V, dt)
+    _call("dtv_tree_build_step", tree.c, S, ctypes.byref(params), int(layer), _ptr(frontier), W_cap, dt, V,
+          _ptr(W), _ptr(done), buf.data_ptr(), buf.numel(), _stream(stream))
+
+
 def tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, P_max: int,
               tree: Tree, ws: Workspace, scale: float | None = None, o: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:

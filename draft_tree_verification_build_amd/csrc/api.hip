@@ -184,6 +184,7 @@ struct OptLayout {
   double* Eprev;
   int* done;
   int* nlayers;
+  int* fin;
   size_t bytes;
 };
 constexpr int kOptCandCap = 4096;
@@ -215,6 +216,7 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
   L.Eprev = c.take<double>(S);
   L.done = c.take<int>(S);
   L.nlayers = c.take<int>(S);
+  L.fin = c.take<int>(S);
   L.bytes = c.off;
   return L;
 }
@@ -511,6 +513,8 @@ int dtv_tree_build_talon(const dtv_tree* tree, int32_t S, const void* draft, int
   const TalonLayout L = talon_layout(ws, S, B, K, V, dtype);
   REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
   dtv::TalonArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Wr = B;
   a.tree = tree_args(tree);
   a.draft = draft;
   a.R = R;
@@ -598,6 +602,42 @@ int dtv_tree_build_spine(const dtv_tree* tree, int32_t S, const int32_t* spine, 
 
 // ---------------------------------------------------------------- OPT-Tree
 
+}  // extern "C"
+
+// The frontier width of OPT-Tree's layer l follows from n and V alone: layer 1 expands the
+// root; layer l keeps min(n, W_l * min(n, V)) nodes, which are layer l+1's frontier.
+static long opt_frontier_width(int layer, int n, int V) {
+  long W = 1;
+  const long per_row = n < V ? n : V;
+  for (int l = 1; l < layer; ++l) {
+    long kept = W * per_row;
+    W = kept > n ? n : kept;
+  }
+  return W;
+}
+
+// Configures and launches OPT-Tree's layer `layer` on the rows `a` points at.
+static int opt_launch_layer(dtv::OptArgs& a, int layer, int dtype, hipStream_t st) {
+  const int n = a.n, V = a.V, nch = a.nch;
+  const long W = opt_frontier_width(layer, n, V);
+  const long per_row = n < V ? n : V;
+  a.layer = layer;
+  a.W = static_cast<int>(W);
+  const long need = (n + W - 1) / W;                 // reported per row so that W*m >= n
+  long K = need > 8 ? need : 8;
+  if (K > per_row) K = per_row;
+  a.K = static_cast<int>(K);
+  long Kc = (K + nch - 1) / nch;
+  if (Kc < 2) Kc = 2;
+  if (Kc > K) Kc = K;
+  a.Kc = static_cast<int>(Kc);
+  a.Kw = layer == 1 ? dtv::opt_root_wave_quota(V, n, dtype == DTV_BF16 ? 1 : 0) : 0;
+  if (a.Kw > 0) return dtv::launch_opt_root(a, dtype == DTV_BF16 ? 1 : 0, st);   // the root layer in one launch
+  return dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st);
+}
+
+extern "C" {
+
 size_t dtv_tree_build_opt_ws_bytes(int32_t S, int32_t n, int32_t V, int32_t max_layers, int dtype) {
   if (S < 1 || n < 1 || V < 1 || max_layers < 1 || !dtype_ok(dtype)) return 0;
   return opt_layout(nullptr, S, n, V, max_layers, dtype).bytes;
@@ -659,33 +699,169 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
   a.Eprev = L.Eprev;
   a.done = L.done;
   a.nlayers = L.nlayers;
+  a.row_base = -1;
   if (dtv::launch_opt_init(a, st)) return launched(-1);
-  // the frontier width of every layer follows from n and V alone: layer 1 expands the
-  // root; layer l keeps min(n, W_l * min(n, V)) nodes, which are layer l+1's frontier
-  long W = 1;
-  const long per_row = n < V ? n : V;
   for (int layer = 1; layer <= max_layers; ++layer) {
-    a.layer = layer;
-    a.W = static_cast<int>(W);
-    const long need = (n + W - 1) / W;                 // reported per row so that W*m >= n
-    long K = need > 8 ? need : 8;
-    if (K > per_row) K = per_row;
-    a.K = static_cast<int>(K);
-    long Kc = (K + nch - 1) / nch;
-    if (Kc < 2) Kc = 2;
-    if (Kc > K) Kc = K;
-    a.Kc = static_cast<int>(Kc);
-    a.Kw = layer == 1 ? dtv::opt_root_wave_quota(V, n, dtype == DTV_BF16 ? 1 : 0) : 0;
-    if (a.Kw > 0) {   // the root layer in one launch
-      if (dtv::launch_opt_root(a, dtype == DTV_BF16 ? 1 : 0, st)) return launched(-1);
-    } else if (dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st)) {
-      return launched(-1);
-    }
-    long kept = W * per_row;
-    if (kept > n) kept = n;
-    W = kept;
+    if (opt_launch_layer(a, layer, dtype, st)) return launched(-1);
   }
   return launched(dtv::launch_opt_finalize(a, st));
+}
+
+// ---------------------------------------------------------------- layer-by-layer builds
+
+static int layered_check(const dtv_tree* tree, int32_t S, const dtv_build_params* p, int dtype, int32_t V,
+                         const int32_t* W, const int32_t* done) {
+  int rc = check_tree(tree);
+  if (rc) return rc;
+  REQUIRE(p != nullptr && W != nullptr && done != nullptr, DTV_EINVAL, "params, W or done is NULL");
+  REQUIRE(dtype_ok(dtype), DTV_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(S >= 1 && V >= 1, DTV_EINVAL, "S=%d V=%d", S, V);
+  if (p->mode == DTV_BUILD_TALON) {
+    REQUIRE(p->B >= 1, DTV_EINVAL, "B=%d", p->B);
+    REQUIRE(p->B + 1 <= tree->n_cap, DTV_ECAPACITY, "B+1=%d exceeds n_cap=%d", p->B + 1, tree->n_cap);
+    REQUIRE(p->K >= 1 && p->K <= 64, DTV_EUNSUPPORTED, "K=%d outside 1..64", p->K);
+    REQUIRE(static_cast<long>(p->B) * p->K <= 4096, DTV_EUNSUPPORTED, "B*K=%ld exceeds 4096",
+            static_cast<long>(p->B) * p->K);
+    REQUIRE(nch_of(V, dtype) <= 32 && nch_of(V, dtype) * p->K <= 2048, DTV_EUNSUPPORTED,
+            "V=%d with K=%d exceeds the merge capacity (chunks * K <= 2048, chunks <= 32)", V, p->K);
+    REQUIRE(p->alpha >= 0.0 && p->alpha <= 1.0, DTV_EINVAL, "alpha=%g outside [0,1]", p->alpha);
+    return DTV_OK;
+  }
+  if (p->mode == DTV_BUILD_OPT) {
+    const int n = p->n;
+    REQUIRE(n >= 1 && n + 1 <= tree->n_cap, DTV_ECAPACITY, "n+1=%d exceeds n_cap=%d", n + 1, tree->n_cap);
+    REQUIRE(n <= 1023, DTV_EUNSUPPORTED, "n=%d exceeds 1023", n);
+    REQUIRE(V <= (1 << 22), DTV_EUNSUPPORTED, "V=%d exceeds 4194304", V);
+    REQUIRE(p->max_layers >= 1 && p->max_layers <= 64, DTV_EUNSUPPORTED, "max_layers=%d outside 1..64",
+            p->max_layers);
+    REQUIRE(p->delta >= 0.0 && isfinite(p->delta), DTV_EINVAL, "delta=%g", p->delta);
+    const int Kmax = n < V ? n : V;
+    REQUIRE(nch_of(V, dtype) <= 64 && static_cast<long>(nch_of(V, dtype)) * Kmax <= 8192, DTV_EUNSUPPORTED,
+            "V=%d with n=%d exceeds the merge capacity", V, n);
+    return DTV_OK;
+  }
+  return fail(DTV_EINVAL, "build mode %d (DTV_BUILD_TALON or DTV_BUILD_OPT)", p->mode);
+}
+
+// TALON's layered workspace: the row lists of B rows, then the loop state [S][8].
+static size_t talon_layered_bytes(int S, const dtv_build_params* p, int V, int dtype) {
+  return talon_layout(nullptr, S, p->B, p->K, V, dtype).bytes + up(static_cast<size_t>(S) * 8 * sizeof(int));
+}
+
+size_t dtv_tree_build_layered_ws_bytes(const dtv_build_params* p, int32_t S, int32_t V, int dtype) {
+  if (p == nullptr || S < 1 || V < 1 || !dtype_ok(dtype)) return 0;
+  if (p->mode == DTV_BUILD_TALON && p->B >= 1 && p->K >= 1) return talon_layered_bytes(S, p, V, dtype);
+  if (p->mode == DTV_BUILD_OPT && p->n >= 1 && p->max_layers >= 1)
+    return opt_layout(nullptr, S, p->n, V, p->max_layers, dtype).bytes;
+  return 0;
+}
+
+// One layer of a layered build: layer 1 from the root rows ([S][V]), layer l >= 2 from the
+// frontier rows ([S][W_cap][V]).
+static int layered_layer(const dtv_tree* tree, int32_t S, const dtv_build_params* p, int32_t layer,
+                         const void* rows, int32_t W_cap, int dtype, int32_t V, int32_t* W, int32_t* done,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int rc = layered_check(tree, S, p, dtype, V, W, done);
+  if (rc) return rc;
+  REQUIRE(rows != nullptr, DTV_EINVAL, "%s is NULL", layer == 1 ? "root_logits" : "frontier_logits");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dtype == DTV_BF16 ? 1 : 0;
+  if (p->mode == DTV_BUILD_TALON) {
+    REQUIRE(layer == 1 || (W_cap >= 1 && W_cap <= p->B), DTV_EINVAL,
+            "W_cap=%d: a frontier holds 1..B=%d nodes", W_cap, p->B);
+    const size_t need = talon_layered_bytes(S, p, V, dtype);
+    REQUIRE(ws != nullptr && ws_bytes >= need, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+    const TalonLayout L = talon_layout(ws, S, p->B, p->K, V, dtype);
+    dtv::TalonArgs a;
+    memset(&a, 0, sizeof(a));
+    a.tree = tree_args(tree);
+    a.draft = rows;
+    a.R = layer == 1 ? 1 : W_cap;
+    a.Wr = a.R;
+    a.V = V;
+    a.S = S;
+    a.B = p->B;
+    a.K = p->K;
+    a.nch = nch_of(V, dtype);
+    a.log_alpha = p->alpha > 0.0 ? log(p->alpha) : -INFINITY;
+    a.hdr = L.hdr;
+    a.st = L.st;
+    a.cval = L.cval;
+    a.cidx = L.cidx;
+    a.tickets = L.tickets;
+    a.rlse = L.rlse;
+    a.rv = L.rv;
+    a.ri = L.ri;
+    a.rcnt = L.rcnt;
+    a.layer = layer;
+    a.state = reinterpret_cast<int*>(static_cast<char*>(ws) + L.bytes);
+    a.w_out = W;
+    a.done_out = done;
+    return launched(dtv::launch_talon_layer(a, dt, st));
+  }
+  const int n = p->n;
+  REQUIRE(layer <= p->max_layers, DTV_EINVAL, "layer %d beyond max_layers=%d", layer, p->max_layers);
+  const long Wl = opt_frontier_width(layer, n, V);
+  REQUIRE(layer == 1 || W_cap >= Wl, DTV_EINVAL, "layer %d's frontier has %ld nodes; frontier_logits holds %d rows",
+          layer, Wl, W_cap);
+  const OptLayout L = opt_layout(ws, S, n, V, p->max_layers, dtype);
+  REQUIRE(ws != nullptr && ws_bytes >= L.bytes, DTV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.bytes);
+  dtv::OptArgs a;
+  memset(&a, 0, sizeof(a));
+  a.tree = tree_args(tree);
+  a.draft = rows;
+  a.R = layer == 1 ? 1 : W_cap;
+  a.V = V;
+  a.S = S;
+  a.n = n;
+  a.nch = nch_of(V, dtype);
+  a.max_layers = p->max_layers;
+  a.delta = p->delta;
+  a.Wcap = n;
+  a.hdr = L.hdr;
+  a.st = L.st;
+  a.cval = L.cval;
+  a.cidx = L.cidx;
+  a.tickets = L.tickets;
+  a.rlse = L.rlse;
+  a.rv = L.rv;
+  a.ri = L.ri;
+  a.rcnt = L.rcnt;
+  a.lo = L.lo;
+  a.ccount = L.ccount;
+  a.ccap = kOptCandCap;
+  a.cand = static_cast<dtv::OptCand*>(L.cand);
+  a.lscore = L.lscore;
+  a.lparent = L.lparent;
+  a.ltoken = L.ltoken;
+  a.bscore = L.bscore;
+  a.blayer = L.blayer;
+  a.bpos = L.bpos;
+  a.bcount = L.bcount;
+  a.Eprev = L.Eprev;
+  a.done = L.done;
+  a.nlayers = L.nlayers;
+  a.row_base = 0;
+  a.fin = L.fin;
+  a.w_out = W;
+  a.done_out = done;
+  a.w_next = static_cast<int>(opt_frontier_width(layer + 1, n, V));
+  if (layer == 1 && dtv::launch_opt_init(a, st)) return launched(-1);
+  if (opt_launch_layer(a, layer, dtype, st)) return launched(-1);
+  if (dtv::launch_opt_report(a, st)) return launched(-1);
+  return launched(dtv::launch_opt_finalize(a, st));
+}
+
+int dtv_tree_build_begin(const dtv_tree* tree, int32_t S, const dtv_build_params* params, const void* root_logits,
+                         int dtype, int32_t V, int32_t* W, int32_t* done, void* ws, size_t ws_bytes, void* stream) {
+  return layered_layer(tree, S, params, 1, root_logits, 1, dtype, V, W, done, ws, ws_bytes, stream);
+}
+
+int dtv_tree_build_step(const dtv_tree* tree, int32_t S, const dtv_build_params* params, int32_t layer,
+                        const void* frontier_logits, int32_t W_cap, int dtype, int32_t V, int32_t* W, int32_t* done,
+                        void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(layer >= 2, DTV_EINVAL, "layer %d: layer 1 is dtv_tree_build_begin's", layer);
+  return layered_layer(tree, S, params, layer, frontier_logits, W_cap, dtype, V, W, done, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- attention

@@ -85,8 +85,12 @@ __global__ __launch_bounds__(kBlock, 4) void talon_rows_kernel(TalonArgs a) {
   const int nch = a.nch;
   const int K = a.K;
   const int c = blockIdx.x % nch;
-  const int rf = blockIdx.x / nch;       // s * B + f
-  const int s = rf / a.B, f = rf % a.B;  // row f of sequence s is draft row f (rows keyed by slot)
+  const int rf = blockIdx.x / nch;         // s * Wr + f
+  const int s = rf / a.Wr, f = rf % a.Wr;  // row f of sequence s is draft row f
+  if (a.state != nullptr && a.layer > 1) {  // layer by layer: the frontier's rows only
+    const int* st = a.state + 8 * s;
+    if (st[4] != 0 || f >= st[2]) return;
+  }
   const char* row = static_cast<const char*>(a.draft) +
                     (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V) * Rw::ESIZE;
   // the exp table and the chunk in one round trip
@@ -156,110 +160,93 @@ __device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int r
   __syncthreads();
 }
 
-// Phase 2: the layer loop of sequence blockIdx.x in one workgroup. The row lists of phase 1
-// (visible after the kernel boundary) are copied into shared memory in one parallel pass,
-// and every step of a layer is a parallel pass over the layer's candidates e = f*K + j
-// (frontier row f, rank j), so no thread walks a dependent chain of shared-memory reads.
-__global__ __launch_bounds__(kBlock) void talon_select_kernel(TalonArgs a) {
-  __shared__ TalonSelSmem sm;
-  const int s = blockIdx.x;
+// One layer of TALON's loop for sequence s on the state in shared memory: sm.cnt draft
+// nodes so far, the frontier (slots sm.start .. sm.start + sm.width - 1), their scores in
+// sm.tscore and every frontier row's list (log p_d and token of its best entries, sorted)
+// at sm.lp / sm.tok[slot * K + rank], sm.rcnt[slot]. Every step of the layer (scores, anchor,
+// gate, cap, slot numbering) is a parallel pass over its candidates e = f*K + j (frontier
+// row f, rank j), so no thread walks a dependent chain of shared-memory reads. Writes the
+// new nodes to the tree and advances the state.
+__device__ void talon_layer(TalonSelSmem& sm, const TalonArgs& a, int layer, size_t tb) {
   const int K = a.K;
-  const int B = a.B;
-  const size_t rf0 = static_cast<size_t>(s) * B;
-  const size_t tb = static_cast<size_t>(s) * a.tree.n_cap;
-  for (int f = threadIdx.x; f < B; f += kBlock) sm.rcnt[f] = a.rcnt[rf0 + f];
-  for (int e = threadIdx.x; e < B * K; e += kBlock) {
-    const int f = e / K;
-    sm.lp[e] = static_cast<double>(a.rv[rf0 * K + e]) - a.rlse[rf0 + f];
-    sm.tok[e] = a.ri[rf0 * K + e];
-  }
-  if (threadIdx.x == 0) {
-    sm.cnt = 0;
-    sm.start = 0;
-    sm.width = 1;
-    sm.layers = 0;
-    sm.tscore[0] = 0.0;
-    sm.tpar[0] = -1;
+  const int W = sm.width, cnt = sm.cnt, start = sm.start;
+  const int room = a.B - cnt;
+  const int n = W * K;
+  // candidate scores s(c) = s(parent) + log p_d(token | parent); frontier row f is slot start + f
+  for (int e = threadIdx.x; e < n; e += kBlock) {
+    const int f = e / K, j = e % K, r = start + f;
+    sm.csc[e] = j < sm.rcnt[r] ? sm.tscore[r] + sm.lp[r * K + j] : -INFINITY;
   }
   __syncthreads();
-  for (int layer = 1;; ++layer) {
-    const int W = sm.width, cnt = sm.cnt, start = sm.start;
-    const int room = B - cnt;
-    const int n = W * K;
-    // candidate scores s(c) = s(parent) + log p_d(token | parent); frontier row f is slot start + f
-    for (int e = threadIdx.x; e < n; e += kBlock) {
-      const int f = e / K, j = e % K, r = start + f;
-      sm.csc[e] = j < sm.rcnt[r] ? sm.tscore[r] + sm.lp[r * K + j] : -INFINITY;
-    }
+  if (layer == 1) {
+    // robust initialisation: the root's Top-K, at most the budget, no gate
+    if (threadIdx.x == 0) sm.kept[0] = sm.rcnt[0] < room ? sm.rcnt[0] : room;
     __syncthreads();
-    if (layer == 1) {
-      // robust initialisation: the root's Top-K, at most the budget, no gate
-      if (threadIdx.x == 0) sm.kept[0] = sm.rcnt[0] < room ? sm.rcnt[0] : room;
+  } else {
+    double mx = -INFINITY;
+    for (int f = threadIdx.x; f < W; f += kBlock) mx = fmax(mx, sm.csc[f * K]);
+    const double anchor = block_max(mx, sm.redd);
+    const double thr = a.log_alpha + anchor;
+    // row lists are sorted, so the gated entries of a row are a prefix of it
+    int tg = 0;
+    for (int f = threadIdx.x; f < W; f += kBlock) {
+      int g = 0;
+      for (int j = 0; j < K; ++j) g += sm.csc[f * K + j] >= thr ? 1 : 0;
+      sm.gated[f] = g;
+      tg += g;
+    }
+    tg = block_sum(tg, sm.redi);
+    if (tg <= room) {
+      for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = sm.gated[f];
       __syncthreads();
     } else {
-      double mx = -INFINITY;
-      for (int f = threadIdx.x; f < W; f += kBlock) mx = fmax(mx, sm.csc[f * K]);
-      const double anchor = block_max(mx, sm.redd);
-      const double thr = a.log_alpha + anchor;
-      // row lists are sorted, so the gated entries of a row are a prefix of it
-      int tg = 0;
-      for (int f = threadIdx.x; f < W; f += kBlock) {
-        int g = 0;
-        for (int j = 0; j < K; ++j) g += sm.csc[f * K + j] >= thr ? 1 : 0;
-        sm.gated[f] = g;
-        tg += g;
-      }
-      tg = block_sum(tg, sm.redi);
-      if (tg <= room) {
-        for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = sm.gated[f];
-        __syncthreads();
-      } else {
-        // budget respect: the `room` best gated candidates by (score desc, parent slot
-        // asc, rank asc) = (key desc, e asc)
-        for (int e = threadIdx.x; e < n; e += kBlock)
-          sm.ckey[e] = (e % K) < sm.gated[e / K] ? dkey(sm.csc[e]) : 0ull;
-        __syncthreads();
-        talon_budget_select(sm, n, K, W, room);
-      }
+      // budget respect: the `room` best gated candidates by (score desc, parent slot
+      // asc, rank asc) = (key desc, e asc)
+      for (int e = threadIdx.x; e < n; e += kBlock)
+        sm.ckey[e] = (e % K) < sm.gated[e / K] ? dkey(sm.csc[e]) : 0ull;
+      __syncthreads();
+      talon_budget_select(sm, n, K, W, room);
     }
-    // new slots in (parent slot, rank) order: row f's kept entries follow those of rows < f
-    int carry = 0;
-    for (int f0 = 0; f0 < W; f0 += kBlock) {
-      const int f = f0 + threadIdx.x;
-      int tot = 0;
-      const int ex = block_exclusive_scan(f < W ? sm.kept[f] : 0, sm.scan, &tot);
-      if (f < W) sm.rowbase[f] = carry + ex;
-      carry += tot;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kBlock) {
-      const int f = e / K, j = e % K;
-      if (j >= sm.kept[f]) continue;
-      const int parent = start + f;
-      const int slot = cnt + 1 + sm.rowbase[f] + j;
-      const double sc = sm.csc[e];
-      sm.tscore[slot] = sc;
-      sm.tpar[slot] = static_cast<short>(parent);
-      const size_t o = tb + slot;
-      a.tree.parent[o] = parent;
-      a.tree.token[o] = sm.tok[parent * K + j];
-      a.tree.depth[o] = layer;
-      a.tree.row[o] = slot;
-      a.tree.score[o] = sc;
-    }
-    if (threadIdx.x == 0) {
-      sm.start = cnt + 1;
-      sm.width = carry;
-      sm.cnt = cnt + carry;
-      sm.layers = layer;
-      sm.carry = carry;
-      if (carry == 0) atomicExch(&a.hdr->err, kErrCapacity);
-    }
-    __syncthreads();
-    if (sm.cnt >= B || sm.carry == 0) break;
   }
+  // new slots in (parent slot, rank) order: row f's kept entries follow those of rows < f
+  int carry = 0;
+  for (int f0 = 0; f0 < W; f0 += kBlock) {
+    const int f = f0 + threadIdx.x;
+    int tot = 0;
+    const int ex = block_exclusive_scan(f < W ? sm.kept[f] : 0, sm.scan, &tot);
+    if (f < W) sm.rowbase[f] = carry + ex;
+    carry += tot;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += kBlock) {
+    const int f = e / K, j = e % K;
+    if (j >= sm.kept[f]) continue;
+    const int parent = start + f;
+    const int slot = cnt + 1 + sm.rowbase[f] + j;
+    const double sc = sm.csc[e];
+    sm.tscore[slot] = sc;
+    sm.tpar[slot] = static_cast<short>(parent);
+    const size_t o = tb + slot;
+    a.tree.parent[o] = parent;
+    a.tree.token[o] = sm.tok[parent * K + j];
+    a.tree.depth[o] = layer;
+    a.tree.row[o] = slot;
+    a.tree.score[o] = sc;
+  }
+  if (threadIdx.x == 0) {
+    sm.start = cnt + 1;
+    sm.width = carry;
+    sm.cnt = cnt + carry;
+    sm.layers = layer;
+    sm.carry = carry;
+    if (carry == 0) atomicExch(&a.hdr->err, kErrCapacity);
+  }
+  __syncthreads();
+}
 
-  // root, counts and ancestor-or-self masks
+// The root's arrays, the node count and every node's ancestor-or-self mask from the parents
+// in sm.tpar (slots 0 .. sm.cnt).
+__device__ void talon_finish(TalonSelSmem& sm, const TalonArgs& a, int s, size_t tb) {
   const int nn = sm.cnt + 1;
   if (threadIdx.x == 0) {
     a.tree.parent[tb] = -1;
@@ -285,6 +272,97 @@ __global__ __launch_bounds__(kBlock) void talon_select_kernel(TalonArgs a) {
     for (int w = 0; w < kMaxWords; ++w)
       if (w < words) an[w] = acc[w];
   }
+}
+
+__device__ __forceinline__ void talon_state_root(TalonSelSmem& sm) {
+  if (threadIdx.x == 0) {
+    sm.cnt = 0;
+    sm.start = 0;
+    sm.width = 1;
+    sm.layers = 0;
+    sm.tscore[0] = 0.0;
+    sm.tpar[0] = -1;
+  }
+}
+
+// Phase 2 of the whole-table build: the layer loop of sequence blockIdx.x in one
+// workgroup, on the row lists of phase 1 (visible after the kernel boundary), copied into
+// shared memory in one parallel pass.
+__global__ __launch_bounds__(kBlock) void talon_select_kernel(TalonArgs a) {
+  __shared__ TalonSelSmem sm;
+  const int s = blockIdx.x;
+  const int K = a.K;
+  const int B = a.B;
+  const size_t rf0 = static_cast<size_t>(s) * B;
+  const size_t tb = static_cast<size_t>(s) * a.tree.n_cap;
+  for (int f = threadIdx.x; f < B; f += kBlock) sm.rcnt[f] = a.rcnt[rf0 + f];
+  for (int e = threadIdx.x; e < B * K; e += kBlock) {
+    const int f = e / K;
+    sm.lp[e] = static_cast<double>(a.rv[rf0 * K + e]) - a.rlse[rf0 + f];
+    sm.tok[e] = a.ri[rf0 * K + e];
+  }
+  talon_state_root(sm);
+  __syncthreads();
+  for (int layer = 1;; ++layer) {
+    talon_layer(sm, a, layer, tb);
+    if (sm.cnt >= B || sm.carry == 0) break;
+  }
+  talon_finish(sm, a, s, tb);
+}
+
+// One layer of the layer-by-layer build for sequence blockIdx.x: the state of the earlier
+// layers comes from the workspace (counts) and the tree (scores and parents of the nodes
+// so far); this call's frontier lists (call rows f < width, reduced by talon_rows_kernel)
+// go to the frontier slots start + f. A finished sequence is left as it is.
+__global__ __launch_bounds__(kBlock) void talon_layer_kernel(TalonArgs a) {
+  __shared__ TalonSelSmem sm;
+  const int s = blockIdx.x;
+  const int K = a.K;
+  const size_t tb = static_cast<size_t>(s) * a.tree.n_cap;
+  int* st = a.state + 8 * s;
+  if (a.layer == 1) {
+    talon_state_root(sm);
+  } else if (threadIdx.x == 0) {
+    sm.cnt = st[0];
+    sm.start = st[1];
+    sm.width = st[2];
+    sm.layers = st[3];
+    sm.carry = st[4];   // done
+  }
+  __syncthreads();
+  if (a.layer > 1 && sm.carry != 0) return;
+  const int W = sm.width, start = sm.start;
+  if (W > a.Wr) {   // the call brought fewer rows than the frontier has nodes
+    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    return;
+  }
+  const size_t rf0 = static_cast<size_t>(s) * a.Wr;
+  for (int f = threadIdx.x; f < W; f += kBlock) {
+    sm.rcnt[start + f] = a.rcnt[rf0 + f];
+    if (a.layer > 1) sm.tscore[start + f] = a.tree.score[tb + start + f];
+  }
+  for (int e = threadIdx.x; e < W * K; e += kBlock) {
+    const int f = e / K;
+    sm.lp[(start + f) * K + e % K] = static_cast<double>(a.rv[rf0 * K + e]) - a.rlse[rf0 + f];
+    sm.tok[(start + f) * K + e % K] = a.ri[rf0 * K + e];
+  }
+  __syncthreads();
+  talon_layer(sm, a, a.layer, tb);
+  const bool done = sm.cnt >= a.B || sm.carry == 0;
+  if (threadIdx.x == 0) {
+    st[0] = sm.cnt;
+    st[1] = sm.start;
+    st[2] = sm.width;
+    st[3] = sm.layers;
+    st[4] = done ? 1 : 0;
+    a.w_out[s] = done ? 0 : sm.width;
+    a.done_out[s] = done ? 1 : 0;
+  }
+  if (!done) return;
+  for (int i = 1 + threadIdx.x; i <= sm.cnt; i += kBlock) sm.tpar[i] = static_cast<short>(a.tree.parent[tb + i]);
+  if (threadIdx.x == 0) sm.tpar[0] = -1;
+  __syncthreads();
+  talon_finish(sm, a, s, tb);
 }
 
 // ------------------------------------------------------------------ GOOSE spine trees
@@ -395,8 +473,19 @@ int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+int launch_talon_layer(const TalonArgs& a, int dtype, hipStream_t st) {
+  const dim3 grid(a.S * a.Wr * a.nch);
+  if (dtype == 1)
+    DTV_LAUNCH(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
+  else
+    DTV_LAUNCH(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  DTV_LAUNCH(talon_layer_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_talon(const TalonArgs& a, int dtype, hipStream_t st) {
-  const dim3 grid(a.S * a.B * a.nch);
+  const dim3 grid(a.S * a.Wr * a.nch);
   if (dtype == 1)
     DTV_LAUNCH(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
   else

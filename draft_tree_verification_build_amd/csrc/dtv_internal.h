@@ -47,20 +47,30 @@ struct TreeArgs {
   int* layers;
 };
 
+// TALON. The whole-table build reduces rows 0..B-1 of `draft` (R rows per sequence, keyed
+// by slot) and runs the layer loop in one launch. The layer-by-layer build reduces, per
+// call, the first W[s] of the Wr rows per sequence of `draft` (the frontier's rows, in
+// frontier order) and runs one layer, keeping the loop's state in the workspace.
 struct TalonArgs {
   TreeArgs tree;
   const void* draft;
   int R, V, S, B, K, nch;
+  int Wr;              // rows reduced per sequence: B (whole table) or the call's row capacity
   double log_alpha;
   WsHeader* hdr;
-  ChunkStat* st;       // [S][B][nch]
-  float* cval;         // [S][B][nch][K]
-  int* cidx;           // [S][B][nch][K]
-  unsigned* tickets;   // [S][B]
-  double* rlse;        // [S][B]
-  float* rv;           // [S][B][K]
-  int* ri;             // [S][B][K]
-  int* rcnt;           // [S][B]
+  ChunkStat* st;       // [S][Wr][nch]
+  float* cval;         // [S][Wr][nch][K]
+  int* cidx;           // [S][Wr][nch][K]
+  unsigned* tickets;   // [S][Wr]
+  double* rlse;        // [S][Wr]
+  float* rv;           // [S][Wr][K]
+  int* ri;             // [S][Wr][K]
+  int* rcnt;           // [S][Wr]
+  // layer-by-layer build only (null otherwise)
+  int layer;           // 1 for the root layer
+  int* state;          // [S][8]: nodes so far, first frontier slot, frontier width, layers, done
+  int* w_out;          // [S] frontier width of the next layer (0 when done)
+  int* done_out;       // [S] 1 when the tree is complete
 };
 
 constexpr int kSpineMaxForks = 128;
@@ -115,6 +125,13 @@ struct OptArgs {
   double* Eprev;          // [S]
   int* done;              // [S]
   int* nlayers;           // [S]
+  // layer by layer: rows of `draft` are the call's frontier rows from row_base on (the
+  // whole-table build has row_base -1 and reads row 1 + (l-2) n + f for layer l's row f)
+  int row_base;
+  int* fin;               // [S] tree written (null: the whole-table build finalizes once)
+  int* w_out;             // [S] frontier width of the next layer (0 when done)
+  int* done_out;          // [S]
+  int w_next;             // frontier width of the next layer while not done
 };
 
 struct RowStatsArgs {
@@ -242,12 +259,14 @@ struct CompactArgs {
 
 int launch_given(const TreeArgs& t, int S, WsHeader* hdr, hipStream_t st);
 int launch_talon(const TalonArgs& a, int dtype, hipStream_t st);
+int launch_talon_layer(const TalonArgs& a, int dtype, hipStream_t st);
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st);
 int launch_opt_init(const OptArgs& a, hipStream_t st);
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
 int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st);
 int opt_root_wave_quota(int V, int n, int dtype);
 int launch_opt_finalize(const OptArgs& a, hipStream_t st);
+int launch_opt_report(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);
 int launch_attn(const AttnArgs& a, int dtype, hipStream_t st);
 int launch_attn_bf16(const AttnArgs& a, hipStream_t st);

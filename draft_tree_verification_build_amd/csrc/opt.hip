@@ -63,6 +63,7 @@ __device__ void bitonic_sort(T* a, int n, Cmp before) {
 }
 
 __device__ __forceinline__ int row_of(const OptArgs& a, int f) {
+  if (a.row_base >= 0) return a.row_base + f;   // the call's own frontier rows, in frontier order
   return a.layer == 1 ? 0 : 1 + (a.layer - 2) * a.n + f;
 }
 
@@ -796,6 +797,13 @@ struct OptFinalSmem {
 __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
   __shared__ OptFinalSmem sm;
   const int s = blockIdx.x;
+  // layer by layer: a sequence is written once, by the first call after its drafting stopped
+  if (a.fin != nullptr) {
+    const int d = a.done[s], f = a.fin[s];
+    if (!d || f) return;
+    __syncthreads();   // every thread has read fin before it is set
+    if (threadIdx.x == 0) a.fin[s] = 1;
+  }
   const int n = a.n;
   const int nb = a.bcount[s];
   const size_t bb = static_cast<size_t>(s) * n;
@@ -879,6 +887,7 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
 __global__ void opt_init_kernel(OptArgs a) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s < a.S) {
+    if (a.fin) a.fin[s] = 0;
     a.done[s] = 0;
     a.bcount[s] = 0;
     a.nlayers[s] = 0;
@@ -888,6 +897,21 @@ __global__ void opt_init_kernel(OptArgs a) {
 }
 
 // ------------------------------------------------------------------ launches
+
+// Layer by layer: the next frontier's width and the done flags, for the caller.
+__global__ void opt_report_kernel(OptArgs a) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < a.S) {
+    const int d = a.done[s];
+    a.w_out[s] = d ? 0 : a.w_next;
+    a.done_out[s] = d ? 1 : 0;
+  }
+}
+
+int launch_opt_report(const OptArgs& a, hipStream_t st) {
+  DTV_LAUNCH(opt_report_kernel, dim3((a.S + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_opt_init(const OptArgs& a, hipStream_t st) {
   DTV_LAUNCH(opt_init_kernel, dim3((a.S + 255) / 256), dim3(256), 0, st, a);

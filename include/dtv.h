@@ -173,6 +173,49 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Layer-by-layer builds (TALON page, sections 5.2.1 and 5.3; OPT-Tree summary, sec. 3).
+ *
+ * TALON's candidate pool for layer l is the expansion of layer l-1's nodes, and its cost
+ * term counts one draft forward pass per layer; OPT-Tree likewise drafts one layer from
+ * the previous one: a drafter produces the rows of a layer's frontier only once the layer
+ * before is chosen. These calls take those rows layer by layer and give the same trees as
+ * dtv_tree_build_talon / dtv_tree_build_opt on the same rows.
+ *
+ * dtv_tree_build_begin takes each sequence's root row (root_logits `[S][V]`) and builds
+ * layer 1; dtv_tree_build_step builds layer `layer` (2, 3, ... in order) from the rows of
+ * its frontier, the nodes of layer layer-1: frontier_logits `[S][W_cap][V]`, row f of
+ * sequence s = the draft row of that sequence's frontier node f. The frontier of a TALON
+ * tree is the nodes the previous call added, in slot order (slots cnt+1 .. cnt+W, where cnt
+ * counts the draft nodes before that call); of an OPT-Tree tree, the previous layer's
+ * nodes in frontier order (frontier position p of layer l has build identity, and tree
+ * row, 1 + (l-1) n + p). Both calls write W[s] (device) = the next layer's frontier width,
+ * 0 once the sequence is done, and done[s] (device) = 1 once its tree is complete; rows
+ * past W[s], and later calls for a done sequence, are not read. A step needs W_cap >= the
+ * frontier width (TALON: W_cap <= B; OPT-Tree: the width is min(n, W_{l-1} min(n, V)),
+ * known in advance). When a sequence is done, its tree arrays, n_nodes, layers and masks
+ * are complete; until then only its nodes so far are (TALON; OPT-Tree writes the tree when
+ * it is done). Limits and tie rules are those of the whole-table calls. The workspace
+ * (dtv_tree_build_layered_ws_bytes) carries the build's state from begin to the last step:
+ * one workspace per build in flight.
+ */
+enum { DTV_BUILD_TALON = 1, DTV_BUILD_OPT = 2 };
+typedef struct {
+  int32_t mode;        /* DTV_BUILD_TALON or DTV_BUILD_OPT */
+  int32_t B, K;        /* TALON: draft-node budget, children per expanded node */
+  double alpha;        /* TALON: confidence gate */
+  int32_t n;           /* OPT-Tree: nodes per layer and in the tree */
+  double delta;        /* OPT-Tree: stop when E_l - E_{l-1} < delta */
+  int32_t max_layers;  /* OPT-Tree: layer cap */
+} dtv_build_params;
+
+size_t dtv_tree_build_layered_ws_bytes(const dtv_build_params* params, int32_t S, int32_t V, int dtype);
+int dtv_tree_build_begin(const dtv_tree* tree, int32_t S, const dtv_build_params* params, const void* root_logits,
+                         int dtype, int32_t V, int32_t* W, int32_t* done, void* ws, size_t ws_bytes, void* stream);
+int dtv_tree_build_step(const dtv_tree* tree, int32_t S, const dtv_build_params* params, int32_t layer,
+                        const void* frontier_logits, int32_t W_cap, int dtype, int32_t V, int32_t* W,
+                        int32_t* done, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Tree attention (OPT-Tree summary, section 2; concept page, "Why it is a win").
  *
  * For node i of sequence s and query head h (KV head kv = h / (Hq / Hkv)):
