@@ -117,12 +117,12 @@ __device__ __forceinline__ uint64_t block_visibility(int kb, int P, int k_hi, co
   return (prefix | tree) & in_range;
 }
 
-// Writes one 32-row group of O: normalised bf16 rows when the keys are not split, else
-// the unnormalised fp32 rows and their (m, l) as partials. A lane holds O rows
-// (i/4)*8 + 4h + i%4 of the group, column nt*32 + lr of tile nt.
+// Writes one 32-row group of O: normalised bf16 rows when the sequence's keys are not
+// split (ns == 1), else the unnormalised fp32 rows and their (m, l) as partials. A lane
+// holds O rows (i/4)*8 + 4h + i%4 of the group, column nt*32 + lr of tile nt.
 template <int D>
 __device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D / 32], const float (*ml)[2],
-                                           int s, int kv, int sp, int grp, int M, int h, int lr) {
+                                           int s, int kv, int sp, int ns, int grp, int M, int h, int lr) {
   constexpr int NT = D / 32;
   const int g = a.g;
   const size_t prow0 = ((static_cast<size_t>(s) * a.Hkv + kv) * a.n_split + sp) * static_cast<size_t>(a.mcap);
@@ -133,7 +133,7 @@ __device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D 
       const int rl = q4 * 8 + 4 * h + b;
       const int rr = grp * 32 + rl;
       if (rr >= M) continue;
-      if (a.n_split == 1) {
+      if (ns == 1) {
         const float l = ml[rl][1];
         const float inv = l > 0.f ? 1.f / l : 0.f;
         __bf16* orow = static_cast<__bf16*>(a.o) +
@@ -146,7 +146,7 @@ __device__ __forceinline__ void o_store(const AttnArgs& a, const f32x16 (&oo)[D 
         for (int nt = 0; nt < NT; ++nt) prow[nt * 32 + lr] = oo[nt][q4 * 4 + b];
       }
     }
-  if (a.n_split > 1 && h == 0) {
+  if (ns > 1 && h == 0) {
     const int rr = grp * 32 + lr;
     if (rr < M) {
       a.part_ml[(prow0 + rr) * 2 + 0] = ml[lr][0];
@@ -204,10 +204,22 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
     if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
   }
+  // the sequence's own row groups over its own tiles (a smaller tree uses fewer tiles, each
+  // with every wave busy, rather than spreading its groups over the planned tiles)
   const int G = (M + 31) / 32;
-  const int gl = tm * G / a.n_mtiles, gh = (tm + 1) * G / a.n_mtiles;
+  const int mt = min(a.n_mtiles, (G + kWaves - 1) / kWaves);
+  if (tm >= mt) return;
+  const int gl = tm * G / mt, gh = (tm + 1) * G / mt;
   if (gl >= gh) return;
   const int T = P + N;
+  // the sequence's own split count: a split past its keys does nothing (the merge reads
+  // only this sequence's splits), and a sequence with one split writes its output directly
+  const int ns = (T + a.kps - 1) / a.kps;
+  if (ns > a.n_split) {   // a prefix longer than the plan's P_max: its keys have no split
+    if (threadIdx.x == 0) atomicExch(&a.hdr->err, kErrCapacity);
+    return;
+  }
+  if (sp >= ns) return;
   const int k_lo = sp * a.kps;
   const int k_hi = min(k_lo + a.kps, T);
 
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + kvoff;
   const uint64_t* anc = a.anc + (static_cast<size_t>(s) * a.n_cap + node) * a.words;
 
-  if (G != Gp) {
+  if (G != Gp || mt != a.n_mtiles) {
     // fewer nodes than planned changes the tiling: this wave's rows are reloaded (a padding
     // row past M reads row 0's query, valid memory, and its output is never stored)
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
@@ -427,7 +439,7 @@ __global__ __launch_bounds__(kBlock, 2) void attn_bf16_kernel(AttnArgs a) {
     ml_s[w][lr][1] = l_tot;
   }
   __syncthreads();
-  if (act) o_store<D>(a, oacc, ml_s[w], s, kv, sp, grp, M, h, lr);
+  if (act) o_store<D>(a, oacc, ml_s[w], s, kv, sp, ns, grp, M, h, lr);
 }
 
 // Merges the key splits of every query row (partials indexed by row): O = sum_q O_q w_q / sum_q l_q w_q
@@ -444,19 +456,20 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   const int kv = head % a.Hkv;
   const int s = head / a.Hkv;
   const size_t pr0 = static_cast<size_t>(head) * a.n_split * rows_per_head + rr;
-  // every split's O row, every (m, l) and the node count are loaded together, one round
-  // trip (rows past g * N hold stale partials in valid workspace memory and are not stored;
-  // splits past n_split re-read the last one and get weight 0)
+  // the sequence's own split count (a sequence with one split has its output written)
+  const int N = a.n_nodes[s];
+  const int ns = (a.P[s] + N + a.kps - 1) / a.kps;
+  if (N > a.n_cap || rr >= a.g * N || ns <= 1 || ns > a.n_split) return;
+  // every split's O row and every (m, l) are loaded together, one round trip (splits past
+  // ns re-read split ns-1 and get weight 0)
   float4 o[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
-    const int qq = min(u, a.n_split - 1);
+    const int qq = min(u, ns - 1);
     o[u] = *reinterpret_cast<const float4*>(&a.part_o[(pr0 + static_cast<size_t>(qq) * rows_per_head) * D + c4 * 4]);
   }
   float w[NS];
-  const float L = attn_split_weights<NS>(a.part_ml + pr0 * 2, static_cast<size_t>(rows_per_head) * 2, a.n_split, w);
-  const int N = a.n_nodes[s];
-  if (N > a.n_cap || rr >= a.g * N) return;
+  const float L = attn_split_weights<NS>(a.part_ml + pr0 * 2, static_cast<size_t>(rows_per_head) * 2, ns, w);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < NS; ++u) {

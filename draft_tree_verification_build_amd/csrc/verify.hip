@@ -38,25 +38,29 @@ __device__ bool walk_compact(const KvCompactView& c, int s, int n_cap, const int
   const int npairs = pair0 < 2 * c.Hkv ? (2 * c.Hkv - pair0 + pstep - 1) / pstep : 0;
   const int per_pair = L * vpr;
   const int total = npairs * per_pair;
-  constexpr int kPer = 4;   // vectors per thread and batch, all loaded before any store
-  for (int b0 = 0; b0 < total; b0 += kBlock * kPer) {
-    uint4 val[kPer];
-    char* dst[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int v = min(b0 + q * kBlock + static_cast<int>(threadIdx.x), total - 1);
-      const int pi = v / per_pair, rem = v % per_pair;
-      const int k = rem / vpr, ch = rem % vpr;
-      const int pair = pair0 + pi * pstep;
-      char* base = ((pair & 1) ? c.v : c.k) +
-                   (static_cast<size_t>(s) * c.Hkv + (pair >> 1)) * c.P_cap * row_bytes;
-      val[q] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(P + spath[k]) * row_bytes + ch * 16);
-      dst[q] = base + static_cast<size_t>(P + k) * row_bytes + ch * 16;
-    }
+  // four 16-byte vectors per thread and batch, all loaded before any store (named registers,
+  // so that they stay in registers across the barrier)
+  auto src_dst = [&](int v, char*& dst) -> const uint4* {
+    const int vc = min(v, total - 1);
+    const int pi = vc / per_pair, rem = vc % per_pair;
+    const int k = rem / vpr, ch = rem % vpr;
+    const int pair = pair0 + pi * pstep;
+    char* base = ((pair & 1) ? c.v : c.k) + (static_cast<size_t>(s) * c.Hkv + (pair >> 1)) * c.P_cap * row_bytes;
+    dst = base + static_cast<size_t>(P + k) * row_bytes + ch * 16;
+    return reinterpret_cast<const uint4*>(base + static_cast<size_t>(P + spath[k]) * row_bytes + ch * 16);
+  };
+  for (int b0 = 0; b0 < total; b0 += kBlock * 4) {
+    const int v0 = b0 + static_cast<int>(threadIdx.x);
+    char *d0, *d1, *d2, *d3;
+    const uint4 x0 = *src_dst(v0, d0);
+    const uint4 x1 = *src_dst(v0 + kBlock, d1);
+    const uint4 x2 = *src_dst(v0 + 2 * kBlock, d2);
+    const uint4 x3 = *src_dst(v0 + 3 * kBlock, d3);
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (b0 + q * kBlock + static_cast<int>(threadIdx.x) < total) *reinterpret_cast<uint4*>(dst[q]) = val[q];
+    if (v0 < total) *reinterpret_cast<uint4*>(d0) = x0;
+    if (v0 + kBlock < total) *reinterpret_cast<uint4*>(d1) = x1;
+    if (v0 + 2 * kBlock < total) *reinterpret_cast<uint4*>(d2) = x2;
+    if (v0 + 3 * kBlock < total) *reinterpret_cast<uint4*>(d3) = x3;
     __syncthreads();
   }
   return true;

@@ -223,7 +223,8 @@ int dtv_tree_build_step(const dtv_tree* tree, int32_t S, const dtv_build_params*
  * over the prefix j < P[s] and the tree keys j = P[s] + a for every ancestor-or-self a
  * of i (the tree's keys and values sit at cache positions P[s] + slot).
  * Layouts: q, o `[S][n_cap][Hq][D]`; k, v `[S][Hkv][P_cap][D]`; P `[S]` (device) with
- * P[s] + n_nodes[s] <= P_cap, and P_max >= every P[s] (host bound, sizes the grid).
+ * P[s] + n_nodes[s] <= P_cap, and P_max >= every P[s] (host bound, sizes the grid; a
+ * larger P[s] is reported as DTV_ECAPACITY by the workspace status).
  * Rows of o for slots >= n_nodes[s] are not written. bf16 runs on MFMA with fp32
  * accumulation; f32 runs in fp32. D must be 64 or 128; Hq % Hkv == 0.
  */
@@ -247,8 +248,8 @@ int dtv_tree_attn(const void* q, const void* k, const void* v, const int32_t* P,
  * keeps the last call's partials: nothing in it must start at zero (every partial a call
  * reads, that call writes first), but calls that may overlap on one GPU (concurrent streams
  * or threads) race on it and must be ordered by the caller. Device-side refusals
- * (n_nodes[s] > n_cap, or P[s] + n_nodes[s] > P_cap) leave those rows of o unwritten and
- * are not reported (dtv_tree_attn reports them through its workspace).
+ * (n_nodes[s] > n_cap, P[s] + n_nodes[s] > P_cap, or P[s] > P_max) leave those rows of o
+ * unwritten and are not reported (dtv_tree_attn reports them through its workspace).
  */
 int dtv_tree_attn_noalloc(const void* q, const void* k, const void* v, const int32_t* P, int32_t P_cap,
                           int32_t P_max, const dtv_tree* tree, int32_t S, int32_t Hq, int32_t Hkv,

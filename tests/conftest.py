@@ -11,3 +11,4 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP library)")
     config.addinivalue_line("markers", "slow: long CPU test")
+    config.addinivalue_line("markers", "sweep: long seeded GPU sweep, run on its own with -m sweep")
