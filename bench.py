@@ -283,7 +283,7 @@ def main():
     from draft_tree_verification_build_amd import api
     every = max(2, args.event_every)
     sampled = list(range(0, args.steps, every))
-    ktimed = set(range(every // 2, args.steps, every))
+    ktimed = set(range(every // 2, args.steps, every)) or {args.steps - 1}
     ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for k in sampled}
     api.kernel_timing(False, reset=True)
     torch.cuda.synchronize()

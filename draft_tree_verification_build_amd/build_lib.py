@@ -25,6 +25,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-result",
+    # a local that hides an outer one has picked the wrong buffer before
+    "-Werror=shadow",
 ]
 
 

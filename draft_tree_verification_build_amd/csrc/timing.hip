@@ -38,8 +38,10 @@ hipEvent_t take_event() {   // caller holds g_mu
     g_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence (cache writeback and invalidation) when the event
+  // completes, which would add its cost to the measured launch and to the next one
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

@@ -206,9 +206,9 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
   // node v is accepted when no node on its root path is bad (slots grow away from the root)
   unsigned long long pick = 0;
   for (int v = threadIdx.x; v < N; v += kBlock) {
-    bool ok = true;
-    for (int u = v; u > 0 && ok; u = sm.par[u]) ok = !sm.bad[u];
-    if (ok) {
+    bool clean = true;
+    for (int u = v; u > 0 && clean; u = sm.par[u]) clean = !sm.bad[u];
+    if (clean) {
       const unsigned long long key2 = (static_cast<unsigned long long>(sm.dep[v]) << 20) |
                                       static_cast<unsigned long long>(0xFFFFF - v);
       pick = key2 > pick ? key2 : pick;
@@ -281,6 +281,14 @@ __device__ __forceinline__ void row_vec(const void* row, int vi, float (&x)[RowT
     x[e] = DT ? bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) : __uint_as_float(w[e]);
 }
 
+template <int DT>
+__device__ __forceinline__ void unit_decode(const uint4 raw, float (&x)[RowT<DT>::VEC]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < RowT<DT>::VEC; ++e)
+    x[e] = DT ? bf16_to_f32(static_cast<uint16_t>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) : __uint_as_float(w[e]);
+}
+
 // The walk's view of the current distribution p at node v: softmax of the target row
 // (pc null) or the normalised residual pc / zc; q is the softmax of the draft row. A
 // "unit" is a 16-byte vector of VEC consecutive logits when `vec` (rows 16-byte aligned,
@@ -303,6 +311,9 @@ struct WalkDist {
   int base;
   const double* tab;
   bool vec;
+  const uint4* tst;   // this workgroup's units of the target / draft row in shared memory
+  const uint4* dst;   // (unit u at index u - u0), or null: read the rows in memory
+  int u0;
 
   __device__ int width() const { return vec ? VEC : 1; }
   __device__ double p(int j) const {
@@ -322,7 +333,10 @@ struct WalkDist {
       for (int e = 0; e < VEC; ++e) out[e] = pc[a * VEC + e - base] / zc;
     } else {
       float x[VEC];
-      row_vec<DT>(trow, a, x);
+      if (tst)
+        unit_decode<DT>(tst[a - u0], x);
+      else
+        row_vec<DT>(trow, a, x);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) out[e] = exp_nonpos(static_cast<double>(x[e]) - lt, tab);
     }
@@ -344,7 +358,10 @@ struct WalkDist {
       return;
     }
     float x[VEC];
-    row_vec<DT>(drow, a, x);
+    if (dst)
+      unit_decode<DT>(dst[a - u0], x);
+    else
+      row_vec<DT>(drow, a, x);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       out[e] = exp_nonpos(static_cast<double>(x[e]) - ld, tab);
@@ -435,11 +452,12 @@ __device__ bool group_exchange(WalkGroup& g, const double* mine, int n, bool own
 constexpr int kStatUnits = 2;   // units per thread and batch
 
 template <int DT>
-__device__ void slice_stats(const void* row0, const void* row1, int nr, const WalkGroup& g, bool vec,
-                            const double* tab, double (*wred)[4], double* out) {
+__device__ void slice_stats(const void* row0, const void* row1, const uint4* st0, const uint4* st1, int nr,
+                            const WalkGroup& g, bool vec, const double* tab, double (*wred)[4], double* out) {
   constexpr int VEC = RowT<DT>::VEC;
   const int w = vec ? VEC : 1;
   const void* rows[2] = {row0, row1};
+  const uint4* sts[2] = {st0, st1};
   const int wv = threadIdx.x >> 6;
   double M[2] = {-INFINITY, -INFINITY}, S[2] = {0.0, 0.0};
   for (int b0 = g.u0; b0 < g.u1; b0 += kBlock * kStatUnits) {   // block-uniform batches
@@ -451,7 +469,9 @@ __device__ void slice_stats(const void* row0, const void* row1, int nr, const Wa
         const int a = b0 + q * kBlock + static_cast<int>(threadIdx.x);
         const bool in = r < nr && a < g.u1;
         if (vec) {
-          if (in) {
+          if (in && sts[r] != nullptr) {
+            unit_decode<DT>(sts[r][a - g.u0], x[r][q]);
+          } else if (in) {
             row_vec<DT>(rows[r], a, x[r][q]);
           } else {
 #pragma unroll
@@ -522,6 +542,16 @@ __device__ void slice_stats(const void* row0, const void* row1, int nr, const Wa
       out[2 * r + 1] = S[r];
     }
   }
+}
+
+// Sum of the G <= 32 slice values vals[0 .. G) by a fixed butterfly over 32 lanes: every
+// wave of every workgroup adds them in the same order, so all get the same bits.
+__device__ __forceinline__ double group_sum(const double* vals, int G) {
+  const int k = threadIdx.x & 31;
+  double t = k < G ? vals[k] : 0.0;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  return t;
 }
 
 // log sum exp of the target (lanes 0..31) and draft (lanes 32..63) rows from the (max, sum)
@@ -618,6 +648,28 @@ __device__ int slice_inverse_cdf(const WalkDist<DT>& d, const WalkGroup& g, doub
   return sm.pick;
 }
 
+// Shared-memory copies of a workgroup's units of a node's two rows: the node the walk is at
+// and the child being tried, whose copies are loaded while the current node's tests and
+// exchanges run (a slice of at most kStageUnits 16-byte units; larger slices read memory).
+constexpr int kStageUnits = 512;
+
+// Issues direct loads of units [g.u0, g.u1) of `row` into lds[0 .. g.u1 - g.u0): wave w's
+// instruction i covers units 256 i + 64 w + lane (lane l of a direct load fills the 16 bytes
+// at 16 l after the load's base); units past u1 reload unit u1 - 1 into the buffer's tail,
+// which nobody reads. Every thread must call it; the data is there after drain() and a
+// barrier.
+__device__ __forceinline__ void stage_issue(const void* row, uint4* lds, const WalkGroup& g) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const int count = g.u1 - g.u0;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint4* src = reinterpret_cast<const uint4*>(row);
+  for (int i0 = 0; i0 < count; i0 += kBlock) {
+    const int j = i0 + 64 * w + lane;
+    const int u = g.u0 + min(j, count - 1);
+    __builtin_amdgcn_global_load_lds(src + u, (lds_void_t*)(lds + i0 + 64 * w), 16, 0, 0);
+  }
+}
+
 // The walk of sequence blockIdx.x / G, shared by its G workgroups (the exchanges need them
 // all resident: the launch keeps the grid within what the device holds).
 template <int DT>
@@ -625,6 +677,8 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   __shared__ SampleSmem sm;
   __shared__ double gvals[kXchStride];
   __shared__ double slice_buf[3][kWalkSlice];   // residuals (two) and q of this slice
+  __shared__ uint4 stage[2][2][kStageUnits];     // [node buffer][target, draft][unit]
+  __shared__ int rowof[kSampleMaxNodes];         // every node's row
   using Rw = RowT<DT>;
   row_smem_init(sm.rs);
   const int s = blockIdx.x / a.G;
@@ -644,6 +698,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     // rows are read at every node the walk may visit, tokens at every child tried: both
     // must lie inside the tables
     const int r = a.tree.row[tb + v];
+    rowof[v] = r;
     if (r < 0 || r >= a.R || (v > 0 && (sm.tok[v] < 0 || sm.tok[v] >= a.V))) sm.flag = 1;
   }
   __syncthreads();   // also publishes the exp table
@@ -687,6 +742,17 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   }
   const double inv32 = 1.0 / 4294967296.0;
   const bool lead = grp.gi == 0;
+  // shared-memory copies of the rows (this workgroup's units): the root's now
+  const bool staged = vec && grp.u1 - grp.u0 <= kStageUnits && grp.u1 > grp.u0;
+  int sbuf = 0;   // stage buffer holding the rows of the node the walk is at
+  auto row_ptr = [&](const void* table, int r) {
+    return static_cast<const char*>(table) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
+  };
+  auto prefetch = [&](int node, int buf) {   // every thread; the rows were checked above
+    stage_issue(row_ptr(a.target, rowof[node]), stage[buf][0], grp);
+    stage_issue(row_ptr(a.draft, rowof[node]), stage[buf][1], grp);
+  };
+  if (staged) prefetch(0, 0);
   int v = 0, A = 0;
   if (lead && threadIdx.x == 0) a.path[tb] = 0;
   if (threadIdx.x == 0) sm.spath[0] = 0;
@@ -701,10 +767,20 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     for (int k = max(n0, 1); k < n1; ++k)
       if (sm.par[k] == v) sm.kids[pos++] = k;
     __syncthreads();
-    const int r = a.tree.row[tb + v];
+    const int r = rowof[v];
     WalkDist<DT> d;
-    d.trow = static_cast<const char*>(a.target) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
-    d.drow = static_cast<const char*>(a.draft) + (static_cast<size_t>(s) * a.R + r) * row_bytes;
+    d.trow = row_ptr(a.target, r);
+    d.drow = row_ptr(a.draft, r);
+    d.tst = staged ? stage[sbuf][0] : nullptr;
+    d.dst = staged ? stage[sbuf][1] : nullptr;
+    d.u0 = grp.u0;
+    // the first child's rows start loading into the other buffer; this node's have landed
+    // once every wave's loads are done and a barrier has passed
+    if (staged) {
+      drain();
+      if (nk > 0) prefetch(sm.kids[0], sbuf ^ 1);
+      __syncthreads();
+    }
     // The node's normalisers: every workgroup reduces its slice of the target row (and of
     // the draft row when children are tried) and the group exchanges the four values.
     // thread 0 starts the loads the first acceptance test needs (the child's logits in both
@@ -719,8 +795,11 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     }
     {
       double st[4];
-      slice_stats<DT>(d.trow, d.drow, nk > 0 ? 2 : 1, grp, vec, sm.rs.exptab, sm.wpair, st);
-      if (!group_exchange(grp, st, 4, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
+      slice_stats<DT>(d.trow, d.drow, d.tst, d.dst, nk > 0 ? 2 : 1, grp, vec, sm.rs.exptab, sm.wpair, st);
+      if (!group_exchange(grp, st, 4, false, 0.0, 0.0, false, gvals, &sm.flag)) {
+        drain();   // no stage load is left in flight
+        return;
+      }
       for (int k = threadIdx.x; k < 4 * grp.G; k += kBlock) sm.lsev[k] = gvals[k];
       merged_lse2(gvals, grp.G, sm.rs.exptab, d.lt, d.ld);
       if (nk == 0) d.ld = 0.0;
@@ -753,6 +832,12 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
         __syncthreads();
         break;
       }
+      // the next child's rows load while this rejection's pass and exchange run (the
+      // rejected child's copies, loaded into the same buffer, have landed by now)
+      if (staged && q + 1 < nk) {
+        drain();
+        prefetch(sm.kids[q + 1], sbuf ^ 1);
+      }
       // rejection: residual (p - q)+ into the other buffer; kept only if it sums to > 0.
       // The owner of the next child's token publishes, for that token, the new residual
       // and the current p (used if the residual sums to 0).
@@ -771,9 +856,11 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
         e1 = d.p(xn);
         e0 = fmax(e1 - d.q(xn), 0.0);   // the entry residual_slice stored for xn
       }
-      if (!group_exchange(grp, &part, 1, owner, e0, e1, xn >= 0, gvals, &sm.flag)) return;
-      double z = 0.0;
-      for (int k = 0; k < grp.G; ++k) z += gvals[k];
+      if (!group_exchange(grp, &part, 1, owner, e0, e1, xn >= 0, gvals, &sm.flag)) {
+        drain();   // no stage load is left in flight
+        return;
+      }
+      const double z = group_sum(gvals, grp.G);
       if (z > 0.0) {
         cur = nxt;
         d.pc = P[cur];
@@ -786,6 +873,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     }
     if (accepted >= 0) {
       v = accepted;
+      sbuf ^= 1;   // the accepted child's rows are in the prefetch buffer
       ++A;
       if (lead && threadIdx.x == 0) a.path[tb + A] = v;
       if (threadIdx.x == 0) sm.spath[A] = v;
@@ -819,10 +907,12 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
           if (e < w) loc += pv[e];
       }
       const double mass = block_sum(loc, sm.rs.redd);
-      if (!group_exchange(grp, &mass, 1, false, 0.0, 0.0, false, gvals, &sm.flag)) return;
+      if (!group_exchange(grp, &mass, 1, false, 0.0, 0.0, false, gvals, &sm.flag)) {
+        drain();   // no stage load is left in flight
+        return;
+      }
     }
-    double total = 0.0;
-    for (int k = 0; k < grp.G; ++k) total += gvals[k];
+    const double total = group_sum(gvals, grp.G);
     const double target = u * total;
     // the first workgroup whose slice takes the running sum past the target draws the
     // token; if rounding leaves the target at the end, the last slice with mass does
