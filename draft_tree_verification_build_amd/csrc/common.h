@@ -43,31 +43,62 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
 
 // ---------------------------------------------------------------- reductions
 
+// Wave-wide reductions (all 64 lanes active; every lane receives the result, the same bits
+// in every lane). Inside each row of 16 lanes, four DPP moves pair lane i with i^1, i^2
+// (quad permutations), then 7-i (half mirror: quads within 8) and 15-i (mirror: 8-lane
+// halves), so each row ends uniform; the four row values are then read from lanes 0, 16,
+// 32 and 48 and combined in a fixed order. No step goes through shared memory.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
+  if constexpr (sizeof(T) == 4) {
+    const int r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(T, r);
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xFFFFFFFFull), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(T, (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) |
+                                     static_cast<uint32_t>(lo));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int lane) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFull), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+    return __builtin_bit_cast(T, (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) |
+                                     static_cast<uint32_t>(lo));
+  }
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));   // row_mirror
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return b > a ? b : a; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o, 64);
-    v = w < v ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return b < a ? b : a; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 
 // Order-preserving 64-bit key of a double: larger value, larger key; -0 and +0 share one.

@@ -255,11 +255,13 @@ __device__ __forceinline__ float bf16key_to_f32(uint32_t k16) {
   return bf16_to_f32(static_cast<uint16_t>((k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu)));
 }
 
-// Reduces the chunk in registers. Writes *st (thread 0) and, when K > 0, the chunk's top-K
-// (value, index) sorted by (value desc, index asc) into out_val/out_idx (global, st_cc).
+// Reduces the chunk in registers. Writes *st and, when K > 0, the chunk's top-K (value,
+// index) sorted by (value desc, index asc) into out_val/out_idx (global, st_cc). The
+// argmax (largest value, lowest index) is the list's first entry when K > 0; only for
+// K = 0 is it looked for separately.
 //
-// Per wave, without block barriers: maximum and its lowest index, float64 sum of
-// exp(x - wave max), valid count. Top-K, for K <= 32: every wave takes the K-th largest of
+// Per wave, without block barriers: maximum (and, for K = 0, its lowest index), float64 sum
+// of exp(x - wave max), valid count. Top-K, for K <= 32: every wave takes the K-th largest of
 // its 64 lane maxima (bisection with one ballot per step); the largest of those, tau, is a
 // lower bound of the chunk's K-th largest value (that wave alone has K values >= tau), so
 // the chunk's top-K are among the values >= tau, usually barely more than K of them. They
@@ -280,12 +282,14 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
   for (int j = 0; j < R::E; ++j) lmk = key[j] > lmk ? key[j] : lmk;
   const uint32_t km = wave_max(lmk);
   int am = 0x7FFFFFFF;
+  if (K == 0) {   // with a list, its first entry (value desc, index asc) is the argmax
 #pragma unroll
-  for (int i = kLoads - 1; i >= 0; --i)
+    for (int i = kLoads - 1; i >= 0; --i)
 #pragma unroll
-    for (int e = R::VEC - 1; e >= 0; --e)
-      if (key[i * R::VEC + e] == km) am = elem_index<DT>(c, i, e);
-  am = wave_min(am);
+      for (int e = R::VEC - 1; e >= 0; --e)
+        if (key[i * R::VEC + e] == km) am = elem_index<DT>(c, i, e);
+    am = wave_min(am);
+  }
   // in-range elements of the chunk (padding has key 0; a stored -inf does not)
   const int nvalid = min(max(V - c * R::CHUNK, 0), R::CHUNK);
   const float mw = (km == 0u) ? -INFINITY : (DT ? bf16key_to_f32(km) : key_to_f32(km));
@@ -316,26 +320,25 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
   if (threadIdx.x == 0) sm.ncand = 0;
   __syncthreads();
 
-  // ---- chunk results
+  // ---- chunk results, read by the workgroup that merges the row: lane q of the last wave
+  //      holds wave q's partials
   const int kk = K < nvalid ? K : nvalid;
-  if (threadIdx.x == 0) {  // read by the workgroup that merges the row
-    uint32_t KM = 0;
-    int AM = 0x7FFFFFFF;
-    float M = -INFINITY;
-    for (int q = 0; q < kWaves; ++q)
-      if (sm.wkey[q] > KM) {
-        KM = sm.wkey[q];
-        M = sm.wmax[q];
-      }
-    double S = 0.0;
-    for (int q = 0; q < kWaves; ++q) {
-      if (sm.wkey[q] == KM && sm.warg[q] < AM) AM = sm.warg[q];
-      if (sm.wkey[q] != 0u) S += sm.wse[q] * exp_nonpos(static_cast<double>(sm.wmax[q]) - static_cast<double>(M), sm.exptab);
+  if (w == kWaves - 1) {
+    const int q = threadIdx.x & 63;
+    const uint32_t kq = q < kWaves ? sm.wkey[q] : 0u;
+    const uint32_t KM = wave_max(kq);
+    const float M = (KM == 0u) ? -INFINITY : (DT ? bf16key_to_f32(KM) : key_to_f32(KM));
+    const int AM = wave_min(q < kWaves && kq == KM ? sm.warg[q] : 0x7FFFFFFF);
+    double term = 0.0;
+    if (q < kWaves && kq != 0u)
+      term = sm.wse[q] * exp_nonpos(static_cast<double>(sm.wmax[q]) - static_cast<double>(M), sm.exptab);
+    const double S = wave_sum(term);
+    if (q == 0) {
+      st_cc(&st->maxv, M);
+      if (K == 0) st_cc(&st->argmax, AM);   // else written with the list's first entry
+      st_cc(&st->sumexp, S);
+      st_cc(&st->cnt, kk);
     }
-    st_cc(&st->maxv, M);
-    st_cc(&st->argmax, AM);
-    st_cc(&st->sumexp, S);
-    st_cc(&st->cnt, kk);
   }
   if (kk <= 0) {
     __syncthreads();
@@ -345,14 +348,33 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
   if (small) {
     uint32_t tau = 1u;
     for (int q = 0; q < kWaves; ++q) tau = sm.wtau[q] > tau ? sm.wtau[q] : tau;
+    // the candidates (keys >= tau) are packed without per-element atomics: a ballot pass
+    // counts the wave's candidates and notes which element slots hold any, one shared-memory
+    // atomic reserves the wave's range, and only those slots (usually a handful) write their
+    // candidates, each at its lane's rank within the wave
+    int wn = 0;
+    uint32_t slots = 0u;   // wave-uniform
+#pragma unroll
+    for (int j = 0; j < R::E; ++j) {
+      const int cj = __popcll(__ballot(key[j] >= tau));
+      wn += cj;
+      slots |= (cj != 0 ? 1u : 0u) << j;
+    }
+    int pos = 0;
+    if ((threadIdx.x & 63) == 0 && wn > 0) pos = atomicAdd(&sm.ncand, wn);
+    pos = __builtin_amdgcn_readfirstlane(pos);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
 #pragma unroll
-      for (int e = 0; e < R::VEC; ++e)
-        if (key[i * R::VEC + e] >= tau) {
-          const int pos = atomicAdd(&sm.ncand, 1);
-          if (pos < kCandCap) sortbuf[pos] = sort_key(x[i * R::VEC + e], elem_index<DT>(c, i, e));
+      for (int e = 0; e < R::VEC; ++e) {
+        if (slots & (1u << (i * R::VEC + e))) {
+          const bool take = key[i * R::VEC + e] >= tau;
+          const unsigned long long m = __ballot(take);
+          const int p = pos + lanes_below(m);
+          if (take && p < kCandCap) sortbuf[p] = sort_key(x[i * R::VEC + e], elem_index<DT>(c, i, e));
+          pos += __popcll(m);
         }
+      }
     __syncthreads();
     const int n = sm.ncand;
     if (n <= kCandCap) {
@@ -363,6 +385,7 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
         if (rank < kk) {
           st_cc(&out_val[rank], sort_key_value(me));
           st_cc(&out_idx[rank], sort_key_index(me));
+          if (rank == 0) st_cc(&st->argmax, sort_key_index(me));
         }
       }
       __syncthreads();
@@ -434,6 +457,7 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
       if (rank < kk) {
         st_cc(&out_val[rank], sort_key_value(me));
         st_cc(&out_idx[rank], sort_key_index(me));
+        if (rank == 0) st_cc(&st->argmax, sort_key_index(me));
       }
     }
   } else {
@@ -441,6 +465,7 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     for (int i = threadIdx.x; i < kk; i += kBlock) {
       st_cc(&out_val[i], sort_key_value(sortbuf[i]));
       st_cc(&out_idx[i], sort_key_index(sortbuf[i]));
+      if (i == 0) st_cc(&st->argmax, sort_key_index(sortbuf[0]));
     }
   }
   __syncthreads();
@@ -464,13 +489,13 @@ struct MergeSmem {
 
 // Merges the ChunkStats and sorted top-K lists of the `nch` chunks of one row (written by
 // other workgroups with st_cc). The lists are first copied into shared memory (one
-// parallel pass of coherent loads). The last wave forms the log-sum-exp while the others
-// rank the entries. When the merged list is no longer than a chunk list (kout <= K), only
-// entries at or above T0 = the largest last entry of a full list can be among the top (that
-// list alone holds K entries at or above T0); wave 0 gathers those (usually a few more than
-// K) and ranks them among themselves. Otherwise, or when more than 64 entries reach T0,
-// every entry's rank is the count of entries of all lists that precede it (counting for
-// <= 1024 entries, else binary search in the sorted lists).
+// parallel pass of coherent loads). The last wave forms the log-sum-exp while wave 0 looks
+// for a bound T: the kout-th largest of the lists' first ceil(kout / nch) entries, which
+// has at least kout entries at or above it, so only entries >= T can be among the top;
+// wave 0 gathers those (usually a few more than kout) and ranks them in registers. When
+// the bound cannot be formed that way or more than 64 entries reach it, every entry's rank
+// is the count of entries of all lists that precede it (counting for <= 1024 entries, else
+// binary search in the sorted lists).
 // Outputs: maxv, argmax, lse (last wave); the top kout (default K) entries (value, index)
 // into rv/ri, all written with st_cc. Requires nch <= 64 and nch * K <= CAP.
 // Returns min(kout, entries).
@@ -516,19 +541,26 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
     return 0;
   }
   const int n = nch * K;
-  bool fast = false;
-  if (want <= K && n <= 1024) {
-    // T0 = the largest K-th entry of a full list; every wave forms it (no barrier needed)
-    unsigned long long t0 = 0ull;
-    if (lane < nch && ms.cnt[lane] >= K) t0 = ms.key[lane * K + K - 1];
-    t0 = wave_max(t0);
-    if (w == 0) {
+  // Fast path (wave 0): a bound T with at least `want` entries at or above it, so that the
+  // merged list is among the entries >= T. Every list is sorted, so T is taken among the
+  // lists' first h = ceil(want / nch) entries: the want-th largest of those. Wave 0 gathers
+  // the entries >= T (usually a few more than want) and ranks them in registers.
+  const int h = (want + nch - 1) / nch;
+  if (w == 0 && n <= 1024 && h <= K && nch * h <= 64) {
+    bool fast = false;
+    const int hc = lane / h, hj = lane % h;
+    const unsigned long long hk = (lane < nch * h && hj < ms.cnt[hc]) ? ms.key[hc * K + hj] : 0ull;
+    if (__popcll(__ballot(hk != 0ull)) >= want) {   // keys are unique and never 0
+      int r = 0;
+      for (int q = 0; q < nch * h; ++q) r += read_lane(hk, q) > hk ? 1 : 0;
+      const unsigned long long sel = __ballot(hk != 0ull && r == want - 1);
+      const unsigned long long T = read_lane(hk, static_cast<int>(__builtin_ctzll(sel)));
       int base = 0;
       for (int e0 = 0; e0 < n; e0 += 64) {
         const int e = e0 + lane;
         const int c = e / K, j = e % K;
         const unsigned long long k = e < n ? ms.key[e] : 0ull;
-        const bool in = e < n && j < ms.cnt[c] && k >= t0;
+        const bool in = e < n && j < ms.cnt[c] && k >= T;
         const unsigned long long m = __ballot(in);
         const int pos = base + lanes_below(m);
         if (in && pos < kMergeFast) ms.cand[pos] = k;
@@ -537,21 +569,19 @@ __device__ int row_merge(const ChunkStat* st, const float* cval, const int* cidx
       fast = base <= kMergeFast;
       if (fast) {
         __builtin_amdgcn_wave_barrier();
-        if (lane < base) {
-          const unsigned long long me = ms.cand[lane];
-          int rank = 0;
-          for (int q = 0; q < base; ++q) rank += ms.cand[q] > me ? 1 : 0;
-          if (rank < kk) {
-            st_cc(&rv[rank], sort_key_value(me));
-            st_cc(&ri[rank], sort_key_index(me));
-          }
+        const unsigned long long me = lane < base ? ms.cand[lane] : 0ull;
+        int rank = 0;
+        for (int q = 0; q < base; ++q) rank += read_lane(me, q) > me ? 1 : 0;
+        if (lane < base && rank < kk) {
+          st_cc(&rv[rank], sort_key_value(me));
+          st_cc(&ri[rank], sort_key_index(me));
         }
       }
-      if (lane == 0) ms.ncand = fast ? 1 : 0;
     }
+    if (lane == 0) ms.ncand = fast ? 1 : 0;
   }
   __syncthreads();
-  if (want <= K && n <= 1024 && ms.ncand != 0) {
+  if (ms.ncand != 0) {
     __syncthreads();   // every wave has read ncand before the next merge may reset it
     return kk;
   }
