@@ -86,6 +86,18 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
   return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
 }
 
+// The same over the two halves of the wave separately: lo receives the result over lanes
+// 0..31, hi over lanes 32..63 (both wave-uniform, the same bits in every lane).
+template <typename T, typename Op>
+__device__ __forceinline__ void half_wave_reduce(T v, Op op, T& lo, T& hi) {
+  v = op(v, dpp_move<0xB1>(v));
+  v = op(v, dpp_move<0x4E>(v));
+  v = op(v, dpp_move<0x141>(v));
+  v = op(v, dpp_move<0x140>(v));
+  lo = op(read_lane(v, 0), read_lane(v, 16));
+  hi = op(read_lane(v, 32), read_lane(v, 48));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
   return wave_reduce(v, [](T a, T b) { return b > a ? b : a; });

@@ -256,6 +256,9 @@ struct SampleSmem {
   int tok[kSampleMaxNodes];
   int kids[kSampleMaxNodes];
   int spath[kSampleMaxNodes];   // the accepted path so far (every workgroup of the group)
+  uint32_t uacc[kSampleMaxNodes];   // every node's acceptance uniform
+  uint32_t ures[kSampleMaxNodes];   // every node's residual (bonus) uniform
+  unsigned long long kmask[kWaves];   // per-wave ballots of a node's children
   double lsev[4 * kSampleMaxGroup];   // the node's slice statistics of every workgroup
   double wpair[kWaves][4];            // per-wave (max, sum) pairs of the two rows
   double wsum[kWaves];
@@ -443,42 +446,52 @@ __device__ bool group_exchange(WalkGroup& g, const double* mine, int n, bool own
 }
 
 // (max, float64 sum of exp(x - max)) of this workgroup's units of nr <= 2 rows, in one pass
-// over memory: every thread loads its units of both rows together, the block takes each
+// over memory: every thread loads its share of both rows together, the block takes each
 // row's maximum (one barrier), then every thread sums exp(x - max) over its values and the
-// block sums those (a second barrier). A slice larger than kStatUnits units per thread is
-// folded batch by batch, rescaling the running sum when a later batch raises the maximum.
-// Thread 0 receives the pairs in out[2 r], out[2 r + 1] (max -inf and sum 0 for an empty
-// slice or r >= nr).
-constexpr int kStatUnits = 2;   // units per thread and batch
+// block sums those (a second barrier). With 16-byte units a thread takes half units (8
+// bytes), so that a slice of a few hundred units keeps all four waves busy. A slice larger
+// than one batch (kStatUnits per thread) is folded batch by batch, rescaling the running sum
+// when a later batch raises the maximum. Thread 0 receives the pairs in out[2 r],
+// out[2 r + 1] (max -inf and sum 0 for an empty slice or r >= nr).
+constexpr int kStatUnits = 2;   // values groups per thread and batch
+
+template <int DT>
+__device__ __forceinline__ void half_decode(const uint2 raw, float (&x)[RowT<DT>::VEC / 2]) {
+  const uint32_t w2[2] = {raw.x, raw.y};
+#pragma unroll
+  for (int e = 0; e < RowT<DT>::VEC / 2; ++e)
+    x[e] = DT ? bf16_to_f32(static_cast<uint16_t>((w2[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)) : __uint_as_float(w2[e]);
+}
 
 template <int DT>
 __device__ void slice_stats(const void* row0, const void* row1, const uint4* st0, const uint4* st1, int nr,
                             const WalkGroup& g, bool vec, const double* tab, double (*wred)[4], double* out) {
-  constexpr int VEC = RowT<DT>::VEC;
-  const int w = vec ? VEC : 1;
+  constexpr int HV = RowT<DT>::VEC / 2;   // values per half unit
+  const int w = vec ? HV : 1;            // values per item: a half unit, or one entry
+  const int i0 = vec ? 2 * g.u0 : g.u0, i1 = vec ? 2 * g.u1 : g.u1;   // this workgroup's items
   const void* rows[2] = {row0, row1};
   const uint4* sts[2] = {st0, st1};
   const int wv = threadIdx.x >> 6;
   double M[2] = {-INFINITY, -INFINITY}, S[2] = {0.0, 0.0};
-  for (int b0 = g.u0; b0 < g.u1; b0 += kBlock * kStatUnits) {   // block-uniform batches
-    float x[2][kStatUnits][VEC];
+  for (int b0 = i0; b0 < i1; b0 += kBlock * kStatUnits) {   // block-uniform batches
+    float x[2][kStatUnits][HV];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int q = 0; q < kStatUnits; ++q) {
-        const int a = b0 + q * kBlock + static_cast<int>(threadIdx.x);
-        const bool in = r < nr && a < g.u1;
+        const int it = b0 + q * kBlock + static_cast<int>(threadIdx.x);
+        const bool in = r < nr && it < i1;
         if (vec) {
-          if (in && sts[r] != nullptr) {
-            unit_decode<DT>(sts[r][a - g.u0], x[r][q]);
-          } else if (in) {
-            row_vec<DT>(rows[r], a, x[r][q]);
+          if (in) {
+            const uint2 raw = sts[r] != nullptr ? reinterpret_cast<const uint2*>(sts[r])[it - i0]
+                                                : reinterpret_cast<const uint2*>(rows[r])[it];
+            half_decode<DT>(raw, x[r][q]);
           } else {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) x[r][q][e] = -INFINITY;
+            for (int e = 0; e < HV; ++e) x[r][q][e] = -INFINITY;
           }
         } else {
-          x[r][q][0] = in ? row_value<DT>(rows[r], a) : -INFINITY;
+          x[r][q][0] = in ? row_value<DT>(rows[r], it) : -INFINITY;
         }
       }
     float tm[2];
@@ -488,7 +501,7 @@ __device__ void slice_stats(const void* row0, const void* row1, const uint4* st0
 #pragma unroll
       for (int q = 0; q < kStatUnits; ++q)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
+        for (int e = 0; e < HV; ++e)
           if (e < w) tm[r] = fmaxf(tm[r], x[r][q][e]);
       tm[r] = wave_max(tm[r]);
     }
@@ -511,10 +524,16 @@ __device__ void slice_stats(const void* row0, const void* row1, const uint4* st0
       ts[r] = 0.0;
       if (bm[r] != -INFINITY) {
 #pragma unroll
-        for (int q = 0; q < kStatUnits; ++q)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (e < w) ts[r] += exp_nonpos(static_cast<double>(x[r][q][e]) - bm[r], tab);
+        for (int q = 0; q < kStatUnits; ++q) {
+          // only items of the slice: a wave with none at a batch position skips its exps
+          if (r < nr && b0 + q * kBlock + static_cast<int>(threadIdx.x) < i1) {
+            if (vec) {
+              ts[r] += exp_nonpos_sum<HV, HV>(x[r][q], bm[r], tab);
+            } else {
+              ts[r] += exp_nonpos(static_cast<double>(x[r][q][0]) - bm[r], tab);
+            }
+          }
+        }
       }
       ts[r] = wave_sum(ts[r]);
     }
@@ -533,7 +552,7 @@ __device__ void slice_stats(const void* row0, const void* row1, const uint4* st0
         M[r] = bm[r];
       }
     }
-    if (b0 + kBlock * kStatUnits < g.u1) __syncthreads();   // read before the next batch writes it
+    if (b0 + kBlock * kStatUnits < i1) __syncthreads();   // read before the next batch writes it
   }
   if (threadIdx.x == 0) {
 #pragma unroll
@@ -544,34 +563,34 @@ __device__ void slice_stats(const void* row0, const void* row1, const uint4* st0
   }
 }
 
-// Sum of the G <= 32 slice values vals[0 .. G) by a fixed butterfly over 32 lanes: every
-// wave of every workgroup adds them in the same order, so all get the same bits.
+// Sum of the G <= 32 slice values vals[0 .. G), lane k % 32 holding value k, by a fixed
+// reduction order: every wave of every workgroup adds them the same way, so all get the
+// same bits.
 __device__ __forceinline__ double group_sum(const double* vals, int G) {
   const int k = threadIdx.x & 31;
-  double t = k < G ? vals[k] : 0.0;
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-  return t;
+  double lo, hi;
+  half_wave_reduce(k < G ? vals[k] : 0.0, [](double x, double y) { return x + y; }, lo, hi);
+  return lo;
 }
 
 // log sum exp of the target (lanes 0..31) and draft (lanes 32..63) rows from the (max, sum)
 // pairs of the G slices, vals[4 k .. 4 k + 3] = (target max, target sum, draft max, draft
-// sum) of slice k: lane l merges slice l % 32 of its row, the wave combines them. Every
-// wave of every workgroup computes it the same way, so all see the same bits.
+// sum) of slice k: lane l merges slice l % 32 of its row, each half of the wave combines
+// them. Every wave of every workgroup computes it the same way, so all see the same bits.
 __device__ __forceinline__ void merged_lse2(const double* vals, int G, const double* tab, double& lt, double& ld) {
   const int lane = threadIdx.x & 63;
   const int k = lane & 31, r = lane >> 5;
   const double m = k < G ? vals[4 * k + 2 * r] : -INFINITY;
   const double sm = k < G ? vals[4 * k + 2 * r + 1] : 0.0;
-  double M = m;
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
-  double t = m == -INFINITY ? 0.0 : sm * exp_nonpos(m - M, tab);
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-  const double l = M + log(t);
-  lt = __shfl(l, 0, 64);
-  ld = __shfl(l, 32, 64);
+  double Mt, Md;
+  half_wave_reduce(m, [](double x, double y) { return y > x ? y : x; }, Mt, Md);
+  const double M = r == 0 ? Mt : Md;
+  double St, Sd;
+  half_wave_reduce(m == -INFINITY ? 0.0 : sm * exp_nonpos(m - M, tab), [](double x, double y) { return x + y; },
+                   St, Sd);
+  const double l = log(r == 0 ? St : Sd);   // one log per lane: the target's in the first half
+  lt = Mt + read_lane(l, 0);
+  ld = Md + read_lane(l, 32);
 }
 
 // One rejection: out = max(p - q, 0) over this workgroup's units (entry j at j - d.base);
@@ -653,20 +672,25 @@ __device__ int slice_inverse_cdf(const WalkDist<DT>& d, const WalkGroup& g, doub
 // exchanges run (a slice of at most kStageUnits 16-byte units; larger slices read memory).
 constexpr int kStageUnits = 512;
 
-// Issues direct loads of units [g.u0, g.u1) of `row` into lds[0 .. g.u1 - g.u0): wave w's
-// instruction i covers units 256 i + 64 w + lane (lane l of a direct load fills the 16 bytes
-// at 16 l after the load's base); units past u1 reload unit u1 - 1 into the buffer's tail,
-// which nobody reads. Every thread must call it; the data is there after drain() and a
-// barrier.
+// Issues direct loads of units [g.u0, g.u1) of `row` into lds[0 .. g.u1 - g.u0). Waves 1..3
+// issue them: a wave's loads finish in order with every later global load of that wave, and
+// wave 0 polls the exchanges, which must not wait for these. Wave w covers the 64-unit
+// blocks at 64 (w - 1) + 192 i (lane l of a direct load fills the 16 bytes at 16 l after
+// the load's base); a block's units past u1 reload unit u1 - 1 into the buffer's tail, which
+// nobody reads. Every block starts below u1 - u0 <= kStageUnits and kStageUnits is a
+// multiple of 64, so every write stays inside the buffer. Every thread must call it; the
+// data is there after drain() and a barrier. Shared-memory reads of the buffers wait for
+// all of a wave's outstanding direct loads (the compiler cannot tell the two buffers
+// apart), so the walk issues a prefetch only after the last read of the current copies.
 __device__ __forceinline__ void stage_issue(const void* row, uint4* lds, const WalkGroup& g) {
   typedef __attribute__((address_space(3))) void lds_void_t;
   const int count = g.u1 - g.u0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (w == 0) return;
   const uint4* src = reinterpret_cast<const uint4*>(row);
-  for (int i0 = 0; i0 < count; i0 += kBlock) {
-    const int j = i0 + 64 * w + lane;
-    const int u = g.u0 + min(j, count - 1);
-    __builtin_amdgcn_global_load_lds(src + u, (lds_void_t*)(lds + i0 + 64 * w), 16, 0, 0);
+  for (int b0 = 64 * (w - 1); b0 < count; b0 += 64 * (kWaves - 1)) {
+    const int u = g.u0 + min(b0 + lane, count - 1);
+    __builtin_amdgcn_global_load_lds(src + u, (lds_void_t*)(lds + b0), 16, 0, 0);
   }
 }
 
@@ -695,6 +719,8 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   for (int v = threadIdx.x; v < N; v += kBlock) {
     sm.par[v] = static_cast<short>(a.tree.parent[tb + v]);
     sm.tok[v] = a.tree.token[tb + v];
+    sm.uacc[v] = a.u_acc[tb + v];
+    sm.ures[v] = a.u_res[tb + v];
     // rows are read at every node the walk may visit, tokens at every child tried: both
     // must lie inside the tables
     const int r = a.tree.row[tb + v];
@@ -757,16 +783,26 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
   if (lead && threadIdx.x == 0) a.path[tb] = 0;
   if (threadIdx.x == 0) sm.spath[0] = 0;
   for (;;) {
-    // children of v in slot order
-    const int seg = (N + kBlock - 1) / kBlock;
-    const int n0 = threadIdx.x * seg, n1 = min(N, n0 + seg);
-    int mine = 0;
-    for (int k = max(n0, 1); k < n1; ++k) mine += (sm.par[k] == v) ? 1 : 0;
+    // children of v in slot order: in each round of kBlock slots every wave ballots its 64,
+    // and a child's place is the count in earlier waves and rounds plus its lane rank
     int nk = 0;
-    int pos = block_exclusive_scan(mine, sm.iwsum, &nk);
-    for (int k = max(n0, 1); k < n1; ++k)
-      if (sm.par[k] == v) sm.kids[pos++] = k;
-    __syncthreads();
+    for (int k0 = 0; k0 < N; k0 += kBlock) {
+      const int k = k0 + static_cast<int>(threadIdx.x);
+      const bool is = k >= 1 && k < N && sm.par[k] == v;
+      const unsigned long long m = __ballot(is);
+      if ((threadIdx.x & 63) == 0) sm.kmask[threadIdx.x >> 6] = m;
+      __syncthreads();
+      int before = nk, tot = nk;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        const int c = __popcll(sm.kmask[q]);
+        before += q < static_cast<int>(threadIdx.x >> 6) ? c : 0;
+        tot += c;
+      }
+      if (is) sm.kids[before + lanes_below(m)] = k;
+      nk = tot;
+      __syncthreads();   // the places are written and kmask is free for the next round
+    }
     const int r = rowof[v];
     WalkDist<DT> d;
     d.trow = row_ptr(a.target, r);
@@ -774,28 +810,30 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     d.tst = staged ? stage[sbuf][0] : nullptr;
     d.dst = staged ? stage[sbuf][1] : nullptr;
     d.u0 = grp.u0;
-    // the first child's rows start loading into the other buffer; this node's have landed
-    // once every wave's loads are done and a barrier has passed
+    // this node's rows have landed once every wave's loads are done and a barrier has passed
     if (staged) {
       drain();
-      if (nk > 0) prefetch(sm.kids[0], sbuf ^ 1);
       __syncthreads();
     }
     // The node's normalisers: every workgroup reduces its slice of the target row (and of
     // the draft row when children are tried) and the group exchanges the four values.
-    // thread 0 starts the loads the first acceptance test needs (the child's logits in both
-    // rows and its uniform), so that they complete during the pass and the exchange
     float t_first = 0.f, d_first = 0.f;
     uint32_t u_first = 0u;
-    if (threadIdx.x == 0 && nk > 0) {
-      const int x = sm.tok[sm.kids[0]];
-      t_first = row_value<DT>(d.trow, x);
-      d_first = row_value<DT>(d.drow, x);
-      u_first = a.u_acc[tb + sm.kids[0]];
-    }
     {
       double st[4];
       slice_stats<DT>(d.trow, d.drow, d.tst, d.dst, nk > 0 ? 2 : 1, grp, vec, sm.rs.exptab, sm.wpair, st);
+      // the first child's rows load into the other buffer during the exchange and the test
+      // (slice_stats ends with a barrier: every read of this node's copies is done)
+      if (staged && nk > 0) prefetch(sm.kids[0], sbuf ^ 1);
+      // thread 0 loads what the first acceptance test needs (the child's logits in both rows
+      // and its uniform) during the exchange. Issued before the pass, these loads would hold
+      // it up: a wave's reads of the staged copies wait for all of its outstanding loads.
+      if (threadIdx.x == 0 && nk > 0) {
+        const int x = sm.tok[sm.kids[0]];
+        t_first = row_value<DT>(d.trow, x);
+        d_first = row_value<DT>(d.drow, x);
+        u_first = sm.uacc[sm.kids[0]];
+      }
       if (!group_exchange(grp, st, 4, false, 0.0, 0.0, false, gvals, &sm.flag)) {
         drain();   // no stage load is left in flight
         return;
@@ -832,24 +870,25 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
         __syncthreads();
         break;
       }
-      // the next child's rows load while this rejection's pass and exchange run (the
-      // rejected child's copies, loaded into the same buffer, have landed by now)
-      if (staged && q + 1 < nk) {
-        drain();
-        prefetch(sm.kids[q + 1], sbuf ^ 1);
-      }
       // rejection: residual (p - q)+ into the other buffer; kept only if it sums to > 0.
       // The owner of the next child's token publishes, for that token, the new residual
       // and the current p (used if the residual sums to 0).
       const int nxt = (cur == 0) ? 1 : 0;
       const double part = residual_slice<DT>(d, P[nxt], grp, sm);
       d.qvalid = true;   // residual_slice ends with a block barrier: the cache is complete
+      // the next child's rows load during this rejection's exchange (after the residual
+      // pass, the last reader of this node's copies; the rejected child's copies, loaded
+      // into the same buffer, have landed by now)
+      if (staged && q + 1 < nk) {
+        drain();
+        prefetch(sm.kids[q + 1], sbuf ^ 1);
+      }
       const int xn = (q + 1 < nk) ? sm.tok[sm.kids[q + 1]] : -1;
       const int xu = vec ? xn / Rw::VEC : xn;
       const bool owner = xn >= 0 && xu >= grp.u0 && xu < grp.u1;
       if (xn >= 0 && threadIdx.x == 0) {   // the next try's draft logit and uniform, during the exchange
         d_first = row_value<DT>(d.drow, xn);
-        u_first = a.u_acc[tb + sm.kids[q + 1]];
+        u_first = sm.uacc[sm.kids[q + 1]];
       }
       double e0 = 0.0, e1 = 0.0;
       if (owner && threadIdx.x == 0) {
@@ -884,7 +923,7 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     // p is still the target's softmax (a leaf, or residuals that summed to 0 every time),
     // they follow from the node's slice statistics, m_g and s_g: s_g exp(m_g - lt); else one
     // pass and an exchange find them.
-    const double u = (static_cast<double>(a.u_res[tb + v]) + 0.5) * inv32;
+    const double u = (static_cast<double>(sm.ures[v]) + 0.5) * inv32;
     if (z_last > 0.0) {
       __syncthreads();
       for (int k = threadIdx.x; k < grp.G; k += kBlock) gvals[k] /= z_last;
