@@ -63,6 +63,22 @@ __device__ __forceinline__ T dpp_move(T v) {
   }
 }
 
+// dpp_move with a row mask: lanes of rows outside ROWMASK, and lanes whose source lies
+// outside their row, receive 0.
+template <int CTRL, int ROWMASK, typename T>
+__device__ __forceinline__ T dpp_move_or0(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, true));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xFFFFFFFFull), CTRL, ROWMASK, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, ROWMASK, 0xF, true);
+    return __builtin_bit_cast(T, (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) |
+                                     static_cast<uint32_t>(lo));
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ T read_lane(T v, int lane) {
   static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values");
@@ -96,6 +112,26 @@ __device__ __forceinline__ void half_wave_reduce(T v, Op op, T& lo, T& hi) {
   v = op(v, dpp_move<0x140>(v));
   lo = op(read_lane(v, 0), read_lane(v, 16));
   hi = op(read_lane(v, 32), read_lane(v, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), in registers: shifts
+// of 1, 2, 4 and 8 inside each 16-lane row (row_shr), then row 0's total goes to row 1 and
+// row 2's to row 3 (row_bcast:15), and rows 0-1's total to rows 2 and 3 (row_bcast:31).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  v = v + dpp_move_or0<0x111, 0xF>(v);
+  v = v + dpp_move_or0<0x112, 0xF>(v);
+  v = v + dpp_move_or0<0x114, 0xF>(v);
+  v = v + dpp_move_or0<0x118, 0xF>(v);
+  v = v + dpp_move_or0<0x142, 0xA>(v);
+  v = v + dpp_move_or0<0x143, 0xC>(v);
+  return v;
+}
+
+// The value of the next lower lane (0 in lane 0): wave_shr:1.
+template <typename T>
+__device__ __forceinline__ T wave_shift_up1(T v) {
+  return dpp_move_or0<0x138, 0xF>(v);
 }
 
 template <typename T>
@@ -166,14 +202,8 @@ __device__ __forceinline__ T block_sum(T v, T* red) {
 template <typename T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  T inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  T exc = __shfl_up(inc, 1, 64);
-  if (lane == 0) exc = T(0);
+  const T inc = wave_inclusive_scan(v);
+  const T exc = wave_shift_up1(inc);
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
   T before = T(0), tot = T(0);

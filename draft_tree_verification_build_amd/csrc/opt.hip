@@ -166,15 +166,10 @@ __device__ __forceinline__ void root_gather(const float (&xv)[RowT<DT>::E], int 
     }
   const int lane = threadIdx.x & 63;
   const int cnt = __popc(bits);
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_inclusive_scan(cnt);
   int base = 0;
   if (lane == 63) base = atomicAdd(&sm.ncand, incl);
-  base = __shfl(base, 63, 64);
+  base = read_lane(base, 63);
   int pos = base + incl - cnt;
 #pragma unroll
   for (int i = 0; i < kLoads; ++i)

@@ -954,16 +954,17 @@ __global__ __launch_bounds__(kBlock) void sample_walk_kernel(SampleArgs a) {
     const double total = group_sum(gvals, grp.G);
     const double target = u * total;
     // the first workgroup whose slice takes the running sum past the target draws the
-    // token; if rounding leaves the target at the end, the last slice with mass does
-    double before = 0.0, mybase = 0.0;
-    int owner = -1, last_pos = 0;
-    for (int k = 0; k < grp.G; ++k) {
-      if (k == grp.gi) mybase = before;
-      if (owner < 0 && gvals[k] > 0.0 && before + gvals[k] > target) owner = k;
-      if (gvals[k] > 0.0) last_pos = k;
-      before += gvals[k];
-    }
-    if (owner < 0) owner = last_pos;
+    // token; if rounding leaves the target at the end, the last slice with mass does. Lane
+    // k of every wave holds slice k's mass and a prefix sum in registers gives the running
+    // sums (the same order in every wave of every workgroup, hence the same bits).
+    const int lk = threadIdx.x & 63;
+    const double gk = lk < grp.G ? gvals[lk] : 0.0;
+    const double incl = wave_inclusive_scan(gk);
+    const double mybase = read_lane(wave_shift_up1(incl), grp.gi);   // the mass before this slice
+    const unsigned long long passed = __ballot(lk < grp.G && gk > 0.0 && incl > target);
+    const unsigned long long massive = __ballot(lk < grp.G && gk > 0.0);
+    const int owner = passed != 0ull ? static_cast<int>(__builtin_ctzll(passed))
+                                     : (massive != 0ull ? 63 - static_cast<int>(__builtin_clzll(massive)) : 0);
     if (grp.gi == owner) {
       int k = slice_inverse_cdf<DT>(d, grp, mybase, target, sm);
       if (threadIdx.x == 0) {
