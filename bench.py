@@ -105,6 +105,11 @@ def algorithmic_work(step, wl):
     return out
 
 
+def talon_rows_name(cfg) -> str:
+    """TALON's row kernel: bf16 rows in 32768-value parts, fp32 rows in chunks."""
+    return "talon_rows_bf16_kernel" if cfg.dtype == "bf16" else "talon_rows_kernel"
+
+
 def kernel_work(step, wl, work):
     """Algorithmic bytes (and flops) of one launch of each kernel of the step, from the
     stage figures: the kernel that streams a stage's rows or keys carries its work, the
@@ -112,7 +117,7 @@ def kernel_work(step, wl, work):
     cfg = wl.cfg
     out = {}
     if cfg.build == "talon":
-        out["talon_rows_kernel"] = dict(work["build"])
+        out[talon_rows_name(cfg)] = dict(work["build"])
     elif cfg.build == "spine":
         out["spine_kernel"] = dict(work["build"])
     elif cfg.build == "opt":
@@ -133,7 +138,7 @@ def kernel_work(step, wl, work):
 # The kernels each stage launches (a stage's time is the HIP-event time of all of them;
 # rocprofv3 --kernel-trace lists them separately, and their averages add up to it).
 STAGE_KERNELS = {
-    "build": lambda c: {"talon": ["talon_rows_kernel", "talon_select_kernel"],
+    "build": lambda c: {"talon": [talon_rows_name(c), "talon_select_kernel"],
                         "spine": ["spine_kernel"],
                         "opt": ["opt_init_kernel", "opt_root_kernel", "opt_rows_kernel", "opt_bound_kernel",
                                 "opt_collect_kernel", "opt_select_kernel", "opt_finalize_kernel"],

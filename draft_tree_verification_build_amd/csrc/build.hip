@@ -11,6 +11,7 @@
 // per row, one workgroup per row chunk), and a second launch runs the whole layer loop
 // of one sequence inside one workgroup on those small per-row lists.
 #include "dtv_internal.h"
+#include "rows_bf16.h"
 #include "rowstats.h"
 #include "select.h"
 
@@ -109,6 +110,28 @@ __global__ __launch_bounds__(kBlock, 4) void talon_rows_kernel(TalonArgs a) {
                             rs, ms);
     if (threadIdx.x == 0) a.rcnt[rf] = n;
   }
+}
+
+// Phase 1 for bf16 rows: one 1024-thread workgroup per (sequence, row f < B, part of 32768
+// values). The workgroup that completes a row merges its parts into the row's Top-K (value,
+// token), count and log-sum-exp; a row of one part is complete on its own.
+__global__ __launch_bounds__(kPartThreads) void talon_rows_bf16_kernel(TalonArgs a) {
+  __shared__ PartSmem sm;
+  const int np = parts_of(a.V);
+  const int p = blockIdx.x % np;
+  const int rf = blockIdx.x / np;          // s * Wr + f
+  const int s = rf / a.Wr, f = rf % a.Wr;  // row f of sequence s is draft row f
+  if (a.state != nullptr && a.layer > 1) {  // layer by layer: the frontier's rows only
+    const int* st = a.state + 8 * s;
+    if (st[4] != 0 || f >= st[2]) return;
+  }
+  const uint16_t* row = static_cast<const uint16_t*>(a.draft) + (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V);
+  const int K = a.K;
+  float* rv = a.rv + static_cast<size_t>(rf) * K;
+  int* ri = a.ri + static_cast<size_t>(rf) * K;
+  const size_t ci = static_cast<size_t>(rf) * a.nch;   // the row's chunk slots hold its parts
+  part_row_reduce(row, a.V, p, np, K, a.cval + ci * K, a.cidx + ci * K, reinterpret_cast<PartStat*>(a.st + ci),
+                  &a.tickets[rf], &a.rlse[rf], rv, ri, &a.rcnt[rf], sm);
 }
 
 struct TalonSelSmem {
@@ -473,24 +496,27 @@ int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// The row phase: bf16 rows in parts (rows_bf16.h), fp32 rows in chunks (rowstats.h).
+static int launch_talon_rows(const TalonArgs& a, int dtype, hipStream_t st) {
+  if (dtype == 1) {
+    const int np = parts_of(a.V);
+    // a row's parts live in its chunk slots, and a merge stages every part's list at once
+    if (np > a.nch || np > kPartMaxParts || np * a.K > kPartMergeCap) return -1;
+    DTV_LAUNCH(talon_rows_bf16_kernel, dim3(a.S * a.Wr * np), dim3(kPartThreads), 0, st, a);
+  } else {
+    DTV_LAUNCH(talon_rows_kernel<0>, dim3(a.S * a.Wr * a.nch), dim3(kBlock), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_talon_layer(const TalonArgs& a, int dtype, hipStream_t st) {
-  const dim3 grid(a.S * a.Wr * a.nch);
-  if (dtype == 1)
-    DTV_LAUNCH(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
-  else
-    DTV_LAUNCH(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return -1;
+  if (launch_talon_rows(a, dtype, st) != 0) return -1;
   DTV_LAUNCH(talon_layer_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_talon(const TalonArgs& a, int dtype, hipStream_t st) {
-  const dim3 grid(a.S * a.Wr * a.nch);
-  if (dtype == 1)
-    DTV_LAUNCH(talon_rows_kernel<1>, grid, dim3(kBlock), 0, st, a);
-  else
-    DTV_LAUNCH(talon_rows_kernel<0>, grid, dim3(kBlock), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return -1;
+  if (launch_talon_rows(a, dtype, st) != 0) return -1;
   DTV_LAUNCH(talon_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

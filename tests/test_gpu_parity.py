@@ -145,6 +145,51 @@ def test_talon_build(name, seed, ov):
         np.testing.assert_array_equal(g[key], g2[key])
 
 
+def plant_special_values(wl, seed):
+    """Rows of the draft table get values that leave the bf16 row kernel's exp table or stress
+    its order keys: +0 and -0, magnitudes below 2^-16 (a subnormal and 2^-17), -inf, values
+    <= -256, and exact ties at a row's maximum; one row also holds a value above 256, which
+    sends its wave to the exponentials shifted by the maximum."""
+    rng = np.random.default_rng(seed)
+    d = wl.draft.copy()
+    S, R, V = d.shape
+    special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x3700, 0xB700, 0xFF80, 0xC3C0, 0xC400],
+                       dtype=np.uint16)
+    for s in range(S):
+        for r in range(min(R, 12)):
+            pos = rng.choice(V, size=min(V, 2 * special.size), replace=False)
+            d[s, r, pos] = np.resize(special, pos.size)
+        # ties at the maximum of rows 1 and 2
+        for r in (1, 2):
+            if r < R:
+                row = orows.decode(d[s, r], "bf16")
+                top = int(np.argmax(row))
+                tie = rng.choice(V, size=min(V, 3), replace=False)
+                d[s, r, tie] = d[s, r, top]
+        if R > 3:
+            d[s, 3, rng.integers(V)] = 0x4396   # 300.0
+    wl.draft = d
+    return wl
+
+
+@pytest.mark.parametrize("V", [128256, 70001, 32000, 5000])
+def test_talon_build_special_values(V):
+    """The bf16 row reduction of the TALON build (table of exponentials with its fix-ups,
+    packed order keys, padding past the row end, single- and multi-part rows) on rows with
+    special values: the tree bit-exact and the scores to 1e-12 against the oracle."""
+    need_gpu()
+    wl = plant_special_values(make_workload("c2_talon_llama3_8b", 31, V=V, P=64), 31)
+    cfg = wl.cfg
+    d = to_device(wl.draft, cfg.dtype, DEV)
+    tree = dtv.Tree(cfg.S, cfg.N, DEV)
+    ws = dtv.Workspace(DEV)
+    dtv.tree_build_talon(tree, d, cfg.B, cfg.K, cfg.alpha, ws)
+    assert ws.status("talon") == 0
+    g = tree_to_numpy(tree)
+    for s in range(cfg.S):
+        assert_tree_equal(g, s, ostep.build_tree(wl, s), tree.words)
+
+
 def attn_reference(wl, g):
     """The float64 oracle's outputs of every sequence, all rows (one product per KV head)."""
     cfg = wl.cfg
