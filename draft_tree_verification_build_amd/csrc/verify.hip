@@ -12,6 +12,7 @@
 // path matches (parent links in shared memory); the deepest accepted node, lowest slot
 // first, ends the path. No workgroup waits on a counter or a fence.
 #include "dtv_internal.h"
+#include "rows_bf16.h"
 #include "rowstats.h"
 
 namespace dtv {
@@ -29,6 +30,7 @@ constexpr long kGreedySpinLimit = 2000000;   // poll rounds (each a memory round
 // writes; a node at depth k has slot >= k, so no later source row is an earlier
 // destination. Every thread of the workgroup calls it. Returns false, touching nothing,
 // when P and the tree do not fit the cache.
+template <int NT = kBlock>
 __device__ bool walk_compact(const KvCompactView& c, int s, int n_cap, const int* spath, int L, int pair0,
                              int pstep) {
   const int P = c.P[s];
@@ -49,18 +51,23 @@ __device__ bool walk_compact(const KvCompactView& c, int s, int n_cap, const int
     dst = base + static_cast<size_t>(P + k) * row_bytes + ch * 16;
     return reinterpret_cast<const uint4*>(base + static_cast<size_t>(P + spath[k]) * row_bytes + ch * 16);
   };
-  for (int b0 = 0; b0 < total; b0 += kBlock * 4) {
+  for (int b0 = 0; b0 < total; b0 += NT * 4) {
     const int v0 = b0 + static_cast<int>(threadIdx.x);
     char *d0, *d1, *d2, *d3;
-    const uint4 x0 = *src_dst(v0, d0);
-    const uint4 x1 = *src_dst(v0 + kBlock, d1);
-    const uint4 x2 = *src_dst(v0 + 2 * kBlock, d2);
-    const uint4 x3 = *src_dst(v0 + 3 * kBlock, d3);
+    uint4 x0, x1, x2, x3;   // loads past the end are not issued
+    const uint4* s0 = src_dst(v0, d0);
+    const uint4* s1 = src_dst(v0 + NT, d1);
+    const uint4* s2 = src_dst(v0 + 2 * NT, d2);
+    const uint4* s3 = src_dst(v0 + 3 * NT, d3);
+    if (v0 < total) x0 = *s0;
+    if (v0 + NT < total) x1 = *s1;
+    if (v0 + 2 * NT < total) x2 = *s2;
+    if (v0 + 3 * NT < total) x3 = *s3;
     __syncthreads();
     if (v0 < total) *reinterpret_cast<uint4*>(d0) = x0;
-    if (v0 + kBlock < total) *reinterpret_cast<uint4*>(d1) = x1;
-    if (v0 + 2 * kBlock < total) *reinterpret_cast<uint4*>(d2) = x2;
-    if (v0 + 3 * kBlock < total) *reinterpret_cast<uint4*>(d3) = x3;
+    if (v0 + NT < total) *reinterpret_cast<uint4*>(d1) = x1;
+    if (v0 + 2 * NT < total) *reinterpret_cast<uint4*>(d2) = x2;
+    if (v0 + 3 * NT < total) *reinterpret_cast<uint4*>(d3) = x3;
     __syncthreads();
   }
   return true;
@@ -73,9 +80,119 @@ struct VerifySmem {
   int tok[kVerifyMaxNodes];     // drafted token
   unsigned char bad[kVerifyMaxNodes];   // 1: token differs from the argmax at the parent
   unsigned long long best[kVerifyMaxNodes];   // largest chunk key of every node
-  unsigned long long redu[kWaves];
+  unsigned long long redu[16];   // per-wave partials (up to 16 waves)
   int flag;
 };
+
+// The walk of sequence s by the 256 threads of one workgroup (every other thread of it has
+// ended): the tree is loaded first, so that its loads are in flight with the first polls;
+// every thread then polls its share of the N * nslot slots (node-major, nslot per node), up
+// to 8 at once, until all have reported, folds them into its node's maximum in shared memory
+// and clears them for the next call; then the tree walk and the compaction.
+template <int NT = kBlock>
+__device__ void greedy_walk(const VerifyArgs& a, int s, int N, int cap, int nch, unsigned long long* slots,
+                            VerifySmem& sm) {
+  const size_t tb = static_cast<size_t>(s) * cap;
+  if (threadIdx.x == 0) sm.flag = 0;
+  __syncthreads();
+  for (int v = threadIdx.x; v < N; v += NT) {
+    sm.best[v] = 0ull;
+    sm.tok[v] = a.tree.token[tb + v];
+    sm.par[v] = static_cast<short>(v == 0 ? -1 : a.tree.parent[tb + v]);
+    sm.dep[v] = static_cast<short>(a.tree.depth[tb + v]);
+    const int r = a.tree.row[tb + v];
+    const int dv = sm.dep[v];
+    // the path is written at the nodes' depths: they must lie inside the tree
+    if (r < 0 || r >= a.R || dv < 0 || dv >= N || (v == 0 && dv != 0)) sm.flag = 1;
+  }
+  __syncthreads();
+  int ok = 1;
+  const int total = N * nch;
+  for (int j0 = 0; j0 < total; j0 += NT * 8) {
+    unsigned long long b[8];
+    long polls = 0;
+    for (;;) {
+      bool all = true;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q * NT + static_cast<int>(threadIdx.x);
+        b[q] = j < total ? ld_cc(&slots[j]) : 1ull;
+        all = all && b[q] != 0ull;
+      }
+      if (all) break;
+      if (++polls > kGreedySpinLimit) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q * NT + static_cast<int>(threadIdx.x);
+      if (j < total) {
+        atomicMax(&sm.best[j / nch], b[q]);
+        slots[j] = 0ull;   // ready for the next call
+      }
+    }
+  }
+  __syncthreads();
+  if (sm.flag) {   // a row outside the table or a depth outside the tree: no path
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrBadRow);
+      a.path_len[s] = 0;
+      a.bonus[s] = -1;
+      if (a.kvc.k != nullptr) a.kvc.P_new[s] = -1;
+    }
+    return;
+  }
+  for (int v = threadIdx.x; v < N; v += NT) {
+    const int am = sort_key_index(sm.best[v]);
+    sm.a[v] = am;
+    if (a.argmax_out) a.argmax_out[tb + v] = am;
+  }
+  if (!ok) atomicExch(&a.hdr->err, kErrTimeout);
+  __syncthreads();
+  // a node is bad when its token is not the target argmax at its parent (or its parent
+  // link is not an earlier slot, which also bounds every walk below)
+  for (int v = threadIdx.x; v < N; v += NT) {
+    const int p = sm.par[v];
+    sm.bad[v] = (v > 0 && (p < 0 || p >= v || sm.tok[v] != sm.a[p])) ? 1 : 0;
+  }
+  __syncthreads();
+  // deepest accepted node, lowest slot among equals: maximise (depth << 20) | (2^20 - 1 - slot);
+  // node v is accepted when no node on its root path is bad (slots grow away from the root)
+  unsigned long long pick = 0;
+  for (int v = threadIdx.x; v < N; v += NT) {
+    bool clean = true;
+    for (int u = v; u > 0 && clean; u = sm.par[u]) clean = !sm.bad[u];
+    if (clean) {
+      const unsigned long long key2 = (static_cast<unsigned long long>(sm.dep[v]) << 20) |
+                                      static_cast<unsigned long long>(0xFFFFF - v);
+      pick = key2 > pick ? key2 : pick;
+    }
+  }
+  {   // the largest pick over the NT / 64 waves
+    pick = wave_max(pick);
+    if ((threadIdx.x & 63) == 0) sm.redu[threadIdx.x >> 6] = pick;
+    __syncthreads();
+    for (int q = 0; q < NT / 64; ++q) pick = sm.redu[q] > pick ? sm.redu[q] : pick;
+  }
+  const int vstar = 0xFFFFF - static_cast<int>(pick & 0xFFFFFull);
+  const int A = static_cast<int>(pick >> 20);
+  if (threadIdx.x == 0) {
+    for (int u = vstar; u >= 0; u = sm.par[u]) {
+      a.path[tb + sm.dep[u]] = u;
+      sm.tok[sm.dep[u]] = u;   // the path, for the compaction (tokens are no longer read)
+    }
+    a.path_len[s] = A + 1;
+    a.bonus[s] = sm.a[vstar];
+  }
+  if (a.kvc.k != nullptr) {
+    __syncthreads();
+    const bool done = walk_compact<NT>(a.kvc, s, cap, sm.tok, A + 1, 0, 1);
+    if (threadIdx.x == 0) a.kvc.P_new[s] = done ? a.kvc.P[s] + A + 1 : -1;
+  }
+}
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
@@ -130,106 +247,77 @@ __global__ __launch_bounds__(kBlock) void verify_greedy_kernel(VerifyArgs a) {
     if (threadIdx.x == 0) st_cc(&slots[static_cast<size_t>(i) * nch + c], best);
   }
   if (i != cap - 1 || c != nch - 1) return;
+  greedy_walk(a, s, N, cap, nch, slots, sm);
+}
 
-  // ---- the walk, by the sequence's last workgroup. The tree is loaded first, so that its
-  //      loads are in flight with the first polls; every thread then polls its share of
-  //      the N * nch chunk slots (node-major), up to 8 at once, until all have reported,
-  //      folds them into its node's maximum in shared memory and clears them for the next
-  //      call.
-  if (threadIdx.x == 0) sm.flag = 0;
-  __syncthreads();
-  for (int v = threadIdx.x; v < N; v += kBlock) {
-    sm.best[v] = 0ull;
-    sm.tok[v] = a.tree.token[tb + v];
-    sm.par[v] = static_cast<short>(v == 0 ? -1 : a.tree.parent[tb + v]);
-    sm.dep[v] = static_cast<short>(a.tree.depth[tb + v]);
-    const int r = a.tree.row[tb + v];
-    const int dv = sm.dep[v];
-    // the path is written at the nodes' depths: they must lie inside the tree
-    if (r < 0 || r >= a.R || dv < 0 || dv >= N || (v == 0 && dv != 0)) sm.flag = 1;
-  }
-  __syncthreads();
-  int ok = 1;
-  const int total = N * nch;
-  for (int j0 = 0; j0 < total; j0 += kBlock * 8) {
-    unsigned long long b[8];
-    long polls = 0;
-    for (;;) {
-      bool all = true;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = j0 + q * kBlock + static_cast<int>(threadIdx.x);
-        b[q] = j < total ? ld_cc(&slots[j]) : 1ull;
-        all = all && b[q] != 0ull;
-      }
-      if (all) break;
-      if (++polls > kGreedySpinLimit) {
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q * kBlock + static_cast<int>(threadIdx.x);
-      if (j < total) {
-        atomicMax(&sm.best[j / nch], b[q]);
-        slots[j] = 0ull;   // ready for the next call
-      }
-    }
-  }
-  __syncthreads();
-  if (sm.flag) {   // a row outside the table or a depth outside the tree: no path
-    if (threadIdx.x == 0) {
-      atomicExch(&a.hdr->err, kErrBadRow);
-      a.path_len[s] = 0;
-      a.bonus[s] = -1;
-      if (a.kvc.k != nullptr) a.kvc.P_new[s] = -1;
-    }
+// bf16 target rows: one 1024-thread workgroup per (sequence, node, part of 32768 values of
+// the node's target row, rows_bf16.h). The part's largest key is found from packed keys and
+// lane maxima; only the lanes that hold it look for its lowest index. The part publishes
+// (key << 32 | ~index) in its slot; the sequence's last workgroup in launch order then walks
+// on 256 of its threads.
+struct VerifyBf16Smem {
+  VerifySmem v;
+  uint32_t wmax[kPartWaves];
+  int wmin[kPartWaves];
+};
+
+__global__ __launch_bounds__(kPartThreads) void verify_greedy_bf16_kernel(VerifyArgs a) {
+  __shared__ VerifyBf16Smem sm;
+  const int np = parts_of(a.V);
+  const int cap = a.tree.n_cap;
+  const int s = blockIdx.x / (cap * np);
+  const int rest = blockIdx.x % (cap * np);
+  const int i = rest / np, p = rest % np;
+  const size_t tb = static_cast<size_t>(s) * cap;
+  const int N = a.tree.n_nodes[s];
+  const int r_slot = a.tree.row[tb + i];
+  if (N > cap || N < 1) {  // n_nodes is device data: refuse rather than read past the tree
+    if (threadIdx.x == 0 && i == 0 && p == 0) atomicExch(&a.hdr->err, kErrCapacity);
     return;
   }
-  for (int v = threadIdx.x; v < N; v += kBlock) {
-    const int am = sort_key_index(sm.best[v]);
-    sm.a[v] = am;
-    if (a.argmax_out) a.argmax_out[tb + v] = am;
-  }
-  if (!ok) atomicExch(&a.hdr->err, kErrTimeout);
-  __syncthreads();
-  // a node is bad when its token is not the target argmax at its parent (or its parent
-  // link is not an earlier slot, which also bounds every walk below)
-  for (int v = threadIdx.x; v < N; v += kBlock) {
-    const int p = sm.par[v];
-    sm.bad[v] = (v > 0 && (p < 0 || p >= v || sm.tok[v] != sm.a[p])) ? 1 : 0;
-  }
-  __syncthreads();
-  // deepest accepted node, lowest slot among equals: maximise (depth << 20) | (2^20 - 1 - slot);
-  // node v is accepted when no node on its root path is bad (slots grow away from the root)
-  unsigned long long pick = 0;
-  for (int v = threadIdx.x; v < N; v += kBlock) {
-    bool clean = true;
-    for (int u = v; u > 0 && clean; u = sm.par[u]) clean = !sm.bad[u];
-    if (clean) {
-      const unsigned long long key2 = (static_cast<unsigned long long>(sm.dep[v]) << 20) |
-                                      static_cast<unsigned long long>(0xFFFFF - v);
-      pick = key2 > pick ? key2 : pick;
+  unsigned long long* slots = a.cbest + tb * np;   // [node][part]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (i < N && (r_slot < 0 || r_slot >= a.R)) {
+    // a row outside the table is never read: the part reports the smallest non-empty key
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrBadRow);
+      st_cc(&slots[static_cast<size_t>(i) * np + p], 1ull);
     }
-  }
-  pick = block_max(pick, sm.redu);
-  const int vstar = 0xFFFFF - static_cast<int>(pick & 0xFFFFFull);
-  const int A = static_cast<int>(pick >> 20);
-  if (threadIdx.x == 0) {
-    for (int u = vstar; u >= 0; u = sm.par[u]) {
-      a.path[tb + sm.dep[u]] = u;
-      sm.tok[sm.dep[u]] = u;   // the path, for the compaction (tokens are no longer read)
-    }
-    a.path_len[s] = A + 1;
-    a.bonus[s] = sm.a[vstar];
-  }
-  if (a.kvc.k != nullptr) {
+  } else if (i < N) {
+    const uint16_t* row = static_cast<const uint16_t*>(a.target) + (static_cast<size_t>(s) * a.R + r_slot) * static_cast<size_t>(a.V);
+    const int vbase = p * kPartVecs;
+    const int vfull = a.V / 8;
+    const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && vfull > 0;
+    PartData d;
+    part_load(row, a.V, vbase, vec, d);
+    const bool clean = vec && vbase + (kPartLoads - 1) * kPartThreads + 64 * w + 63 < vfull;
+    uint32_t k2[kPartWords], g4[kPartLoads], lm;
+    part_keys(d, clean, row, a.V, vbase, vec, k2, g4, lm);
+    const uint32_t km = wave_max(lm);
+    if (lane == 0) sm.wmax[w] = km;
     __syncthreads();
-    const bool done = walk_compact(a.kvc, s, cap, sm.tok, A + 1, 0, 1);
-    if (threadIdx.x == 0) a.kvc.P_new[s] = done ? a.kvc.P[s] + A + 1 : -1;
+    uint32_t M = lane < kPartWaves ? sm.wmax[lane] : 0u;
+    M = row16_reduce(M, [](uint32_t x, uint32_t y) { return y > x ? y : x; });
+    // the lowest index holding M: a lane's values ascend in index with (word, half)
+    int idx = 0x7FFFFFFF;
+    if (lm == M) {
+#pragma unroll
+      for (int j = 0; j < kPartWords; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (idx == 0x7FFFFFFF && key_half(k2[j], h) == M) idx = part_index(vbase, j, h);
+    }
+    idx = wave_min(idx);
+    if (lane == 0) sm.wmin[w] = idx;
+    __syncthreads();
+    int I = lane < kPartWaves ? sm.wmin[lane] : 0x7FFFFFFF;
+    I = row16_reduce(I, [](int x, int y) { return y < x ? y : x; });
+    // every part holds a value of the row (p * 32768 < V), so M != 0 and the key is never 0
+    if (threadIdx.x == 0) st_cc(&slots[static_cast<size_t>(i) * np + p], part_sort_key(M, I));
   }
+  if (i != cap - 1 || p != np - 1) return;
+  if (threadIdx.x >= kBlock) return;   // the walk runs on 256 threads
+  greedy_walk<kBlock>(a, s, N, cap, np, slots, sm.v);
 }
 
 // ------------------------------------------------------------------ rejection sampling
@@ -1019,11 +1107,13 @@ int sample_walk_max_blocks(int dtype) {
 }
 
 int launch_verify_greedy(const VerifyArgs& a, int S, int dtype, hipStream_t st) {
-  const dim3 grid(S * a.tree.n_cap * a.nch);
-  if (dtype == 1)
-    DTV_LAUNCH(verify_greedy_kernel<1>, grid, dim3(kBlock), 0, st, a);
-  else
-    DTV_LAUNCH(verify_greedy_kernel<0>, grid, dim3(kBlock), 0, st, a);
+  if (dtype == 1) {   // parts of 32768 values; their slots fit the workspace's chunk slots
+    const int np = parts_of(a.V);
+    if (np > a.nch) return -1;
+    DTV_LAUNCH(verify_greedy_bf16_kernel, dim3(S * a.tree.n_cap * np), dim3(kPartThreads), 0, st, a);
+  } else {
+    DTV_LAUNCH(verify_greedy_kernel<0>, dim3(S * a.tree.n_cap * a.nch), dim3(kBlock), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
