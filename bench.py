@@ -121,7 +121,7 @@ def kernel_work(step, wl, work):
     elif cfg.build == "spine":
         out["spine_kernel"] = dict(work["build"])
     elif cfg.build == "opt":
-        out["opt_rows_kernel+opt_root_kernel"] = dict(work["build"])
+        out["opt_rows_bf16_kernel+opt_rows_kernel+opt_root_kernel"] = dict(work["build"])
     else:
         out["given_tree_kernel"] = dict(work["build"])
     att = "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
@@ -140,7 +140,8 @@ def kernel_work(step, wl, work):
 STAGE_KERNELS = {
     "build": lambda c: {"talon": [talon_rows_name(c), "talon_select_kernel"],
                         "spine": ["spine_kernel"],
-                        "opt": ["opt_init_kernel", "opt_root_kernel", "opt_rows_kernel", "opt_bound_kernel",
+                        "opt": ["opt_init_kernel", "opt_root_kernel", "opt_rows_bf16_kernel", "opt_rows_kernel",
+                                "opt_bound_kernel",
                                 "opt_collect_kernel", "opt_select_kernel", "opt_finalize_kernel"],
                         "given": ["given_tree_kernel"]}[c.build],
     "attention": lambda c: (["attn_bf16_kernel", "attn_combine_rows_kernel"] if c.dtype == "bf16"

@@ -164,6 +164,7 @@ SpineLayout spine_layout(void* ws, int S, int F, int K, int V, int dtype) {
 struct OptLayout {
   dtv::WsHeader* hdr;
   dtv::ChunkStat* st;
+  float* cmax;
   float* cval;
   int* cidx;
   unsigned* tickets;
@@ -196,6 +197,7 @@ OptLayout opt_layout(void* ws, int S, int n, int V, int max_layers, int dtype) {
   OptLayout L;
   L.hdr = c.take<dtv::WsHeader>(1);
   L.st = c.take<dtv::ChunkStat>(rows * nch);
+  L.cmax = c.take<float>(rows * nch);
   L.cval = c.take<float>(rows * nch * Kmax);
   L.cidx = c.take<int>(rows * nch * Kmax);
   L.tickets = c.take<unsigned>(rows);
@@ -631,8 +633,10 @@ static int opt_launch_layer(dtv::OptArgs& a, int layer, int dtype, hipStream_t s
   if (Kc < 2) Kc = 2;
   if (Kc > K) Kc = K;
   a.Kc = static_cast<int>(Kc);
-  a.Kw = layer == 1 ? dtv::opt_root_wave_quota(V, n, dtype == DTV_BF16 ? 1 : 0) : 0;
-  if (a.Kw > 0) return dtv::launch_opt_root(a, dtype == DTV_BF16 ? 1 : 0, st);   // the root layer in one launch
+  const int dt = dtype == DTV_BF16 ? 1 : 0;
+  a.Kw = layer == 1 ? dtv::opt_root_wave_quota(V, n, dt) : 0;
+  if (layer == 1 && (a.Kw > 0 || dtv::opt_root_one_workgroup(V, n, dt)))
+    return dtv::launch_opt_root(a, dt, st);   // the root layer in one launch
   return dtv::launch_opt_layer(a, dtype == DTV_BF16 ? 1 : 0, st);
 }
 
@@ -678,6 +682,7 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
   a.Wcap = n;
   a.hdr = L.hdr;
   a.st = L.st;
+  a.cmax = L.cmax;
   a.cval = L.cval;
   a.cidx = L.cidx;
   a.tickets = L.tickets;
@@ -700,7 +705,9 @@ int dtv_tree_build_opt(const dtv_tree* tree, int32_t S, const void* draft, int d
   a.done = L.done;
   a.nlayers = L.nlayers;
   a.row_base = -1;
-  if (dtv::launch_opt_init(a, st)) return launched(-1);
+  // the one-workgroup root launch sets the per-call state itself
+  if (!dtv::opt_root_one_workgroup(V, n, dtype == DTV_BF16 ? 1 : 0) && dtv::launch_opt_init(a, st))
+    return launched(-1);
   for (int layer = 1; layer <= max_layers; ++layer) {
     if (opt_launch_layer(a, layer, dtype, st)) return launched(-1);
   }
@@ -820,6 +827,7 @@ static int layered_layer(const dtv_tree* tree, int32_t S, const dtv_build_params
   a.Wcap = n;
   a.hdr = L.hdr;
   a.st = L.st;
+  a.cmax = L.cmax;
   a.cval = L.cval;
   a.cidx = L.cidx;
   a.tickets = L.tickets;

@@ -104,6 +104,7 @@ struct OptArgs {
   int Kw;                      // root layer in one launch: lane maxima per full wave (0: not used)
   WsHeader* hdr;
   ChunkStat* st;          // [S][Wcap][nch]
+  float* cmax;            // [S][Wcap][nch] largest value of every chunk of the frontier rows
   float* cval;            // [S][Wcap][nch][Kmax]
   int* cidx;
   unsigned* tickets;      // [S][Wcap]
@@ -265,6 +266,9 @@ int launch_opt_init(const OptArgs& a, hipStream_t st);
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st);
 int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st);
 int opt_root_wave_quota(int V, int n, int dtype);
+// The root layer in one 1024-thread workgroup per sequence (bf16, V <= 32768, ceil(V/8) >= n);
+// that launch also sets the per-call state (no init launch needed before it).
+bool opt_root_one_workgroup(int V, int n, int dtype);
 int launch_opt_finalize(const OptArgs& a, hipStream_t st);
 int launch_opt_report(const OptArgs& a, hipStream_t st);
 int launch_row_stats(const RowStatsArgs& a, int dtype, hipStream_t st);

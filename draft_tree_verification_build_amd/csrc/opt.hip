@@ -20,6 +20,7 @@
 // (W x chunks), opt_select (1 per sequence); then opt_finalize once. A sequence whose
 // drafting has stopped makes every later launch return at once.
 #include "dtv_internal.h"
+#include "rows_bf16.h"
 #include "rowstats.h"
 #include "select.h"
 
@@ -104,11 +105,61 @@ __global__ __launch_bounds__(kBlock, 4) void opt_rows_kernel(OptArgs a) {
   const size_t ci = rf * a.nch + c;
   // each chunk reports its top Kc (nch * Kc >= K): the row's merged K are then the best of
   // those, a subset of the row's candidates, which is all the lower bound needs
-  chunk_reduce<DT>(x, key, c, a.V, a.Kc, &a.st[ci], a.cval + ci * a.Kc, a.cidx + ci * a.Kc, sortbuf, rs);
+  chunk_reduce<DT>(x, key, c, a.V, a.Kc, &a.st[ci], a.cval + ci * a.Kc, a.cidx + ci * a.Kc, sortbuf, rs,
+                   &a.cmax[ci]);
   if (!last_arrival(&a.tickets[rf], a.nch, &rs.flag)) return;
   const int n = row_merge(a.st + rf * a.nch, a.cval + rf * a.nch * a.Kc, a.cidx + rf * a.nch * a.Kc, a.nch, a.Kc,
                           nullptr, nullptr, &a.rlse[rf], a.rv + rf * a.K, a.ri + rf * a.K, rs, ms, a.K);
   if (threadIdx.x == 0) st_cc(&a.rcnt[rf], n);
+}
+
+// bf16 rows in 32768-value parts (rows_bf16.h): the row's log-sum-exp and top-K as above,
+// and the maximum of each of its 8192-value chunks for the gathering pass. K <= 64. Rows of
+// one part go two to a 1024-thread workgroup (one workgroup of 16 waves fills a compute
+// unit's registers): the second row's words are requested once the first row's have landed,
+// and arrive while the first is reduced; the exp table is copied once for both. Longer rows
+// take one workgroup per part.
+__global__ __launch_bounds__(kPartThreads) void opt_rows_bf16_kernel(OptArgs a) {
+  __shared__ PartSmem sm;
+  const int np = parts_of(a.V);
+  const int K = a.K;
+  const auto row_ptr = [&](int s, int f) {
+    return static_cast<const uint16_t*>(a.draft) + (static_cast<size_t>(s) * a.R + row_of(a, f)) * static_cast<size_t>(a.V);
+  };
+  if (np == 1) {
+    const int pairs = (a.W + 1) >> 1;
+    const int s = blockIdx.x / pairs;
+    const int f0 = 2 * (blockIdx.x % pairs);
+    if (a.done[s]) return;
+    const bool two = f0 + 1 < a.W;
+    const uint16_t* r0 = row_ptr(s, f0);
+    const uint16_t* r1 = row_ptr(s, two ? f0 + 1 : f0);
+    const bool vec1 = ((reinterpret_cast<uintptr_t>(r1) & 15u) == 0) && a.V / 8 > 0;
+    part_tables_issue(sm);
+    PartData d0, d1;
+    part_load(r0, a.V, 0, ((reinterpret_cast<uintptr_t>(r0) & 15u) == 0) && a.V / 8 > 0, d0);
+    const size_t rf0 = static_cast<size_t>(s) * a.Wcap + f0;
+    part_row_reduce_loaded(d0, r0, a.V, 0, 1, K, nullptr, nullptr, nullptr, nullptr, &a.rlse[rf0], a.rv + rf0 * K,
+                           a.ri + rf0 * K, &a.rcnt[rf0], sm, a.cmax + rf0 * a.nch,
+                           [&] { if (two) part_load(r1, a.V, 0, vec1, d1); });
+    if (!two) return;
+    __syncthreads();   // the first row's waves are done with shared memory
+    const size_t rf1 = rf0 + 1;
+    part_row_reduce_loaded(d1, r1, a.V, 0, 1, K, nullptr, nullptr, nullptr, nullptr, &a.rlse[rf1], a.rv + rf1 * K,
+                           a.ri + rf1 * K, &a.rcnt[rf1], sm, a.cmax + rf1 * a.nch, [] {});
+    return;
+  }
+  int bid = blockIdx.x;
+  const int p = bid % np;
+  bid /= np;
+  const int f = bid % a.W;
+  const int s = bid / a.W;
+  if (a.done[s]) return;
+  const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
+  const size_t ci = rf * a.nch;   // the row's chunk slots hold its parts' records
+  part_row_reduce(row_ptr(s, f), a.V, p, np, K, a.cval + ci * K, a.cidx + ci * K,
+                  reinterpret_cast<PartStat*>(a.st + ci), &a.tickets[rf], &a.rlse[rf], a.rv + rf * K, a.ri + rf * K,
+                  &a.rcnt[rf], sm, a.cmax + ci);
 }
 
 // ------------------------------------------------------------------ 1'. the root layer in one launch
@@ -370,6 +421,198 @@ __global__ __launch_bounds__(kBlock) void opt_root_kernel(OptArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 1''. the bf16 root layer in one workgroup
+//
+// A bf16 root row of at most 32768 values fits one 1024-thread workgroup in registers, 32
+// values a lane (rows_bf16.h's part layout). The exp table gives the log-sum-exp. A lane
+// whose maximum reaches a threshold holds at least one value at or above it, so the n-th
+// largest of the 1024 lane maxima bounds the row's n-th largest value from below (wave 0
+// bisects it while the other waves sum); for logits of a smooth distribution about 1.5 n
+// values reach it. They are gathered and ranked exactly through buckets of their 16-bit
+// value keys, one key a bucket when the keys span at most 1024 (else equal slices of the
+// span): an entry's rank is the count of entries in higher buckets plus the members of its
+// own bucket with a larger (key, index) sort key. Entries ranked below n are layer 1, which
+// is also the first best list; the workgroup sets the sequence's per-call state. Applies
+// when lanes 0..n-1 all hold values, i.e. ceil(V / 8) >= n.
+
+constexpr int kRootPartCand = 4096;   // gathered entries at or above the bound
+constexpr int kRootPartBuckets = kPartThreads;
+
+struct OptRootPartSmem {
+  PartSmem ps;                            // tables; after the sums, the grouped keys and the kept scores
+  uint32_t lmax[kPartThreads];            // every lane's largest key
+  unsigned long long cand[kRootPartCand];
+  int kbs[kRootPartCand];                 // (bucket << 16) | place within the bucket
+  int bcnt[kRootPartBuckets];
+  int bbase[kRootPartBuckets];
+  int wred[kPartWaves];
+  double dred[kPartWaves];
+  uint32_t tau, kmax;
+  int ncand;
+  double lse;
+};
+static_assert(sizeof(double) * kExpBf16Entries >= sizeof(unsigned long long) * kRootPartCand + sizeof(double) * 1024,
+              "the grouped keys and the kept scores fit the table's space");
+
+bool opt_root_one_workgroup(int V, int n, int dtype) {
+  return dtype == 1 && V <= kPartValues && (V + 7) / 8 >= n && n <= 1024;
+}
+
+__global__ __launch_bounds__(kPartThreads) void opt_root_bf16_kernel(OptArgs a) {
+  __shared__ OptRootPartSmem sm;
+  const int s = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int V = a.V, n = a.n;
+  const uint16_t* row = static_cast<const uint16_t*>(a.draft) + static_cast<size_t>(s) * a.R * static_cast<size_t>(V);
+  const int vfull = V / 8;
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && vfull > 0;
+  part_tables_issue(sm.ps);
+  PartData d;
+  part_load(row, V, 0, vec, d);
+  const bool clean = vec && (kPartLoads - 1) * kPartThreads + 64 * w + 63 < vfull;
+  uint32_t k2[kPartWords], g4[kPartLoads], lm;
+  part_keys(d, clean, row, V, 0, vec, k2, g4, lm);
+  sm.lmax[threadIdx.x] = lm;
+  const uint32_t km = wave_max(lm);
+  sm.bcnt[threadIdx.x] = 0;
+  if (lane == 0) sm.ps.wtau[w] = km;
+  if (threadIdx.x == 0) sm.ncand = 0;
+  drain();          // this wave's table pieces have landed
+  __syncthreads();  // every wave's have, and the lane maxima are visible
+
+  // ---- wave 0: the n-th largest lane maximum (lanes 0..n-1 hold values: count(>= 1) >= n)
+  if (w == 0) {
+    uint32_t v[kPartWaves];
+#pragma unroll
+    for (int q = 0; q < kPartWaves; ++q) v[q] = sm.lmax[64 * q + lane];
+    const uint32_t KM = wave_max(lane < kPartWaves ? sm.ps.wtau[lane] : 0u);
+    uint32_t lo = 1u, hi = KM + 1u;   // count(>= lo) >= n > count(>= hi)
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < kPartWaves; ++q) c += __popcll(__ballot(v[q] >= mid));
+      if (c >= n) lo = mid; else hi = mid;
+    }
+    if (lane == 0) {
+      sm.tau = lo;
+      sm.kmax = KM;
+    }
+  }
+  double sum;
+  float shift;
+  part_wave_exp(d, k2, km, clean, 0, V, sm.ps, sum, shift);
+  if (lane == 0) {
+    sm.ps.wsum[w] = sum;
+    sm.ps.wshift[w] = shift;
+  }
+  __syncthreads();   // the bound and the partials
+
+  // ---- every value at or above the bound; wave 1 forms the log-sum-exp meanwhile
+  const uint32_t tau = sm.tau;
+  if (__ballot(lm >= tau) != 0ull) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kPartWords; ++j) c += ((k2[j] & 0xFFFFu) >= tau ? 1 : 0) + ((k2[j] >> 16) >= tau ? 1 : 0);
+    const int incl = wave_inclusive_scan(c);
+    int base = 0;
+    if (lane == 63) base = atomicAdd(&sm.ncand, incl);
+    base = read_lane(base, 63);
+    int pos = base + incl - c;
+#pragma unroll
+    for (int j = 0; j < kPartWords; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t k = key_half(k2[j], h);
+        if (k >= tau) {
+          if (pos < kRootPartCand) sm.cand[pos] = part_sort_key(k, part_index(0, j, h));
+          ++pos;
+        }
+      }
+  }
+  if (w == 1) {
+    float M;
+    double S;
+    merge_partials<true>(lane < kPartWaves ? sm.ps.wsum[lane] : 0.0, lane < kPartWaves ? sm.ps.wshift[lane] : 0.0f,
+                         sm.ps.e64, M, S);
+    if (lane == 0) sm.lse = static_cast<double>(M) + log(S);
+  }
+  __syncthreads();
+  const int C = sm.ncand;
+  if (C > kRootPartCand) {   // far more entries tie at the bound than the buffer holds: refuse
+    if (threadIdx.x == 0) {
+      atomicExch(&a.hdr->err, kErrCapacity);
+      a.done[s] = 1;
+      a.bcount[s] = 0;
+      a.nlayers[s] = 0;
+    }
+    return;
+  }
+  // ---- exact ranks through buckets of the value keys, largest first
+  const uint32_t KM = sm.kmax;
+  const uint32_t span = KM - tau + 1u;
+  const bool exact = span <= static_cast<uint32_t>(kRootPartBuckets);
+  for (int e = threadIdx.x; e < C; e += kPartThreads) {
+    const uint32_t k = static_cast<uint32_t>(sm.cand[e] >> 32);
+    const int b = static_cast<int>(exact ? KM - k : ((KM - k) * static_cast<uint32_t>(kRootPartBuckets)) / span);
+    sm.kbs[e] = (b << 16) | atomicAdd(&sm.bcnt[b], 1);
+  }
+  __syncthreads();
+  {
+    const int x = sm.bcnt[threadIdx.x];
+    const int incl = wave_inclusive_scan(x);
+    if (lane == 63) sm.wred[w] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < kPartWaves; ++q) before += q < w ? sm.wred[q] : 0;
+    sm.bbase[threadIdx.x] = before + incl - x;
+  }
+  __syncthreads();
+  unsigned long long* mkey = reinterpret_cast<unsigned long long*>(sm.ps.tab);   // the table is no longer read
+  double* ksc = sm.ps.tab + kRootPartCand;
+  for (int e = threadIdx.x; e < C; e += kPartThreads) {
+    const int kb = sm.kbs[e];
+    mkey[sm.bbase[kb >> 16] + (kb & 0xFFFF)] = sm.cand[e];
+  }
+  __syncthreads();
+  const double lse = sm.lse;
+  const size_t lb = static_cast<size_t>(s) * a.max_layers * n;   // layer 1 of sequence s
+  const size_t bb = static_cast<size_t>(s) * n;
+  for (int e = threadIdx.x; e < C; e += kPartThreads) {
+    const unsigned long long me = sm.cand[e];
+    const int b = sm.kbs[e] >> 16;
+    const int b0 = sm.bbase[b], bn = sm.bcnt[b];
+    if (b0 >= n) continue;   // the whole bucket ranks at or past n
+    int r = b0;
+    for (int q = 0; q < bn; ++q) r += mkey[b0 + q] > me ? 1 : 0;
+    if (r >= n) continue;
+    const double sc = 0.0 + (static_cast<double>(part_key_value(me)) - lse);
+    a.lscore[lb + r] = sc;
+    a.lparent[lb + r] = 0;
+    a.ltoken[lb + r] = part_key_index(me);
+    a.bscore[bb + r] = sc;
+    a.blayer[bb + r] = 1;
+    a.bpos[bb + r] = r;
+    ksc[r] = sc;
+  }
+  __syncthreads();
+  // E_1 = sum of exp(score) over the best list (C >= n: each of lanes 0..n-1 reaches tau)
+  double E = static_cast<int>(threadIdx.x) < n ? exp(ksc[threadIdx.x]) : 0.0;
+  E = wave_sum(E);
+  if (lane == 0) sm.dred[w] = E;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int q = 0; q < kPartWaves; ++q) t += sm.dred[q];
+    a.bcount[s] = n;
+    a.Eprev[s] = t;
+    a.nlayers[s] = 1;
+    a.ccount[s] = 0u;
+    a.done[s] = (t < a.delta || 1 >= a.max_layers) ? 1 : 0;   // gain over the empty tree
+  }
+}
+
 // ------------------------------------------------------------------ 2. lower bound
 
 struct OptBoundSmem {
@@ -429,12 +672,15 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   }
   __syncthreads();
   // the n-th largest reported score bounds the layer's n-th best score from below, and so
-  // does anything below it: one radix pass finds the 11-bit digit bucket that holds the
-  // n-th largest key, and the bucket's lowest key is the bound (a few more candidates pass
-  // it than pass the exact n-th score, for a fraction of the selection's passes)
+  // does anything below it: radix passes narrow the n-th largest key down to a prefix that
+  // fixes at least the exponent and 8 mantissa bits (one pass when the reported scores share
+  // their sign and upper exponent bits, two when they span, say, (-1, -8]), and the lowest
+  // key under that prefix is the bound: it lies within 2^-8 (relative) of the n-th score,
+  // so a few more candidates pass it than pass the exact n-th score, for a fraction of the
+  // selection's passes
   double lo = -INFINITY;
   if (total >= a.n) {
-    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs, 1);
+    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs, 64, 0, 52 - 8);
     const unsigned long long k = cut.prefix;
     const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
     lo = __longlong_as_double(static_cast<long long>(u));
@@ -463,7 +709,7 @@ __global__ __launch_bounds__(kBlock) void opt_collect_kernel(OptArgs a) {
   const size_t rf = static_cast<size_t>(s) * a.Wcap + f;
   const double base = parent_score(a, s, f);
   const double lse = a.rlse[rf];
-  const float cmax = a.st[rf * a.nch + c].maxv;
+  const float cmax = a.cmax[rf * a.nch + c];
   if (done) return;
   // a chunk whose largest logit cannot reach lo has no candidate: skip reading it
   if (!(base + (static_cast<double>(cmax) - lse) >= lo)) return;
@@ -914,10 +1160,20 @@ int launch_opt_init(const OptArgs& a, hipStream_t st) {
 }
 
 
+// bf16 rows go through the part kernel when its lists and merge hold them.
+static bool opt_part_rows(const OptArgs& a) {
+  const int np = parts_of(a.V);
+  return a.K <= 64 && np <= a.nch && np <= kPartMaxParts && np * a.K <= kPartMergeCap;
+}
+
 int launch_opt_layer(OptArgs a, int dtype, hipStream_t st) {
   const dim3 rows(a.S * a.W * a.nch);
   const bool big = a.Kc > 32;
-  if (dtype == 1) {
+  if (dtype == 1 && opt_part_rows(a)) {
+    const int np = parts_of(a.V);
+    const int wg = np == 1 ? a.S * ((a.W + 1) / 2) : a.S * a.W * np;   // rows of one part go in pairs
+    DTV_LAUNCH(opt_rows_bf16_kernel, dim3(wg), dim3(kPartThreads), 0, st, a);
+  } else if (dtype == 1) {
     if (big)
       DTV_LAUNCH((opt_rows_kernel<1, true>), rows, dim3(kBlock), 0, st, a);
     else
@@ -960,6 +1216,10 @@ int opt_root_wave_quota(int V, int n, int dtype) {
 }
 
 int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st) {
+  if (opt_root_one_workgroup(a.V, a.n, dtype)) {
+    DTV_LAUNCH(opt_root_bf16_kernel, dim3(a.S), dim3(kPartThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const dim3 grid(a.S * a.nch);
   if (dtype == 1)
     DTV_LAUNCH(opt_root_kernel<1>, grid, dim3(kBlock), 0, st, a);

@@ -66,6 +66,7 @@ struct alignas(16) PartSmem {
   float wshift[kPartWaves];
   uint32_t wtau[kPartWaves];
   uint32_t rmax[4 * kPartWaves];   // row maxima (rows of 16 lanes)
+  uint32_t cmk[kPartWaves][2];     // each wave's maximum keys of the part's 8192-value chunks, two per word
   uint32_t tau;                    // the part's bound (row maxima)
   int wcnt[kPartWaves];            // candidates of each wave (beyond kPartSlots: overflow)
   int ncand2;                      // entries of the exact fallback (packed from slot[0][0])
@@ -282,6 +283,31 @@ __device__ __forceinline__ double part_shifted_sum(const uint32_t (&k2)[kPartWor
   return exp_nonpos_sum<2 * kPartWords>(x, static_cast<double>(m), e64);
 }
 
+// The wave's (shift, sum) partial, in every lane: the table sum (with the correction for
+// values outside the table) when every value is below 256, else the sum shifted by the wave
+// maximum (key km). Wave-uniform control flow.
+__device__ __forceinline__ void part_wave_exp(const PartData& d, const uint32_t (&k2)[kPartWords], uint32_t km,
+                                              bool clean, int vbase, int V, const PartSmem& sm, double& sum,
+                                              float& shift) {
+  sum = 0.0;
+  shift = 0.0f;
+  const bool huge = km >= bf16_order_key(0x4380u);   // some value >= 256 (or +inf, NaN)
+  if (!huge) {   // the table, and for a value outside it (|x| < 2^-16 or x <= -256) exp(x) - 1
+    if (clean) {
+      if (!part_table_sum<false>(d, sm, vbase, V, sum)) sum += part_table_fixup<false>(d, vbase, V, sm.e64);
+    } else {
+      if (!part_table_sum<true>(d, sm, vbase, V, sum)) sum += part_table_fixup<true>(d, vbase, V, sm.e64);
+    }
+  } else if (km != 0u) {
+    const float m = bf16_key_value(km);
+    if (m != -INFINITY) {
+      shift = m;
+      sum = part_shifted_sum(k2, m, sm.e64);
+    }
+  }
+  sum = wave_sum(sum);
+}
+
 // Number of the wave's values with key >= thr (wave-uniform).
 __device__ __forceinline__ int part_count_ge(const uint32_t (&k2)[kPartWords], uint32_t thr) {
   int n = 0;
@@ -474,17 +500,23 @@ __device__ __forceinline__ void part_merge_wide(const PartStat* ps, const float*
 // ps[p] (st_cc), the part counts itself in `ticket` (zero between calls; the last part
 // resets it), and the workgroup of the row's last part merges the row's parts (pval0/pidx0:
 // part 0's slots, part q's at q * K; ps: part 0's record) into lse, rcnt, rv/ri.
-__device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int p, int np, int K, float* pval0,
-                                                int* pidx0, PartStat* ps, unsigned* ticket, double* lse, float* rv,
-                                                int* ri, int* rcnt, PartSmem& sm) {
+// `cmax`, if given, receives the largest value of each of the row's 8192-value chunks that
+// the part holds (chunk 4 p + i is the part's i-th load; -inf for a chunk of padding only).
+//
+// part_row_reduce_loaded takes the part's words already requested (part_load) after the
+// tables (part_tables_issue), and calls `next` once every wave's table pieces and the
+// part's words have landed: a caller may request its next part's words there, so that they
+// arrive while this part is reduced. Waves that have no more to do return early; no block
+// barrier follows such a return, so a caller may place one after the call.
+template <typename Next>
+__device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16_t* row, int V, int p, int np, int K,
+                                                       float* pval0, int* pidx0, PartStat* ps, unsigned* ticket,
+                                                       double* lse, float* rv, int* ri, int* rcnt, PartSmem& sm,
+                                                       float* cmax, Next&& next) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int vbase = p * kPartVecs;
   const int vfull = V / 8;
   const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && vfull > 0;
-  // the tables first: the keys wait for the data loads, which are issued after them
-  part_tables_issue(sm);
-  PartData d;
-  part_load(row, V, vbase, vec, d);
   // the wave's values all lie in the row (its last vector is a full one)
   const bool clean = vec && vbase + (kPartLoads - 1) * kPartThreads + 64 * w + 63 < vfull;
   uint32_t k2[kPartWords];
@@ -498,6 +530,16 @@ __device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int 
   rm = max(rm, dpp_move<0x141>(rm));
   rm = max(rm, dpp_move<0x140>(rm));
   const uint32_t km = max(max(read_lane(rm, 0), read_lane(rm, 16)), max(read_lane(rm, 32), read_lane(rm, 48)));
+  if (cmax != nullptr) {   // the wave's maximum key of each load, two loads per packed reduction
+    const auto pmax = [](uint32_t x, uint32_t y) { return as_u32(__builtin_elementwise_max(as_u16x2(x), as_u16x2(y))); };
+    const auto hmax = [](uint32_t g) { return max(g & 0xFFFFu, g >> 16); };
+    const uint32_t m01 = wave_reduce(hmax(g4[0]) | (hmax(g4[1]) << 16), pmax);
+    const uint32_t m23 = wave_reduce(hmax(g4[2]) | (hmax(g4[3]) << 16), pmax);
+    if (lane == 0) {
+      sm.cmk[w][0] = m01;
+      sm.cmk[w][1] = m23;
+    }
+  }
   // A lower bound of the part's K-th largest value. K <= 16: the K-th largest of the part's
   // 64 row maxima. Larger K: the largest over the waves of each wave's K-th largest lane
   // maximum. Either way at least K values reach it.
@@ -518,6 +560,17 @@ __device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int 
   if (threadIdx.x == 0) sm.ncand2 = 0;
   drain();          // this wave's table pieces have landed
   __syncthreads();  // every wave's have, and the row maxima are visible
+  if (cmax != nullptr && w == kPartWaves - 1 && lane < kPartLoads) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int q = 0; q < kPartWaves; ++q) {
+      const uint32_t pk = sm.cmk[q][lane >> 1];
+      m = max(m, (lane & 1) ? pk >> 16 : pk & 0xFFFFu);
+    }
+    const int c = p * kPartLoads + lane;
+    if (c * (kPartValues / kPartLoads) < V) cmax[c] = m != 0u ? bf16_key_value(m) : -INFINITY;
+  }
+  next();
 
   // ---- the bound: wave 0 bisects the 64 row maxima (one per lane) before its own sum
   if (by_rows && w == 0) {
@@ -535,26 +588,9 @@ __device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int 
   }
 
   // ---- the wave's exponentials: table, else shifted by the wave maximum
-  double sum = 0.0;
-  float shift = 0.0f;
-  const bool huge = km >= bf16_order_key(0x4380u);   // some value >= 256 (or +inf, NaN)
-  if (!huge) {   // the table, and for a value outside it (|x| < 2^-16 or x <= -256) exp(x) - 1
-    if (clean) {
-      if (!part_table_sum<false>(d, sm, vbase, V, sum)) sum += part_table_fixup<false>(d, vbase, V, sm.e64);
-    } else {
-      if (!part_table_sum<true>(d, sm, vbase, V, sum)) sum += part_table_fixup<true>(d, vbase, V, sm.e64);
-    }
-  } else {
-    sum = 0.0;
-    if (km != 0u) {
-      const float m = bf16_key_value(km);
-      if (m != -INFINITY) {
-        shift = m;
-        sum = part_shifted_sum(k2, m, sm.e64);
-      }
-    }
-  }
-  sum = wave_sum(sum);
+  double sum;
+  float shift;
+  part_wave_exp(d, k2, km, clean, vbase, V, sm, sum, shift);
   if (by_rows) __syncthreads();   // the bound is visible
   const uint32_t tau = by_rows ? sm.tau : wave_max(lane < kPartWaves ? sm.wtau[lane] : 0u);
 
@@ -698,6 +734,16 @@ __device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int 
     return;
   }
   if (last_arrival(ticket, np, &sm.flag)) part_merge_wide(ps, pval0, pidx0, np, K, lse, rv, ri, rcnt, sm);
+}
+
+__device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int p, int np, int K, float* pval0,
+                                                int* pidx0, PartStat* ps, unsigned* ticket, double* lse, float* rv,
+                                                int* ri, int* rcnt, PartSmem& sm, float* cmax = nullptr) {
+  // the tables first: the keys wait for the data loads, which are issued after them
+  part_tables_issue(sm);
+  PartData d;
+  part_load(row, V, p * kPartVecs, ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && V / 8 > 0, d);
+  part_row_reduce_loaded(d, row, V, p, np, K, pval0, pidx0, ps, ticket, lse, rv, ri, rcnt, sm, cmax, [] {});
 }
 
 }  // namespace dtv

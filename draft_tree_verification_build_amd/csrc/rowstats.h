@@ -258,7 +258,7 @@ __device__ __forceinline__ float bf16key_to_f32(uint32_t k16) {
 // Reduces the chunk in registers. Writes *st and, when K > 0, the chunk's top-K (value,
 // index) sorted by (value desc, index asc) into out_val/out_idx (global, st_cc). The
 // argmax (largest value, lowest index) is the list's first entry when K > 0; only for
-// K = 0 is it looked for separately.
+// K = 0 is it looked for separately. `cmax`, if given, receives the chunk's maximum too.
 //
 // Per wave, without block barriers: maximum (and, for K = 0, its lowest index), float64 sum
 // of exp(x - wave max), valid count. Top-K, for K <= 32: every wave takes the K-th largest of
@@ -273,7 +273,7 @@ __device__ __forceinline__ float bf16key_to_f32(uint32_t k16) {
 template <int DT>
 __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key)[RowT<DT>::E], int c,
                              int V, int K, ChunkStat* st, float* out_val, int* out_idx,
-                             unsigned long long* sortbuf, RowSmem& sm) {
+                             unsigned long long* sortbuf, RowSmem& sm, float* cmax = nullptr) {
   using R = RowT<DT>;
   const int w = threadIdx.x >> 6;
   // ---- wave max, lowest index of the max, sum of exp, valid count
@@ -335,6 +335,7 @@ __device__ void chunk_reduce(const float (&x)[RowT<DT>::E], const uint32_t (&key
     const double S = wave_sum(term);
     if (q == 0) {
       st_cc(&st->maxv, M);
+      if (cmax != nullptr) st_cc(cmax, M);
       if (K == 0) st_cc(&st->argmax, AM);   // else written with the list's first entry
       st_cc(&st->sumexp, S);
       st_cc(&st->cnt, kk);

@@ -41,9 +41,12 @@ struct RadixCut {
 // from below. With group_max > 0 it also stops once the group that holds the k-th largest
 // key has at most group_max members and is not taken whole (group set): the caller then
 // ranks those members by full key (and its tie order) itself, which costs less than the
-// remaining passes. Every thread of the block must call it; all get the same result.
+// remaining passes. With min_unresolved, the selection also stops once at most that many
+// low bits are left unresolved (a bound: the prefix then fixes the key to within 2^that).
+// Every thread of the block must call it; all get the same result.
 __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs,
-                                                   int max_passes = 64, int group_max = 0) {
+                                                   int max_passes = 64, int group_max = 0,
+                                                   int min_unresolved = 0) {
   static_assert(kRadixBins % kBlock == 0, "whole bins per thread");
   unsigned long long kmax = 0ull, kmin = ~0ull;
   for (int e = threadIdx.x; e < n; e += kBlock) {
@@ -77,7 +80,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
   cut.all_in = false;
   cut.group = false;
   const int t = threadIdx.x;
-  for (int pass = 0; unresolved > 0 && pass < max_passes; ++pass) {
+  for (int pass = 0; unresolved > min_unresolved && pass < max_passes; ++pass) {
     const int w = unresolved < kRadixBits ? unresolved : kRadixBits;
     const int shift = unresolved - w;
     const unsigned dmask = (1u << w) - 1u;

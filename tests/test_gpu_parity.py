@@ -515,6 +515,12 @@ OPT_CASES = [
     # root layer in one launch with fp32 rows, and with heavy bf16 ties at the n-th value
     ("c4_opt_llama2_7b", 46, {"P": 16, "V": 20000, "n": 300, "max_layers": 3, "dtype": "f32"}),
     ("c4_opt_llama2_7b", 47, {"P": 16, "V": 32000, "n": 512, "max_layers": 2, "draft_sigma": 0.05, "S": 2}),
+    # bf16 rows of odd length (every other row not 16-byte aligned), root in one workgroup
+    ("c4_opt_llama2_7b", 48, {"P": 16, "V": 9001, "n": 300, "max_layers": 3, "S": 2}),
+    # one-workgroup root at its limit: exactly n lanes hold values (ceil(V / 8) == n); odd
+    # frontier width (the last row pair holds one row)
+    ("c4_opt_llama2_7b", 49, {"P": 16, "V": 4000, "n": 500, "max_layers": 3}),
+    ("c4_opt_llama2_7b", 50, {"P": 16, "V": 5000, "n": 301, "max_layers": 3, "S": 3}),
 ]
 
 
