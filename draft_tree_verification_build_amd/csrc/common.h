@@ -156,9 +156,10 @@ __device__ __forceinline__ unsigned long long dkey(double d) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Block-wide reductions; `red` is a __shared__ scratch of at least kWaves entries of T.
-// Every thread returns the result. Contains two __syncthreads().
-template <typename T>
+// Block-wide reductions over NW waves (kBlock threads by default); `red` is a __shared__
+// scratch of at least NW entries of T. Every thread returns the result. Contains two
+// __syncthreads().
+template <typename T, int NW = kWaves>
 __device__ __forceinline__ T block_max(T v, T* red) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6;
@@ -166,12 +167,12 @@ __device__ __forceinline__ T block_max(T v, T* red) {
   __syncthreads();
   T r = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
+  for (int i = 1; i < NW; ++i) r = red[i] > r ? red[i] : r;
   __syncthreads();
   return r;
 }
 
-template <typename T>
+template <typename T, int NW = kWaves>
 __device__ __forceinline__ T block_min(T v, T* red) {
   v = wave_min(v);
   const int w = threadIdx.x >> 6;
@@ -179,12 +180,12 @@ __device__ __forceinline__ T block_min(T v, T* red) {
   __syncthreads();
   T r = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = red[i] < r ? red[i] : r;
+  for (int i = 1; i < NW; ++i) r = red[i] < r ? red[i] : r;
   __syncthreads();
   return r;
 }
 
-template <typename T>
+template <typename T, int NW = kWaves>
 __device__ __forceinline__ T block_sum(T v, T* red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
@@ -192,14 +193,14 @@ __device__ __forceinline__ T block_sum(T v, T* red) {
   __syncthreads();
   T r = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r += red[i];
+  for (int i = 1; i < NW; ++i) r += red[i];
   __syncthreads();
   return r;
 }
 
-// Exclusive prefix sum over the block in thread order (wave scans, then wave offsets).
-// `wsum` is shared scratch of at least kWaves entries; *total receives the block sum.
-template <typename T>
+// Exclusive prefix sum over the block (NW waves) in thread order (wave scans, then wave
+// offsets). `wsum` is shared scratch of at least NW entries; *total receives the block sum.
+template <typename T, int NW = kWaves>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const T inc = wave_inclusive_scan(v);
@@ -208,7 +209,7 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* wsum, T* total) {
   __syncthreads();
   T before = T(0), tot = T(0);
 #pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
+  for (int q = 0; q < NW; ++q) {
     if (q < w) before += wsum[q];
     tot += wsum[q];
   }

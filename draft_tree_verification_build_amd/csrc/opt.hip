@@ -43,11 +43,11 @@ __device__ __forceinline__ unsigned long long front_key(const OptCand& c) {
 }
 
 // In-place bitonic sort of n (power of two) elements of shared memory by `before`.
-template <typename T, typename Cmp>
+template <int NT = kBlock, typename T, typename Cmp>
 __device__ void bitonic_sort(T* a, int n, Cmp before) {
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += kBlock) {
+      for (int i = threadIdx.x; i < n; i += NT) {
         const int p = i ^ j;
         if (p > i) {
           const T x = a[i], y = a[p];
@@ -621,18 +621,19 @@ struct OptBoundSmem {
   int cnt[1024];
   double ps[1024];    // parent score of each frontier row
   double lse[1024];   // its log-sum-exp
-  int wsum[kWaves];
+  int wsum[kMaxBlockWaves];
   RadixSmem rs;
 };
 
-__global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void opt_bound_kernel(OptArgs a) {
   __shared__ OptBoundSmem sm;
   const int s = blockIdx.x;
   if (a.done[s]) return;
   // the reported candidates: the top-m of every row (m = K), packed row after row
   // per row: list length (scanned to offsets), parent score and log-sum-exp, read once
   int carry = 0;
-  for (int f0 = 0; f0 < a.W; f0 += kBlock) {
+  for (int f0 = 0; f0 < a.W; f0 += NT) {
     const int f = f0 + threadIdx.x;
     const int fc = f < a.W ? f : a.W - 1;
     const size_t rf = static_cast<size_t>(s) * a.Wcap + fc;
@@ -640,7 +641,7 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
     const double ps = parent_score(a, s, fc);
     const double lse = a.rlse[rf];
     int tot = 0;
-    const int ex = block_exclusive_scan(cnt, sm.wsum, &tot);
+    const int ex = block_exclusive_scan<int, NT / 64>(cnt, sm.wsum, &tot);
     if (f < a.W) {
       sm.off[f] = carry + ex;
       sm.cnt[f] = cnt;
@@ -655,7 +656,7 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   // whole rows: their list values are loaded unconditionally (all addresses are in the
   // workspace), eight at a time in flight, and placed after the row's earlier entries
   const int K = a.K;
-  for (int f = threadIdx.x; f < a.W; f += kBlock) {
+  for (int f = threadIdx.x; f < a.W; f += NT) {
     const float* rv = a.rv + (static_cast<size_t>(s) * a.Wcap + f) * K;
     const double ps = sm.ps[f], lse = sm.lse[f];
     const int cnt = sm.cnt[f], off = sm.off[f];
@@ -680,7 +681,7 @@ __global__ __launch_bounds__(kBlock) void opt_bound_kernel(OptArgs a) {
   // selection's passes
   double lo = -INFINITY;
   if (total >= a.n) {
-    const RadixCut cut = radix_topk_cut(sm.key, total, a.n, sm.rs, 64, 0, 52 - 8);
+    const RadixCut cut = radix_topk_cut<NT>(sm.key, total, a.n, sm.rs, 64, 0, 52 - 8);
     const unsigned long long k = cut.prefix;
     const unsigned long long u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
     lo = __longlong_as_double(static_cast<long long>(u));
@@ -785,13 +786,14 @@ struct OptSelectSmem {
   int memb[1024];                  // kept candidates grouped by parent
   int kslot[1024];                 // a kept candidate's slot in its parent's group
   double kscore[1024];             // a kept candidate's score, by frontier position
-  int scan[kWaves];
-  double red[kWaves];
+  int scan[kMaxBlockWaves];
+  double red[kMaxBlockWaves];
   RadixSmem rs;
   int ntie, nkept, nout;
 };
 
-__global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void opt_select_kernel(OptArgs a) {
   __shared__ OptSelectSmem sm;
   const int s = blockIdx.x;
   if (a.done[s]) return;
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   }
   // (unrolled so that a thread's global loads are all in flight before its first store)
 #pragma unroll 8
-  for (int e = threadIdx.x; e < C; e += kBlock) {
+  for (int e = threadIdx.x; e < C; e += NT) {
     const OptCand cd = a.cand[static_cast<size_t>(s) * a.ccap + e];
     sm.u.in.c[e] = cd;
     sm.u.in.key[e] = dkey(cd.score);
@@ -821,10 +823,10 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   if (C > n) {
     // radix cut of the n best: a boundary group taken whole needs no tie order; a small
     // one (or the keys tied at the n-th full key) is ranked by (score desc, frontier order)
-    const RadixCut cut = radix_topk_cut(sm.u.in.key, C, n, sm.rs, 64, kOptGroupMax);
+    const RadixCut cut = radix_topk_cut<NT>(sm.u.in.key, C, n, sm.rs, 64, kOptGroupMax);
     const unsigned long long T = cut.prefix;
     const int rem = cut.all_in ? 0 : cut.rem;
-    for (int e = threadIdx.x; e < C; e += kBlock) {
+    for (int e = threadIdx.x; e < C; e += NT) {
       const unsigned long long k = sm.u.in.key[e];
       const unsigned long long km = k & cut.mask;
       if (cut.all_in ? (km >= T) : (km > T)) {
@@ -848,7 +850,7 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     }
     const int nt = sm.ntie;
     const int above = sm.nkept;   // = n - rem
-    for (int t = threadIdx.x; t < nt; t += kBlock) {
+    for (int t = threadIdx.x; t < nt; t += NT) {
       const unsigned long long me = sm.tkey[t];
       int before = 0;
       if (cut.group) {   // full score key desc, then frontier order
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
       if (before < rem) sm.keep_idx[above + before] = sm.tidx[t];
     }
   } else {
-    for (int e = threadIdx.x; e < C; e += kBlock) sm.keep_idx[e] = e;
+    for (int e = threadIdx.x; e < C; e += NT) sm.keep_idx[e] = e;
   }
   __syncthreads();
   // ---- frontier order (parent position asc, logit desc, token asc) numbers the next
@@ -872,9 +874,9 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   //      group larger than kOptBucketMax (the root layer) is numbered by a bitonic sort.
   const int l0 = a.layer - 1;
   const size_t lb = (static_cast<size_t>(s) * a.max_layers + l0) * n;
-  for (int f = threadIdx.x; f < a.W; f += kBlock) sm.cntp[f] = 0;
+  for (int f = threadIdx.x; f < a.W; f += NT) sm.cntp[f] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < kept; i += kBlock) {
+  for (int i = threadIdx.x; i < kept; i += NT) {
     const OptCand cd = sm.u.in.c[sm.keep_idx[i]];
     sm.fkey[i] = front_key(cd);
     sm.kslot[i] = atomicAdd(&sm.cntp[cd.fj >> 22], 1);
@@ -882,28 +884,29 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   __syncthreads();
   {
     int mb = 0;
-    for (int f = threadIdx.x; f < a.W; f += kBlock) mb = max(mb, sm.cntp[f]);
-    mb = block_max(mb, sm.scan);
+    for (int f = threadIdx.x; f < a.W; f += NT) mb = max(mb, sm.cntp[f]);
+    mb = block_max<int, NT / 64>(mb, sm.scan);
     if (mb > kOptBucketMax) {
       // one large group: sort all kept candidates by frontier key
       const int P2 = pow2_at_least(kept > 0 ? kept : 1);   // <= 1024
-      OptKept mine[4];
+      constexpr int kPer = 1024 / NT;   // entries a thread holds (kept <= n <= 1024)
+      OptKept mine[kPer];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = threadIdx.x + q * kBlock;
+      for (int q = 0; q < kPer; ++q) {
+        const int i = threadIdx.x + q * NT;
         mine[q].key = i < kept ? sm.fkey[i] : ~0ull;
         mine[q].score = i < kept ? sm.u.in.c[sm.keep_idx[i]].score : -INFINITY;
         mine[q].pos = i;
       }
       __syncthreads();   // the sort area overlaps the candidates
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = threadIdx.x + q * kBlock;
+      for (int q = 0; q < kPer; ++q) {
+        const int i = threadIdx.x + q * NT;
         if (i < P2) sm.u.srt.k[i] = mine[q];
       }
       __syncthreads();
-      bitonic_sort(sm.u.srt.k, P2, [](const OptKept& x, const OptKept& y) { return x.key < y.key; });
-      for (int r = threadIdx.x; r < kept; r += kBlock) {
+      bitonic_sort<NT>(sm.u.srt.k, P2, [](const OptKept& x, const OptKept& y) { return x.key < y.key; });
+      for (int r = threadIdx.x; r < kept; r += NT) {
         const OptKept k = sm.u.srt.k[r];
         a.lscore[lb + r] = k.score;
         a.lparent[lb + r] = static_cast<int>(k.key >> 54);
@@ -912,20 +915,20 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
       }
     } else {
       int carry = 0;
-      for (int f0 = 0; f0 < a.W; f0 += kBlock) {
+      for (int f0 = 0; f0 < a.W; f0 += NT) {
         const int f = f0 + threadIdx.x;
         int tot = 0;
-        const int ex = block_exclusive_scan(f < a.W ? sm.cntp[f] : 0, sm.scan, &tot);
+        const int ex = block_exclusive_scan<int, NT / 64>(f < a.W ? sm.cntp[f] : 0, sm.scan, &tot);
         if (f < a.W) sm.basep[f] = carry + ex;
         carry += tot;
       }
       __syncthreads();
-      for (int i = threadIdx.x; i < kept; i += kBlock) {
+      for (int i = threadIdx.x; i < kept; i += NT) {
         const int f = static_cast<int>(sm.fkey[i] >> 54);
         sm.memb[sm.basep[f] + sm.kslot[i]] = i;
       }
       __syncthreads();
-      for (int i = threadIdx.x; i < kept; i += kBlock) {
+      for (int i = threadIdx.x; i < kept; i += NT) {
         const unsigned long long me = sm.fkey[i];
         const int f = static_cast<int>(me >> 54);
         const int b0 = sm.basep[f], bn = sm.cntp[f];
@@ -945,13 +948,13 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
   const int nb = a.bcount[s];
   const size_t bb = static_cast<size_t>(s) * n;
 #pragma unroll 4
-  for (int e = threadIdx.x; e < nb; e += kBlock) {
+  for (int e = threadIdx.x; e < nb; e += NT) {
     const double sc = a.bscore[bb + e];
     sm.u.best.score[e] = sc;
     sm.u.best.key[e] = dkey(sc);
     sm.u.best.info[e] = (a.blayer[bb + e] << 16) | a.bpos[bb + e];
   }
-  for (int r = threadIdx.x; r < kept; r += kBlock) {
+  for (int r = threadIdx.x; r < kept; r += NT) {
     const double sc = sm.kscore[r];
     sm.u.best.score[nb + r] = sc;
     sm.u.best.key[nb + r] = dkey(sc);
@@ -974,10 +977,10 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
     part += exp(sc);
   };
   if (M2 <= n) {
-    for (int e = threadIdx.x; e < M2; e += kBlock) emit(e);
+    for (int e = threadIdx.x; e < M2; e += NT) emit(e);
   } else {
-    const RadixCut cut = radix_topk_cut(sm.u.best.key, M2, n, sm.rs, 64, kOptGroupMax);
-    for (int e = threadIdx.x; e < M2; e += kBlock) {
+    const RadixCut cut = radix_topk_cut<NT>(sm.u.best.key, M2, n, sm.rs, 64, kOptGroupMax);
+    for (int e = threadIdx.x; e < M2; e += NT) {
       const unsigned long long k = sm.u.best.key[e];
       const unsigned long long km = k & cut.mask;
       if (cut.all_in ? (km >= cut.prefix) : (km > cut.prefix)) {
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
       return;
     }
     const int nt = sm.ntie;
-    for (int t = threadIdx.x; t < nt; t += kBlock) {
+    for (int t = threadIdx.x; t < nt; t += NT) {
       const unsigned long long me = sm.tkey[t];
       int before = 0;
       if (cut.group) {   // full score key desc, then (layer, position)
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__(kBlock) void opt_select_kernel(OptArgs a) {
       if (before < cut.rem) emit(sm.tidx[t]);
     }
   }
-  const double E = block_sum(part, sm.red);
+  const double E = block_sum<double, NT / 64>(part, sm.red);
   if (threadIdx.x == 0) {
     a.bcount[s] = nnew;
     const double gain = E - a.Eprev[s];
@@ -1032,10 +1035,11 @@ struct OptFinalSmem {
   int wpre[64 * 1024 / 32];        // chosen nodes in earlier words
   int lp[1024];      // (layer << 16) | position of each chosen node, sorted
   short par[1025];
-  int scan[kWaves];
+  int scan[kMaxBlockWaves];
 };
 
-__global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void opt_finalize_kernel(OptArgs a) {
   __shared__ OptFinalSmem sm;
   const int s = blockIdx.x;
   // layer by layer: a sequence is written once, by the first call after its drafting stopped
@@ -1051,21 +1055,21 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
   // the chosen nodes by (layer, position): a presence bitmap over (layer, position) and
   // prefix counts of its words give every node its rank (the keys are distinct)
   const int nwords = a.max_layers * 32;
-  for (int w = threadIdx.x; w < nwords; w += kBlock) sm.bits[w] = 0u;
+  for (int w = threadIdx.x; w < nwords; w += NT) sm.bits[w] = 0u;
   __syncthreads();
-  for (int e = threadIdx.x; e < nb; e += kBlock) {
+  for (int e = threadIdx.x; e < nb; e += NT) {
     const int b = (a.blayer[bb + e] - 1) * 1024 + a.bpos[bb + e];
     atomicOr(&sm.bits[b >> 5], 1u << (b & 31));
   }
   __syncthreads();
   {
-    const int per = (nwords + kBlock - 1) / kBlock;   // contiguous words per thread
+    const int per = (nwords + NT - 1) / NT;   // contiguous words per thread
     const int w0 = threadIdx.x * per;
     int loc = 0;
     for (int q = 0; q < per; ++q)
       if (w0 + q < nwords) loc += __popc(sm.bits[w0 + q]);
     int tot = 0;
-    int run = block_exclusive_scan(loc, sm.scan, &tot);
+    int run = block_exclusive_scan<int, NT / 64>(loc, sm.scan, &tot);
     for (int q = 0; q < per; ++q)
       if (w0 + q < nwords) {
         sm.wpre[w0 + q] = run;
@@ -1073,7 +1077,7 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
       }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < nb; e += kBlock) {
+  for (int e = threadIdx.x; e < nb; e += NT) {
     const int layer = a.blayer[bb + e], pos = a.bpos[bb + e];
     const int b = (layer - 1) * 1024 + pos;
     const int r = sm.wpre[b >> 5] + __popc(sm.bits[b >> 5] & ((1u << (b & 31)) - 1u));
@@ -1092,7 +1096,7 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
     a.tree.n_nodes[s] = nb + 1;
     a.tree.layers[s] = a.nlayers[s];
   }
-  for (int e = threadIdx.x; e < nb; e += kBlock) {
+  for (int e = threadIdx.x; e < nb; e += NT) {
     const int layer = sm.lp[e] >> 16, pos = sm.lp[e] & 0xFFFF;
     const size_t lb = (static_cast<size_t>(s) * a.max_layers + (layer - 1)) * n + pos;
     int pslot = 0;
@@ -1116,7 +1120,7 @@ __global__ __launch_bounds__(kBlock) void opt_finalize_kernel(OptArgs a) {
     a.tree.score[o] = a.lscore[lb];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i <= nb; i += kBlock) {
+  for (int i = threadIdx.x; i <= nb; i += NT) {
     uint64_t* an = a.tree.anc + (tb + i) * words;
     for (int w = 0; w < words; ++w) an[w] = 0ull;
     for (int j = i; j >= 0; j = (j > 0) ? sm.par[j] : -1) an[j >> 6] |= 1ull << (j & 63);
@@ -1185,14 +1189,14 @@ int launch_opt_layer(OptArgs a, int dtype, hipStream_t st) {
       DTV_LAUNCH((opt_rows_kernel<0, false>), rows, dim3(kBlock), 0, st, a);
   }
   if (hipGetLastError() != hipSuccess) return -1;
-  DTV_LAUNCH(opt_bound_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_bound_kernel<kPartThreads>, dim3(a.S), dim3(kPartThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (dtype == 1)
     DTV_LAUNCH(opt_collect_kernel<1>, rows, dim3(kBlock), 0, st, a);
   else
     DTV_LAUNCH(opt_collect_kernel<0>, rows, dim3(kBlock), 0, st, a);
   if (hipGetLastError() != hipSuccess) return -1;
-  DTV_LAUNCH(opt_select_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_select_kernel<kPartThreads>, dim3(a.S), dim3(kPartThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -1229,7 +1233,7 @@ int launch_opt_root(const OptArgs& a, int dtype, hipStream_t st) {
 }
 
 int launch_opt_finalize(const OptArgs& a, hipStream_t st) {
-  DTV_LAUNCH(opt_finalize_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+  DTV_LAUNCH(opt_finalize_kernel<kPartThreads>, dim3(a.S), dim3(kPartThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

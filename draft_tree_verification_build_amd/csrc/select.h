@@ -7,14 +7,14 @@ namespace dtv {
 
 constexpr int kRadixBits = 11;                  // digit width of a pass
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kRadixPer = kRadixBins / kBlock;  // bins owned by a thread in the scan
+constexpr int kMaxBlockWaves = 16;             // 1024-thread workgroups
 
 struct RadixSmem {
   int hist[kRadixBins];   // counts of the pass; zero between passes
   int digit, rem, cnt;
-  int scan[kWaves];
-  unsigned long long red[kWaves];
-  unsigned long long red2[kWaves];
+  int scan[kMaxBlockWaves];
+  unsigned long long red[kMaxBlockWaves];
+  unsigned long long red2[kMaxBlockWaves];
 };
 
 // Result of radix_topk_cut: the keys k with (k & mask) > prefix are all among the top k;
@@ -43,13 +43,15 @@ struct RadixCut {
 // ranks those members by full key (and its tie order) itself, which costs less than the
 // remaining passes. With min_unresolved, the selection also stops once at most that many
 // low bits are left unresolved (a bound: the prefix then fixes the key to within 2^that).
-// Every thread of the block must call it; all get the same result.
+// Every thread of the block (NT threads) must call it; all get the same result.
+template <int NT = kBlock>
 __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key, int n, int k, RadixSmem& rs,
                                                    int max_passes = 64, int group_max = 0,
                                                    int min_unresolved = 0) {
-  static_assert(kRadixBins % kBlock == 0, "whole bins per thread");
+  static_assert(kRadixBins % NT == 0 && NT / 64 <= kMaxBlockWaves, "whole bins per thread");
+  constexpr int kRadixPer = kRadixBins / NT;  // bins owned by a thread in the scan
   unsigned long long kmax = 0ull, kmin = ~0ull;
-  for (int e = threadIdx.x; e < n; e += kBlock) {
+  for (int e = threadIdx.x; e < n; e += NT) {
     const unsigned long long x = key[e];
     if (x != 0ull) {
       kmax = x > kmax ? x : kmax;
@@ -66,7 +68,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
   for (int q = 0; q < kRadixPer; ++q) rs.hist[threadIdx.x * kRadixPer + q] = 0;
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
+  for (int q = 0; q < NT / 64; ++q) {
     kmax = rs.red[q] > kmax ? rs.red[q] : kmax;
     kmin = rs.red2[q] < kmin ? rs.red2[q] : kmin;
   }
@@ -84,7 +86,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
     const int w = unresolved < kRadixBits ? unresolved : kRadixBits;
     const int shift = unresolved - w;
     const unsigned dmask = (1u << w) - 1u;
-    for (int e = t; e < n; e += kBlock) {
+    for (int e = t; e < n; e += NT) {
       const unsigned long long x = key[e];
       if (x != 0ull && (x & cut.mask) == cut.prefix) atomicAdd(&rs.hist[(x >> shift) & dmask], 1);
     }
@@ -102,7 +104,7 @@ __device__ __forceinline__ RadixCut radix_topk_cut(const unsigned long long* key
       mine += c[q];
     }
     int tot = 0;
-    const int above = block_exclusive_scan(mine, rs.scan, &tot);
+    const int above = block_exclusive_scan<int, NT / 64>(mine, rs.scan, &tot);
     if (above < cut.rem && cut.rem <= above + mine) {
       int acc = above;
 #pragma unroll
