@@ -121,13 +121,15 @@ def kernel_work(step, wl, work):
     elif cfg.build == "spine":
         out["spine_kernel"] = dict(work["build"])
     elif cfg.build == "opt":
-        out["opt_rows_bf16_kernel+opt_rows_kernel+opt_root_kernel"] = dict(work["build"])
+        out["opt_rows_bf16_kernel+opt_rows_kernel+opt_root_bf16_kernel+opt_root_kernel"] = dict(work["build"])
     else:
         out["given_tree_kernel"] = dict(work["build"])
     att = "attn_bf16_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
     out[att] = dict(work["attention"])
     if cfg.verify == "greedy":
-        out["verify_greedy_kernel"] = dict(work["verify_compact"] if step.fuse_compact else work["verify"])
+        # bf16 rows go through the part kernel, fp32 rows through the chunk kernel
+        out["verify_greedy_bf16_kernel+verify_greedy_kernel"] = dict(work["verify_compact"] if step.fuse_compact
+                                                                     else work["verify"])
     else:
         out["sample_walk_kernel"] = dict(work["verify_compact"] if step.fuse_compact else work["verify"])
     if not step.fuse_compact:
@@ -140,15 +142,18 @@ def kernel_work(step, wl, work):
 STAGE_KERNELS = {
     "build": lambda c: {"talon": [talon_rows_name(c), "talon_select_kernel"],
                         "spine": ["spine_kernel"],
-                        "opt": ["opt_init_kernel", "opt_root_kernel", "opt_rows_bf16_kernel", "opt_rows_kernel",
+                        "opt": ["opt_init_kernel", "opt_root_bf16_kernel", "opt_root_kernel", "opt_rows_bf16_kernel",
+                                "opt_rows_kernel",
                                 "opt_bound_kernel",
                                 "opt_collect_kernel", "opt_select_kernel", "opt_finalize_kernel"],
                         "given": ["given_tree_kernel"]}[c.build],
     "attention": lambda c: (["attn_bf16_kernel", "attn_combine_rows_kernel"] if c.dtype == "bf16"
                             else ["attn_f32_kernel"]),
-    "verify": lambda c: (["verify_greedy_kernel"] if c.verify == "greedy" else ["sample_walk_kernel"]),
+    "verify": lambda c: (["verify_greedy_bf16_kernel", "verify_greedy_kernel"] if c.verify == "greedy"
+                         else ["sample_walk_kernel"]),
     "compact": lambda c: ["compact_kernel"],
-    "verify_compact": lambda c: (["verify_greedy_kernel (compacts the cache)"] if c.verify == "greedy"
+    "verify_compact": lambda c: (["verify_greedy_bf16_kernel or verify_greedy_kernel (compacts the cache)"]
+                                 if c.verify == "greedy"
                                  else ["sample_walk_kernel (compacts the cache)"]),
 }
 
