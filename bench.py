@@ -119,7 +119,7 @@ def kernel_work(step, wl, work):
     if cfg.build == "talon":
         out[talon_rows_name(cfg)] = dict(work["build"])
     elif cfg.build == "spine":
-        out["spine_kernel"] = dict(work["build"])
+        out["spine_bf16_kernel+spine_kernel"] = dict(work["build"])
     elif cfg.build == "opt":
         out["opt_rows_bf16_kernel+opt_rows_kernel+opt_root_bf16_kernel+opt_root_kernel"] = dict(work["build"])
     else:
@@ -141,7 +141,7 @@ def kernel_work(step, wl, work):
 # rocprofv3 --kernel-trace lists them separately, and their averages add up to it).
 STAGE_KERNELS = {
     "build": lambda c: {"talon": [talon_rows_name(c), "talon_select_kernel"],
-                        "spine": ["spine_kernel"],
+                        "spine": ["spine_bf16_kernel", "spine_kernel"],
                         "opt": ["opt_init_kernel", "opt_root_bf16_kernel", "opt_root_kernel", "opt_rows_bf16_kernel",
                                 "opt_rows_kernel",
                                 "opt_bound_kernel",

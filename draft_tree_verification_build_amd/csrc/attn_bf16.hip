@@ -12,9 +12,9 @@
 //   unit so that one's softmax overlaps the other's MFMAs. The ceil(M/32) row groups of a
 //   KV head are spread evenly over the tiles, so ragged row counts do not leave a tile
 //   nearly empty.
-// * K/V are double-buffered in LDS (K row-major, V transposed in fragment order): the
-//   global loads of block b+1 are issued before block b is computed and land in the other
-//   buffer afterwards, one barrier per 64-key block. Every load is unconditional (clamped to
+// * K/V are double-buffered in LDS, both row-major as in HBM (V is transposed by the
+//   fragment reads, not in memory): the global loads of block b+1 are issued before block
+//   b is computed and land in the other buffer afterwards, one barrier per 64-key block. Every load is unconditional (clamped to
 //   a valid key) so all of them are in flight together; every LDS access is a
 //   conflict-free 16-byte access.
 // * The tree mask and the key-range tail are applied only in blocks that need them, from

@@ -401,6 +401,29 @@ __global__ __launch_bounds__(kBlock) void talon_layer_kernel(TalonArgs a) {
 // completes a fork row merges its chunks and writes that fork's branch nodes. Branch
 // scores are log p_d(token | fork) (spine nodes carry no draft score).
 
+// The root and the spine chain of sequence s (nt threads of one workgroup).
+__device__ __forceinline__ void spine_chain(const SpineArgs& a, int s, size_t tb, int nt) {
+  const int words = a.tree.words;
+  for (int k = threadIdx.x; k <= a.n_spine; k += nt) {
+    const size_t o = tb + k;
+    a.tree.parent[o] = k - 1;
+    a.tree.token[o] = (k == 0) ? -1 : a.spine[static_cast<size_t>(s) * a.n_spine + k - 1];
+    a.tree.depth[o] = k;
+    a.tree.row[o] = k;
+    a.tree.score[o] = 0.0;
+    uint64_t* an = a.tree.anc + o * words;
+    for (int w = 0; w < words; ++w) {  // bits 0..k
+      const int lo = w * 64;
+      const int nb = k + 1 - lo;
+      an[w] = nb <= 0 ? 0ull : (nb >= 64 ? ~0ull : ((1ull << nb) - 1ull));
+    }
+  }
+  if (threadIdx.x == 0) {
+    a.tree.n_nodes[s] = a.n_nodes;
+    a.tree.layers[s] = 1;
+  }
+}
+
 constexpr int kSpineMaxK = 65;
 
 template <int DT>
@@ -430,26 +453,7 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   drain();
   __syncthreads();
 
-  if (f == 0 && c == 0) {  // root and spine chain of sequence s
-    for (int k = threadIdx.x; k <= a.n_spine; k += kBlock) {
-      const size_t o = tb + k;
-      a.tree.parent[o] = k - 1;
-      a.tree.token[o] = (k == 0) ? -1 : a.spine[static_cast<size_t>(s) * a.n_spine + k - 1];
-      a.tree.depth[o] = k;
-      a.tree.row[o] = k;
-      a.tree.score[o] = 0.0;
-      uint64_t* an = a.tree.anc + o * words;
-      for (int w = 0; w < words; ++w) {  // bits 0..k
-        const int lo = w * 64;
-        const int nb = k + 1 - lo;
-        an[w] = nb <= 0 ? 0ull : (nb >= 64 ? ~0ull : ((1ull << nb) - 1ull));
-      }
-    }
-    if (threadIdx.x == 0) {
-      a.tree.n_nodes[s] = a.n_nodes;
-      a.tree.layers[s] = 1;
-    }
-  }
+  if (f == 0 && c == 0) spine_chain(a, s, tb, kBlock);   // root and spine chain of sequence s
   const int wf = a.width[f];
   if (wf <= 0) return;
   const int kf = wf + 1 < a.V ? wf + 1 : a.V;   // one spare for the skipped spine token
@@ -487,7 +491,59 @@ __global__ __launch_bounds__(kBlock, 4) void spine_kernel(SpineArgs a) {
   }
 }
 
+// bf16 fork rows of at most one part (V <= 32768): one 1024-thread workgroup per (sequence,
+// fork) reduces the whole row with the part reducer (rows_bf16.h: table-driven float64
+// exponentials, packed 16-bit keys), so no chunk merge and no ticket are needed, and then
+// writes the fork's branch nodes itself.
+__global__ __launch_bounds__(kPartThreads) void spine_bf16_kernel(SpineArgs a) {
+  __shared__ PartSmem sm;
+  __shared__ int list_len;
+  const int f = blockIdx.x % a.F;
+  const int s = blockIdx.x / a.F;
+  const int cap = a.tree.n_cap;
+  const size_t tb = static_cast<size_t>(s) * cap;
+  const int words = a.tree.words;
+  if (f == 0) spine_chain(a, s, tb, kPartThreads);   // root and spine chain of sequence s
+  const int wf = a.width[f];
+  if (wf <= 0) return;
+  const int kf = wf + 1 < a.V ? wf + 1 : a.V;   // one spare for the skipped spine token
+  const size_t rf = static_cast<size_t>(s) * a.F + f;
+  const uint16_t* row = static_cast<const uint16_t*>(a.draft) + (static_cast<size_t>(s) * a.R + f) * static_cast<size_t>(a.V);
+  float* const rv = a.rv + rf * a.K;
+  int* const ri = a.ri + rf * a.K;
+  part_row_reduce(row, a.V, 0, 1, kf, nullptr, nullptr, nullptr, nullptr, &a.rlse[rf], rv, ri, &list_len, sm);
+  __syncthreads();   // the row's list, log-sum-exp and length are in
+  // list entry r becomes branch j = r, or r - 1 after the skipped spine token
+  const int r = threadIdx.x;
+  if (r >= kf || r >= list_len) return;
+  const int skip = (f < a.n_spine) ? a.spine[static_cast<size_t>(s) * a.n_spine + f] : -1;
+  const int tok = ri[r];
+  if (tok == skip) return;
+  int j = r;
+  for (int q = 0; q < r; ++q) j -= ri[q] == skip ? 1 : 0;
+  if (j >= wf) return;
+  const int slot = 1 + a.n_spine + a.offset[f] + j;
+  const size_t o = tb + slot;
+  a.tree.parent[o] = f;
+  a.tree.token[o] = tok;
+  a.tree.depth[o] = f + 1;
+  a.tree.row[o] = slot;
+  a.tree.score[o] = static_cast<double>(rv[r]) - a.rlse[rf];
+  uint64_t* an = a.tree.anc + o * words;
+  for (int w = 0; w < words; ++w) {  // bits 0..f plus the node itself
+    const int lo = w * 64;
+    const int nb = f + 1 - lo;
+    uint64_t bits = nb <= 0 ? 0ull : (nb >= 64 ? ~0ull : ((1ull << nb) - 1ull));
+    if ((slot >> 6) == w) bits |= 1ull << (slot & 63);
+    an[w] = bits;
+  }
+}
+
 int launch_spine(const SpineArgs& a, int dtype, hipStream_t st) {
+  if (dtype == 1 && parts_of(a.V) == 1 && a.K <= kPartSlots) {
+    DTV_LAUNCH(spine_bf16_kernel, dim3(a.S * a.F), dim3(kPartThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const dim3 grid(a.S * a.F * a.nch);
   if (dtype == 1)
     DTV_LAUNCH(spine_kernel<1>, grid, dim3(kBlock), 0, st, a);
