@@ -157,7 +157,34 @@ struct TalonSelSmem {
 // every key with that prefix is taken (the keys above the prefix and that whole group), or
 // the prefix is the full room-th largest key T and, of the keys equal to T, those with the
 // lowest e are taken. Requires more than `room` candidates.
+//
+// With at most 64 frontier rows and a small room, wave 0 merges the rows' sorted lists
+// instead: lane f holds the head of row f's gated prefix (keys do not increase along a row,
+// and e grows with f and with the rank), and each of `room` steps takes the largest head,
+// the lowest row among equal ones, and advances that row. No block barrier is needed until
+// the counts are written; the radix passes cost several barriers each.
+constexpr int kTalonHeadMergeRoom = 16;
+
 __device__ void talon_budget_select(TalonSelSmem& sm, int n, int K, int W, int room) {
+  if (W <= 64 && room <= kTalonHeadMergeRoom) {
+    if (threadIdx.x < 64) {
+      const int f = threadIdx.x;
+      const int g = f < W ? sm.gated[f] : 0;
+      int j = 0;
+      unsigned long long head = g > 0 ? sm.ckey[f * K] : 0ull;
+      for (int t = 0; t < room; ++t) {   // more than `room` candidates: a head is never 0 here
+        const unsigned long long top = wave_max(head);
+        const int win = __builtin_ctzll(__ballot(head == top));
+        if (f == win) {
+          ++j;
+          head = j < g ? sm.ckey[f * K + j] : 0ull;
+        }
+      }
+      if (f < W) sm.kept[f] = j;
+    }
+    __syncthreads();
+    return;
+  }
   const RadixCut cut = radix_topk_cut(sm.ckey, n, room, sm.rs);
   for (int f = threadIdx.x; f < W; f += kBlock) sm.kept[f] = 0;
   __syncthreads();

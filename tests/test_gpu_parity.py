@@ -145,6 +145,36 @@ def test_talon_build(name, seed, ov):
         np.testing.assert_array_equal(g[key], g2[key])
 
 
+@pytest.mark.parametrize("B,kept", [(13, [3, 3, 2, 1]), (20, [4, 4, 4, 4]), (9, [2, 1, 1, 1])])
+def test_talon_budget_cut_through_a_tie(B, kept):
+    """TALON's budget cut through groups of exactly equal path scores of different parents
+    (TALON page, 5.2.1: the cap keeps the best remaining-budget candidates; ties go to the
+    lower parent slot, then the lower rank). The root row's four best tokens share one logit
+    and their four rows are identical (whose second and third values are also equal), so the
+    layer-2 pool of 16 holds a group of four equal scores (rank 0) and one of eight (ranks 1
+    and 2); with no gate the cut of B - 4 falls inside a group: B = 13 keeps rank 0 and five
+    of the eight, B = 9 one of the eight. The tree is compared with the oracle's, whose
+    layer-2 children per parent are checked first so that the cut really splits a group."""
+    need_gpu()
+    wl = make_workload("c2_talon_llama3_8b", 19, V=5000, P=64, B=B, K=4, alpha=0.0)
+    d = wl.draft.copy()
+    d[0, 0, 10:14] = 0x41F0   # 30.0, above every other logit of the row
+    d[0, 2] = d[0, 1]
+    d[0, 3] = d[0, 1]
+    d[0, 4] = d[0, 1]
+    wl.draft = d
+    cfg = wl.cfg
+    ot = ostep.build_tree(wl, 0)
+    assert ot.token[1:5] == [10, 11, 12, 13]
+    assert [sum(1 for p in ot.parent if p == v) for v in range(1, 5)] == kept
+    dd = to_device(wl.draft, cfg.dtype, DEV)
+    tree = dtv.Tree(cfg.S, cfg.N, DEV)
+    ws = dtv.Workspace(DEV)
+    dtv.tree_build_talon(tree, dd, cfg.B, cfg.K, cfg.alpha, ws)
+    assert ws.status("talon") == 0
+    assert_tree_equal(tree_to_numpy(tree), 0, ot, tree.words)
+
+
 def plant_special_values(wl, seed):
     """Rows of the draft table get values that leave the bf16 row kernel's exp table or stress
     its order keys: +0 and -0, magnitudes below 2^-16 (a subnormal and 2^-17), -inf, values
