@@ -30,6 +30,17 @@ __global__ __launch_bounds__(kBlock) void given_tree_kernel(TreeArgs t, WsHeader
     return;
   }
   const size_t base = static_cast<size_t>(s) * cap;
+  // the parents in shared memory first (all loads in flight together), so that each node's
+  // walk to the root is a chain of shared-memory reads, not of global loads
+  __shared__ int par[kMaxWords * 64];
+  constexpr int kPer = kMaxWords * 64 / kBlock;
+  int pv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) pv[u] = t.parent[base + min(static_cast<int>(threadIdx.x) + u * kBlock, N - 1)];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (static_cast<int>(threadIdx.x) + u * kBlock < N) par[threadIdx.x + u * kBlock] = pv[u];
+  __syncthreads();
   for (int i = threadIdx.x; i < N; i += kBlock) {
     uint64_t acc[kMaxWords];
 #pragma unroll
@@ -42,7 +53,7 @@ __global__ __launch_bounds__(kBlock) void given_tree_kernel(TreeArgs t, WsHeader
 #pragma unroll
       for (int u = 0; u < kMaxWords; ++u)
         if (u == w) acc[u] |= 1ull << (j & 63);
-      const int p = t.parent[base + j];
+      const int p = par[j];
       if (p < 0 || p >= j) {
         ok = false;
         break;

@@ -27,6 +27,7 @@
 namespace dtv {
 
 constexpr int kOptMergeCap = 8192;  // chunks * K of one row merge
+constexpr int kOptMaxWords = 16;    // ancestor-mask words of a tree of at most 1024 slots
 constexpr int kOptLdsCand = 4096;   // candidates selected in shared memory
 
 struct OptCand {
@@ -1120,10 +1121,21 @@ __global__ __launch_bounds__(NT) void opt_finalize_kernel(OptArgs a) {
     a.tree.score[o] = a.lscore[lb];
   }
   __syncthreads();
+  // every node's ancestor-or-self mask, built in registers from the parents in shared memory
+  // and stored once
   for (int i = threadIdx.x; i <= nb; i += NT) {
+    uint64_t acc[kOptMaxWords];
+#pragma unroll
+    for (int w = 0; w < kOptMaxWords; ++w) acc[w] = 0ull;
+    for (int j = i; j >= 0; j = (j > 0) ? sm.par[j] : -1) {
+#pragma unroll
+      for (int u = 0; u < kOptMaxWords; ++u)
+        if (u == (j >> 6)) acc[u] |= 1ull << (j & 63);
+    }
     uint64_t* an = a.tree.anc + (tb + i) * words;
-    for (int w = 0; w < words; ++w) an[w] = 0ull;
-    for (int j = i; j >= 0; j = (j > 0) ? sm.par[j] : -1) an[j >> 6] |= 1ull << (j & 63);
+#pragma unroll
+    for (int w = 0; w < kOptMaxWords; ++w)
+      if (w < words) an[w] = acc[w];
   }
 }
 
