@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kPartThreads) void talon_rows_bf16_kernel(TalonArgs
   int* ri = a.ri + static_cast<size_t>(rf) * K;
   const size_t ci = static_cast<size_t>(rf) * a.nch;   // the row's chunk slots hold its parts
   part_row_reduce(row, a.V, p, np, K, a.cval + ci * K, a.cidx + ci * K, reinterpret_cast<PartStat*>(a.st + ci),
-                  &a.tickets[rf], &a.rlse[rf], rv, ri, &a.rcnt[rf], sm);
+                  &a.tickets[rf], &a.rlse[rf], rv, ri, &a.rcnt[rf], sm, nullptr, &a.hdr->err, true);
 }
 
 struct TalonSelSmem {

@@ -141,13 +141,13 @@ __global__ __launch_bounds__(kPartThreads) void opt_rows_bf16_kernel(OptArgs a) 
     part_load(r0, a.V, 0, ((reinterpret_cast<uintptr_t>(r0) & 15u) == 0) && a.V / 8 > 0, d0);
     const size_t rf0 = static_cast<size_t>(s) * a.Wcap + f0;
     part_row_reduce_loaded(d0, r0, a.V, 0, 1, K, nullptr, nullptr, nullptr, nullptr, &a.rlse[rf0], a.rv + rf0 * K,
-                           a.ri + rf0 * K, &a.rcnt[rf0], sm, a.cmax + rf0 * a.nch,
+                           a.ri + rf0 * K, &a.rcnt[rf0], sm, a.cmax + rf0 * a.nch, &a.hdr->err, false,
                            [&] { if (two) part_load(r1, a.V, 0, vec1, d1); });
     if (!two) return;
     __syncthreads();   // the first row's waves are done with shared memory
     const size_t rf1 = rf0 + 1;
     part_row_reduce_loaded(d1, r1, a.V, 0, 1, K, nullptr, nullptr, nullptr, nullptr, &a.rlse[rf1], a.rv + rf1 * K,
-                           a.ri + rf1 * K, &a.rcnt[rf1], sm, a.cmax + rf1 * a.nch, [] {});
+                           a.ri + rf1 * K, &a.rcnt[rf1], sm, a.cmax + rf1 * a.nch, &a.hdr->err, false, [] {});
     return;
   }
   int bid = blockIdx.x;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kPartThreads) void opt_rows_bf16_kernel(OptArgs a) 
   const size_t ci = rf * a.nch;   // the row's chunk slots hold its parts' records
   part_row_reduce(row_ptr(s, f), a.V, p, np, K, a.cval + ci * K, a.cidx + ci * K,
                   reinterpret_cast<PartStat*>(a.st + ci), &a.tickets[rf], &a.rlse[rf], a.rv + rf * K, a.ri + rf * K,
-                  &a.rcnt[rf], sm, a.cmax + ci);
+                  &a.rcnt[rf], sm, a.cmax + ci, &a.hdr->err);
 }
 
 // ------------------------------------------------------------------ 1'. the root layer in one launch

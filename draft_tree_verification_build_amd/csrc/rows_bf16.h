@@ -450,6 +450,78 @@ __device__ __forceinline__ void part_merge_wave(const PartStat* ps, const float*
   }
 }
 
+// With poll_ok (a caller whose chunk-list area holds nothing else between calls, so that the
+// slots below are zero whenever a call starts), rows of np parts with np * (K + 2) <= 64
+// (and np <= 16) merge without a ticket: every part publishes
+// its list as K 64-bit sort keys (the empty marker 1 past its length; a real key is at least
+// 2^32) and its record as two 64-bit words ((count << 32) | shift bits, and the complement
+// of the sum's bits), each store a value that no unwritten (zero) slot holds. The row's last
+// part in launch order (p = np - 1) then polls all np * (K + 2) words in one wave until none
+// is zero, merges them and zeroes them for the next call. The parts it waits for come
+// earlier in launch order, so they are resident or done while it polls.
+constexpr long kPartSpinLimit = 2000000;   // polls (each a memory round trip) before a timeout
+
+__device__ __forceinline__ unsigned long long* part_poll_slots(float* pval0) {
+  // the row's chunk-list area holds np * K 64-bit slots (np * K * 8 + 4 <= nch * K * 4 bytes
+  // for every row of two or more parts); the slots start at its first 8-byte boundary
+  const uintptr_t a = (reinterpret_cast<uintptr_t>(pval0) + 7u) & ~static_cast<uintptr_t>(7u);
+  return reinterpret_cast<unsigned long long*>(a);
+}
+
+__device__ __forceinline__ bool part_poll_merge(unsigned long long* slots, PartStat* ps, int np, int K, double* lse,
+                                                float* rv, int* ri, int* rcnt, int* err, PartSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  const int n = np * K, nw = np * (K + 2);
+  unsigned long long* src = nullptr;
+  if (lane < n) src = slots + lane;
+  else if (lane < nw) src = reinterpret_cast<unsigned long long*>(&ps[(lane - n) >> 1]) + ((lane - n) & 1);
+  unsigned long long v = 1ull;
+  long polls = 0;
+  if (src != nullptr) {
+    v = ld_cc(src);
+    while (v == 0ull && ++polls <= kPartSpinLimit) {
+      __builtin_amdgcn_s_sleep(1);
+      v = ld_cc(src);
+    }
+  }
+  if (__ballot(v == 0ull) != 0ull) {   // a part never reported
+    if (lane == 0) {
+      if (err != nullptr) atomicExch(err, kErrTimeout);
+      *rcnt = 0;
+    }
+    return false;
+  }
+  if (src != nullptr) st_cc(src, 0ull);   // ready for the next call
+  if (lane >= n && lane < nw) {
+    const int q = (lane - n) >> 1;
+    if (((lane - n) & 1) == 0) {
+      sm.pcnt[q] = static_cast<int>(v >> 32);
+      sm.pshift[q] = __uint_as_float(static_cast<uint32_t>(v));
+    } else {
+      sm.psum[q] = __longlong_as_double(static_cast<long long>(~v));
+    }
+  }
+  const unsigned long long me = (lane < n && v != 1ull) ? v : 0ull;
+  if (lane < n) sm.cand[lane] = me;
+  __builtin_amdgcn_wave_barrier();
+  const int pc = lane < np ? sm.pcnt[lane] : 0;
+  const int total = row16_reduce(pc, [](int a, int b) { return a + b; });
+  const int kk = K < total ? K : total;
+  const int r = lds_rank(sm.cand, n, me);
+  if (me != 0ull && r < kk) {
+    rv[r] = part_key_value(me);
+    ri[r] = part_key_index(me);
+  }
+  float M;
+  double S;
+  merge_partials<true>(lane < np ? sm.psum[lane] : 0.0, lane < np ? sm.pshift[lane] : 0.0f, sm.e64, M, S);
+  if (lane == 0) {
+    *lse = static_cast<double>(M) + log(S);
+    *rcnt = kk;
+  }
+  return true;
+}
+
 // The same for any np * K <= kPartMergeCap (= kPartThreads), by the whole workgroup.
 __device__ __forceinline__ void part_merge_wide(const PartStat* ps, const float* pval, const int* pidx, int np,
                                                 int K, double* lse, float* rv, int* ri, int* rcnt, PartSmem& sm) {
@@ -512,7 +584,7 @@ template <typename Next>
 __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16_t* row, int V, int p, int np, int K,
                                                        float* pval0, int* pidx0, PartStat* ps, unsigned* ticket,
                                                        double* lse, float* rv, int* ri, int* rcnt, PartSmem& sm,
-                                                       float* cmax, Next&& next) {
+                                                       float* cmax, int* err, bool poll_ok, Next&& next) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int vbase = p * kPartVecs;
   const int vfull = V / 8;
@@ -628,6 +700,8 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
   // ---- rank
   const bool whole = np == 1;
   const bool wide = !whole && (np * K > 64 || np > 16);   // the row merge needs the whole workgroup
+  const bool poll = poll_ok && !whole && np <= 16 && np * (K + 2) <= 64;   // merged without a ticket
+  unsigned long long* const pslot = poll ? part_poll_slots(pval0) + static_cast<size_t>(p) * K : nullptr;
   const int nvalid = min(max(V - p * kPartValues, 0), kPartValues);
   const int kk = K < nvalid ? K : nvalid;
   float* const ov = whole ? rv : pval0 + static_cast<size_t>(p) * K;
@@ -676,11 +750,14 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
         if (whole) {
           ov[r] = part_key_value(me);
           oi[r] = part_key_index(me);
+        } else if (poll) {
+          st_cc(&pslot[r], me);
         } else {
           st_cc(&ov[r], part_key_value(me));
           st_cc(&oi[r], part_key_index(me));
         }
       }
+      if (poll && lane >= kk && lane < K) st_cc(&pslot[lane], 1ull);   // the empty marker
     }
   } else {   // rank by counting, a candidate per thread, over every wave's slots
     const int* cnts = sm.wcnt;
@@ -695,10 +772,16 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
         for (int q2 = 0; q2 < kPartWaves; ++q2) r += lds_rank(sm.slot[q2], min(cnts[q2], kPartSlots), me);
       }
       if (r < kk) {
-        st_cc(&ov[r], part_key_value(me));
-        st_cc(&oi[r], part_key_index(me));
+        if (poll) {
+          st_cc(&pslot[r], me);
+        } else {
+          st_cc(&ov[r], part_key_value(me));
+          st_cc(&oi[r], part_key_index(me));
+        }
       }
     }
+    if (poll && static_cast<int>(threadIdx.x) >= kk && static_cast<int>(threadIdx.x) < K)
+      st_cc(&pslot[threadIdx.x], 1ull);   // the empty marker
     drain();
     __syncthreads();   // every list entry is stored
     if (w > 1 && !wide) return;
@@ -712,6 +795,10 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
       if (whole) {
         *lse = static_cast<double>(M) + log(S);
         *rcnt = kk;
+      } else if (poll) {
+        unsigned long long* rw = reinterpret_cast<unsigned long long*>(&ps[p]);
+        st_cc(&rw[0], (static_cast<unsigned long long>(kk) << 32) | __float_as_uint(M));
+        st_cc(&rw[1], ~static_cast<unsigned long long>(__double_as_longlong(S)));
       } else {
         st_cc(&ps[p].shift, M);
         st_cc(&ps[p].cnt, kk);
@@ -720,6 +807,11 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
     }
   }
   if (whole) return;
+  if (poll) {   // the row's last part merges; its own words are polled like the others'
+    if (p != np - 1 || w != 0) return;
+    part_poll_merge(part_poll_slots(pval0), ps, np, K, lse, rv, ri, rcnt, err, sm);
+    return;
+  }
   if (!wide) {   // waves 0 and 1 (the others have ended): their stores complete, then wave 0's ticket
     drain();
     __syncthreads();
@@ -738,12 +830,14 @@ __device__ __forceinline__ void part_row_reduce_loaded(PartData& d, const uint16
 
 __device__ __forceinline__ void part_row_reduce(const uint16_t* row, int V, int p, int np, int K, float* pval0,
                                                 int* pidx0, PartStat* ps, unsigned* ticket, double* lse, float* rv,
-                                                int* ri, int* rcnt, PartSmem& sm, float* cmax = nullptr) {
+                                                int* ri, int* rcnt, PartSmem& sm, float* cmax = nullptr,
+                                                int* err = nullptr, bool poll_ok = false) {
   // the tables first: the keys wait for the data loads, which are issued after them
   part_tables_issue(sm);
   PartData d;
   part_load(row, V, p * kPartVecs, ((reinterpret_cast<uintptr_t>(row) & 15u) == 0) && V / 8 > 0, d);
-  part_row_reduce_loaded(d, row, V, p, np, K, pval0, pidx0, ps, ticket, lse, rv, ri, rcnt, sm, cmax, [] {});
+  part_row_reduce_loaded(d, row, V, p, np, K, pval0, pidx0, ps, ticket, lse, rv, ri, rcnt, sm, cmax, err, poll_ok,
+                         [] {});
 }
 
 }  // namespace dtv
