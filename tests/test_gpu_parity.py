@@ -120,6 +120,11 @@ TALON_CASES = [
     # no gate and a wide second layer (40 frontier rows of 40, 1600 candidates for 60
     # slots): the radix budget selection past the small-pool path
     ("c2_talon_llama3_8b", 18, {"V": 2000, "P": 64, "B": 100, "K": 40, "alpha": 0.0}),
+    # rows of four parts whose lists and records exceed one wave's polled words (4 * (15 + 2)
+    # > 64): the part merge by ticket in one wave; and of three parts with 3 * 24 > 64 list
+    # entries: the merge by the whole workgroup
+    ("c2_talon_llama3_8b", 20, {"P": 64, "B": 40, "K": 15}),
+    ("c2_talon_llama3_8b", 21, {"V": 70001, "P": 64, "B": 40, "K": 24}),
 ]
 
 
@@ -411,6 +416,8 @@ SPINE_CASES = [
     # widths falling linearly with depth, zero at the deepest forks (the adaptive topology)
     ("c3_goose_spine", 38, {"P": 16, "V": 3000, "n_spine": 12, "n_forks": 12,
                             "spine_widths": (5, 4, 3, 2, 1, 1, 0, 0, 0, 0, 0, 0)}),
+    # bf16 fork rows longer than one 32768-value part: the chunk kernel with its merge
+    ("c3_goose_spine", 39, {"P": 16, "V": 40000, "n_spine": 6, "n_forks": 7, "fork_width": 3}),
 ]
 
 
@@ -551,6 +558,8 @@ OPT_CASES = [
     # frontier width (the last row pair holds one row)
     ("c4_opt_llama2_7b", 49, {"P": 16, "V": 4000, "n": 500, "max_layers": 3}),
     ("c4_opt_llama2_7b", 50, {"P": 16, "V": 5000, "n": 301, "max_layers": 3, "S": 3}),
+    # bf16 frontier rows of two parts: the part merge by ticket
+    ("c4_opt_llama2_7b", 51, {"P": 16, "V": 40000, "n": 64, "max_layers": 3}),
 ]
 
 
