@@ -124,6 +124,9 @@ TALON_CASES = [
     # > 64): the part merge by ticket in one wave; and of three parts with 3 * 24 > 64 list
     # entries: the merge by the whole workgroup
     ("c2_talon_llama3_8b", 20, {"P": 64, "B": 40, "K": 15}),
+    # two sequences of the full shape: 480 part workgroups, more than the device holds at
+    # once, so a row's merging part may poll while later rows' parts still wait for a slot
+    ("c2_talon_llama3_8b", 22, {"P": 64, "S": 2}),
     ("c2_talon_llama3_8b", 21, {"V": 70001, "P": 64, "B": 40, "K": 24}),
 ]
 
