@@ -240,7 +240,7 @@ struct AttnPlan {
 };
 // Query rows of a KV head: M = g * n_cap (GQA heads packed), in ceil(M/32) groups of 32;
 // a bf16 tile is 4 waves of one group each. The key range of every tile is split into
-// n_split ranges (multiples of 64 keys, at least 256) chosen by a time model: workgroups run
+// n_split ranges (multiples of 64 keys, at least 128) chosen by a time model: workgroups run
 // in rounds of the device's resident slots (two per compute unit), a round costs one
 // 64-key block per block of its ranges, and every split adds an fp32 partial (m, l, O) per
 // query row that is written and read back once; measured on MI355X, a 64-key block round
@@ -253,7 +253,7 @@ AttnPlan attn_plan(int S, int n_cap, int Hq, int Hkv, int P_max, int D) {
   const int G = (M + 31) / 32;
   p.n_mtiles = (G + dtv::kWaves - 1) / dtv::kWaves;
   p.mcap = G * 32;
-  const int min_keys = 256;
+  const int min_keys = 128;
   const long tiles = static_cast<long>(S) * Hkv * p.n_mtiles;
   const long slots = 2L * device_cus();
   const double partial_bytes = 2.0 * S * Hkv * static_cast<double>(p.mcap) * (D + 2) * 4.0;   // per split
