@@ -482,10 +482,10 @@ __global__ __launch_bounds__(kBlock) void attn_combine_rows_kernel(AttnArgs a) {
   const float inv = L > 0.f ? 1.f / L : 0.f;
   __bf16* orow = static_cast<__bf16*>(a.o) +
                  ((static_cast<size_t>(s) * a.n_cap + rr / a.g) * a.Hq + kv * a.g + rr % a.g) * D + c4 * 4;
-  orow[0] = static_cast<__bf16>(acc.x * inv);
-  orow[1] = static_cast<__bf16>(acc.y * inv);
-  orow[2] = static_cast<__bf16>(acc.z * inv);
-  orow[3] = static_cast<__bf16>(acc.w * inv);
+  const auto bits = [](float x) { return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x))); };
+  // the four outputs in one 8-byte store
+  *reinterpret_cast<uint2*>(orow) =
+      make_uint2(bits(acc.x * inv) | (bits(acc.y * inv) << 16), bits(acc.z * inv) | (bits(acc.w * inv) << 16));
 }
 
 int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
@@ -499,19 +499,31 @@ int launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.n_split > 1) {
     const int rpb = kBlock / (a.D / 4);
     const dim3 blocks(a.S * a.Hkv * ((a.mcap + rpb - 1) / rpb));
-    // one register per split of a row's partials: 8, 16 or 32 loads in flight per thread
-    const int ns = a.n_split <= 8 ? 8 : (a.n_split <= 16 ? 16 : kAttnMaxSplit);
+    // one register per split of a row's partials, all loads in flight at once; the variant
+    // with the fewest slots that hold n_split (a slot past a sequence's splits re-reads its
+    // last split, a load that still takes issue slots)
+    const int n = a.n_split;
     if (a.D == 128) {
-      if (ns == 8)
+      if (n <= 2)
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 2>), blocks, dim3(kBlock), 0, st, a);
+      else if (n <= 4)
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 4>), blocks, dim3(kBlock), 0, st, a);
+      else if (n <= 8)
         DTV_LAUNCH((attn_combine_rows_kernel<128, 8>), blocks, dim3(kBlock), 0, st, a);
-      else if (ns == 16)
+      else if (n <= 12)
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 12>), blocks, dim3(kBlock), 0, st, a);
+      else if (n <= 16)
         DTV_LAUNCH((attn_combine_rows_kernel<128, 16>), blocks, dim3(kBlock), 0, st, a);
+      else if (n <= 24)
+        DTV_LAUNCH((attn_combine_rows_kernel<128, 24>), blocks, dim3(kBlock), 0, st, a);
       else
         DTV_LAUNCH((attn_combine_rows_kernel<128, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
     } else {
-      if (ns == 8)
+      if (n <= 4)
+        DTV_LAUNCH((attn_combine_rows_kernel<64, 4>), blocks, dim3(kBlock), 0, st, a);
+      else if (n <= 8)
         DTV_LAUNCH((attn_combine_rows_kernel<64, 8>), blocks, dim3(kBlock), 0, st, a);
-      else if (ns == 16)
+      else if (n <= 16)
         DTV_LAUNCH((attn_combine_rows_kernel<64, 16>), blocks, dim3(kBlock), 0, st, a);
       else
         DTV_LAUNCH((attn_combine_rows_kernel<64, kAttnMaxSplit>), blocks, dim3(kBlock), 0, st, a);
